@@ -1,0 +1,351 @@
+"""CPU oracle of the multi-probe SPSA step (plain, slow, obviously correct).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with the
+HIP path and imports nothing from the product package.
+
+Element-wise parts (direction generator, perturbation, update, bf16 rounding)
+are plain C in ``zo_oracle.c``; the model forwards are numpy in fp64, with
+numpy's matmul as the only library primitive for a contraction.
+
+What is computed, and where the pages state it:
+
+* The loop (ZOO blog "Backprop 없이 Transformer를 학습시킨다", section
+  "backprop의 메모리 세금", flowchart): draw N random directions, perturb
+  W +- eps*z_i, evaluate only the loss, form the SPSA estimate, update
+  W <- W - eta * g_hat, repeat.
+* Two forwards per probe at +1 and -1 times the perturbation (same page,
+  section "zero-order optimization이란"), so g_i = (L+_i - L-_i) / (2 eps)
+  and g_hat = (1/N) sum_i g_i z_i.
+* Gaussian directions (gist.science 2605.15622 summary, P1), regenerated from
+  a seed rather than stored (same page P5; FedSPZO summary, section 2
+  "통신 프로토콜").
+* In-place, inference-mode training: the weights themselves are perturbed and
+  restored, nothing else is kept (ZOO blog, "zero-order optimization이란" and
+  the OPT-30B in-place paragraph of the 1.5-SPSA section).
+
+Readings where the pages are silent are listed in the repository's design
+notes; the ones that fix arithmetic are repeated at each function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the C part of the oracle (single-threaded, no fp contraction)."""
+    src = os.path.join(_HERE, "zo_oracle.c")
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall",
+                           "-o", tmp, src, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P, U64, U32, F = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_float
+        L.oracle_philox4x32_10.argtypes = [P, P, P]
+        L.oracle_rng_words.argtypes = [U64, U32, U64, U64, P]
+        L.oracle_box_muller_f64.argtypes = [U32, U32, ctypes.POINTER(ctypes.c_double)]
+        L.oracle_box_muller_f64.restype = ctypes.c_double
+        L.oracle_gauss.argtypes = [U64, U32, U64, U64, P]
+        L.oracle_gauss_at.argtypes = [U64, U32, P, U64, P]
+        L.oracle_bf16_from_f32.argtypes = [F]
+        L.oracle_bf16_from_f32.restype = ctypes.c_uint16
+        L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
+        L.oracle_bf16_from_f64.restype = ctypes.c_uint16
+        for name in ("oracle_perturb_f32", "oracle_perturb_bf16"):
+            getattr(L, name).argtypes = [P, U64, U64, U64, U32, F]
+        for name in ("oracle_perturb_f32_at", "oracle_perturb_bf16_at"):
+            getattr(L, name).argtypes = [P, P, U64, U64, U32, F]
+        for name in ("oracle_update_f32", "oracle_update_bf16"):
+            getattr(L, name).argtypes = [P, U64, U64, U64, U32, P]
+        for name in ("oracle_update_f32_at", "oracle_update_bf16_at"):
+            getattr(L, name).argtypes = [P, P, U64, U64, U32, P]
+        L.oracle_bf16_compare_range.argtypes = [U32, U32, P]
+        L.oracle_bf16_compare_range.restype = U64
+        L.oracle_round_bf16_array.argtypes = [P, U64]
+        L.oracle_round_f32_array.argtypes = [P, U64]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ====================================================================== RNG
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def rng_words(seed: int, probe: int, j0: int, n: int) -> np.ndarray:
+    out = np.zeros(n, np.uint32)
+    lib().oracle_rng_words(seed, probe, j0, n, _ptr(out))
+    return out
+
+
+def box_muller_f64(x_even: int, x_odd: int):
+    zo = ctypes.c_double()
+    ze = lib().oracle_box_muller_f64(x_even, x_odd, ctypes.byref(zo))
+    return ze, zo.value
+
+
+def gauss(seed: int, probe: int, j0: int, n: int) -> np.ndarray:
+    """Direction z_probe at elements j0..j0+n-1 (fp32, rounded once from fp64)."""
+    z = np.zeros(n, np.float32)
+    lib().oracle_gauss(seed, probe, j0, n, _ptr(z))
+    return z
+
+
+def gauss_at(seed: int, probe: int, idx: np.ndarray) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.uint64)
+    z = np.zeros(idx.size, np.float32)
+    lib().oracle_gauss_at(seed, probe, _ptr(idx), idx.size, _ptr(z))
+    return z
+
+
+# ================================================================ bfloat16
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (ties to even) of each fp64 entry, kept as fp64."""
+    y = np.array(x, dtype=np.float64, order="C", copy=True)
+    lib().oracle_round_bf16_array(_ptr(y), y.size)
+    return y
+
+
+def f32_round(x: np.ndarray) -> np.ndarray:
+    y = np.array(x, dtype=np.float64, order="C", copy=True)
+    lib().oracle_round_f32_array(_ptr(y), y.size)
+    return y
+
+
+def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ====================================================== parameter arena layout
+# Every parameter of a model lives in one flat arena; tensors are placed in
+# declaration order, each starting at a multiple of 64 elements.  Element j of
+# the arena uses direction element j (the layout is an interface both sides
+# state independently; a test checks they agree).
+ALIGN = 64
+
+
+def _align(x: int) -> int:
+    return (x + ALIGN - 1) // ALIGN * ALIGN
+
+
+def param_shapes(desc: dict) -> list:
+    kind = desc["kind"]
+    if kind == "lsq":
+        return [("W", (desc["d_in"], desc["d_out"]))]
+    if kind == "mlp":
+        return [("W1", (desc["hidden"], desc["d_in"])), ("W2", (desc["classes"], desc["hidden"]))]
+    if kind == "decoder":
+        d, f, v, s = desc["d"], desc["ffn"], desc["vocab"], desc["max_seq"]
+        out = [("tok_emb", (v, d)), ("pos_emb", (s, d))]
+        for layer in range(desc["layers"]):
+            p = f"l{layer}."
+            out += [(p + "ln1_g", (d,)), (p + "ln1_b", (d,)), (p + "w_qkv", (3 * d, d)),
+                    (p + "w_o", (d, d)), (p + "ln2_g", (d,)), (p + "ln2_b", (d,)),
+                    (p + "w_up", (f, d)), (p + "w_down", (d, f))]
+        out += [("lnf_g", (d,)), ("lnf_b", (d,))]
+        return out
+    raise ValueError(kind)
+
+
+def param_layout(desc: dict):
+    """[(name, offset, shape)], total arena elements."""
+    off = 0
+    out = []
+    for name, shape in param_shapes(desc):
+        off = _align(off)
+        out.append((name, off, shape))
+        off += int(np.prod(shape))
+    return out, _align(off)
+
+
+def unpack(desc: dict, arena_f64: np.ndarray) -> dict:
+    layout, _ = param_layout(desc)
+    return {name: arena_f64[off:off + int(np.prod(shape))].reshape(shape)
+            for name, off, shape in layout}
+
+
+# ================================================================== models
+def gelu_erf(x: np.ndarray) -> np.ndarray:
+    from scipy.special import erf
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def logsumexp_rows(a: np.ndarray) -> np.ndarray:
+    m = a.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(a - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def lsq_loss(W: np.ndarray, X: np.ndarray, Y: np.ndarray) -> float:
+    """L = ||X W - Y||_F^2 / (2n): the normalisation whose gradient is
+    X^T (X W - Y) / n."""
+    W, X, Y = (np.asarray(a, np.float64) for a in (W, X, Y))
+    r = X @ W - Y
+    return float((r * r).sum() / (2.0 * X.shape[0]))
+
+
+def lsq_grad(W, X, Y) -> np.ndarray:
+    W, X, Y = (np.asarray(a, np.float64) for a in (W, X, Y))
+    return X.T @ (X @ W - Y) / X.shape[0]
+
+
+def mlp_loss(W1, W2, X, labels) -> float:
+    """Mean cross-entropy of logits = GELU(X W1^T) W2^T (no biases)."""
+    W1, W2, X = (np.asarray(a, np.float64) for a in (W1, W2, X))
+    h = gelu_erf(X @ W1.T)
+    logits = h @ W2.T
+    lse = logsumexp_rows(logits)
+    return float(np.mean(lse - logits[np.arange(X.shape[0]), labels]))
+
+
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def decoder_loss(desc: dict, params: dict, tokens: np.ndarray, round_bf16: bool = True) -> float:
+    """Causal-LM mean cross-entropy of a pre-LN decoder.
+
+    Embedding + learned positions; per block h += W_o Attn(LN1 h),
+    h += W_down act(W_up LN2 h); final LN; LM head tied to the token embedding.
+    No linear biases, LN eps 1e-5, attention scale 1/sqrt(d_h), causal mask.
+    Loss = mean over the B*(S-1) next-token positions.
+
+    bf16 rounding points (when ``round_bf16``): embedding sum, every LN output,
+    every GEMM output (QKV, attention output, O, up after the activation, down),
+    both residual sums.  Everything else (softmax, LN statistics, logits, CE)
+    is exact fp64.
+    """
+    R = bf16_round if round_bf16 else (lambda a: a)
+    act = gelu_erf if desc["act"] == "gelu" else (lambda a: np.maximum(a, 0.0))
+    B, S = tokens.shape
+    d, H = desc["d"], desc["heads"]
+    dh = d // H
+    p = params
+    h = R(p["tok_emb"][tokens] + p["pos_emb"][:S][None, :, :])           # [B,S,d]
+    mask = np.triu(np.ones((S, S), dtype=bool), k=1)
+    for layer in range(desc["layers"]):
+        q = f"l{layer}."
+        x = R(layer_norm(h, p[q + "ln1_g"], p[q + "ln1_b"]))
+        qkv = R(x @ p[q + "w_qkv"].T)                                      # [B,S,3d]
+        Q = qkv[..., :d].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
+        K = qkv[..., d:2 * d].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
+        V = qkv[..., 2 * d:].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
+        s = (Q @ K.transpose(0, 1, 3, 2)) / np.sqrt(dh)                   # [B,H,S,S]
+        s[..., mask] = -np.inf
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.exp(s)
+        P = e / e.sum(axis=-1, keepdims=True)
+        o = R((P @ V).transpose(0, 2, 1, 3).reshape(B, S, d))
+        h = R(h + R(o @ p[q + "w_o"].T))
+        x = R(layer_norm(h, p[q + "ln2_g"], p[q + "ln2_b"]))
+        u = R(act(x @ p[q + "w_up"].T))
+        h = R(h + R(u @ p[q + "w_down"].T))
+    x = R(layer_norm(h, p["lnf_g"], p["lnf_b"]))
+    logits = x[:, :-1, :] @ p["tok_emb"].T                                 # [B,S-1,V]
+    tgt = tokens[:, 1:]
+    lse = logsumexp_rows(logits)
+    picked = np.take_along_axis(logits, tgt[..., None], axis=-1)[..., 0]
+    return float(np.mean(lse - picked))
+
+
+# ============================================================ arena helpers
+class Arena:
+    """A model's flat parameter vector in its storage dtype ('f32' or 'bf16')."""
+
+    def __init__(self, desc: dict, data: np.ndarray):
+        self.desc = desc
+        self.dtype = "bf16" if data.dtype == np.uint16 else "f32"
+        assert data.dtype in (np.uint16, np.float32)
+        self.data = np.ascontiguousarray(data)
+
+    def copy(self) -> "Arena":
+        return Arena(self.desc, self.data.copy())
+
+    def values(self) -> np.ndarray:
+        if self.dtype == "bf16":
+            return bf16_bits_to_f64(self.data)
+        return self.data.astype(np.float64)
+
+    def perturb(self, seed: int, probe: int, sigma: float) -> None:
+        """w <- round_storage(w + sigma * z_probe), every element of the arena."""
+        fn = lib().oracle_perturb_bf16 if self.dtype == "bf16" else lib().oracle_perturb_f32
+        fn(_ptr(self.data), self.data.size, 0, seed, probe, float(np.float32(sigma)))
+
+    def update(self, seed: int, coeffs: np.ndarray) -> None:
+        """w <- round_storage(w + sum_i c_i z_i), every element of the arena."""
+        c = np.ascontiguousarray(coeffs, dtype=np.float64)
+        fn = lib().oracle_update_bf16 if self.dtype == "bf16" else lib().oracle_update_f32
+        fn(_ptr(self.data), self.data.size, 0, seed, c.size, _ptr(c))
+
+
+def model_loss(arena: Arena, batch: dict, round_bf16: bool = True) -> float:
+    desc = arena.desc
+    prm = unpack(desc, arena.values())
+    if desc["kind"] == "lsq":
+        return lsq_loss(prm["W"], batch["X"], batch["Y"])
+    if desc["kind"] == "mlp":
+        return mlp_loss(prm["W1"], prm["W2"], batch["X"], batch["labels"])
+    return decoder_loss(desc, prm, batch["tokens"], round_bf16=round_bf16)
+
+
+# ==================================================================== step
+def spsa_step(arena: Arena, batch: dict, seed: int, n_probes: int, eps: float, lr: float,
+              mode: str = "inplace", round_bf16: bool = True):
+    """One multi-probe SPSA step; updates ``arena`` in place.
+
+    inplace: for each probe i, W += eps z_i; L+ ; W -= 2 eps z_i; L- ;
+             W += eps z_i (restore), all on the stored weights.
+    fused:   each evaluation sees round_storage(W_t +- eps z_i) of the same W_t.
+    Then g_i = (L+_i - L-_i) / (2 eps) with eps taken at fp32 precision,
+    c_i = -lr * g_i / N, and W <- round_storage(W + sum_i c_i z_i).
+    Returns (losses [2N] as L+_0, L-_0, L+_1, ..., g [N]).
+    """
+    sig = float(np.float32(eps))
+    losses = np.zeros(2 * n_probes)
+    for i in range(n_probes):
+        if mode == "inplace":
+            arena.perturb(seed, i, sig)
+            losses[2 * i] = model_loss(arena, batch, round_bf16)
+            arena.perturb(seed, i, -2.0 * sig)
+            losses[2 * i + 1] = model_loss(arena, batch, round_bf16)
+            arena.perturb(seed, i, sig)
+        elif mode == "fused":
+            a = arena.copy()
+            a.perturb(seed, i, sig)
+            losses[2 * i] = model_loss(a, batch, round_bf16)
+            a = arena.copy()
+            a.perturb(seed, i, -sig)
+            losses[2 * i + 1] = model_loss(a, batch, round_bf16)
+        else:
+            raise ValueError(mode)
+    g = (losses[0::2] - losses[1::2]) / (2.0 * sig)
+    c = -lr * g / n_probes
+    if np.all(np.isfinite(losses)):
+        arena.update(seed, c)
+    return losses, g
