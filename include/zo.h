@@ -1,0 +1,232 @@
+/*
+ * zo.h -- C ABI of the multi-probe SPSA (zeroth-order) training step on one
+ * AMD MI355X (gfx950).
+ *
+ * The step, as the pages state it (ZOO blog "Backprop 없이 Transformer를
+ * 학습시킨다", section "backprop의 메모리 세금", loop flowchart, and section
+ * "zero-order optimization이란"):
+ *   for each of N random directions z_i: evaluate the loss at W + eps z_i and
+ *   at W - eps z_i (forward only, no backprop); g_i = (L+_i - L-_i) / (2 eps);
+ *   W <- W - eta * g_hat with g_hat = (1/N) sum_i g_i z_i; repeat.
+ * Directions are Gaussian and rebuilt from a seed, never stored
+ * ("0 차 최적화는 미탐구된 것이지, 저전력이 아니다", P1 and P5; FedSPZO
+ * summary, section 2, "통신 프로토콜").  Training is in place, inference-mode:
+ * the weights are the only model state (ZOO blog, 1.5-SPSA section).
+ *
+ * Direction stream: element j of direction i under step seed s is word j % 4
+ * of Philox4x32-10(counter = (q lo, q hi, i, 0), key = (s lo, s hi)),
+ * q = j / 4, mapped to a Gaussian by Box-Muller on word pairs (0,1) and (2,3):
+ * u_r = ((x_even >> 8) + 1) 2^-24, u_t = (x_odd >> 8) 2^-24,
+ * z_even = sqrt(-2 ln u_r) cos(2 pi u_t), z_odd = sqrt(-2 ln u_r) sin(2 pi u_t).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device memory the caller allocated and owns
+ *    (e.g. from PyTorch); the library only borrows them for the call and never
+ *    frees them.  "host" pointers are read before the call returns.
+ *  - Work is enqueued on the caller's stream `s` (a hipStream_t; NULL is the
+ *    default stream) and is asynchronous: results are valid after the caller
+ *    synchronises that stream.  The library allocates no device memory.
+ *  - Arguments are validated before anything is launched: an error return
+ *    means nothing was enqueued (except ZO_ERR_HIP, which reports a failed
+ *    launch).  No C++ exception crosses this boundary.  zo_last_error() gives
+ *    a message for the last failure on the calling thread.
+ *  - Storage rounding D: identity for fp32 weights, round to nearest even for
+ *    bf16 weights.
+ */
+#ifndef ZO_H
+#define ZO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* zo_stream; /* a hipStream_t */
+
+typedef enum {
+    ZO_OK = 0,
+    ZO_ERR_INVALID = -1,     /* bad argument: null, size, alignment, overlap */
+    ZO_ERR_UNSUPPORTED = -2, /* dtype or shape this build does not handle */
+    ZO_ERR_HIP = -3,         /* a HIP launch or runtime call failed */
+    ZO_ERR_NONFINITE = -4,   /* a loss was NaN or infinite */
+    ZO_ERR_WORKSPACE = -5    /* workspace smaller than zo_workspace_bytes() */
+} zo_status;
+
+typedef enum { ZO_F32 = 0, ZO_BF16 = 1 } zo_dtype;
+
+typedef enum { ZO_MODEL_LSQ = 0, ZO_MODEL_MLP = 1, ZO_MODEL_DECODER = 2 } zo_model_kind;
+
+typedef enum { ZO_ACT_GELU = 0, ZO_ACT_RELU = 1 } zo_act;
+
+typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1 } zo_mode;
+
+/*
+ * Model description.  Fields a kind does not use must be 0.
+ *  LSQ:     loss = ||X W - Y||_F^2 / (2 batch); W [d_in][d_out] fp32.
+ *  MLP:     loss = mean_b CE(GELU(X W1^T) W2^T, label_b); W1 [hidden][d_in],
+ *           W2 [classes][hidden] fp32; no biases.
+ *  DECODER: pre-LN decoder, bf16 weights: token embedding [vocab][d_model],
+ *           learned positions [max_seq][d_model], per layer ln1 gain/bias [d],
+ *           W_qkv [3d][d], W_o [d][d], ln2 gain/bias [d], W_up [ffn][d],
+ *           W_down [d][ffn]; final LN gain/bias; LM head tied to the token
+ *           embedding; no linear biases; act GELU (erf) or ReLU; loss = mean
+ *           next-token CE over batch*(seq-1) positions.
+ * `batch` (and `seq` for the decoder) is the largest batch forward_loss/step
+ * will be given; it sizes the workspace.
+ */
+typedef struct {
+    int32_t kind;  /* zo_model_kind */
+    int32_t dtype; /* zo_dtype: F32 for LSQ/MLP, BF16 for DECODER */
+    int64_t batch;
+    int64_t seq;
+    int64_t d_in, d_out;             /* LSQ, MLP (d_in) */
+    int64_t hidden, classes;         /* MLP */
+    int64_t layers, d_model, heads, ffn, vocab, max_seq; /* DECODER */
+    int32_t act;                     /* zo_act, DECODER */
+    int32_t reserved;
+} zo_model_desc;
+
+/* One parameter tensor inside the flat parameter arena. */
+typedef struct {
+    char name[32];
+    uint64_t offset; /* element offset in the arena = its direction index */
+    int64_t shape[2];
+    int32_t ndim;
+    int32_t reserved;
+} zo_param_info;
+
+/*
+ * Batch.  Device pointers, row-major.
+ *  LSQ: x fp32 [batch][d_in], y fp32 [batch][d_out].
+ *  MLP: x fp32 [batch][d_in], labels int32 [batch] in [0, classes).
+ *  DECODER: tokens int32 [batch][seq] in [0, vocab), seq <= max_seq.
+ * `batch` and `seq` may be smaller than the model's maximum.
+ */
+typedef struct {
+    const void* x;
+    const void* y;
+    const int32_t* labels;
+    const int32_t* tokens;
+    int64_t batch;
+    int64_t seq;
+} zo_batch;
+
+/* A perturbation applied on the fly: weights seen = D(W + sigma * z_probe). */
+typedef struct {
+    uint64_t seed;
+    uint32_t probe;
+    float sigma;
+} zo_pert;
+
+typedef struct {
+    uint64_t seed;     /* this step's direction seed */
+    uint32_t n_probes; /* N >= 1 */
+    float eps;         /* perturbation scale */
+    float lr;          /* eta */
+    int32_t mode;      /* zo_mode */
+} zo_step_cfg;
+
+typedef struct zo_model zo_model;
+
+/* ---------------------------------------------------------------- layout */
+
+/*
+ * Parameter arena layout of a model: tensors in the order listed above, each
+ * starting at a multiple of 64 elements; *total = arena length (a multiple of
+ * 64).  Writes at most `cap` entries to `out` (host) and the count to *n_out.
+ * Every arena element, padding included, is perturbed and updated; arena
+ * element j uses direction element j.
+ */
+zo_status zo_param_layout(const zo_model_desc* desc, zo_param_info* out, int32_t cap, int32_t* n_out,
+                          uint64_t* total);
+
+/* Device workspace the model needs for its largest batch (bytes). */
+zo_status zo_workspace_bytes(const zo_model_desc* desc, size_t* bytes);
+
+/*
+ * Creates a model over caller-owned device memory: `params` is the arena
+ * (n_params elements of desc->dtype, 256-byte aligned, exactly the layout's
+ * total), `workspace` at least zo_workspace_bytes() bytes (256-byte aligned).
+ * Neither may overlap the other.  *out is a host object holding only
+ * descriptors; release it with zo_model_destroy.
+ */
+zo_status zo_model_create(const zo_model_desc* desc, void* params, uint64_t n_params, void* workspace,
+                          size_t ws_bytes, zo_model** out);
+zo_status zo_model_destroy(zo_model* m);
+
+/* ------------------------------------------------------------- the step */
+
+/*
+ * In-place perturbation of every parameter: w <- D(fma(sigma, z_probe, w)).
+ * The +eps / -2 eps / +eps sequence restores W to within rounding.
+ */
+zo_status zo_perturb(zo_model* m, uint64_t seed, uint32_t probe, float sigma, zo_stream s);
+
+/*
+ * Forward-only loss evaluations (no activations kept beyond the call).
+ * perts == NULL or n_perts == 0: one loss at the stored weights -> loss_dev[0].
+ * Otherwise loss_dev[k] = loss at D(W + perts[k].sigma z_{perts[k].probe});
+ * the weights in memory are not modified (the perturbation is applied inside
+ * the kernels, tile by tile).  loss_dev: device, fp64, >= max(1, n_perts).
+ * perts: host array.
+ */
+zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, int32_t n_perts,
+                          double* loss_dev, zo_stream s);
+
+/*
+ * Fused update: c_i = fp32(-lr * g_i / N) from g_dev[0..N) (device, fp64),
+ * then w <- D(w + sum_{i<N} c_i z_i) for every parameter, every z_i
+ * regenerated from `seed`.  When any g_i is not finite nothing is written.
+ */
+zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double* g_dev, float lr,
+                    zo_stream s);
+
+/*
+ * One SPSA step.  mode INPLACE: for i < N: perturb(+eps), L+, perturb(-2 eps),
+ * L-, perturb(+eps).  mode FUSED: every evaluation sees D(W +- eps z_i) of the
+ * unmodified W (one launch covers all 2N evaluations where the model allows).
+ * Then g_i = (L+_i - L-_i) / (2 eps) and zo_update.
+ * losses_dev: device fp64 [2N] as (L+_0, L-_0, L+_1, ...); g_dev: device fp64
+ * [N].  A non-finite loss leaves W unchanged by the update (in place: after
+ * the restore passes); the caller sees it in losses_dev / g_dev.
+ */
+zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev,
+                  double* g_dev, zo_stream s);
+
+/* ------------------------------------------------- model-free buffer path */
+
+/*
+ * The perturb and update passes on a raw buffer w (device, n elements of
+ * `dtype`, 16-byte aligned) whose element 0 is direction element j0
+ * (j0 % 4 == 0).  Same arithmetic as zo_perturb / zo_update.
+ */
+zo_status zo_perturb_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
+                            float sigma, zo_stream s);
+zo_status zo_update_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
+                           const double* g_dev, float lr, zo_stream s);
+
+/* g_dev[i] = (losses_dev[2i] - losses_dev[2i+1]) / (2 (double)eps), i < n. */
+zo_status zo_gscalar(const double* losses_dev, uint32_t n, float eps, double* g_dev, zo_stream s);
+
+/* ---------------------------------------------------------------- debug */
+
+/*
+ * Direction elements j0 .. j0+n-1 of `probe` under `seed`: raw Philox words
+ * (words_dev, uint32) and/or Gaussians (z_dev, fp32); either may be NULL.
+ */
+zo_status zo_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words_dev,
+                       float* z_dev, zo_stream s);
+
+/* Box-Muller map alone: pairs_dev [n][2] words -> z_dev [n][2] (z_even, z_odd). */
+zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float* z_dev, zo_stream s);
+
+const char* zo_status_str(zo_status st);
+const char* zo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZO_H */

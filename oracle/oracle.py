@@ -79,6 +79,7 @@ def lib():
         L.oracle_bf16_compare_range.restype = U64
         L.oracle_round_bf16_array.argtypes = [P, U64]
         L.oracle_round_f32_array.argtypes = [P, U64]
+        L.oracle_box_muller_f64_array.argtypes = [P, U64, P]
         _lib = L
     return _lib
 
@@ -107,6 +108,14 @@ def box_muller_f64(x_even: int, x_odd: int):
     zo = ctypes.c_double()
     ze = lib().oracle_box_muller_f64(x_even, x_odd, ctypes.byref(zo))
     return ze, zo.value
+
+
+def box_muller_f64_array(pairs: np.ndarray) -> np.ndarray:
+    """pairs uint32 [n][2] -> fp64 [n][2] (z_even, z_odd)."""
+    p = np.ascontiguousarray(pairs, dtype=np.uint32)
+    out = np.zeros(p.shape, np.float64)
+    lib().oracle_box_muller_f64_array(_ptr(p), p.shape[0], _ptr(out))
+    return out
 
 
 def gauss(seed: int, probe: int, j0: int, n: int) -> np.ndarray:

@@ -289,3 +289,13 @@ void oracle_round_f32_array(double* x, uint64_t n)
     for (uint64_t t = 0; t < n; ++t)
         x[t] = (double)(float)x[t];
 }
+
+/* Box-Muller over an array of word pairs: out[2t], out[2t+1] in fp64. */
+void oracle_box_muller_f64_array(const uint32_t* pairs, uint64_t n_pairs, double* out)
+{
+    for (uint64_t t = 0; t < n_pairs; ++t) {
+        double zo;
+        out[2 * t] = oracle_box_muller_f64(pairs[2 * t], pairs[2 * t + 1], &zo);
+        out[2 * t + 1] = zo;
+    }
+}

@@ -1,0 +1,365 @@
+// C ABI of the SPSA step: argument validation, the parameter arena layout,
+// model dispatch and step sequencing.  Every check runs before the first
+// launch, so a rejected call enqueues nothing.
+//
+// Step sequencing follows the ZOO blog ("Backprop 없이 Transformer를
+// 학습시킨다"): two forwards per probe at +1 and -1 times the perturbation
+// (section "zero-order optimization이란") inside the loop of the flowchart in
+// section "backprop의 메모리 세금" (perturb, loss only, estimate, update).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zo_internal.hpp"
+#include "zo_models.hpp"
+
+namespace zo {
+
+static thread_local char g_err[512] = "";
+
+zo_status fail(zo_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+zo_status check_launch(const char* what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ZO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ZO_OK;
+}
+
+static uint64_t align64(uint64_t x) { return (x + 63) / 64 * 64; }
+
+// Tensors of a model in declaration order (the arena layout).
+static zo_status build_layout(const zo_model_desc* d, std::vector<zo_param_info>& out, uint64_t& total)
+{
+    out.clear();
+    auto add = [&](const std::string& name, int64_t r, int64_t c) {
+        zo_param_info p;
+        memset(&p, 0, sizeof p);
+        snprintf(p.name, sizeof p.name, "%s", name.c_str());
+        p.shape[0] = r;
+        p.shape[1] = c;
+        p.ndim = c > 0 ? 2 : 1;
+        out.push_back(p);
+    };
+    switch (d->kind) {
+        case ZO_MODEL_LSQ:
+            add("W", d->d_in, d->d_out);
+            break;
+        case ZO_MODEL_MLP:
+            add("W1", d->hidden, d->d_in);
+            add("W2", d->classes, d->hidden);
+            break;
+        case ZO_MODEL_DECODER: {
+            const int64_t D = d->d_model;
+            add("tok_emb", d->vocab, D);
+            add("pos_emb", d->max_seq, D);
+            for (int64_t l = 0; l < d->layers; ++l) {
+                const std::string p = "l" + std::to_string(l) + ".";
+                add(p + "ln1_g", D, 0);
+                add(p + "ln1_b", D, 0);
+                add(p + "w_qkv", 3 * D, D);
+                add(p + "w_o", D, D);
+                add(p + "ln2_g", D, 0);
+                add(p + "ln2_b", D, 0);
+                add(p + "w_up", d->ffn, D);
+                add(p + "w_down", D, d->ffn);
+            }
+            add("lnf_g", D, 0);
+            add("lnf_b", D, 0);
+            break;
+        }
+        default:
+            return fail(ZO_ERR_INVALID, "unknown model kind %d", d->kind);
+    }
+    uint64_t off = 0;
+    for (auto& p : out) {
+        off = align64(off);
+        p.offset = off;
+        off += (uint64_t)p.shape[0] * (uint64_t)(p.ndim == 2 ? p.shape[1] : 1);
+    }
+    total = align64(off);
+    return ZO_OK;
+}
+
+static zo_status validate_desc(const zo_model_desc* d)
+{
+    if (!d) return fail(ZO_ERR_INVALID, "null model description");
+    if (d->batch <= 0) return fail(ZO_ERR_INVALID, "batch must be positive");
+    switch (d->kind) {
+        case ZO_MODEL_LSQ:
+            if (d->dtype != ZO_F32) return fail(ZO_ERR_UNSUPPORTED, "least squares is fp32 only");
+            if (d->d_in <= 0 || d->d_out <= 0) return fail(ZO_ERR_INVALID, "d_in, d_out must be positive");
+            break;
+        case ZO_MODEL_MLP:
+            if (d->dtype != ZO_F32) return fail(ZO_ERR_UNSUPPORTED, "MLP is fp32 only");
+            if (d->d_in <= 0 || d->hidden <= 0 || d->classes <= 0)
+                return fail(ZO_ERR_INVALID, "d_in, hidden, classes must be positive");
+            break;
+        case ZO_MODEL_DECODER:
+            if (d->dtype != ZO_BF16) return fail(ZO_ERR_UNSUPPORTED, "decoder is bf16 only");
+            if (d->layers <= 0 || d->d_model <= 0 || d->heads <= 0 || d->ffn <= 0 || d->vocab <= 0 ||
+                d->max_seq <= 0 || d->seq <= 0 || d->seq > d->max_seq)
+                return fail(ZO_ERR_INVALID, "decoder sizes must be positive and seq <= max_seq");
+            if (d->d_model % d->heads) return fail(ZO_ERR_INVALID, "d_model must divide into heads");
+            if (d->act != ZO_ACT_GELU && d->act != ZO_ACT_RELU) return fail(ZO_ERR_INVALID, "bad activation");
+            break;
+        default:
+            return fail(ZO_ERR_INVALID, "unknown model kind %d", d->kind);
+    }
+    return model_check_shape(*d);
+}
+
+static size_t dtype_size(int dtype) { return dtype == ZO_F32 ? 4 : 2; }
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const char* pa = (const char*)a;
+    const char* pb = (const char*)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace zo
+
+using namespace zo;
+
+struct zo_model {
+    zo_model_desc desc;
+    void* params;
+    uint64_t n_params;
+    void* workspace;
+    size_t ws_bytes;
+    std::vector<zo_param_info> layout;
+};
+
+extern "C" {
+
+const char* zo_status_str(zo_status st)
+{
+    switch (st) {
+        case ZO_OK: return "ok";
+        case ZO_ERR_INVALID: return "invalid argument";
+        case ZO_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+        case ZO_ERR_HIP: return "HIP error";
+        case ZO_ERR_NONFINITE: return "non-finite loss";
+        case ZO_ERR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+const char* zo_last_error(void) { return g_err; }
+
+zo_status zo_param_layout(const zo_model_desc* desc, zo_param_info* out, int32_t cap, int32_t* n_out,
+                          uint64_t* total)
+{
+    if (zo_status st = validate_desc(desc)) return st;
+    if (!n_out || !total || (cap > 0 && !out)) return fail(ZO_ERR_INVALID, "null output pointer");
+    std::vector<zo_param_info> v;
+    uint64_t t = 0;
+    if (zo_status st = build_layout(desc, v, t)) return st;
+    for (int32_t k = 0; k < cap && k < (int32_t)v.size(); ++k) out[k] = v[k];
+    *n_out = (int32_t)v.size();
+    *total = t;
+    return ZO_OK;
+}
+
+zo_status zo_workspace_bytes(const zo_model_desc* desc, size_t* bytes)
+{
+    if (zo_status st = validate_desc(desc)) return st;
+    if (!bytes) return fail(ZO_ERR_INVALID, "null output pointer");
+    *bytes = model_workspace_bytes(*desc);
+    return ZO_OK;
+}
+
+zo_status zo_model_create(const zo_model_desc* desc, void* params, uint64_t n_params, void* workspace,
+                          size_t ws_bytes, zo_model** out)
+{
+    if (zo_status st = validate_desc(desc)) return st;
+    if (!out || !params) return fail(ZO_ERR_INVALID, "null params or output");
+    std::vector<zo_param_info> v;
+    uint64_t total = 0;
+    if (zo_status st = build_layout(desc, v, total)) return st;
+    if (n_params != total)
+        return fail(ZO_ERR_INVALID, "arena has %llu elements, layout needs %llu", (unsigned long long)n_params,
+                    (unsigned long long)total);
+    if ((uintptr_t)params % 256 || (uintptr_t)workspace % 256)
+        return fail(ZO_ERR_INVALID, "params and workspace must be 256-byte aligned");
+    const size_t need = model_workspace_bytes(*desc);
+    if (ws_bytes < need || (need && !workspace))
+        return fail(ZO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    if (workspace && overlap(params, n_params * dtype_size(desc->dtype), workspace, ws_bytes))
+        return fail(ZO_ERR_INVALID, "params and workspace overlap");
+    zo_model* m = new (std::nothrow) zo_model;
+    if (!m) return fail(ZO_ERR_INVALID, "out of host memory");
+    m->desc = *desc;
+    m->params = params;
+    m->n_params = n_params;
+    m->workspace = workspace;
+    m->ws_bytes = ws_bytes;
+    m->layout = v;
+    *out = m;
+    return ZO_OK;
+}
+
+zo_status zo_model_destroy(zo_model* m)
+{
+    delete m;
+    return ZO_OK;
+}
+
+static ModelView view_of(const zo_model* m)
+{
+    ModelView v;
+    v.desc = m->desc;
+    v.params = m->params;
+    v.workspace = m->workspace;
+    v.ws_bytes = m->ws_bytes;
+    v.offsets.reserve(m->layout.size());
+    for (const auto& p : m->layout) v.offsets.push_back(p.offset);
+    return v;
+}
+
+zo_status zo_perturb(zo_model* m, uint64_t seed, uint32_t probe, float sigma, zo_stream s)
+{
+    if (!m) return fail(ZO_ERR_INVALID, "null model");
+    return launch_perturb(m->params, m->desc.dtype, m->n_params, 0, seed, probe, sigma, (hipStream_t)s);
+}
+
+static zo_status validate_batch(const zo_model* m, const zo_batch* b)
+{
+    if (!b) return fail(ZO_ERR_INVALID, "null batch");
+    const zo_model_desc& d = m->desc;
+    if (b->batch <= 0 || b->batch > d.batch) return fail(ZO_ERR_INVALID, "batch size out of range");
+    switch (d.kind) {
+        case ZO_MODEL_LSQ:
+            if (!b->x || !b->y) return fail(ZO_ERR_INVALID, "least squares needs x and y");
+            break;
+        case ZO_MODEL_MLP:
+            if (!b->x || !b->labels) return fail(ZO_ERR_INVALID, "MLP needs x and labels");
+            break;
+        case ZO_MODEL_DECODER:
+            if (!b->tokens) return fail(ZO_ERR_INVALID, "decoder needs tokens");
+            if (b->seq < 2 || b->seq > d.seq) return fail(ZO_ERR_INVALID, "seq must be in 2..desc.seq");
+            break;
+    }
+    return model_check_batch(d, *b);
+}
+
+zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, int32_t n_perts,
+                          double* loss_dev, zo_stream s)
+{
+    if (!m || !loss_dev) return fail(ZO_ERR_INVALID, "null model or loss buffer");
+    if (zo_status st = validate_batch(m, b)) return st;
+    if (n_perts < 0 || (n_perts > 0 && !perts)) return fail(ZO_ERR_INVALID, "bad perturbation list");
+    if (n_perts > kMaxEvalsPerCall) return fail(ZO_ERR_INVALID, "at most %d perturbations per call", kMaxEvalsPerCall);
+    return model_forward(view_of(m), *b, n_perts ? perts : nullptr, n_perts, loss_dev, (hipStream_t)s);
+}
+
+zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double* g_dev, float lr, zo_stream s)
+{
+    if (!m || !g_dev) return fail(ZO_ERR_INVALID, "null model or g");
+    if (n_probes == 0) return fail(ZO_ERR_INVALID, "n_probes must be >= 1");
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, seed, n_probes, g_dev, lr, (hipStream_t)s);
+}
+
+zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev, double* g_dev,
+                  zo_stream s)
+{
+    if (!m || !cfg || !losses_dev || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (zo_status st = validate_batch(m, b)) return st;
+    const uint32_t N = cfg->n_probes;
+    if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
+    if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
+    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
+    hipStream_t st = (hipStream_t)s;
+    const ModelView v = view_of(m);
+    const float sig = cfg->eps;
+    const float sig2 = -2.0f * cfg->eps;
+    if (cfg->mode == ZO_MODE_INPLACE) {
+        for (uint32_t i = 0; i < N; ++i) {
+            zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st);
+            if (r) return r;
+            zo_status f1 = model_forward(v, *b, nullptr, 0, losses_dev + 2 * i, st);
+            // the restore sequence always completes once a probe has started
+            zo_status r2 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig2, st);
+            zo_status f2 = f1 ? f1 : model_forward(v, *b, nullptr, 0, losses_dev + 2 * i + 1, st);
+            zo_status r3 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st);
+            if (f1) return f1;
+            if (r2) return r2;
+            if (f2) return f2;
+            if (r3) return r3;
+        }
+    } else {
+        std::vector<zo_pert> perts(2 * (size_t)N);
+        for (uint32_t i = 0; i < N; ++i) {
+            perts[2 * i] = zo_pert{cfg->seed, i, sig};
+            perts[2 * i + 1] = zo_pert{cfg->seed, i, -sig};
+        }
+        for (uint32_t k = 0; k < 2 * N; k += kMaxEvalsPerCall) {
+            const int32_t cnt = (int32_t)std::min<uint32_t>(kMaxEvalsPerCall, 2 * N - k);
+            if (zo_status r = model_forward(v, *b, perts.data() + k, cnt, losses_dev + k, st)) return r;
+        }
+    }
+    if (zo_status r = launch_gscalar(losses_dev, N, cfg->eps, g_dev, st)) return r;
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
+}
+
+static zo_status check_buffer(const void* w, int32_t dtype, uint64_t j0)
+{
+    if (!w) return fail(ZO_ERR_INVALID, "null buffer");
+    if (dtype != ZO_F32 && dtype != ZO_BF16) return fail(ZO_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+    if ((uintptr_t)w % 16) return fail(ZO_ERR_INVALID, "buffer must be 16-byte aligned");
+    if (j0 % 4) return fail(ZO_ERR_INVALID, "j0 must be a multiple of 4");
+    return ZO_OK;
+}
+
+zo_status zo_perturb_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
+                            float sigma, zo_stream s)
+{
+    if (zo_status st = check_buffer(w, dtype, j0)) return st;
+    if (n == 0) return ZO_OK;
+    return launch_perturb(w, dtype, n, j0, seed, probe, sigma, (hipStream_t)s);
+}
+
+zo_status zo_update_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
+                           const double* g_dev, float lr, zo_stream s)
+{
+    if (zo_status st = check_buffer(w, dtype, j0)) return st;
+    if (!g_dev) return fail(ZO_ERR_INVALID, "null g");
+    if (n_probes == 0) return fail(ZO_ERR_INVALID, "n_probes must be >= 1");
+    if (n == 0) return ZO_OK;
+    return launch_update(w, dtype, n, j0, seed, n_probes, g_dev, lr, (hipStream_t)s);
+}
+
+zo_status zo_gscalar(const double* losses_dev, uint32_t n, float eps, double* g_dev, zo_stream s)
+{
+    if (!losses_dev || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (n == 0) return ZO_OK;
+    return launch_gscalar(losses_dev, n, eps, g_dev, (hipStream_t)s);
+}
+
+zo_status zo_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words_dev, float* z_dev,
+                       zo_stream s)
+{
+    if (!words_dev && !z_dev) return fail(ZO_ERR_INVALID, "both outputs null");
+    return launch_debug_rng(seed, probe, j0, n, words_dev, z_dev, (hipStream_t)s);
+}
+
+zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float* z_dev, zo_stream s)
+{
+    if (!pairs_dev || !z_dev) return fail(ZO_ERR_INVALID, "null argument");
+    return launch_debug_box_muller(pairs_dev, n_pairs, z_dev, (hipStream_t)s);
+}
+
+}  // extern "C"

@@ -1,0 +1,333 @@
+// Memory-bound passes of the SPSA step over a flat parameter vector:
+//   perturb: w <- D(fma(sigma, z_i, w))          (in-place +eps / -2 eps / +eps)
+//   update:  w <- D(w + sum_i c_i z_i)           (every z_i regenerated)
+// where D is the storage rounding (identity for fp32, round-to-nearest-even for
+// bf16).  The loop of the method (ZOO blog "Backprop 없이 Transformer를
+// 학습시킨다", section "backprop의 메모리 세금", flowchart) perturbs W along N
+// random directions, evaluates losses only, and applies W <- W - eta * g_hat;
+// the weights are modified in place, inference-mode, with no copy (same page,
+// 1.5-SPSA section: OPT-30B trained in place).
+//
+// Layout: each block iteration covers 2048 consecutive elements; for fp32 a
+// thread owns two float4 (one per half, so every load instruction of a wave is
+// one contiguous 1 KiB run), for bf16 one 16-byte vector of 8 elements.  All
+// HBM traffic is 16-byte vector loads and stores, one read and one write per
+// element.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+
+#include "zo_internal.hpp"
+#include "zo_rng.hpp"
+
+namespace zo {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kElemsPerIter = kThreads * 8;
+
+// ---- bf16 storage conversions --------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 f = {lo, hi};
+    bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float* f)
+{
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f)
+{
+    return uint4{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                 pack_bf16(f[6], f[7])};
+}
+
+// Gaussian for one element j (slow path for ragged tails and debug).
+__device__ __forceinline__ float gauss1(Key key, uint32_t probe, uint64_t j)
+{
+    float4 z = gauss4(key, probe, j >> 2);
+    switch (j & 3u) {
+        case 0: return z.x;
+        case 1: return z.y;
+        case 2: return z.z;
+        default: return z.w;
+    }
+}
+
+__device__ __forceinline__ float load_elem(const float* w, uint64_t i) { return w[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* w, uint64_t i) { return __uint_as_float((uint32_t)w[i] << 16); }
+__device__ __forceinline__ void store_elem(float* w, uint64_t i, float v) { w[i] = v; }
+__device__ __forceinline__ void store_elem(uint16_t* w, uint64_t i, float v) { w[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu); }
+
+// ---------------------------------------------------------------- perturb
+__global__ __launch_bounds__(kThreads) void perturb_f32(float* __restrict__ w, uint64_t n_full,
+                                                         uint64_t j0, Key key, uint32_t probe,
+                                                         float sigma)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t ea = base + 4 * threadIdx.x;
+        const uint64_t eb = ea + kElemsPerIter / 2;
+        float4 wa = *reinterpret_cast<const float4*>(w + ea);
+        float4 wb = *reinterpret_cast<const float4*>(w + eb);
+        const float4 za = gauss4(key, probe, (j0 + ea) >> 2);
+        const float4 zb = gauss4(key, probe, (j0 + eb) >> 2);
+        wa.x = fmaf(sigma, za.x, wa.x); wa.y = fmaf(sigma, za.y, wa.y);
+        wa.z = fmaf(sigma, za.z, wa.z); wa.w = fmaf(sigma, za.w, wa.w);
+        wb.x = fmaf(sigma, zb.x, wb.x); wb.y = fmaf(sigma, zb.y, wb.y);
+        wb.z = fmaf(sigma, zb.z, wb.z); wb.w = fmaf(sigma, zb.w, wb.w);
+        *reinterpret_cast<float4*>(w + ea) = wa;
+        *reinterpret_cast<float4*>(w + eb) = wb;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void perturb_bf16(uint16_t* __restrict__ w, uint64_t n_full,
+                                                          uint64_t j0, Key key, uint32_t probe,
+                                                          float sigma)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 8 * threadIdx.x;
+        uint4 v = *reinterpret_cast<const uint4*>(w + e);
+        const float4 za = gauss4(key, probe, (j0 + e) >> 2);
+        const float4 zb = gauss4(key, probe, ((j0 + e) >> 2) + 1);
+        float f[8];
+        unpack8(v, f);
+        f[0] = fmaf(sigma, za.x, f[0]); f[1] = fmaf(sigma, za.y, f[1]);
+        f[2] = fmaf(sigma, za.z, f[2]); f[3] = fmaf(sigma, za.w, f[3]);
+        f[4] = fmaf(sigma, zb.x, f[4]); f[5] = fmaf(sigma, zb.y, f[5]);
+        f[6] = fmaf(sigma, zb.z, f[6]); f[7] = fmaf(sigma, zb.w, f[7]);
+        *reinterpret_cast<uint4*>(w + e) = pack8(f);
+    }
+}
+
+// Elements [start, n) one thread each (ragged tail, < kElemsPerIter).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void perturb_tail(T* __restrict__ w, uint64_t start, uint64_t n,
+                                                          uint64_t j0, Key key, uint32_t probe,
+                                                          float sigma)
+{
+    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    store_elem(w, i, fmaf(sigma, gauss1(key, probe, j0 + i), load_elem(w, i)));
+}
+
+// ----------------------------------------------------------------- update
+// Coefficients c_i = fp32(-lr * g_i / N) into LDS; returns false when any g_i
+// is not finite (then the block writes nothing).
+__device__ __forceinline__ bool load_coeffs(const double* __restrict__ g, uint32_t n_probes, float lr,
+                                            float* c_lds, int* bad_lds)
+{
+    if (threadIdx.x == 0) *bad_lds = 0;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n_probes; i += kThreads) {
+        const double gi = g[i];
+        if (!isfinite(gi)) *bad_lds = 1;
+        c_lds[i] = (float)((-(double)lr * gi) / (double)n_probes);
+    }
+    __syncthreads();
+    return *bad_lds == 0;
+}
+
+constexpr uint32_t kMaxProbes = 1024;
+
+__global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, uint64_t n_full, uint64_t j0,
+                                                        Key key, uint32_t n_probes,
+                                                        const double* __restrict__ g, float lr)
+{
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t ea = base + 4 * threadIdx.x;
+        const uint64_t eb = ea + kElemsPerIter / 2;
+        float4 aa = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+        for (uint32_t i = 0; i < n_probes; ++i) {
+            const float ci = c[i];
+            const float4 za = gauss4(key, i, (j0 + ea) >> 2);
+            const float4 zb = gauss4(key, i, (j0 + eb) >> 2);
+            aa.x = fmaf(ci, za.x, aa.x); aa.y = fmaf(ci, za.y, aa.y);
+            aa.z = fmaf(ci, za.z, aa.z); aa.w = fmaf(ci, za.w, aa.w);
+            ab.x = fmaf(ci, zb.x, ab.x); ab.y = fmaf(ci, zb.y, ab.y);
+            ab.z = fmaf(ci, zb.z, ab.z); ab.w = fmaf(ci, zb.w, ab.w);
+        }
+        float4 wa = *reinterpret_cast<const float4*>(w + ea);
+        float4 wb = *reinterpret_cast<const float4*>(w + eb);
+        wa.x += aa.x; wa.y += aa.y; wa.z += aa.z; wa.w += aa.w;
+        wb.x += ab.x; wb.y += ab.y; wb.z += ab.z; wb.w += ab.w;
+        *reinterpret_cast<float4*>(w + ea) = wa;
+        *reinterpret_cast<float4*>(w + eb) = wb;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w, uint64_t n_full,
+                                                         uint64_t j0, Key key, uint32_t n_probes,
+                                                         const double* __restrict__ g, float lr)
+{
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 8 * threadIdx.x;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (uint32_t i = 0; i < n_probes; ++i) {
+            const float ci = c[i];
+            const float4 za = gauss4(key, i, (j0 + e) >> 2);
+            const float4 zb = gauss4(key, i, ((j0 + e) >> 2) + 1);
+            acc[0] = fmaf(ci, za.x, acc[0]); acc[1] = fmaf(ci, za.y, acc[1]);
+            acc[2] = fmaf(ci, za.z, acc[2]); acc[3] = fmaf(ci, za.w, acc[3]);
+            acc[4] = fmaf(ci, zb.x, acc[4]); acc[5] = fmaf(ci, zb.y, acc[5]);
+            acc[6] = fmaf(ci, zb.z, acc[6]); acc[7] = fmaf(ci, zb.w, acc[7]);
+        }
+        const uint4 v = *reinterpret_cast<const uint4*>(w + e);
+        float f[8];
+        unpack8(v, f);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] += acc[t];
+        *reinterpret_cast<uint4*>(w + e) = pack8(f);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void update_tail(T* __restrict__ w, uint64_t start, uint64_t n,
+                                                         uint64_t j0, Key key, uint32_t n_probes,
+                                                         const double* __restrict__ g, float lr)
+{
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
+    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p, j0 + i), acc);
+    store_elem(w, i, load_elem(w, i) + acc);
+}
+
+// ------------------------------------------------------------ g scalars
+__global__ void gscalar_kernel(const double* __restrict__ losses, uint32_t n, double two_sigma,
+                               double* __restrict__ g)
+{
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) g[i] = (losses[2 * i] - losses[2 * i + 1]) / two_sigma;
+}
+
+// ------------------------------------------------------------------ debug
+__global__ __launch_bounds__(kThreads) void debug_rng_kernel(Key key, uint32_t probe, uint64_t j0, uint64_t n,
+                                                              uint32_t* __restrict__ words,
+                                                              float* __restrict__ z)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= n) return;
+    const uint64_t j = j0 + t;
+    if (words) {
+        const uint64_t q = j >> 2;
+        uint32_t c0 = (uint32_t)q, c1 = (uint32_t)(q >> 32), c2 = probe, c3 = 0u;
+        philox4x32_10(c0, c1, c2, c3, key);
+        const uint32_t sel = (uint32_t)(j & 3u);
+        words[t] = sel == 0 ? c0 : sel == 1 ? c1 : sel == 2 ? c2 : c3;
+    }
+    if (z) z[t] = gauss1(key, probe, j);
+}
+
+__global__ __launch_bounds__(kThreads) void debug_box_muller_kernel(const uint32_t* __restrict__ pairs,
+                                                                     uint64_t n_pairs, float* __restrict__ z)
+{
+    const uint64_t t = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= n_pairs) return;
+    float a, b;
+    box_muller(pairs[2 * t], pairs[2 * t + 1], a, b);
+    z[2 * t] = a;
+    z[2 * t + 1] = b;
+}
+
+int grid_for(uint64_t n_full)
+{
+    // enough blocks to fill 256 CUs several times over; the loop strides the rest
+    const uint64_t iters = n_full / kElemsPerIter;
+    const uint64_t cap = 256ull * 16ull;
+    return (int)(iters < cap ? (iters ? iters : 1) : cap);
+}
+
+}  // namespace
+
+zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
+                         float sigma, hipStream_t s)
+{
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    if (n_full) {
+        if (dtype == ZO_F32)
+            perturb_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, probe, sigma);
+        else
+            perturb_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, probe, sigma);
+    }
+    if (n > n_full) {
+        const int blocks = (int)((n - n_full + kThreads - 1) / kThreads);
+        if (dtype == ZO_F32)
+            perturb_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, probe, sigma);
+        else
+            perturb_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, probe, sigma);
+    }
+    return check_launch("perturb");
+}
+
+zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
+                        const double* g, float lr, hipStream_t s)
+{
+    if (n_probes == 0 || n_probes > kMaxProbes)
+        return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    if (n_full) {
+        if (dtype == ZO_F32)
+            update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, n_probes, g, lr);
+        else
+            update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, n_probes, g, lr);
+    }
+    if (n > n_full) {
+        const int blocks = (int)((n - n_full + kThreads - 1) / kThreads);
+        if (dtype == ZO_F32)
+            update_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, n_probes, g, lr);
+        else
+            update_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, n_probes, g, lr);
+    }
+    return check_launch("update");
+}
+
+zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s)
+{
+    gscalar_kernel<<<(n + 63) / 64, 64, 0, s>>>(losses, n, 2.0 * (double)sigma, g);
+    return check_launch("gscalar");
+}
+
+zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words, float* z,
+                           hipStream_t s)
+{
+    if (n == 0) return ZO_OK;
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    debug_rng_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(key, probe, j0, n, words, z);
+    return check_launch("debug_rng");
+}
+
+zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s)
+{
+    if (n_pairs == 0) return ZO_OK;
+    debug_box_muller_kernel<<<(unsigned)((n_pairs + kThreads - 1) / kThreads), kThreads, 0, s>>>(pairs, n_pairs, z);
+    return check_launch("debug_box_muller");
+}
+
+}  // namespace zo

@@ -1,0 +1,29 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/zo.h"
+
+namespace zo {
+
+// Records a message for zo_last_error() and returns `st`.
+zo_status fail(zo_status st, const char* fmt, ...);
+// Checks the last launch on this thread; returns ZO_OK or ZO_ERR_HIP.
+zo_status check_launch(const char* what);
+
+// ---- element-wise kernels (zo_elementwise.hip) ----
+// w[0..n) is direction element j0 .. j0+n-1; j0 % 4 == 0, w 16-byte aligned.
+zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
+                         float sigma, hipStream_t s);
+// w += sum_i c_i z_i, c_i = fp32(-lr * g_i / N) from fp64 g on the device;
+// nothing is written when any g_i is not finite.
+zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
+                        const double* g, float lr, hipStream_t s);
+zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words,
+                           float* z, hipStream_t s);
+zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);
+// g_i = (L[2i] - L[2i+1]) / (2 (double)sigma), i < n
+zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s);
+
+}  // namespace zo

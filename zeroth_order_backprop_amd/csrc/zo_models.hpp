@@ -1,0 +1,44 @@
+// Forward-only loss evaluation of the three model families, host side.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/zo.h"
+
+namespace zo {
+
+// Most losses one forward_loss call evaluates (probe-batched fused mode).
+constexpr int kMaxEvalsPerCall = 64;
+
+struct ModelView {
+    zo_model_desc desc;
+    void* params;
+    void* workspace;
+    size_t ws_bytes;
+    std::vector<uint64_t> offsets;  // arena offset of each tensor, layout order
+};
+
+zo_status model_check_shape(const zo_model_desc& d);
+zo_status model_check_batch(const zo_model_desc& d, const zo_batch& b);
+size_t model_workspace_bytes(const zo_model_desc& d);
+// perts == nullptr: one loss at the stored weights into loss[0].
+zo_status model_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n_perts,
+                        double* loss, hipStream_t s);
+
+// per family (zo_fp32_models.hip, zo_decoder.hip)
+zo_status lsq_check(const zo_model_desc& d);
+size_t lsq_workspace(const zo_model_desc& d);
+zo_status lsq_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
+                      hipStream_t s);
+zo_status mlp_check(const zo_model_desc& d);
+size_t mlp_workspace(const zo_model_desc& d);
+zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
+                      hipStream_t s);
+zo_status decoder_check(const zo_model_desc& d);
+size_t decoder_workspace(const zo_model_desc& d);
+zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
+                          hipStream_t s);
+
+}  // namespace zo
