@@ -1,0 +1,209 @@
+"""Benchmark of the multi-probe SPSA step on one MI355X.
+
+Default workload: the 2-layer MLP classifier in fp32 (1024 -> 4096 GELU -> 10,
+batch 256 synthetic N(0,1) inputs, labels from a fixed random teacher
+projection), N = 16 probes, eps = 1e-3, lr = 1e-3, perturbed-tile (fused)
+mode: every step evaluates 2N = 32 losses and applies one fused update.
+
+Prints one JSON line: probe-evals/s of the whole step, the dominant kernel's
+roofline (live HIP-event timing of its launches over the timed region), the
+perturb / update passes' HBM GB/s on a 1.3e9-element parameter buffer (the
+OPT-1.3B-shaped count), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SPSA probe-evals/sec per model + perturb/update HBM GB/s (frac. of peak)"
+HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mlp", choices=["mlp", "lsq"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-passes", action="store_true", help="skip the perturb/update pass measurement")
+    return p.parse_args()
+
+
+def build_mlp(torch, zo, inputs):
+    import numpy as np
+    B, D, H, C = 256, 1024, 4096, 10
+    inp = inputs.mlp_inputs(0, batch=B, d_in=D, hidden=H, classes=C)
+    desc = zo.make_desc(zo.ZO_MODEL_MLP, batch=B, d_in=D, hidden=H, classes=C)
+    layout, total = zo.param_layout(desc)
+    arena = np.zeros(total, np.float32)
+    for name, off, shape in layout:
+        arena[off:off + int(np.prod(shape))] = inp[name].ravel()
+    model = zo.Model(desc, torch.from_numpy(arena).cuda())
+    x = torch.from_numpy(inp["X"]).cuda()
+    lab = torch.from_numpy(inp["labels"]).cuda()
+    batch = zo.make_batch(x=x, labels=lab, batch=B)
+    info = {
+        "workload": "2-layer MLP classifier fp32 1024->4096(GELU)->10, batch 256, cross-entropy; "
+                    "N=16 probes, eps=1e-3, lr=1e-3; perturbed-tile (fused) mode",
+        "probes": 16, "eps": 1e-3, "lr": 1e-3, "mode": "fused", "batch": B,
+        "params": int(total),
+        # algorithmic flops of one evaluation: X W1^T and H W2^T
+        "flops_per_eval": 2.0 * B * D * H + 2.0 * B * H * C,
+        "dtype": "f32", "kernel": "gemm_f32", "peak_tflops": FP32_PEAK_TFLOPS,
+        "oracle_desc": {"kind": "mlp", "batch": B, "d_in": D, "hidden": H, "classes": C},
+        "oracle_batch": {"X": inp["X"], "labels": inp["labels"]}, "arena": arena,
+    }
+    return model, batch, (x, lab), info
+
+
+def build_lsq(torch, zo, inputs):
+    import numpy as np
+    n, D, O = 512, 256, 256
+    inp = inputs.lsq_inputs(0, n=n, d_in=D, d_out=O)
+    desc = zo.make_desc(zo.ZO_MODEL_LSQ, batch=n, d_in=D, d_out=O)
+    _, total = zo.param_layout(desc)
+    arena = inp["W"].ravel().copy()
+    model = zo.Model(desc, torch.from_numpy(arena).cuda())
+    x = torch.from_numpy(inp["X"]).cuda()
+    y = torch.from_numpy(inp["Y"]).cuda()
+    batch = zo.make_batch(x=x, y=y, batch=n)
+    info = {
+        "workload": "least squares fp32 W 256x256, X 512x256, MSE/2; N=4 probes, eps=1e-3, lr=1e-2; fused mode",
+        "probes": 4, "eps": 1e-3, "lr": 1e-2, "mode": "fused", "batch": n, "params": int(total),
+        "flops_per_eval": 2.0 * n * D * O, "dtype": "f32", "kernel": "gemm_f32", "peak_tflops": FP32_PEAK_TFLOPS,
+        "oracle_desc": {"kind": "lsq", "n": n, "d_in": D, "d_out": O},
+        "oracle_batch": {"X": inp["X"], "Y": inp["Y"]}, "arena": arena,
+    }
+    return model, batch, (x, y), info
+
+
+def measure_passes(torch, zo):
+    """Perturb and update passes over an OPT-1.3B-sized parameter count."""
+    n = 1_315_311_616
+    out = {}
+    for name, dtype, tdt, esz in (("bf16", zo.ZO_BF16, torch.bfloat16, 2), ("f32", zo.ZO_F32, torch.float32, 4)):
+        w = torch.zeros(n, dtype=tdt, device="cuda")
+        g = torch.ones(1, dtype=torch.float64, device="cuda")
+        zo.perturb_buffer(w, n, 0, 1, 0, 1e-3, dtype)
+        zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype)
+        torch.cuda.synchronize()
+        zo.timing_reset()
+        zo.timing_enable(True)
+        for r in range(5):
+            zo.perturb_buffer(w, n, 0, 1, r, 1e-3, dtype)
+            zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype)
+        torch.cuda.synchronize()
+        zo.timing_enable(False)
+        for fam in ("perturb", "update"):
+            ms, k = zo.timing_query(fam)
+            t = ms / k * 1e-3
+            gbs = 2.0 * n * esz / t / 1e9
+            out[f"{fam}_{name}"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                    "ms": round(t * 1e3, 4), "elements": n, "probes": 1}
+        zo.timing_reset()
+        del w
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(info):
+    """The oracle as it stands, single-threaded, on a bounded sample: one
+    fused-mode step of the same workload with fewer probes."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oracle
+    probes = 2 if info["oracle_desc"]["kind"] == "mlp" else 4
+    arena = oracle.Arena(info["oracle_desc"], info["arena"].copy())
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.spsa_step(arena, info["oracle_batch"], seed=reps, n_probes=probes, eps=info["eps"],
+                             lr=info["lr"], mode="fused")
+            reps += 1
+            if time.perf_counter() - t0 > 8.0:
+                break
+        t = time.perf_counter() - t0
+    evals = 2 * probes * reps
+    return {"value": round(evals / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} oracle SPSA step(s) of the same workload with N={probes} probes "
+                      f"({evals} evaluations + update), single-threaded, {t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the step shards by probes, see the design notes", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from zeroth_order_backprop_amd import inputs, zo
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
+    N = info["probes"]
+    losses = torch.zeros(2 * N, dtype=torch.float64, device="cuda")
+    g = torch.zeros(N, dtype=torch.float64, device="cuda")
+    mode = zo.ZO_MODE_FUSED
+    for t in range(args.warmup):
+        model.step(batch, t, N, info["eps"], info["lr"], mode, losses, g)
+    torch.cuda.synchronize()
+    zo.timing_reset()
+    zo.timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(args.steps):
+        model.step(batch, args.warmup + t, N, info["eps"], info["lr"], mode, losses, g)
+    stop.record()
+    torch.cuda.synchronize()
+    zo.timing_enable(False)
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    evals_per_s = 2 * N * args.steps / (total_ms * 1e-3)
+    k_ms, k_n = zo.timing_query(info["kernel"])
+    k_avg_s = k_ms / k_n * 1e-3
+    flops_per_launch = 2 * N * info["flops_per_eval"]
+    achieved = flops_per_launch / k_avg_s / 1e12
+    kernels = {}
+    for fam in ("gemm_f32", "reduce", "update", "perturb"):
+        ms, n = zo.timing_query(fam)
+        if n:
+            kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / args.steps}
+    zo.timing_reset()
+    final = losses.cpu().numpy()
+    line = {
+        "metric": METRIC, "value": round(evals_per_s, 2), "unit": "probe-evals/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": info["dtype"],
+        "data": "synthetic (seeded N(0,1) inputs, random-init weights; no dataset)",
+        "config": {"workload": info["workload"], "probes": N, "batch": info["batch"], "params": info["params"],
+                   "mode": info["mode"], "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
+                     "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4), "traffic": None,
+                     "kernel": f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch",
+                     "avg_launch_us": round(k_avg_s * 1e6, 2)},
+        "kernels": kernels,
+        "last_losses_mean": float(final.mean()),
+    }
+    if not args.no_passes:
+        line["perturb_update"] = measure_passes(torch, zo)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(info)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

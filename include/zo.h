@@ -222,6 +222,21 @@ zo_status zo_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, u
 /* Box-Muller map alone: pairs_dev [n][2] words -> z_dev [n][2] (z_even, z_odd). */
 zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float* z_dev, zo_stream s);
 
+/* ------------------------------------------------------------ timing */
+
+/*
+ * Kernel timing, a measurement aid.  While enabled, every kernel launch of the
+ * library is bracketed by HIP events recorded on the launch's own stream and
+ * grouped by family: "perturb", "update", "gemm_f32", "reduce", "gemm_bf16",
+ * "attention", "layernorm", "embed", "lm_head", "debug".  zo_timing_query
+ * returns the summed elapsed milliseconds and the launch count of one family
+ * since the last reset; it synchronises the recorded events, so call it after
+ * the stream work is complete.  Not thread-safe across concurrent callers.
+ */
+zo_status zo_timing_enable(int32_t on);
+zo_status zo_timing_reset(void);
+zo_status zo_timing_query(const char* family, double* total_ms, int64_t* launches);
+
 const char* zo_status_str(zo_status st);
 const char* zo_last_error(void);
 

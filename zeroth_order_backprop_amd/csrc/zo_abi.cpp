@@ -38,6 +38,44 @@ zo_status check_launch(const char* what)
     return ZO_OK;
 }
 
+// ---------------------------------------------------------------- timing
+namespace {
+struct TimedLaunch {
+    std::string family;
+    hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event()
+{
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+KernelTimer::KernelTimer(const char* family, hipStream_t s) : slot_(-1), s_(s)
+{
+    if (!g_timing) return;
+    TimedLaunch t{family, take_event(), take_event()};
+    if (!t.start || !t.stop) return;
+    hipEventRecord(t.start, s);
+    g_timed.push_back(t);
+    slot_ = (int)g_timed.size() - 1;
+}
+
+KernelTimer::~KernelTimer()
+{
+    if (slot_ >= 0) hipEventRecord(g_timed[slot_].stop, s_);
+}
+
 static uint64_t align64(uint64_t x) { return (x + 63) / 64 * 64; }
 
 // Tensors of a model in declaration order (the arena layout).
@@ -159,6 +197,40 @@ const char* zo_status_str(zo_status st)
 }
 
 const char* zo_last_error(void) { return g_err; }
+
+zo_status zo_timing_enable(int32_t on)
+{
+    g_timing = on != 0;
+    return ZO_OK;
+}
+
+zo_status zo_timing_reset(void)
+{
+    for (auto& t : g_timed) {
+        g_event_pool.push_back(t.start);
+        g_event_pool.push_back(t.stop);
+    }
+    g_timed.clear();
+    return ZO_OK;
+}
+
+zo_status zo_timing_query(const char* family, double* total_ms, int64_t* launches)
+{
+    if (!family || !total_ms || !launches) return fail(ZO_ERR_INVALID, "null argument");
+    double sum = 0.0;
+    int64_t n = 0;
+    for (auto& t : g_timed) {
+        if (t.family != family) continue;
+        if (hipEventSynchronize(t.stop) != hipSuccess) return fail(ZO_ERR_HIP, "event synchronise failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) return fail(ZO_ERR_HIP, "event elapsed failed");
+        sum += ms;
+        ++n;
+    }
+    *total_ms = sum;
+    *launches = n;
+    return ZO_OK;
+}
 
 zo_status zo_param_layout(const zo_model_desc* desc, zo_param_info* out, int32_t cap, int32_t* n_out,
                           uint64_t* total)

@@ -269,6 +269,7 @@ zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t s
 {
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    KernelTimer timer("perturb", s);
     if (n_full) {
         if (dtype == ZO_F32)
             perturb_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, probe, sigma);
@@ -292,6 +293,7 @@ zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t se
         return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    KernelTimer timer("update", s);
     if (n_full) {
         if (dtype == ZO_F32)
             update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, n_probes, g, lr);
@@ -310,6 +312,7 @@ zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t se
 
 zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s)
 {
+    KernelTimer timer("reduce", s);
     gscalar_kernel<<<(n + 63) / 64, 64, 0, s>>>(losses, n, 2.0 * (double)sigma, g);
     return check_launch("gscalar");
 }
@@ -319,6 +322,7 @@ zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t 
 {
     if (n == 0) return ZO_OK;
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    KernelTimer timer("debug", s);
     debug_rng_kernel<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(key, probe, j0, n, words, z);
     return check_launch("debug_rng");
 }
@@ -326,6 +330,7 @@ zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t 
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s)
 {
     if (n_pairs == 0) return ZO_OK;
+    KernelTimer timer("debug", s);
     debug_box_muller_kernel<<<(unsigned)((n_pairs + kThreads - 1) / kThreads), kThreads, 0, s>>>(pairs, n_pairs, z);
     return check_launch("debug_box_muller");
 }

@@ -12,6 +12,20 @@ zo_status fail(zo_status st, const char* fmt, ...);
 // Checks the last launch on this thread; returns ZO_OK or ZO_ERR_HIP.
 zo_status check_launch(const char* what);
 
+// Brackets the launches made during its lifetime with HIP events on `s` when
+// timing is enabled (zo_timing_enable); a no-op otherwise.
+class KernelTimer {
+public:
+    KernelTimer(const char* family, hipStream_t s);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer&) = delete;
+    KernelTimer& operator=(const KernelTimer&) = delete;
+
+private:
+    int slot_;
+    hipStream_t s_;
+};
+
 // ---- element-wise kernels (zo_elementwise.hip) ----
 // w[0..n) is direction element j0 .. j0+n-1; j0 % 4 == 0, w 16-byte aligned.
 zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,

@@ -3,14 +3,6 @@
 #include "zo_models.hpp"
 
 namespace zo {
-zo_status lsq_check(const zo_model_desc&) { return ZO_OK; }
-size_t lsq_workspace(const zo_model_desc&) { return 0; }
-zo_status lsq_forward(const ModelView&, const zo_batch&, const zo_pert*, int, double*, hipStream_t)
-{ return fail(ZO_ERR_UNSUPPORTED, "least squares forward not built"); }
-zo_status mlp_check(const zo_model_desc&) { return ZO_OK; }
-size_t mlp_workspace(const zo_model_desc&) { return 0; }
-zo_status mlp_forward(const ModelView&, const zo_batch&, const zo_pert*, int, double*, hipStream_t)
-{ return fail(ZO_ERR_UNSUPPORTED, "MLP forward not built"); }
 zo_status decoder_check(const zo_model_desc&) { return ZO_OK; }
 size_t decoder_workspace(const zo_model_desc&) { return 0; }
 zo_status decoder_forward(const ModelView&, const zo_batch&, const zo_pert*, int, double*, hipStream_t)

@@ -20,6 +20,7 @@ EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
     "zo_forward_loss", "zo_update", "zo_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
+    "zo_timing_enable", "zo_timing_reset", "zo_timing_query",
 ]
 
 
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
         "zo_gscalar": [P, U32, F, P, P],
         "zo_debug_rng": [U64, U32, U64, U64, P, P, P],
         "zo_debug_box_muller": [P, U64, P, P],
+        "zo_timing_enable": [I32],
+        "zo_timing_reset": [],
+        "zo_timing_query": [ctypes.c_char_p, P, P],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -132,6 +136,23 @@ def debug_rng(seed, probe, j0, n, words=None, z=None, stream=None):
 
 def debug_box_muller(pairs, n_pairs, z, stream=None):
     check(lib().zo_debug_box_muller(_ptr(pairs), n_pairs, _ptr(z), _stream(stream)), "zo_debug_box_muller")
+
+
+# ------------------------------------------------------------------ timing
+def timing_enable(on: bool = True) -> None:
+    check(lib().zo_timing_enable(1 if on else 0), "zo_timing_enable")
+
+
+def timing_reset() -> None:
+    check(lib().zo_timing_reset(), "zo_timing_reset")
+
+
+def timing_query(family: str):
+    """(total ms, launches) of one kernel family since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    check(lib().zo_timing_query(family.encode(), ctypes.byref(ms), ctypes.byref(n)), "zo_timing_query")
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------ models
