@@ -26,6 +26,12 @@ METRIC = "SPSA probe-evals/sec per model + perturb/update HBM GB/s (frac. of pea
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 BF16_PEAK_TFLOPS = 2500.0
+# HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE, scaled by the same counters on a plain copy of known size
+# (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
+# taken on -- set to None when that kernel changes.
+TRAFFIC = {"gemm_f32:mlp:r1": 34.1e6 + 21.0e6}
+KERNEL_REV = {"mlp": "gemm_f32:mlp:r1", "lsq": None}
 
 
 def parse():
@@ -104,6 +110,19 @@ def measure_passes(torch, zo):
             zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype)
         torch.cuda.synchronize()
         zo.timing_enable(False)
+        # plain copy of the same size: the HBM reference for these passes
+        c = torch.empty_like(w)
+        c.copy_(w)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for r in range(5):
+            c.copy_(w)
+        ev1.record()
+        torch.cuda.synchronize()
+        tc = ev0.elapsed_time(ev1) / 5 * 1e-3
+        out[f"copy_{name}"] = {"GB/s": round(2.0 * n * esz / tc / 1e9, 1), "ms": round(tc * 1e3, 4),
+                               "elements": n, "kind": "torch copy_, reference"}
+        del c
         for fam in ("perturb", "update"):
             ms, k = zo.timing_query(fam)
             t = ms / k * 1e-3
@@ -192,7 +211,8 @@ def main():
         "config": {"workload": info["workload"], "probes": N, "batch": info["batch"], "params": info["params"],
                    "mode": info["mode"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
-                     "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
+                     "traffic": TRAFFIC.get(KERNEL_REV[args.workload] or "", None),
                      "kernel": f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch",
                      "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "kernels": kernels,
