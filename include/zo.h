@@ -222,6 +222,25 @@ zo_status zo_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, u
 /* Box-Muller map alone: pairs_dev [n][2] words -> z_dev [n][2] (z_even, z_odd). */
 zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float* z_dev, zo_stream s);
 
+/*
+ * Single decoder kernels, for testing them in isolation (bf16 buffers, device):
+ *  zo_debug_gemm_bf16: C[M][N] = epi(A[M][K] W[N][K]^T), fp32 accumulation,
+ *    epi 0: bf16 store, 1: GELU then bf16, 2: ReLU then bf16,
+ *    3: residual C = bf16(C + bf16(product)); K % 64 == 0.
+ *  zo_debug_attention: out[B*S][H*dh] = causal softmax(Q K^T / sqrt(dh)) V per
+ *    (sequence, head) from qkv[B*S][3*H*dh] (Q, K, V blocks of H*dh columns,
+ *    head h at columns h*dh); dh in {64, 128}.
+ *  zo_debug_layernorm: x[r] = bf16((h[r] - mean) / sqrt(var + 1e-5) * g + b).
+ * The causal attention follows the decoder's definition (scale 1/sqrt(dh),
+ * keys at positions <= the query's).
+ */
+zo_status zo_debug_gemm_bf16(const void* A_dev, const void* W_dev, void* C_dev, int32_t M, int32_t N, int32_t K,
+                             int32_t epi, zo_stream s);
+zo_status zo_debug_attention(const void* qkv_dev, void* out_dev, int32_t B, int32_t S, int32_t H, int32_t dh,
+                             zo_stream s);
+zo_status zo_debug_layernorm(const void* h_dev, const void* g_dev, const void* b_dev, void* x_dev, int32_t rows,
+                             int32_t d, zo_stream s);
+
 /* ------------------------------------------------------------ timing */
 
 /*

@@ -237,7 +237,24 @@ def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5) -
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
-def decoder_loss(desc: dict, params: dict, tokens: np.ndarray, round_bf16: bool = True) -> float:
+def causal_attention(qkv: np.ndarray, heads: int) -> np.ndarray:
+    """softmax(Q K^T / sqrt(dh) + causal mask) V per sequence and head, fp64.
+    qkv [B][S][3d] with Q, K, V blocks of d columns, head h at h*dh."""
+    B, S, three_d = qkv.shape
+    d = three_d // 3
+    dh = d // heads
+    Q = qkv[..., :d].reshape(B, S, heads, dh).transpose(0, 2, 1, 3)
+    K = qkv[..., d:2 * d].reshape(B, S, heads, dh).transpose(0, 2, 1, 3)
+    V = qkv[..., 2 * d:].reshape(B, S, heads, dh).transpose(0, 2, 1, 3)
+    s = (Q @ K.transpose(0, 1, 3, 2)) / np.sqrt(dh)                       # [B,H,S,S]
+    s[..., np.triu(np.ones((S, S), dtype=bool), k=1)] = -np.inf
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    P = e / e.sum(axis=-1, keepdims=True)
+    return (P @ V).transpose(0, 2, 1, 3).reshape(B, S, d)
+
+
+def decoder_loss(desc: dict, params, tokens: np.ndarray, round_bf16: bool = True) -> float:
     """Causal-LM mean cross-entropy of a pre-LN decoder.
 
     Embedding + learned positions; per block h += W_o Attn(LN1 h),
@@ -248,39 +265,32 @@ def decoder_loss(desc: dict, params: dict, tokens: np.ndarray, round_bf16: bool 
     bf16 rounding points (when ``round_bf16``): embedding sum, every LN output,
     every GEMM output (QKV, attention output, O, up after the activation, down),
     both residual sums.  Everything else (softmax, LN statistics, logits, CE)
-    is exact fp64.
+    is exact fp64.  ``params`` maps tensor names to fp64 arrays (any mapping,
+    so large models can be fetched tensor by tensor).
     """
     R = bf16_round if round_bf16 else (lambda a: a)
     act = gelu_erf if desc["act"] == "gelu" else (lambda a: np.maximum(a, 0.0))
     B, S = tokens.shape
-    d, H = desc["d"], desc["heads"]
-    dh = d // H
     p = params
     h = R(p["tok_emb"][tokens] + p["pos_emb"][:S][None, :, :])           # [B,S,d]
-    mask = np.triu(np.ones((S, S), dtype=bool), k=1)
     for layer in range(desc["layers"]):
         q = f"l{layer}."
         x = R(layer_norm(h, p[q + "ln1_g"], p[q + "ln1_b"]))
         qkv = R(x @ p[q + "w_qkv"].T)                                      # [B,S,3d]
-        Q = qkv[..., :d].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
-        K = qkv[..., d:2 * d].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
-        V = qkv[..., 2 * d:].reshape(B, S, H, dh).transpose(0, 2, 1, 3)
-        s = (Q @ K.transpose(0, 1, 3, 2)) / np.sqrt(dh)                   # [B,H,S,S]
-        s[..., mask] = -np.inf
-        s = s - s.max(axis=-1, keepdims=True)
-        e = np.exp(s)
-        P = e / e.sum(axis=-1, keepdims=True)
-        o = R((P @ V).transpose(0, 2, 1, 3).reshape(B, S, d))
+        o = R(causal_attention(qkv, desc["heads"]))
         h = R(h + R(o @ p[q + "w_o"].T))
         x = R(layer_norm(h, p[q + "ln2_g"], p[q + "ln2_b"]))
         u = R(act(x @ p[q + "w_up"].T))
         h = R(h + R(u @ p[q + "w_down"].T))
     x = R(layer_norm(h, p["lnf_g"], p["lnf_b"]))
-    logits = x[:, :-1, :] @ p["tok_emb"].T                                 # [B,S-1,V]
+    emb = p["tok_emb"]
     tgt = tokens[:, 1:]
-    lse = logsumexp_rows(logits)
-    picked = np.take_along_axis(logits, tgt[..., None], axis=-1)[..., 0]
-    return float(np.mean(lse - picked))
+    total = 0.0
+    for b in range(B):  # one sequence at a time keeps the logits block small
+        logits = x[b, :-1, :] @ emb.T                                      # [S-1,V]
+        lse = logsumexp_rows(logits)
+        total += float(np.sum(lse - logits[np.arange(S - 1), tgt[b]]))
+    return total / (B * (S - 1))
 
 
 # ============================================================ arena helpers

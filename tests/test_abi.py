@@ -43,9 +43,9 @@ DESCS = {
              "max_seq": 512, "act": "gelu"},
             dict(kind=zo.ZO_MODEL_DECODER, batch=8, seq=512, layers=12, d_model=768, heads=12, ffn=3072,
                  vocab=32000, max_seq=512, act=zo.ZO_ACT_GELU)),
-    "odd": ({"kind": "decoder", "layers": 1, "d": 40, "heads": 5, "ffn": 72, "vocab": 33,
+    "odd": ({"kind": "decoder", "layers": 1, "d": 128, "heads": 2, "ffn": 192, "vocab": 33,
              "max_seq": 7, "act": "relu"},
-            dict(kind=zo.ZO_MODEL_DECODER, batch=1, seq=7, layers=1, d_model=40, heads=5, ffn=72,
+            dict(kind=zo.ZO_MODEL_DECODER, batch=1, seq=7, layers=1, d_model=128, heads=2, ffn=192,
                  vocab=33, max_seq=7, act=zo.ZO_ACT_RELU)),
 }
 
@@ -99,6 +99,8 @@ def test_validation_rejects_before_launch():
                                  ws, ctypes.byref(h)) == zo.ZO_ERR_INVALID
     bad = zo.make_desc(**dict(DESCS["gpt"][1], d_model=770))
     assert L.zo_workspace_bytes(ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == zo.ZO_ERR_INVALID
+    bad = zo.make_desc(**dict(DESCS["gpt"][1], heads=24))  # head dim 32: unsupported
+    assert L.zo_workspace_bytes(ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == zo.ZO_ERR_UNSUPPORTED
     bad = zo.make_desc(**dict(DESCS["lsq"][1], dtype=zo.ZO_BF16))
     assert L.zo_workspace_bytes(ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == zo.ZO_ERR_UNSUPPORTED
 

@@ -434,4 +434,22 @@ zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float
     return launch_debug_box_muller(pairs_dev, n_pairs, z_dev, (hipStream_t)s);
 }
 
+zo_status zo_debug_gemm_bf16(const void* A_dev, const void* W_dev, void* C_dev, int32_t M, int32_t N, int32_t K,
+                             int32_t epi, zo_stream s)
+{
+    return debug_gemm_bf16(A_dev, W_dev, C_dev, M, N, K, epi, (hipStream_t)s);
+}
+
+zo_status zo_debug_attention(const void* qkv_dev, void* out_dev, int32_t B, int32_t S, int32_t H, int32_t dh,
+                             zo_stream s)
+{
+    return debug_attention(qkv_dev, out_dev, B, S, H, dh, (hipStream_t)s);
+}
+
+zo_status zo_debug_layernorm(const void* h_dev, const void* g_dev, const void* b_dev, void* x_dev, int32_t rows,
+                             int32_t d, zo_stream s)
+{
+    return debug_layernorm(h_dev, g_dev, b_dev, x_dev, rows, d, (hipStream_t)s);
+}
+
 }  // extern "C"

@@ -1,0 +1,766 @@
+// Forward-only loss of the bf16 pre-LN decoder (GPT-small and OPT shapes) for
+// the SPSA step: token + learned-position embedding, L blocks of
+// h += W_o Attn(LN1 h), h += W_down act(W_up LN2 h), final LN, LM head tied to
+// the token embedding, mean next-token cross-entropy over batch*(seq-1)
+// positions.  The loss is a forward-only evaluation of the SPSA loop (ZOO blog
+// "Backprop 없이 Transformer를 학습시킨다", section "backprop의 메모리 세금":
+// loss only, no backprop, no stored activations beyond the current layer).
+//
+// Precision: bf16 weights and activations, fp32 MFMA accumulation, rounding to
+// bf16 at: embedding sum, LN outputs, every GEMM output (after the
+// activation), both residual sums, attention output.  LN statistics and
+// softmax are fp32; the LM-head logits never leave fp32 and the loss is fp64.
+//
+// Every kernel can apply a perturbation on the fly (weights seen =
+// bf16(fma(sigma, z, w)) with z regenerated for the element's arena index),
+// which is how the perturbed-tile (fused) mode evaluates W +- eps z without
+// writing W; with sigma = 0 and no direction the stored weights are used.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "zo_internal.hpp"
+#include "zo_models.hpp"
+#include "zo_rng.hpp"
+
+namespace zo {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;
+
+constexpr int kThreads = 256;
+
+// A perturbation applied while reading weights.
+struct Pert {
+    Key key;
+    uint32_t probe;
+    float sigma;
+    int on;  // 0: stored weights as they are
+};
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ bf16_t f2bf(float x) { return (bf16_t)(pack2(x, 0.0f) & 0xFFFFu); }
+
+__device__ __forceinline__ float round_bf(float x) { return bf2f(f2bf(x)); }
+
+// 8 consecutive bf16 weights starting at arena index j (j % 8 == 0 not
+// required, j % 4 == 0 required), perturbed in place in the uint4.
+__device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p)
+{
+    const float4 za = gauss4(p.key, p.probe, j >> 2);
+    const float4 zb = gauss4(p.key, p.probe, (j >> 2) + 1);
+    float f[8] = {bf2f(v.x & 0xFFFF), bf2f(v.x >> 16), bf2f(v.y & 0xFFFF), bf2f(v.y >> 16),
+                  bf2f(v.z & 0xFFFF), bf2f(v.z >> 16), bf2f(v.w & 0xFFFF), bf2f(v.w >> 16)};
+    const float z[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = fmaf(p.sigma, z[t], f[t]);
+    return uint4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+}
+
+// One perturbed weight (slow path: LN parameters, ragged ends).
+__device__ __forceinline__ float weight1(const bf16_t* w, uint64_t i, uint64_t dir, const Pert& p)
+{
+    float v = bf2f(w[i]);
+    if (p.on) {
+        const uint64_t j = dir + i;
+        const float4 z = gauss4(p.key, p.probe, j >> 2);
+        const uint32_t s = (uint32_t)(j & 3u);
+        const float zz = s == 0 ? z.x : s == 1 ? z.y : s == 2 ? z.z : z.w;
+        v = round_bf(fmaf(p.sigma, zz, v));
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sumf(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sumd(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ============================================================ embedding
+// h[t][c] = bf16(tok_emb[tok[t]][c] + pos_emb[t % S][c]); one block per token.
+__global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restrict__ tokens, int S, int d,
+                                                          const bf16_t* __restrict__ tok_emb, uint64_t tok_dir,
+                                                          const bf16_t* __restrict__ pos_emb, uint64_t pos_dir,
+                                                          Pert p, bf16_t* __restrict__ h)
+{
+    const int t = blockIdx.x;
+    const int tok = tokens[t];
+    const int s = t % S;
+    const uint64_t te = (uint64_t)tok * d, pe = (uint64_t)s * d;
+    for (int c = threadIdx.x; c < d; c += kThreads) {
+        const float a = weight1(tok_emb, te + c, tok_dir, p);
+        const float b = weight1(pos_emb, pe + c, pos_dir, p);
+        h[(size_t)t * d + c] = f2bf(a + b);
+    }
+}
+
+// ============================================================ LayerNorm
+// x[t] = bf16((h[t] - mean) / sqrt(var + 1e-5) * g + b), fp32 statistics;
+// one block per row, two passes over the row held in registers (d <= 8192).
+constexpr int kLnMaxPer = 32;  // elements per thread: d <= 256 * 32
+__global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __restrict__ h, int d,
+                                                              const bf16_t* __restrict__ g, uint64_t g_dir,
+                                                              const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
+                                                              bf16_t* __restrict__ x)
+{
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const bf16_t* row = h + (size_t)t * d;
+    float v[kLnMaxPer];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxPer; ++k) {
+        const int c = threadIdx.x + k * kThreads;
+        v[k] = c < d ? bf2f(row[c]) : 0.f;
+        s += v[k];
+    }
+    s = wave_sumf(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
+    __syncthreads();
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxPer; ++k) {
+        const int c = threadIdx.x + k * kThreads;
+        const float dv = c < d ? v[k] - mean : 0.f;
+        q = fmaf(dv, dv, q);
+    }
+    q = wave_sumf(q);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = q;
+    __syncthreads();
+    const float var = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + 1e-5f);
+#pragma unroll
+    for (int k = 0; k < kLnMaxPer; ++k) {
+        const int c = threadIdx.x + k * kThreads;
+        if (c < d) {
+            const float gg = weight1(g, c, g_dir, p), bb = weight1(b, c, b_dir, p);
+            x[(size_t)t * d + c] = f2bf(fmaf((v[k] - mean) * rstd, gg, bb));
+        }
+    }
+}
+
+// ============================================================ bf16 GEMM
+// C[M][N] = A[M][K] * W[N][K]^T, bf16 in, fp32 accumulate (MFMA 32x32x16).
+// 256 threads = 2x2 waves; each wave owns a (BM/2) x (BN/2) tile of 32x32
+// MFMA blocks.  LDS holds two stages of A and B with rows padded by 8 bf16
+// (16 B) so the b128 fragment reads of 32 consecutive rows spread over all
+// banks.  Global loads for stage k+1 are in flight during stage k's MFMAs.
+enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RELU = 2, EPI_RESID = 3, EPI_LMHEAD = 4 };
+
+struct GemmParams {
+    const bf16_t* A;  // [M][K]
+    const bf16_t* W;  // [N][K]
+    uint64_t w_dir;   // arena index of W[0][0]
+    bf16_t* C;        // [M][N] (EPI_STORE / GELU / RELU) or the residual h (EPI_RESID, [M][N])
+    int M, N, K;
+    // LM head: per (n_tile, row) running max / sum of exp, and the target logit
+    float* lm_max;
+    float* lm_sum;
+    float* lm_pick;
+    const int32_t* tokens;  // targets: row r's target is tokens[r + 1] (same sequence)
+    int S;
+};
+
+__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// Linear tile index -> (tm, tn): consecutive workgroups land on consecutive
+// XCDs, so give each XCD a contiguous range of tiles, and walk tiles in
+// groups of 8 M-tiles so neighbours share A rows and W columns in L2.
+__device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& tn)
+{
+    const int total = nbm * nbn;
+    int t = b;
+    if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
+    constexpr int G = 8;
+    const int group = t / (G * nbn);
+    const int first = group * G;
+    const int gsize = min(nbm - first, G);
+    const int r = t % (G * nbn);
+    tm = first + r % gsize;
+    tn = r / gsize;
+}
+
+template <int BM, int BN, int EPI, bool PERT>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert p)
+{
+    constexpr int BK = 64;
+    constexpr int LDK = BK + 8;  // padded row (bf16)
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int A_CH = BM * BK / 8, B_CH = BN * BK / 8;  // 16-byte chunks per stage
+    constexpr int A_PER = A_CH / kThreads, B_PER = B_CH / kThreads;
+    static_assert(A_CH % kThreads == 0 && B_CH % kThreads == 0, "tile / thread mismatch");
+    extern __shared__ __align__(16) bf16_t lds[];
+    // stage st: A tile at lds + st * BM * LDK, B tile at lds + 2 BM LDK + st * BN * LDK
+    auto As = [&](int st) { return lds + st * (BM * LDK); };
+    auto Bs = [&](int st) { return lds + 2 * (BM * LDK) + st * (BN * LDK); };
+
+    const int M = g.M, N = g.N, K = g.K;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+
+    uint4 ra[A_PER], rb[B_PER];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int t = 0; t < A_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            const int gm = m0 + r, gk = k0 + kc;
+            ra[t] = (gm < M && gk < K) ? *reinterpret_cast<const uint4*>(g.A + (size_t)gm * K + gk)
+                                       : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int t = 0; t < B_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            const int gn = n0 + r, gk = k0 + kc;
+            rb[t] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(g.W + (size_t)gn * K + gk)
+                                       : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int stage, int k0) {
+#pragma unroll
+        for (int t = 0; t < A_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            *reinterpret_cast<uint4*>(As(stage) + r * LDK + kc) = ra[t];
+        }
+#pragma unroll
+        for (int t = 0; t < B_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            uint4 v = rb[t];
+            if constexpr (PERT) {
+                const int gn = n0 + r, gk = k0 + kc;
+                if (gn < N && gk < K) v = perturb8(v, g.w_dir + (uint64_t)gn * K + gk, p);
+            }
+            *reinterpret_cast<uint4*>(Bs(stage) + r * LDK + kc) = v;
+        }
+    };
+
+    const int KT = (K + BK - 1) / BK;
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) load((kt + 1) * BK);
+#pragma unroll
+        for (int ks = 0; ks < BK; ks += 16) {
+            bf16x8 af[RB], bfr[CB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(As(cur) + (wm * WM + i * 32 + lr) * LDK + ks + 8 * lh);
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(Bs(cur) + (wn * WN + j * 32 + lr) * LDK + ks + 8 * lh);
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store(cur ^ 1, (kt + 1) * BK);
+        __syncthreads();
+    }
+
+    // accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr
+    if constexpr (EPI != EPI_LMHEAD) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (row >= M || col >= N) continue;
+                    float v = acc[i][j][r];
+                    bf16_t* dst = g.C + (size_t)row * N + col;
+                    if constexpr (EPI == EPI_GELU) v = gelu_f(v);
+                    if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
+                    if constexpr (EPI == EPI_RESID) v = bf2f(*dst) + round_bf(v);
+                    *dst = f2bf(v);
+                }
+    } else {
+        // Fused cross-entropy partials over this tile's BN vocabulary columns:
+        // per row the max and the sum of exp(logit - max), plus the target
+        // logit when the target column lies in this tile.
+        __shared__ float part_m[2][BM], part_s[2][BM];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int row = m0 + lrow;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (col < N) mx = fmaxf(mx, acc[i][j][r]);
+                }
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float se = 0.f;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (col < N) se += __expf(acc[i][j][r] - mx);
+                }
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+                if (lr == 0) {
+                    part_m[wn][lrow] = mx;
+                    part_s[wn][lrow] = se;
+                }
+                if (row < M && (row % g.S) != g.S - 1) {
+                    const int target = g.tokens[row + 1];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int col = n0 + wn * WN + j * 32 + lr;
+                        if (col == target) g.lm_pick[row] = acc[i][j][r];
+                    }
+                }
+            }
+        __syncthreads();
+        for (int lrow = tid; lrow < BM; lrow += kThreads) {
+            const int row = m0 + lrow;
+            if (row >= M) continue;
+            const float m1 = part_m[0][lrow], m2 = part_m[1][lrow];
+            const float mx = fmaxf(m1, m2);
+            float se = 0.f;
+            if (m1 > -INFINITY) se += part_s[0][lrow] * __expf(m1 - mx);
+            if (m2 > -INFINITY) se += part_s[1][lrow] * __expf(m2 - mx);
+            g.lm_max[(size_t)tn * M + row] = mx;
+            g.lm_sum[(size_t)tn * M + row] = se;
+        }
+    }
+}
+
+// Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1,
+// tile partials combined in fixed order; each block sums its 256 rows in fp64.
+__global__ __launch_bounds__(kThreads) void ce_rows_kernel(const float* __restrict__ lm_max,
+                                                            const float* __restrict__ lm_sum,
+                                                            const float* __restrict__ lm_pick, int n_tiles, int M,
+                                                            int S, double* __restrict__ block_sum)
+{
+    __shared__ double red[4];
+    const int row = blockIdx.x * kThreads + threadIdx.x;
+    double v = 0.0;
+    if (row < M && row % S != S - 1) {
+        float mx = -INFINITY;
+        for (int t = 0; t < n_tiles; ++t) mx = fmaxf(mx, lm_max[(size_t)t * M + row]);
+        double se = 0.0;
+        for (int t = 0; t < n_tiles; ++t) {
+            const float m = lm_max[(size_t)t * M + row];
+            if (m > -INFINITY) se += (double)lm_sum[(size_t)t * M + row] * exp((double)m - (double)mx);
+        }
+        v = ((double)mx + log(se)) - (double)lm_pick[row];
+    }
+    v = wave_sumd(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) block_sum[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// loss = (sum of block sums, fixed order) / (B (S-1))
+__global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __restrict__ block_sum, int n_blocks,
+                                                             int M, int S, double* __restrict__ loss)
+{
+    __shared__ double red[4];
+    double v = 0.0;
+    for (int i = threadIdx.x; i < n_blocks; i += kThreads) v += block_sum[i];
+    v = wave_sumd(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) *loss = (((red[0] + red[1]) + red[2]) + red[3]) / (double)((M / S) * (S - 1));
+}
+
+// ============================================================ attention
+// Causal softmax(Q K^T / sqrt(dh)) V per (sequence, head), flash style.  The
+// wave computes S^T = K Q^T for 32 queries (one per lane column) so the
+// running max / sum of each query live in one lane; P^T goes straight from
+// the accumulators into the B operand of O^T = V^T P^T (the contraction
+// order over keys is the same permutation on both operands).  P is rounded to
+// bf16 for the MFMA; max, sums and rescaling are fp32.
+// Block: 4 waves x 32 queries = 128 queries; keys in tiles of 32.
+template <int DH>
+__global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H,
+                                                              bf16_t* __restrict__ out)
+{
+    constexpr int BQ = 128, BKV = 32;
+    constexpr int KS = DH / 16;   // MFMA k-steps over the head dim for S^T
+    constexpr int OT = DH / 32;   // 32-row blocks of O^T
+    constexpr int LDK = DH + 8;   // K tile row (bf16), padded
+    constexpr int LDV = BKV + 8;  // V^T tile row (bf16), padded
+    __shared__ __align__(16) bf16_t Ks[BKV * LDK];
+    __shared__ __align__(16) bf16_t Vt[DH * LDV];
+
+    const int qblocks = (S + BQ - 1) / BQ;
+    // heaviest (latest) query blocks first
+    const int qb = qblocks - 1 - (blockIdx.x % qblocks);
+    const int bh = blockIdx.x / qblocks;
+    const int b = bh / H, hd = bh % H;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int q0 = qb * BQ;
+    const int qw = q0 + wave * 32;  // this wave's first query
+    const int myq = qw + lr;        // this lane's query (S^T column)
+    const size_t row_stride = 3 * (size_t)d;
+    const bf16_t* base = qkv + (size_t)b * S * row_stride;
+    const int qoff = hd * DH, koff = d + hd * DH, voff = 2 * d + hd * DH;
+    const float scale = 1.0f / sqrtf((float)DH);
+
+    // Q^T as the B operand: lane (lr = query, lh) holds dh 8 lh + 16 ks .. +7
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (myq < S)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(base + (size_t)myq * row_stride + qoff + 16 * ks + 8 * lh);
+        else
+            qf[ks] = bf16x8{};
+    }
+    f32x16 o[OT];
+#pragma unroll
+    for (int t = 0; t < OT; ++t) o[t] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int kv_end = min(S, q0 + BQ);  // causal: keys < last query of the block
+    for (int k0 = 0; k0 < kv_end; k0 += BKV) {
+        __syncthreads();
+        // K tile [BKV][DH] and V^T tile [DH][BKV]
+        for (int c = tid; c < BKV * DH / 8; c += kThreads) {
+            const int kr = c / (DH / 8), dc = 8 * (c % (DH / 8));
+            const int key = k0 + kr;
+            uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (key < S) {
+                kv = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
+                vv = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + voff + dc);
+            }
+            *reinterpret_cast<uint4*>(Ks + kr * LDK + dc) = kv;
+            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Vt[(dc + 2 * e) * LDV + kr] = (bf16_t)(w4[e] & 0xFFFFu);
+                Vt[(dc + 2 * e + 1) * LDV + kr] = (bf16_t)(w4[e] >> 16);
+            }
+        }
+        __syncthreads();
+        if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
+        // S^T [32 keys][32 queries]
+        f32x16 st = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + lr * LDK + 16 * ks + 8 * lh);
+            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st, 0, 0, 0);
+        }
+        // element r: key k0 + 8 (r/4) + 4 lh + r%4, query myq
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            float v = st[r] * scale;
+            if (key > myq || key >= S) v = -INFINITY;
+            st[r] = v;
+            tmax = fmaxf(tmax, v);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+        float psum = 0.f;
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = (st[r] == -INFINITY) ? 0.f : __expf(st[r] - m_new);
+            pv[r] = round_bf(e);
+            psum += pv[r];
+        }
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < OT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        // O^T += V^T P^T over the 32 keys in two MFMA k-steps; step s uses
+        // accumulator elements 8s .. 8s+7, i.e. keys 16 s + 8 (t/4) + 4 lh + t%4
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 pb;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pb[t] = (__bf16)pv[8 * s + t];
+#pragma unroll
+            for (int t = 0; t < OT; ++t) {
+                // A = V^T rows dh = 32 t + lr, the same 8 keys in the same order
+                const bf16_t* vr = Vt + (32 * t + lr) * LDV + 16 * s + 4 * lh;
+                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+                const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[t], 0, 0, 0);
+            }
+        }
+    }
+    if (myq >= S) return;
+    const float inv = 1.0f / l_run;
+    // O^T element r of block t: dh 32 t + 8 (r/4) + 4 lh + r%4, query myq
+    bf16_t* dst = out + ((size_t)b * S + myq) * d + hd * DH;
+#pragma unroll
+    for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[32 * t + 8 * (r >> 2) + 4 * lh + (r & 3)] = f2bf(o[t][r] * inv);
+}
+
+// ============================================================ host side
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+template <int BM, int BN, int EPI, bool PERT>
+zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
+{
+    constexpr int LDK = 64 + 8;
+    const size_t lds = (size_t)(2 * BM * LDK + 2 * BN * LDK) * sizeof(bf16_t);
+    auto kern = gemm_bf16_kernel<BM, BN, EPI, PERT>;
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
+        attr = true;
+    }
+    const int blocks = cdiv(gp.M, BM) * cdiv(gp.N, BN);
+    KernelTimer timer(fam, s);
+    kern<<<blocks, kThreads, lds, s>>>(gp, p);
+    return check_launch("bf16 GEMM");
+}
+
+// Tile choice: 256x256 when the grid still fills the 256 CUs, else 128x128.
+template <int EPI, bool PERT>
+zo_status gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
+{
+    if constexpr (EPI != EPI_LMHEAD) {
+        const long big = (long)cdiv(gp.M, 256) * cdiv(gp.N, 256);
+        if (big >= 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
+    }
+    return launch_gemm<128, 128, EPI, PERT>(gp, p, s, fam);
+}
+
+template <int EPI>
+zo_status gemm_any(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
+{
+    return p.on ? gemm<EPI, true>(gp, p, s, fam) : gemm<EPI, false>(gp, p, s, fam);
+}
+
+struct DecoderWs {
+    bf16_t *h, *x, *qkv, *att, *u;
+    float *lm_max, *lm_sum, *lm_pick;
+    double* ce_part;
+    size_t bytes;
+};
+
+constexpr int kLmTile = 128;
+
+DecoderWs carve(const zo_model_desc& d, void* base)
+{
+    const size_t M = (size_t)d.batch * d.seq;
+    const size_t D = d.d_model, F = d.ffn;
+    const size_t tiles = cdiv((int)d.vocab, kLmTile);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return (char*)base + o;
+    };
+    DecoderWs w;
+    w.h = (bf16_t*)take(M * D * 2);
+    w.x = (bf16_t*)take(M * D * 2);
+    w.qkv = (bf16_t*)take(M * 3 * D * 2);
+    w.att = (bf16_t*)take(M * D * 2);
+    w.u = (bf16_t*)take(M * F * 2);
+    w.lm_max = (float*)take(tiles * M * 4);
+    w.lm_sum = (float*)take(tiles * M * 4);
+    w.lm_pick = (float*)take(M * 4);
+    w.ce_part = (double*)take((M + kThreads - 1) / kThreads * 8);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
+zo_status decoder_check(const zo_model_desc& d)
+{
+    const int64_t dh = d.d_model / d.heads;
+    if (dh != 64 && dh != 128) return fail(ZO_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    if (d.d_model % 64 || d.ffn % 64) return fail(ZO_ERR_UNSUPPORTED, "d_model and ffn must be multiples of 64");
+    if (d.d_model > kThreads * kLnMaxPer) return fail(ZO_ERR_UNSUPPORTED, "d_model too large for LayerNorm");
+    if (d.batch * d.seq > (1 << 24) || d.vocab > (1 << 24)) return fail(ZO_ERR_UNSUPPORTED, "shape too large");
+    return ZO_OK;
+}
+
+size_t decoder_workspace(const zo_model_desc& d) { return carve(d, nullptr).bytes; }
+
+zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
+                          hipStream_t s)
+{
+    const zo_model_desc& d = m.desc;
+    const int B = (int)b.batch, S = (int)b.seq, D = (int)d.d_model, F = (int)d.ffn, V = (int)d.vocab;
+    const int H = (int)d.heads, dh = D / H, L = (int)d.layers;
+    const int M = B * S;
+    DecoderWs w = carve(d, m.workspace);
+    const bf16_t* P = (const bf16_t*)m.params;
+    // tensor order: tok_emb, pos_emb, per layer (ln1_g, ln1_b, w_qkv, w_o, ln2_g, ln2_b, w_up, w_down), lnf_g, lnf_b
+    auto off = [&](int idx) { return m.offsets[idx]; };
+    const int n_evals = n == 0 ? 1 : n;
+    for (int e = 0; e < n_evals; ++e) {
+        Pert p = {};
+        if (n) {
+            p.key = Key{(uint32_t)perts[e].seed, (uint32_t)(perts[e].seed >> 32)};
+            p.probe = perts[e].probe;
+            p.sigma = perts[e].sigma;
+            p.on = 1;
+        }
+        {
+            KernelTimer t("embed", s);
+            embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, P + off(0), off(0), P + off(1), off(1), p, w.h);
+            if (zo_status st = check_launch("embed")) return st;
+        }
+        for (int l = 0; l < L; ++l) {
+            const int t0 = 2 + 8 * l;
+            {
+                KernelTimer t("layernorm", s);
+                layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p,
+                                                         w.x);
+                if (zo_status st = check_launch("layernorm")) return st;
+            }
+            GemmParams gq = {};
+            gq.A = w.x; gq.W = P + off(t0 + 2); gq.w_dir = off(t0 + 2); gq.C = w.qkv; gq.M = M; gq.N = 3 * D; gq.K = D;
+            if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
+            {
+                KernelTimer t("attention", s);
+                const int blocks = B * H * cdiv(S, 128);
+                if (dh == 64)
+                    attention_kernel<64><<<blocks, kThreads, 0, s>>>(w.qkv, S, D, H, w.att);
+                else
+                    attention_kernel<128><<<blocks, kThreads, 0, s>>>(w.qkv, S, D, H, w.att);
+                if (zo_status st = check_launch("attention")) return st;
+            }
+            GemmParams go = {};
+            go.A = w.att; go.W = P + off(t0 + 3); go.w_dir = off(t0 + 3); go.C = w.h; go.M = M; go.N = D; go.K = D;
+            if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
+            {
+                KernelTimer t("layernorm", s);
+                layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5),
+                                                         off(t0 + 5), p, w.x);
+                if (zo_status st = check_launch("layernorm")) return st;
+            }
+            GemmParams gu = {};
+            gu.A = w.x; gu.W = P + off(t0 + 6); gu.w_dir = off(t0 + 6); gu.C = w.u; gu.M = M; gu.N = F; gu.K = D;
+            zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16")
+                                                : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16");
+            if (su) return su;
+            GemmParams gd = {};
+            gd.A = w.u; gd.W = P + off(t0 + 7); gd.w_dir = off(t0 + 7); gd.C = w.h; gd.M = M; gd.N = D; gd.K = F;
+            if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16")) return st;
+        }
+        const int tf = 2 + 8 * L;
+        {
+            KernelTimer t("layernorm", s);
+            layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x);
+            if (zo_status st = check_launch("layernorm")) return st;
+        }
+        GemmParams gl = {};
+        gl.A = w.x; gl.W = P + off(0); gl.w_dir = off(0); gl.M = M; gl.N = V; gl.K = D;
+        gl.lm_max = w.lm_max; gl.lm_sum = w.lm_sum; gl.lm_pick = w.lm_pick; gl.tokens = b.tokens; gl.S = S;
+        if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
+        {
+            KernelTimer t("reduce", s);
+            const int nb = cdiv(M, kThreads);
+            ce_rows_kernel<<<nb, kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, cdiv(V, kLmTile), M, S, w.ce_part);
+            ce_final_kernel<<<1, kThreads, 0, s>>>(w.ce_part, nb, M, S, loss + e);
+            if (zo_status st = check_launch("ce reduce")) return st;
+        }
+    }
+    return ZO_OK;
+}
+
+// ------------------------------------------------------------ debug entries
+zo_status debug_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int epi, hipStream_t s)
+{
+    if (!A || !W || !C || M <= 0 || N <= 0 || K <= 0) return fail(ZO_ERR_INVALID, "bad GEMM arguments");
+    if (K % 64) return fail(ZO_ERR_UNSUPPORTED, "K must be a multiple of 64");
+    GemmParams g = {};
+    g.A = (const bf16_t*)A; g.W = (const bf16_t*)W; g.C = (bf16_t*)C; g.M = M; g.N = N; g.K = K;
+    Pert p = {};
+    switch (epi) {
+        case 0: return gemm_any<EPI_STORE>(g, p, s, "gemm_bf16");
+        case 1: return gemm_any<EPI_GELU>(g, p, s, "gemm_bf16");
+        case 2: return gemm_any<EPI_RELU>(g, p, s, "gemm_bf16");
+        case 3: return gemm_any<EPI_RESID>(g, p, s, "gemm_bf16");
+    }
+    return fail(ZO_ERR_INVALID, "epilogue must be 0..3");
+}
+
+zo_status debug_attention(const void* qkv, void* out, int B, int S, int H, int dh, hipStream_t s)
+{
+    if (!qkv || !out || B <= 0 || S <= 0 || H <= 0) return fail(ZO_ERR_INVALID, "bad attention arguments");
+    if (dh != 64 && dh != 128) return fail(ZO_ERR_UNSUPPORTED, "head dim must be 64 or 128");
+    const int blocks = B * H * cdiv(S, 128);
+    KernelTimer t("attention", s);
+    if (dh == 64)
+        attention_kernel<64><<<blocks, kThreads, 0, s>>>((const bf16_t*)qkv, S, H * dh, H, (bf16_t*)out);
+    else
+        attention_kernel<128><<<blocks, kThreads, 0, s>>>((const bf16_t*)qkv, S, H * dh, H, (bf16_t*)out);
+    return check_launch("attention");
+}
+
+zo_status debug_layernorm(const void* h, const void* g, const void* b, void* x, int rows, int d, hipStream_t s)
+{
+    if (!h || !g || !b || !x || rows <= 0 || d <= 0) return fail(ZO_ERR_INVALID, "bad LayerNorm arguments");
+    if (d > kThreads * kLnMaxPer) return fail(ZO_ERR_UNSUPPORTED, "row too long");
+    Pert p = {};
+    KernelTimer t("layernorm", s);
+    layernorm_kernel<<<rows, kThreads, 0, s>>>((const bf16_t*)h, d, (const bf16_t*)g, 0, (const bf16_t*)b, 0, p,
+                                               (bf16_t*)x);
+    return check_launch("layernorm");
+}
+
+}  // namespace zo

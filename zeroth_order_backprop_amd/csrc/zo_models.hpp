@@ -41,4 +41,9 @@ size_t decoder_workspace(const zo_model_desc& d);
 zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
                           hipStream_t s);
 
+// kernel-level debug entry points (zo_decoder.hip)
+zo_status debug_gemm_bf16(const void* A, const void* W, void* C, int M, int N, int K, int epi, hipStream_t s);
+zo_status debug_attention(const void* qkv, void* out, int B, int S, int H, int dh, hipStream_t s);
+zo_status debug_layernorm(const void* h, const void* g, const void* b, void* x, int rows, int d, hipStream_t s);
+
 }  // namespace zo

@@ -21,6 +21,7 @@ EXPORTS = [
     "zo_forward_loss", "zo_update", "zo_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
     "zo_timing_enable", "zo_timing_reset", "zo_timing_query",
+    "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
 ]
 
 
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
         "zo_gscalar": [P, U32, F, P, P],
         "zo_debug_rng": [U64, U32, U64, U64, P, P, P],
         "zo_debug_box_muller": [P, U64, P, P],
+        "zo_debug_gemm_bf16": [P, P, P, I32, I32, I32, I32, P],
+        "zo_debug_attention": [P, P, I32, I32, I32, I32, P],
+        "zo_debug_layernorm": [P, P, P, P, I32, I32, P],
         "zo_timing_enable": [I32],
         "zo_timing_reset": [],
         "zo_timing_query": [ctypes.c_char_p, P, P],
@@ -136,6 +140,19 @@ def debug_rng(seed, probe, j0, n, words=None, z=None, stream=None):
 
 def debug_box_muller(pairs, n_pairs, z, stream=None):
     check(lib().zo_debug_box_muller(_ptr(pairs), n_pairs, _ptr(z), _stream(stream)), "zo_debug_box_muller")
+
+
+def debug_gemm_bf16(A, W, C, M, N, K, epi=0, stream=None):
+    check(lib().zo_debug_gemm_bf16(_ptr(A), _ptr(W), _ptr(C), M, N, K, epi, _stream(stream)), "zo_debug_gemm_bf16")
+
+
+def debug_attention(qkv, out, B, S, H, dh, stream=None):
+    check(lib().zo_debug_attention(_ptr(qkv), _ptr(out), B, S, H, dh, _stream(stream)), "zo_debug_attention")
+
+
+def debug_layernorm(h, g, b, x, rows, d, stream=None):
+    check(lib().zo_debug_layernorm(_ptr(h), _ptr(g), _ptr(b), _ptr(x), rows, d, _stream(stream)),
+          "zo_debug_layernorm")
 
 
 # ------------------------------------------------------------------ timing
