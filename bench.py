@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="mlp", choices=["mlp", "lsq"])
+    p.add_argument("--workload", default="mlp", choices=["mlp", "lsq", "gpt", "opt1.3b", "opt30b"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-passes", action="store_true", help="skip the perturb/update pass measurement")
     return p.parse_args()
@@ -91,6 +91,51 @@ def build_lsq(torch, zo, inputs):
         "oracle_batch": {"X": inp["X"], "Y": inp["Y"]}, "arena": arena,
     }
     return model, batch, (x, y), info
+
+
+DECODERS = {
+    # name: layers, d, heads, ffn, vocab, batch, seq, act, probes
+    "gpt": (12, 768, 12, 3072, 32000, 8, 512, "gelu", 32),
+    "opt1.3b": (24, 2048, 32, 8192, 50272, 8, 2048, "relu", 1),
+    "opt30b": (48, 7168, 56, 28672, 50272, 8, 2048, "relu", 1),
+}
+
+
+def build_decoder(torch, zo, inputs, name):
+    L, D, H, F, V, B, S, act, N = DECODERS[name]
+    desc = zo.make_desc(zo.ZO_MODEL_DECODER, batch=B, seq=S, layers=L, d_model=D, heads=H, ffn=F, vocab=V,
+                        max_seq=S, act=zo.ZO_ACT_GELU if act == "gelu" else zo.ZO_ACT_RELU)
+    layout, total = zo.param_layout(desc)
+    arena = torch.empty(total, dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    for pname, off, shape in layout:
+        n = 1
+        for x in shape:
+            n *= x
+        view = arena[off:off + n]
+        if pname.endswith("_g"):
+            view.fill_(1.0)
+        elif pname.endswith("_b"):
+            view.zero_()
+        else:
+            view.normal_(0.0, 0.02, generator=gen)
+    model = zo.Model(desc, arena)
+    tok = torch.from_numpy(inputs.zipf_tokens(0, B, S, V)).cuda()
+    batch = zo.make_batch(tokens=tok, batch=B, seq=S)
+    M = B * S
+    gemm_flops = L * (2.0 * M * D * 3 * D + 2.0 * M * D * D + 2 * 2.0 * M * D * F)
+    attn_flops = L * 2.0 * B * H * S * S * (D // H)  # causal half of 4 B H S^2 dh
+    head_flops = 2.0 * M * D * V
+    info = {
+        "workload": f"decoder {name}: {L} layers, d={D}, {H} heads, FFN {F}, vocab {V}, bf16; batch {B} x seq {S} "
+                    f"Zipf(1.1) tokens; N={N} probes, eps=1e-3, lr=1e-3; in-place mode",
+        "probes": N, "eps": 1e-3, "lr": 1e-3, "mode": "inplace", "batch": B, "params": int(total),
+        "flops_per_eval": gemm_flops + attn_flops + head_flops, "gemm_flops_per_eval": gemm_flops,
+        "head_flops_per_eval": head_flops, "attn_flops_per_eval": attn_flops,
+        "dtype": "bf16", "kernel": "gemm_bf16", "peak_tflops": BF16_PEAK_TFLOPS,
+    }
+    return model, batch, (tok,), info
 
 
 def measure_passes(torch, zo):
@@ -170,11 +215,14 @@ def main():
 
     from zeroth_order_backprop_amd import inputs, zo
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
+    if args.workload in DECODERS:
+        model, batch, keep, info = build_decoder(torch, zo, inputs, args.workload)
+    else:
+        model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     N = info["probes"]
     losses = torch.zeros(2 * N, dtype=torch.float64, device="cuda")
     g = torch.zeros(N, dtype=torch.float64, device="cuda")
-    mode = zo.ZO_MODE_FUSED
+    mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
     for t in range(args.warmup):
         model.step(batch, t, N, info["eps"], info["lr"], mode, losses, g)
     torch.cuda.synchronize()
@@ -194,13 +242,25 @@ def main():
     evals_per_s = 2 * N * args.steps / (total_ms * 1e-3)
     k_ms, k_n = zo.timing_query(info["kernel"])
     k_avg_s = k_ms / k_n * 1e-3
-    flops_per_launch = 2 * N * info["flops_per_eval"]
+    if info["kernel"] == "gemm_bf16":
+        # layer GEMMs of all evaluations: algorithmic flops / summed launch time
+        flops_per_launch = 2 * N * info["gemm_flops_per_eval"] * args.steps / k_n
+    else:
+        flops_per_launch = 2 * N * info["flops_per_eval"]
     achieved = flops_per_launch / k_avg_s / 1e12
     kernels = {}
-    for fam in ("gemm_f32", "reduce", "update", "perturb"):
+    for fam in ("gemm_f32", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
+                "perturb"):
         ms, n = zo.timing_query(fam)
         if n:
-            kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / args.steps}
+            kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / args.steps,
+                            "ms_per_step": round(ms / args.steps, 3)}
+    if "lm_head" in kernels:
+        t = kernels["lm_head"]["ms_per_step"] * 1e-3
+        kernels["lm_head"]["TFLOP/s"] = round(2 * N * info["head_flops_per_eval"] / t / 1e12, 1)
+    if "attention" in kernels:
+        t = kernels["attention"]["ms_per_step"] * 1e-3
+        kernels["attention"]["TFLOP/s"] = round(2 * N * info["attn_flops_per_eval"] / t / 1e12, 1)
     zo.timing_reset()
     final = losses.cpu().numpy()
     line = {
@@ -212,15 +272,16 @@ def main():
                    "mode": info["mode"], "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
                      "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
-                     "traffic": TRAFFIC.get(KERNEL_REV[args.workload] or "", None),
-                     "kernel": f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch",
+                     "traffic": TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
+                     "kernel": (f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch"
+                                if info["kernel"] == "gemm_f32" else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
                      "avg_launch_us": round(k_avg_s * 1e6, 2)},
         "kernels": kernels,
         "last_losses_mean": float(final.mean()),
     }
     if not args.no_passes:
         line["perturb_update"] = measure_passes(torch, zo)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and "oracle_desc" in info:
         line["cpu_baseline"] = cpu_baseline(info)
     print(json.dumps(line), flush=True)
 
