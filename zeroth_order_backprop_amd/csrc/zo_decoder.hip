@@ -210,6 +210,94 @@ __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& t
     tn = r / gsize;
 }
 
+// Writes one block tile's accumulators (see the GEMM kernels below).
+// Accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr.
+template <int BM, int BN, int EPI, int RB, int CB>
+__device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn)
+{
+    constexpr int WM = BM / 2, WN = BN / 2;
+    const int M = g.M, N = g.N;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+    if constexpr (EPI != EPI_LMHEAD) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (row >= M || col >= N) continue;
+                    float v = acc[i][j][r];
+                    bf16_t* dst = g.C + (size_t)row * N + col;
+                    if constexpr (EPI == EPI_GELU) v = gelu_f(v);
+                    if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
+                    if constexpr (EPI == EPI_RESID) v = bf2f(*dst) + round_bf(v);
+                    *dst = f2bf(v);
+                }
+    } else {
+        // Fused cross-entropy partials over this tile's BN vocabulary columns:
+        // per row the max and the sum of exp(logit - max), plus the target
+        // logit when the target column lies in this tile.
+        __shared__ float part_m[2][BM], part_s[2][BM];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                const int row = m0 + lrow;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (col < N) mx = fmaxf(mx, acc[i][j][r]);
+                }
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float se = 0.f;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (col < N) se += __expf(acc[i][j][r] - mx);
+                }
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+                if (lr == 0) {
+                    part_m[wn][lrow] = mx;
+                    part_s[wn][lrow] = se;
+                }
+                if (row < M && (row % g.S) != g.S - 1) {
+                    const int target = g.tokens[row + 1];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int col = n0 + wn * WN + j * 32 + lr;
+                        if (col == target) g.lm_pick[row] = acc[i][j][r];
+                    }
+                }
+            }
+        __syncthreads();
+        for (int lrow = tid; lrow < BM; lrow += kThreads) {
+            const int row = m0 + lrow;
+            if (row >= M) continue;
+            const float m1 = part_m[0][lrow], m2 = part_m[1][lrow];
+            const float mx = fmaxf(m1, m2);
+            float se = 0.f;
+            if (m1 > -INFINITY) se += part_s[0][lrow] * __expf(m1 - mx);
+            if (m2 > -INFINITY) se += part_s[1][lrow] * __expf(m2 - mx);
+            g.lm_max[(size_t)tn * M + row] = mx;
+            g.lm_sum[(size_t)tn * M + row] = se;
+        }
+    }
+}
+
+template <int BM, int BN, int EPI, int RB, int CB>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn)
+{
+    gemm_epilogue_impl<BM, BN, EPI, RB, CB>(g, acc, m0, n0, tn);
+}
+
 template <int BM, int BN, int EPI, bool PERT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert p)
 {
@@ -305,77 +393,108 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
         __syncthreads();
     }
 
-    // accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr
-    if constexpr (EPI != EPI_LMHEAD) {
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
+}
+
+// The same product with the stage tiles written to LDS directly by the loads
+// (global_load_lds, 16 B per lane) for the stored-weight path: no register
+// staging, STAGES-deep ring of BK = 32 slices, prefetch distance STAGES - 1.
+// LDS rows are 64 B (4 chunks of 16 B) and unpadded; chunk c of row r sits at
+// position c ^ ((r >> 2) & 3), so the 32 rows a fragment read touches spread
+// over all banks.  Rows past M or N load a clamped (valid) row and are never
+// stored.  The barrier is a bare s_barrier after each wave has waited for its
+// own share of the stage (vmcnt), so the later stages stay in flight.
+template <int BM, int BN, int EPI, int STAGES>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
+{
+    constexpr int BK = 32;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int A_INS = BM * 4 / kThreads, B_INS = BN * 4 / kThreads;
+    constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
+    constexpr int STAGE = (BM + BN) * BK;
+    static_assert(A_INS * kThreads == BM * 4 && B_INS * kThreads == BN * 4, "tile / thread mismatch");
+    extern __shared__ __align__(16) bf16_t lds[];
+
+    const int M = g.M, N = g.N, K = g.K;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    f32x16 acc[RB][CB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int j = 0; j < CB; ++j)
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+
+    const int KT = K / BK;
+    auto issue = [&](int kt) {
+        bf16_t* sa = lds + (kt % STAGES) * STAGE;
+        bf16_t* sb = sa + BM * BK;
+        const int k0 = kt * BK;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int col = n0 + wn * WN + j * 32 + lr;
-                    if (row >= M || col >= N) continue;
-                    float v = acc[i][j][r];
-                    bf16_t* dst = g.C + (size_t)row * N + col;
-                    if constexpr (EPI == EPI_GELU) v = gelu_f(v);
-                    if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
-                    if constexpr (EPI == EPI_RESID) v = bf2f(*dst) + round_bf(v);
-                    *dst = f2bf(v);
-                }
-    } else {
-        // Fused cross-entropy partials over this tile's BN vocabulary columns:
-        // per row the max and the sum of exp(logit - max), plus the target
-        // logit when the target column lies in this tile.
-        __shared__ float part_m[2][BM], part_s[2][BM];
+        for (int j = 0; j < A_INS; ++j) {
+            const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+            const int gm = min(m0 + row, M - 1);
+            const bf16_t* src = g.A + (size_t)gm * K + k0 + 8 * lc;
+            bf16_t* dst = sa + (j * kThreads + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+        for (int j = 0; j < B_INS; ++j) {
+            const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+            const int gn = min(n0 + row, N - 1);
+            const bf16_t* src = g.W + (size_t)gn * K + k0 + 8 * lc;
+            bf16_t* dst = sb + (j * kThreads + wave * 64) * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+    // vmcnt wait with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+    auto wait_vm = [](int n) {
+        if (n >= 2 * INS) __builtin_amdgcn_s_waitcnt(((2 * INS) & 15) | (((2 * INS) >> 4) << 14) | (7 << 4) | (15 << 8));
+        else if (n >= INS) __builtin_amdgcn_s_waitcnt((INS & 15) | ((INS >> 4) << 14) | (7 << 4) | (15 << 8));
+        else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    };
+    static_assert(2 * INS < 64, "vmcnt range");
+    static_assert(STAGES <= 4, "at most two stages may stay in flight at a wait");
+
+    for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
+    for (int kt = 0; kt < KT; ++kt) {
+        // stages kt+1 .. min(kt+STAGES-2, KT-1) may remain outstanding
+        const int ahead = min(STAGES - 2, KT - 1 - kt);
+        wait_vm(ahead * INS);
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+        const bf16_t* sa = lds + (kt % STAGES) * STAGE;
+        const bf16_t* sb = sa + BM * BK;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                const int row = m0 + lrow;
-                float mx = -INFINITY;
+        for (int ks = 0; ks < 2; ++ks) {
+            const int lc = 2 * ks + lh;
+            bf16x8 af[RB], bfr[CB];
 #pragma unroll
-                for (int j = 0; j < CB; ++j) {
-                    const int col = n0 + wn * WN + j * 32 + lr;
-                    if (col < N) mx = fmaxf(mx, acc[i][j][r]);
-                }
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-                float se = 0.f;
-#pragma unroll
-                for (int j = 0; j < CB; ++j) {
-                    const int col = n0 + wn * WN + j * 32 + lr;
-                    if (col < N) se += __expf(acc[i][j][r] - mx);
-                }
-#pragma unroll
-                for (int o = 16; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
-                if (lr == 0) {
-                    part_m[wn][lrow] = mx;
-                    part_s[wn][lrow] = se;
-                }
-                if (row < M && (row % g.S) != g.S - 1) {
-                    const int target = g.tokens[row + 1];
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) {
-                        const int col = n0 + wn * WN + j * 32 + lr;
-                        if (col == target) g.lm_pick[row] = acc[i][j][r];
-                    }
-                }
+            for (int i = 0; i < RB; ++i) {
+                const int row = wm * WM + i * 32 + lr;
+                af[i] = *reinterpret_cast<const bf16x8*>(sa + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8);
             }
-        __syncthreads();
-        for (int lrow = tid; lrow < BM; lrow += kThreads) {
-            const int row = m0 + lrow;
-            if (row >= M) continue;
-            const float m1 = part_m[0][lrow], m2 = part_m[1][lrow];
-            const float mx = fmaxf(m1, m2);
-            float se = 0.f;
-            if (m1 > -INFINITY) se += part_s[0][lrow] * __expf(m1 - mx);
-            if (m2 > -INFINITY) se += part_s[1][lrow] * __expf(m2 - mx);
-            g.lm_max[(size_t)tn * M + row] = mx;
-            g.lm_sum[(size_t)tn * M + row] = se;
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const int row = wn * WN + j * 32 + lr;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     }
+    // the epilogue may reuse LDS (LM head): every wave must be done reading it
+    asm volatile("s_barrier" ::: "memory");
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
 }
 
 // Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1,
@@ -558,18 +677,35 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 template <int BM, int BN, int EPI, bool PERT>
 zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
-    constexpr int LDK = 64 + 8;
-    const size_t lds = (size_t)(2 * BM * LDK + 2 * BN * LDK) * sizeof(bf16_t);
-    auto kern = gemm_bf16_kernel<BM, BN, EPI, PERT>;
-    static bool attr = false;
-    if (!attr) {
-        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
-        attr = true;
-    }
     const int blocks = cdiv(gp.M, BM) * cdiv(gp.N, BN);
-    KernelTimer timer(fam, s);
-    kern<<<blocks, kThreads, lds, s>>>(gp, p);
+    if constexpr (PERT) {
+        // perturbed tiles pass through registers: z is applied before the LDS store
+        constexpr int LDK = 64 + 8;
+        const size_t lds = (size_t)(2 * BM * LDK + 2 * BN * LDK) * sizeof(bf16_t);
+        auto kern = gemm_bf16_kernel<BM, BN, EPI, true>;
+        static bool attr = false;
+        if (!attr) {
+            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+                hipSuccess)
+                return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
+            attr = true;
+        }
+        KernelTimer timer(fam, s);
+        kern<<<blocks, kThreads, lds, s>>>(gp, p);
+    } else {
+        constexpr int STAGES = 4;
+        const size_t lds = (size_t)STAGES * (BM + BN) * 32 * sizeof(bf16_t);
+        auto kern = gemm_bf16_dma_kernel<BM, BN, EPI, STAGES>;
+        static bool attr = false;
+        if (!attr) {
+            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+                hipSuccess)
+                return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
+            attr = true;
+        }
+        KernelTimer timer(fam, s);
+        kern<<<blocks, kThreads, lds, s>>>(gp);
+    }
     return check_launch("bf16 GEMM");
 }
 
