@@ -192,6 +192,29 @@ def param_layout(desc: dict):
     return out, _align(off)
 
 
+class LazyParams:
+    """Tensor-by-tensor fp64 view of a bf16 arena held elsewhere (e.g. a large
+    model in device memory): `fetch(offset, count)` returns the bf16 bit
+    patterns of arena[offset:offset+count].  Only `keep` tensors are cached,
+    so a forward pass holds one layer's weights at a time."""
+
+    def __init__(self, desc: dict, fetch, keep=("tok_emb",)):
+        self.layout = {name: (off, shape) for name, off, shape in param_layout(desc)[0]}
+        self.fetch = fetch
+        self.keep = set(keep)
+        self.cache = {}
+
+    def __getitem__(self, name):
+        if name in self.cache:
+            return self.cache[name]
+        off, shape = self.layout[name]
+        bits = self.fetch(off, int(np.prod(shape)))
+        v = bf16_bits_to_f64(bits).reshape(shape)
+        if name in self.keep:
+            self.cache[name] = v
+        return v
+
+
 def unpack(desc: dict, arena_f64: np.ndarray) -> dict:
     layout, _ = param_layout(desc)
     return {name: arena_f64[off:off + int(np.prod(shape))].reshape(shape)

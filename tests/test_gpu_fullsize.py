@@ -1,0 +1,245 @@
+"""GPU parity at the configured full sizes, in the launch configuration the
+benchmark times (GPT-small, OPT-1.3B and OPT-30B shapes, bf16 arenas of
+109.9M / 1.315B / 29.97B parameters in HBM).
+
+The oracle cannot evaluate these models on whole batches in seconds, so:
+* perturb and update run on the whole arena and are checked on sampled
+  elements (random, both ends, and indices past 2^34 where the counter's high
+  word is non-zero);
+* real-shape GEMMs are checked on sampled outputs, each an O(K) dot product;
+* forward losses run through the full-width models at reduced tokens (the
+  GPT-small shape on its full 8 x 512 batch);
+* the full in-place step (8 x 2048 tokens) is checked through properties that
+  hold at any size: W is restored by +eps / -2 eps / +eps exactly as the
+  oracle restores the sampled elements, and the update moved every sampled
+  element by the same multiple c of its direction value, c = -lr g / N.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from zeroth_order_backprop_amd import inputs, zo
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ZTOL = 1e-6
+
+SHAPES = {
+    "gpt": dict(layers=12, d=768, heads=12, ffn=3072, vocab=32000, batch=8, seq=512, act="gelu"),
+    "opt1.3b": dict(layers=24, d=2048, heads=32, ffn=8192, vocab=50272, batch=8, seq=2048, act="relu"),
+    "opt30b": dict(layers=48, d=7168, heads=56, ffn=28672, vocab=50272, batch=8, seq=2048, act="relu"),
+}
+
+
+def odesc_of(sh):
+    return {"kind": "decoder", "layers": sh["layers"], "d": sh["d"], "heads": sh["heads"], "ffn": sh["ffn"],
+            "vocab": sh["vocab"], "max_seq": sh["seq"], "act": sh["act"]}
+
+
+class Full:
+    """A full-size model in HBM, weights N(0, 0.02^2) from torch's seeded
+    device generator (LN gain 1, bias 0)."""
+
+    def __init__(self, name):
+        sh = SHAPES[name]
+        self.sh = sh
+        self.desc = zo.make_desc(zo.ZO_MODEL_DECODER, batch=sh["batch"], seq=sh["seq"], layers=sh["layers"],
+                                 d_model=sh["d"], heads=sh["heads"], ffn=sh["ffn"], vocab=sh["vocab"],
+                                 max_seq=sh["seq"], act=zo.ZO_ACT_GELU if sh["act"] == "gelu" else zo.ZO_ACT_RELU)
+        self.layout, self.total = zo.param_layout(self.desc)
+        self.arena = torch.empty(self.total, dtype=torch.bfloat16, device=DEV)
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(1234)
+        for pname, off, shape in self.layout:
+            n = int(np.prod(shape))
+            v = self.arena[off:off + n]
+            if pname.endswith("_g"):
+                v.fill_(1.0)
+            elif pname.endswith("_b"):
+                v.zero_()
+            else:
+                v.normal_(0.0, 0.02, generator=gen)
+        self.model = zo.Model(self.desc, self.arena)
+
+    def bits_at(self, idx: np.ndarray) -> np.ndarray:
+        t = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+        return self.arena.view(torch.int16)[t].cpu().numpy().view(np.uint16)
+
+    def fetch(self, off, count):
+        return self.arena.view(torch.int16)[off:off + count].cpu().numpy().view(np.uint16)
+
+    def close(self):
+        del self.model
+        del self.arena
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+_models = {}
+
+
+def full(name):
+    if name not in _models:
+        for other in list(_models):  # keep one large model resident at a time
+            _models.pop(other).close()
+        _models[name] = Full(name)
+    return _models[name]
+
+
+def teardown_module(module):
+    for name in list(_models):
+        _models.pop(name).close()
+
+
+def sample_indices(total, seed=0, n=1 << 17):
+    rng = np.random.default_rng(seed)
+    idx = [rng.integers(0, total, n, dtype=np.int64), np.arange(0, 4096), np.arange(total - 4096, total)]
+    for edge in (1 << 32, 1 << 34, 3 << 33):
+        if edge + 4096 < total:
+            idx.append(np.arange(edge - 2048, edge + 2048))
+    return np.unique(np.concatenate(idx)).astype(np.uint64)
+
+
+def ulp_bf16(x):
+    a = np.maximum(np.abs(x), 2.0**-126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def check_bf16_boundary(w_before, sigma_times_z, got, want):
+    """GPU and oracle bf16 results may differ only where the exact value lies
+    within |sigma| * (z tolerance) (+ one fp32 rounding) of the rounding
+    midpoint between them."""
+    bad = got != want
+    assert np.mean(bad) < 1e-3
+    if bad.any():
+        exact = w_before[bad] + sigma_times_z[bad]
+        mid = 0.5 * (got[bad] + want[bad])
+        slack = np.abs(sigma_times_z[bad]) * ZTOL * 1.01 + np.spacing(np.abs(exact).astype(np.float32))
+        assert (np.abs(exact - mid) <= slack).all()
+
+
+@pytest.mark.parametrize("name", ["gpt", "opt1.3b", "opt30b"])
+def test_fullsize_perturb_update_sampled(name):
+    m = full(name)
+    idx = sample_indices(m.total)
+    w0 = m.bits_at(idx)
+    eps = float(np.float32(1e-3))
+    m.model.perturb(7, 0, eps)
+    torch.cuda.synchronize()
+    w1 = m.bits_at(idx)
+    want = w0.copy()
+    oracle.lib().oracle_perturb_bf16_at(oracle._ptr(want), oracle._ptr(idx), idx.size, 7, 0, eps)
+    z = oracle.gauss_at(7, 0, idx).astype(np.float64)
+    check_bf16_boundary(oracle.bf16_bits_to_f64(w0), eps * z, oracle.bf16_bits_to_f64(w1),
+                        oracle.bf16_bits_to_f64(want))
+    # fused update with N = 1 over the whole arena
+    g = torch.tensor([3.5], dtype=torch.float64, device=DEV)
+    m.model.update(7, 1, g, 1e-3)
+    torch.cuda.synchronize()
+    w2 = m.bits_at(idx)
+    c = np.array([-float(np.float32(1e-3)) * 3.5])
+    want2 = w1.copy()
+    oracle.lib().oracle_update_bf16_at(oracle._ptr(want2), oracle._ptr(idx), idx.size, 7, 1, oracle._ptr(c))
+    check_bf16_boundary(oracle.bf16_bits_to_f64(w1), c[0] * z, oracle.bf16_bits_to_f64(w2),
+                        oracle.bf16_bits_to_f64(want2))
+
+
+@pytest.mark.parametrize("M,N,K,epi", [(16384, 21504, 7168, 0), (16384, 7168, 28672, 3), (16384, 8192, 2048, 2),
+                                       (4096, 3072, 768, 1)])
+def test_real_shape_gemm_sampled_outputs(M, N, K, epi):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(M + N + K)
+    A = torch.randn(M, K, device=DEV, generator=gen).to(torch.bfloat16)
+    W = (0.02 * torch.randn(N, K, device=DEV, generator=gen)).to(torch.bfloat16)
+    C = torch.randn(M, N, device=DEV, generator=gen).to(torch.bfloat16)
+    rng = np.random.default_rng(K)
+    rows = rng.integers(0, M, 256)
+    cols = rng.integers(0, N, 256)
+    c0 = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
+    zo.debug_gemm_bf16(A, W, C, M, N, K, epi)
+    torch.cuda.synchronize()
+    got = C[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
+    a = A[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    w = W[torch.from_numpy(cols).to(DEV)].float().cpu().numpy().astype(np.float64)
+    prod = np.einsum("ik,ik->i", a, w)
+    acc_err = K * 2.0**-24 * np.einsum("ik,ik->i", np.abs(a), np.abs(w))
+    if epi == 0:
+        want = oracle.bf16_round(prod)
+    elif epi == 1:
+        want = oracle.bf16_round(oracle.gelu_erf(prod))
+    elif epi == 2:
+        want = oracle.bf16_round(np.maximum(prod, 0.0))
+    else:
+        want = oracle.bf16_round(c0 + oracle.bf16_round(prod))
+        acc_err = acc_err + ulp_bf16(np.abs(prod) + acc_err)
+    tol = ulp_bf16(np.maximum(np.abs(got), np.abs(want))) * 1.0001 + 1.2 * acc_err
+    assert (np.abs(got - want) <= tol).all()
+
+
+@pytest.mark.parametrize("name,batch,seq", [("opt1.3b", 1, 128), ("opt30b", 1, 16)])
+def test_fullwidth_forward_reduced_tokens(name, batch, seq):
+    m = full(name)
+    tokens = inputs.zipf_tokens(11, batch, seq, m.sh["vocab"])
+    tok = torch.from_numpy(tokens).to(DEV)
+    b = zo.make_batch(tokens=tok, batch=batch, seq=seq)
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    m.model.forward_loss(b, out)
+    torch.cuda.synchronize()
+    got = out.item()
+    params = oracle.LazyParams(odesc_of(m.sh), m.fetch)
+    want = oracle.decoder_loss(odesc_of(m.sh), params, tokens)
+    assert got == pytest.approx(want, rel=2e-3)
+
+
+def test_gpt_full_batch_forward():
+    """GPT-small shape on its configured 8 x 512 batch, the whole forward."""
+    m = full("gpt")
+    tokens = inputs.zipf_tokens(0, 8, 512, 32000)
+    tok = torch.from_numpy(tokens).to(DEV)
+    b = zo.make_batch(tokens=tok, batch=8, seq=512)
+    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    eps = float(np.float32(1e-3))
+    m.model.forward_loss(b, out, perts=[(5, 0, eps)])  # perturbed on the fly, W untouched
+    torch.cuda.synchronize()
+    a = oracle.Arena(odesc_of(m.sh), m.fetch(0, m.total).copy())
+    a.perturb(5, 0, eps)
+    want = oracle.model_loss(a, {"tokens": tokens})
+    assert out[0].item() == pytest.approx(want, rel=2e-3)
+
+
+@pytest.mark.parametrize("name", ["opt1.3b", "opt30b"])
+def test_fullsize_inplace_step_properties(name):
+    """The full in-place step on 8 x 2048 tokens, N = 1, as the benchmark runs it."""
+    m = full(name)
+    sh = m.sh
+    tok = torch.from_numpy(inputs.zipf_tokens(0, sh["batch"], sh["seq"], sh["vocab"])).to(DEV)
+    b = zo.make_batch(tokens=tok, batch=sh["batch"], seq=sh["seq"])
+    idx = sample_indices(m.total, seed=1, n=1 << 16)
+    w0 = m.bits_at(idx)
+    losses = torch.zeros(2, dtype=torch.float64, device=DEV)
+    g = torch.zeros(1, dtype=torch.float64, device=DEV)
+    lr, eps, seed = 1e-3, 1e-3, 21
+    m.model.step(b, seed, 1, eps, lr, zo.ZO_MODE_INPLACE, losses, g)
+    torch.cuda.synchronize()
+    L = losses.cpu().numpy()
+    gg = g.item()
+    assert np.isfinite(L).all()
+    assert abs(L.mean() - np.log(sh["vocab"])) < 1.5
+    assert gg == (L[0] - L[1]) / (2 * float(np.float32(eps)))
+    w1 = oracle.bf16_bits_to_f64(m.bits_at(idx))
+    # the oracle's restore sequence on the sampled elements
+    restored = w0.copy()
+    L_ = oracle.lib()
+    for sg in (eps, -2 * eps, eps):
+        L_.oracle_perturb_bf16_at(oracle._ptr(restored), oracle._ptr(idx), idx.size, seed, 0,
+                                  float(np.float32(sg)))
+    r = oracle.bf16_bits_to_f64(restored)
+    z = oracle.gauss_at(seed, 0, idx).astype(np.float64)
+    c = float(np.float32(-lr * gg / 1))
+    # every sampled element moved by c z from its restored value, up to bf16
+    # rounding and rare restore-drift flips
+    step = w1 - r
+    tol = ulp_bf16(np.maximum(np.abs(w1), np.abs(r))) * 1.5
+    ok = np.abs(step - c * z) <= tol
+    assert np.mean(ok) > 0.999

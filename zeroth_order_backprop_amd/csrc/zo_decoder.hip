@@ -123,49 +123,70 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restri
 }
 
 // ============================================================ LayerNorm
-// x[t] = bf16((h[t] - mean) / sqrt(var + 1e-5) * g + b), fp32 statistics;
-// one block per row, two passes over the row held in registers (d <= 8192).
-constexpr int kLnMaxPer = 32;  // elements per thread: d <= 256 * 32
-__global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __restrict__ h, int d,
+// x[t] = bf16((h[t] - mean) / sqrt(var + 1e-5) * g + b), fp32 statistics.
+// One wave per row (4 rows per block, no LDS): lane l holds the 4-element
+// groups l, l + 64, ... of the row in registers (8-byte loads), the mean and
+// the variance come from wave reductions.
+constexpr int kLnMaxQuads = 32;  // d <= 64 lanes * 32 groups * 4 = 8192
+__global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __restrict__ h, int rows, int d,
                                                               const bf16_t* __restrict__ g, uint64_t g_dir,
                                                               const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
                                                               bf16_t* __restrict__ x)
 {
-    __shared__ float red[4];
-    const int t = blockIdx.x;
-    const bf16_t* row = h + (size_t)t * d;
-    float v[kLnMaxPer];
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= rows) return;
+    const int nq = d >> 2;
+    const uint2* row = reinterpret_cast<const uint2*>(h + (size_t)t * d);
+    float v[kLnMaxQuads][4];
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < kLnMaxPer; ++k) {
-        const int c = threadIdx.x + k * kThreads;
-        v[k] = c < d ? bf2f(row[c]) : 0.f;
-        s += v[k];
-    }
-    s = wave_sumf(s);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-    __syncthreads();
-    const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
-    __syncthreads();
-    float q = 0.f;
-#pragma unroll
-    for (int k = 0; k < kLnMaxPer; ++k) {
-        const int c = threadIdx.x + k * kThreads;
-        const float dv = c < d ? v[k] - mean : 0.f;
-        q = fmaf(dv, dv, q);
-    }
-    q = wave_sumf(q);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = q;
-    __syncthreads();
-    const float var = ((red[0] + red[1]) + (red[2] + red[3])) / (float)d;
-    const float rstd = 1.0f / sqrtf(var + 1e-5f);
-#pragma unroll
-    for (int k = 0; k < kLnMaxPer; ++k) {
-        const int c = threadIdx.x + k * kThreads;
-        if (c < d) {
-            const float gg = weight1(g, c, g_dir, p), bb = weight1(b, c, b_dir, p);
-            x[(size_t)t * d + c] = f2bf(fmaf((v[k] - mean) * rstd, gg, bb));
+    for (int k = 0; k < kLnMaxQuads; ++k) {
+        const int q = lane + 64 * k;
+        if (q < nq) {
+            const uint2 u = row[q];
+            v[k][0] = bf2f(u.x & 0xFFFF); v[k][1] = bf2f(u.x >> 16);
+            v[k][2] = bf2f(u.y & 0xFFFF); v[k][3] = bf2f(u.y >> 16);
+        } else {
+            v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0.f;
         }
+        s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+    }
+    const float mean = wave_sumf(s) / (float)d;
+    float q2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxQuads; ++k) {
+        if (lane + 64 * k < nq) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dv = v[k][e] - mean;
+                q2 = fmaf(dv, dv, q2);
+            }
+        }
+    }
+    const float var = wave_sumf(q2) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + 1e-5f);
+    uint2* out = reinterpret_cast<uint2*>(x + (size_t)t * d);
+#pragma unroll
+    for (int k = 0; k < kLnMaxQuads; ++k) {
+        const int q = lane + 64 * k;
+        if (q >= nq) continue;
+        float o[4];
+        if (p.on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 4 * q + e;
+                o[e] = fmaf((v[k][e] - mean) * rstd, weight1(g, c, g_dir, p), weight1(b, c, b_dir, p));
+            }
+        } else {
+            const uint2 gg = reinterpret_cast<const uint2*>(g)[q];
+            const uint2 bb = reinterpret_cast<const uint2*>(b)[q];
+            const float gv[4] = {bf2f(gg.x & 0xFFFF), bf2f(gg.x >> 16), bf2f(gg.y & 0xFFFF), bf2f(gg.y >> 16)};
+            const float bv[4] = {bf2f(bb.x & 0xFFFF), bf2f(bb.x >> 16), bf2f(bb.y & 0xFFFF), bf2f(bb.y >> 16)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = fmaf((v[k][e] - mean) * rstd, gv[e], bv[e]);
+        }
+        out[q] = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
     }
 }
 
@@ -497,30 +518,47 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
     gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
 }
 
-// Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1,
-// tile partials combined in fixed order; each block sums its 256 rows in fp64.
+// Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1.
+// A block covers 64 rows; its 4 waves take every 4th vocabulary tile and merge
+// (max, sum of exp) online in fp64, then the 4 partial results are merged in
+// fixed order; each block writes the fp64 sum of its rows' losses.
 __global__ __launch_bounds__(kThreads) void ce_rows_kernel(const float* __restrict__ lm_max,
                                                             const float* __restrict__ lm_sum,
                                                             const float* __restrict__ lm_pick, int n_tiles, int M,
                                                             int S, double* __restrict__ block_sum)
 {
-    __shared__ double red[4];
-    const int row = blockIdx.x * kThreads + threadIdx.x;
+    __shared__ double pm[4][64], ps[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 64 + lane;
+    double m = -INFINITY, se = 0.0;
+    if (row < M) {
+        for (int t = wave; t < n_tiles; t += 4) {
+            const double tm = (double)lm_max[(size_t)t * M + row];
+            if (tm == -INFINITY) continue;
+            const double ts = (double)lm_sum[(size_t)t * M + row];
+            if (tm > m) {
+                se = se * exp(m - tm) + ts;
+                m = tm;
+            } else {
+                se += ts * exp(tm - m);
+            }
+        }
+    }
+    pm[wave][lane] = m;
+    ps[wave][lane] = se;
+    __syncthreads();
+    if (wave != 0) return;
     double v = 0.0;
     if (row < M && row % S != S - 1) {
-        float mx = -INFINITY;
-        for (int t = 0; t < n_tiles; ++t) mx = fmaxf(mx, lm_max[(size_t)t * M + row]);
-        double se = 0.0;
-        for (int t = 0; t < n_tiles; ++t) {
-            const float m = lm_max[(size_t)t * M + row];
-            if (m > -INFINITY) se += (double)lm_sum[(size_t)t * M + row] * exp((double)m - (double)mx);
-        }
-        v = ((double)mx + log(se)) - (double)lm_pick[row];
+        double mx = pm[0][lane];
+        for (int w = 1; w < 4; ++w) mx = fmax(mx, pm[w][lane]);
+        double tot = 0.0;
+        for (int w = 0; w < 4; ++w)
+            if (pm[w][lane] > -INFINITY) tot += ps[w][lane] * exp(pm[w][lane] - mx);
+        v = (mx + log(tot)) - (double)lm_pick[row];
     }
     v = wave_sumd(v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) block_sum[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+    if (lane == 0) block_sum[blockIdx.x] = v;
 }
 
 // loss = (sum of block sums, fixed order) / (B (S-1))
@@ -755,7 +793,7 @@ DecoderWs carve(const zo_model_desc& d, void* base)
     w.lm_max = (float*)take(tiles * M * 4);
     w.lm_sum = (float*)take(tiles * M * 4);
     w.lm_pick = (float*)take(M * 4);
-    w.ce_part = (double*)take((M + kThreads - 1) / kThreads * 8);
+    w.ce_part = (double*)take((M + 63) / 64 * 8);
     w.bytes = off;
     return w;
 }
@@ -767,7 +805,7 @@ zo_status decoder_check(const zo_model_desc& d)
     const int64_t dh = d.d_model / d.heads;
     if (dh != 64 && dh != 128) return fail(ZO_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if (d.d_model % 64 || d.ffn % 64) return fail(ZO_ERR_UNSUPPORTED, "d_model and ffn must be multiples of 64");
-    if (d.d_model > kThreads * kLnMaxPer) return fail(ZO_ERR_UNSUPPORTED, "d_model too large for LayerNorm");
+    if (d.d_model > 64 * 4 * kLnMaxQuads) return fail(ZO_ERR_UNSUPPORTED, "d_model too large for LayerNorm");
     if (d.batch * d.seq > (1 << 24) || d.vocab > (1 << 24)) return fail(ZO_ERR_UNSUPPORTED, "shape too large");
     return ZO_OK;
 }
@@ -803,7 +841,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             const int t0 = 2 + 8 * l;
             {
                 KernelTimer t("layernorm", s);
-                layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p,
+                layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p,
                                                          w.x);
                 if (zo_status st = check_launch("layernorm")) return st;
             }
@@ -824,7 +862,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
             {
                 KernelTimer t("layernorm", s);
-                layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5),
+                layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5),
                                                          off(t0 + 5), p, w.x);
                 if (zo_status st = check_launch("layernorm")) return st;
             }
@@ -840,7 +878,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         const int tf = 2 + 8 * L;
         {
             KernelTimer t("layernorm", s);
-            layernorm_kernel<<<M, kThreads, 0, s>>>(w.h, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x);
+            layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x);
             if (zo_status st = check_launch("layernorm")) return st;
         }
         GemmParams gl = {};
@@ -849,7 +887,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
         {
             KernelTimer t("reduce", s);
-            const int nb = cdiv(M, kThreads);
+            const int nb = cdiv(M, 64);
             ce_rows_kernel<<<nb, kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, cdiv(V, kLmTile), M, S, w.ce_part);
             ce_final_kernel<<<1, kThreads, 0, s>>>(w.ce_part, nb, M, S, loss + e);
             if (zo_status st = check_launch("ce reduce")) return st;
@@ -891,11 +929,11 @@ zo_status debug_attention(const void* qkv, void* out, int B, int S, int H, int d
 zo_status debug_layernorm(const void* h, const void* g, const void* b, void* x, int rows, int d, hipStream_t s)
 {
     if (!h || !g || !b || !x || rows <= 0 || d <= 0) return fail(ZO_ERR_INVALID, "bad LayerNorm arguments");
-    if (d > kThreads * kLnMaxPer) return fail(ZO_ERR_UNSUPPORTED, "row too long");
+    if (d > 64 * 4 * kLnMaxQuads || d % 4) return fail(ZO_ERR_UNSUPPORTED, "row length must be a multiple of 4, <= 8192");
     Pert p = {};
     KernelTimer t("layernorm", s);
-    layernorm_kernel<<<rows, kThreads, 0, s>>>((const bf16_t*)h, d, (const bf16_t*)g, 0, (const bf16_t*)b, 0, p,
-                                               (bf16_t*)x);
+    layernorm_kernel<<<cdiv(rows, 4), kThreads, 0, s>>>((const bf16_t*)h, rows, d, (const bf16_t*)g, 0,
+                                                        (const bf16_t*)b, 0, p, (bf16_t*)x);
     return check_launch("layernorm");
 }
 
