@@ -70,21 +70,22 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 enum { EPI_LSQ = 0, EPI_MLP = 1 };
 
 // C[M][N] = X * B, B_KN: B = W ([K][N]);  else B = W^T (W is [N][K]).
-// 256 threads = 4 waves in a 2x2 grid over the BM x BN block tile; each wave
-// owns (BM/2) x (BN/2) as 32x32 MFMA tiles, for NV weight variants at once.
-template <int BM, int BN, int BK, bool B_KN, int NV, int EPI>
-__global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev)
+// NT threads = NT/64 waves in a (NT/128) x 2 grid over the BM x BN block
+// tile; each wave owns a WM x WN piece as 32x32 MFMA tiles, for NV weight
+// variants at once.
+template <int BM, int BN, int BK, bool B_KN, int NV, int EPI, int NT>
+__global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
 {
+    constexpr int kThreads = NT;
+    constexpr int WAVES_M = NT / 128;
     extern __shared__ __align__(16) float smem[];
     constexpr int SA = BK + 4;  // padded LDS row stride (floats)
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int WM = BM / WAVES_M, WN = BN / 2;
     constexpr int RB = WM / 32, CB = WN / 32;
     constexpr int A_VEC = BM * BK / 4;  // float4 per A tile
     constexpr int B_VEC = BN * BK / 4;  // quads per B tile
     constexpr int A_PER = (A_VEC + kThreads - 1) / kThreads;
     constexpr int B_PER = (B_VEC + kThreads - 1) / kThreads;
-    float* As = smem;
-    float* Bs = As + BM * SA;  // NV tiles of BN * SA
 
     const int g = blockIdx.z;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31, lh = lane >> 5;
+    static_assert(RB >= 1 && CB >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
 
     f32x16 acc[NV][RB][CB];
 #pragma unroll
@@ -109,7 +111,17 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
 #pragma unroll
             for (int j = 0; j < CB; ++j) acc[v][i][j] = f32x16{};
 
-    float4 ra[A_PER], rb[B_PER];
+    float4 ra[A_PER], rb[B_PER], zb[B_PER];
+    // LDS stage st: A tile at smem + st * STAGE, then NV B tiles
+    constexpr int STAGE = BM * SA + NV * BN * SA;
+    auto As = [&](int st) { return smem + st * STAGE; };
+    auto Bs = [&](int st, int v) { return smem + st * STAGE + BM * SA + v * BN * SA; };
+    auto b_coords = [&](int i, int k0, int& ln, int& lk, int& gn, int& gk) {
+        if (!B_KN) { ln = i / (BK / 4); lk = 4 * (i % (BK / 4)); }
+        else { lk = i / (BN / 4); ln = 4 * (i % (BN / 4)); }
+        gn = n0 + ln;
+        gk = k0 + lk;
+    };
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int t = 0; t < A_PER; ++t) {
@@ -122,21 +134,31 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
 #pragma unroll
         for (int t = 0; t < B_PER; ++t) {
             const int i = tid + t * kThreads;
-            int gn, gk;
-            if (!B_KN) { gn = n0 + i / (BK / 4); gk = k0 + 4 * (i % (BK / 4)); }
-            else { gk = k0 + i / (BN / 4); gn = n0 + 4 * (i % (BN / 4)); }
+            int ln, lk, gn, gk;
+            b_coords(i, k0, ln, lk, gn, gk);
             const bool ok = i < B_VEC && gn < N && gk < K;
             const size_t idx = B_KN ? (size_t)gk * N + gn : (size_t)gn * K + gk;
             rb[t] = ok ? *reinterpret_cast<const float4*>(a.W + idx) : float4{0.f, 0.f, 0.f, 0.f};
         }
     };
-    auto store_tiles = [&](int k0) {
+    // direction values of B quad t of the tile at k0 (zero outside the matrix)
+    auto gen_z = [&](int t, int k0) {
+        const int i = tid + t * kThreads;
+        int ln, lk, gn, gk;
+        b_coords(i, k0, ln, lk, gn, gk);
+        zb[t] = float4{0.f, 0.f, 0.f, 0.f};
+        if (pert && i < B_VEC && gn < N && gk < K) {
+            const size_t idx = B_KN ? (size_t)gk * N + gn : (size_t)gn * K + gk;
+            zb[t] = gauss4(key, probe, (a.w_dir + idx) >> 2);
+        }
+    };
+    auto store_tiles = [&](int st, int k0) {
 #pragma unroll
         for (int t = 0; t < A_PER; ++t) {
             const int i = tid + t * kThreads;
             if (i < A_VEC) {
                 const int r = i / (BK / 4), c4 = i % (BK / 4);
-                *reinterpret_cast<float4*>(As + r * SA + 4 * c4) = ra[t];
+                *reinterpret_cast<float4*>(As(st) + r * SA + 4 * c4) = ra[t];
             }
         }
 #pragma unroll
@@ -144,20 +166,15 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
             const int i = tid + t * kThreads;
             if (i >= B_VEC) continue;
             int ln, lk, gn, gk;
-            if (!B_KN) { ln = i / (BK / 4); lk = 4 * (i % (BK / 4)); gn = n0 + ln; gk = k0 + lk; }
-            else { lk = i / (BN / 4); ln = 4 * (i % (BN / 4)); gk = k0 + lk; gn = n0 + ln; }
-            float4 z = {0.f, 0.f, 0.f, 0.f};
-            if (pert && gn < N && gk < K) {
-                const size_t idx = B_KN ? (size_t)gk * N + gn : (size_t)gn * K + gk;
-                z = gauss4(key, probe, (a.w_dir + idx) >> 2);
-            }
+            b_coords(i, k0, ln, lk, gn, gk);
+            const float4 z = zb[t];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 float4 w = rb[t];
                 w.x = fmaf(sig[v], z.x, w.x); w.y = fmaf(sig[v], z.y, w.y);
                 w.z = fmaf(sig[v], z.z, w.z); w.w = fmaf(sig[v], z.w, w.w);
                 // outside the matrix the tile is zero: fma(sigma, 0, 0) = 0
-                float* Bv = Bs + v * BN * SA;
+                float* Bv = Bs(st, v);
                 if (!B_KN) {
                     *reinterpret_cast<float4*>(Bv + ln * SA + lk) = w;
                 } else {
@@ -169,10 +186,14 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
     };
 
     load_tiles(0);
+#pragma unroll
+    for (int t = 0; t < B_PER; ++t) gen_z(t, 0);
+    store_tiles(0, 0);
+    __syncthreads();
+    int cur = 0;
     for (int k0 = 0; k0 < K; k0 += BK) {
-        store_tiles(k0);
-        __syncthreads();
-        if (k0 + BK < K) load_tiles(k0 + BK);  // in flight during the MFMAs
+        const bool more = k0 + BK < K;
+        if (more) load_tiles(k0 + BK);  // in flight during the MFMAs
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 8) {
             // lane (lr, lh) supplies k = kk + 4 lh + s in MFMA step s: the
@@ -180,13 +201,12 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
             f32x4 af[RB], bf[NV][CB];
 #pragma unroll
             for (int i = 0; i < RB; ++i)
-                af[i] = *reinterpret_cast<const f32x4*>(As + (wm * WM + i * 32 + lr) * SA + kk + 4 * lh);
+                af[i] = *reinterpret_cast<const f32x4*>(As(cur) + (wm * WM + i * 32 + lr) * SA + kk + 4 * lh);
 #pragma unroll
             for (int v = 0; v < NV; ++v)
 #pragma unroll
                 for (int j = 0; j < CB; ++j)
-                    bf[v][j] = *reinterpret_cast<const f32x4*>(Bs + v * BN * SA + (wn * WN + j * 32 + lr) * SA +
-                                                               kk + 4 * lh);
+                    bf[v][j] = *reinterpret_cast<const f32x4*>(Bs(cur, v) + (wn * WN + j * 32 + lr) * SA + kk + 4 * lh);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -197,13 +217,23 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
                         for (int j = 0; j < CB; ++j)
                             acc[v][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[v][j][s], acc[v][i][j],
                                                                                 0, 0, 0);
+            // the next tile's direction values, spread over this tile's MFMA
+            // groups so the VALU work overlaps the matrix cores
+            if (more) {
+#pragma unroll
+                for (int t = 0; t < B_PER; ++t)
+                    if ((t * (BK / 8)) / B_PER == kk / 8) gen_z(t, k0 + BK);
+            }
         }
+        if (more) store_tiles(cur ^ 1, k0 + BK);
         __syncthreads();
+        cur ^= 1;
     }
 
     // accumulator element r of a 32x32 tile: row 8 (r/4) + 4 lh + r%4, col lr
     if constexpr (EPI == EPI_LSQ) {
-        __shared__ double wsum[NV][4];
+        constexpr int NW = NT / 64;
+        __shared__ double wsum[NV][NW];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             double s = 0.0;
@@ -225,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void fgemm_kernel(GemmArgs a, EvalList ev
         }
         __syncthreads();
         if (tid < NV) {
-            const double t = ((wsum[tid][0] + wsum[tid][1]) + wsum[tid][2]) + wsum[tid][3];
+            double t = 0.0;
+            for (int w = 0; w < NW; ++w) t += wsum[tid][w];
             const int blk = blockIdx.y * gridDim.x + blockIdx.x;
             a.part[(size_t)ev.out[g][tid] * gridDim.x * gridDim.y + blk] = t;
         }
@@ -298,29 +329,42 @@ __global__ __launch_bounds__(kThreads) void lsq_reduce(const double* __restrict_
     if (threadIdx.x == 0) loss[e] = (((ws[0] + ws[1]) + ws[2]) + ws[3]) / (2.0 * (double)M);
 }
 
-// loss[e] = mean_b (logsumexp(logits_b) - logits_b[y_b]), logits summed over
-// the hidden tiles in fixed order in fp64.
-__global__ __launch_bounds__(kThreads) void mlp_ce(const float* __restrict__ part, int n_tiles, int M, int C,
-                                                    const int32_t* __restrict__ labels, double* __restrict__ loss)
+// Cross-entropy of each row from the logit partials.  Block (chunk, e)
+// covers rows 64 chunk .. +63 of evaluation e; wave w sums the hidden tiles
+// t = w, w+4, ... in fp64, the four partial logits are added in fixed order,
+// and the block writes the fp64 sum of its rows' losses.
+__global__ __launch_bounds__(kThreads) void mlp_ce_rows(const float* __restrict__ part, int n_tiles, int M, int C,
+                                                         const int32_t* __restrict__ labels,
+                                                         double* __restrict__ chunk_sum)
 {
-    __shared__ double ws[4];
-    const int e = blockIdx.x;
-    double s = 0.0;
-    for (int m = threadIdx.x; m < M; m += kThreads) {
-        double lg[kMaxClasses];
+    __shared__ double lg_w[4][64][kMaxClasses + 1];
+    const int e = blockIdx.y, chunk = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = chunk * 64 + lane;
+    double lg[kMaxClasses];
 #pragma unroll
-        for (int c = 0; c < kMaxClasses; ++c) lg[c] = 0.0;
-        for (int t = 0; t < n_tiles; ++t) {
+    for (int c = 0; c < kMaxClasses; ++c) lg[c] = 0.0;
+    if (m < M) {
+        for (int t = wave; t < n_tiles; t += 4) {
             const float* p = part + (((size_t)e * n_tiles + t) * M + m) * C;
 #pragma unroll
             for (int c = 0; c < kMaxClasses; ++c)
                 if (c < C) lg[c] += (double)p[c];
         }
-        const int y = labels[m];
-        double mx = lg[0], picked = 0.0;
+    }
 #pragma unroll
-        for (int c = 1; c < kMaxClasses; ++c)
+    for (int c = 0; c < kMaxClasses; ++c) lg_w[wave][lane][c] = lg[c];
+    __syncthreads();
+    if (wave != 0) return;
+    double v = 0.0;
+    if (m < M) {
+        const int y = labels[m];
+        double mx = -INFINITY, picked = 0.0;
+#pragma unroll
+        for (int c = 0; c < kMaxClasses; ++c) {
+            lg[c] = ((lg_w[0][lane][c] + lg_w[1][lane][c]) + lg_w[2][lane][c]) + lg_w[3][lane][c];
             if (c < C) mx = fmax(mx, lg[c]);
+        }
         double se = 0.0;
 #pragma unroll
         for (int c = 0; c < kMaxClasses; ++c)
@@ -328,12 +372,21 @@ __global__ __launch_bounds__(kThreads) void mlp_ce(const float* __restrict__ par
                 se += exp(lg[c] - mx);
                 if (c == y) picked = lg[c];
             }
-        s += (mx + log(se)) - picked;
+        v = (mx + log(se)) - picked;
     }
+    v = wave_sum(v);
+    if (lane == 0) chunk_sum[(size_t)e * gridDim.x + chunk] = v;
+}
+
+// loss[e] = (sum of evaluation e's chunk sums, fixed order) / M
+__global__ __launch_bounds__(64) void mlp_ce_final(const double* __restrict__ chunk_sum, int n_chunks, int M,
+                                                   double* __restrict__ loss)
+{
+    const int e = blockIdx.x;
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n_chunks; i += 64) s += chunk_sum[(size_t)e * n_chunks + i];
     s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) loss[e] = (((ws[0] + ws[1]) + ws[2]) + ws[3]) / (double)M;
+    if (threadIdx.x == 0) loss[e] = s / (double)M;
 }
 
 // ---------------------------------------------------------------- host side
@@ -371,16 +424,16 @@ int make_evals(const zo_pert* perts, int n, EvalList& ev)
     return nv;
 }
 
-template <int BM, int BN, int BK, bool B_KN, int NV, int EPI>
+template <int BM, int BN, int BK, bool B_KN, int NV, int EPI, int NT>
 zo_status launch_fgemm(const GemmArgs& a, const EvalList& ev, hipStream_t s)
 {
     constexpr int SA = BK + 4;
-    size_t lds = (size_t)(BM * SA + NV * BN * SA) * sizeof(float);
+    size_t lds = (size_t)2 * (BM * SA + NV * BN * SA) * sizeof(float);
     if (EPI == EPI_MLP) {
         const size_t epi = (size_t)(BM * (BN + 1) + NV * a.C * BN) * sizeof(float);
         lds = lds > epi ? lds : epi;
     }
-    auto kern = fgemm_kernel<BM, BN, BK, B_KN, NV, EPI>;
+    auto kern = fgemm_kernel<BM, BN, BK, B_KN, NV, EPI, NT>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
@@ -389,7 +442,7 @@ zo_status launch_fgemm(const GemmArgs& a, const EvalList& ev, hipStream_t s)
     }
     dim3 grid(cdiv(a.N, BN), cdiv(a.M, BM), ev.n_groups);
     KernelTimer timer("gemm_f32", s);
-    kern<<<grid, kThreads, lds, s>>>(a, ev);
+    kern<<<grid, NT, lds, s>>>(a, ev);
     return check_launch("fp32 fused GEMM");
 }
 
@@ -425,8 +478,8 @@ zo_status lsq_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
     a.K = (int)d.d_in;
     a.Y = (const float*)b.y;
     a.part = (double*)m.workspace;
-    zo_status st = nv == 2 ? launch_fgemm<LSQ_BM, LSQ_BN, LSQ_BK, true, 2, EPI_LSQ>(a, ev, s)
-                           : launch_fgemm<LSQ_BM, LSQ_BN, LSQ_BK, true, 1, EPI_LSQ>(a, ev, s);
+    zo_status st = nv == 2 ? launch_fgemm<LSQ_BM, LSQ_BN, LSQ_BK, true, 2, EPI_LSQ, 256>(a, ev, s)
+                           : launch_fgemm<LSQ_BM, LSQ_BN, LSQ_BK, true, 1, EPI_LSQ, 256>(a, ev, s);
     if (st) return st;
     const int n_blocks = cdiv(a.M, LSQ_BM) * cdiv(a.N, LSQ_BN);
     const int n_evals = n == 0 ? 1 : n;
@@ -445,10 +498,15 @@ zo_status mlp_check(const zo_model_desc& d)
     return ZO_OK;
 }
 
-size_t mlp_workspace(const zo_model_desc& d)
+size_t mlp_part_bytes(const zo_model_desc& d)
 {
     const size_t tiles = cdiv((int)d.hidden, MLP_BN);
     return (kMaxEvalsPerCall * tiles * d.batch * d.classes * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t mlp_workspace(const zo_model_desc& d)
+{
+    return mlp_part_bytes(d) + kMaxEvalsPerCall * (size_t)cdiv((int)d.batch, 64) * sizeof(double);
 }
 
 zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
@@ -468,12 +526,16 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
     a.w2_dir = m.offsets[1];
     a.C = (int)d.classes;
     a.logit_part = (float*)m.workspace;
-    zo_status st = nv == 2 ? launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 2, EPI_MLP>(a, ev, s)
-                           : launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 1, EPI_MLP>(a, ev, s);
+    zo_status st = nv == 2 ? launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 2, EPI_MLP, 512>(a, ev, s)
+                           : launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 1, EPI_MLP, 512>(a, ev, s);
     if (st) return st;
     const int n_evals = n == 0 ? 1 : n;
+    double* chunk_sum = (double*)((char*)m.workspace + mlp_part_bytes(d));
+    const int n_chunks = cdiv(a.M, 64);
     KernelTimer timer("reduce", s);
-    mlp_ce<<<n_evals, kThreads, 0, s>>>(a.logit_part, cdiv(a.N, MLP_BN), a.M, a.C, b.labels, loss);
+    mlp_ce_rows<<<dim3(n_chunks, n_evals), kThreads, 0, s>>>(a.logit_part, cdiv(a.N, MLP_BN), a.M, a.C, b.labels,
+                                                              chunk_sum);
+    mlp_ce_final<<<n_evals, 64, 0, s>>>(chunk_sum, n_chunks, a.M, loss);
     return check_launch("mlp cross-entropy");
 }
 
