@@ -580,13 +580,14 @@ __global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __rest
 // running max / sum of each query live in one lane; P^T goes straight from
 // the accumulators into the B operand of O^T = V^T P^T (the contraction
 // order over keys is the same permutation on both operands).  P is rounded to
-// bf16 for the MFMA; max, sums and rescaling are fp32.
-// Block: 4 waves x 32 queries = 128 queries; keys in tiles of 32.
+// bf16 for the MFMA; max, sums and rescaling are fp32, exponentials are exp2
+// of scores pre-scaled by log2(e) / sqrt(dh).
+// Block: 4 waves x 32 queries = 128 queries; keys in tiles of 64.
 template <int DH>
 __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H,
                                                               bf16_t* __restrict__ out)
 {
-    constexpr int BQ = 128, BKV = 32;
+    constexpr int BQ = 128, BKV = 64;
     constexpr int KS = DH / 16;   // MFMA k-steps over the head dim for S^T
     constexpr int OT = DH / 32;   // 32-row blocks of O^T
     constexpr int LDK = DH + 8;   // K tile row (bf16), padded
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
     const size_t row_stride = 3 * (size_t)d;
     const bf16_t* base = qkv + (size_t)b * S * row_stride;
     const int qoff = hd * DH, koff = d + hd * DH, voff = 2 * d + hd * DH;
-    const float scale = 1.0f / sqrtf((float)DH);
+    const float c = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
 
     // Q^T as the B operand: lane (lr = query, lh) holds dh 8 lh + 16 ks .. +7
     bf16x8 qf[KS];
@@ -621,14 +622,14 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
     f32x16 o[OT];
 #pragma unroll
     for (int t = 0; t < OT; ++t) o[t] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;  // in log2 units
 
     const int kv_end = min(S, q0 + BQ);  // causal: keys < last query of the block
     for (int k0 = 0; k0 < kv_end; k0 += BKV) {
         __syncthreads();
         // K tile [BKV][DH] and V^T tile [DH][BKV]
-        for (int c = tid; c < BKV * DH / 8; c += kThreads) {
-            const int kr = c / (DH / 8), dc = 8 * (c % (DH / 8));
+        for (int cc = tid; cc < BKV * DH / 8; cc += kThreads) {
+            const int kr = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
             const int key = k0 + kr;
             uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
             if (key < S) {
@@ -645,34 +646,49 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
         }
         __syncthreads();
         if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
-        // S^T [32 keys][32 queries]
-        f32x16 st = f32x16{};
+        // S^T [64 keys][32 queries] as two 32x32 blocks
+        f32x16 st[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + lr * LDK + 16 * ks + 8 * lh);
-            st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st, 0, 0, 0);
+        for (int hblk = 0; hblk < 2; ++hblk) {
+            st[hblk] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8*>(Ks + (32 * hblk + lr) * LDK + 16 * ks + 8 * lh);
+                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[hblk], 0, 0, 0);
+            }
         }
-        // element r: key k0 + 8 (r/4) + 4 lh + r%4, query myq
+        // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
+        const bool diag = k0 + BKV - 1 > qw;  // some key of the tile may follow some query of the wave
         float tmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            float v = st[r] * scale;
-            if (key > myq || key >= S) v = -INFINITY;
-            st[r] = v;
-            tmax = fmaxf(tmax, v);
-        }
+        for (int hblk = 0; hblk < 2; ++hblk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = st[hblk][r] * c;
+                if (diag) {
+                    const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    if (key > myq || key >= S) v = -INFINITY;
+                }
+                st[hblk][r] = v;
+                tmax = fmaxf(tmax, v);
+            }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         float psum = 0.f;
-        float pv[16];
+        bf16x8 pb[2][2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e = (st[r] == -INFINITY) ? 0.f : __expf(st[r] - m_new);
-            pv[r] = round_bf(e);
-            psum += pv[r];
-        }
+        for (int hblk = 0; hblk < 2; ++hblk)
+#pragma unroll
+            for (int sblk = 0; sblk < 2; ++sblk)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float e = __builtin_amdgcn_exp2f(st[hblk][8 * sblk + t] - m_new);  // exp2(-inf) = 0
+                    const __bf16 eb = (__bf16)e;
+                    pb[hblk][sblk][t] = eb;
+                    psum += (float)eb;
+                }
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -680,24 +696,23 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
         for (int t = 0; t < OT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        // O^T += V^T P^T over the 32 keys in two MFMA k-steps; step s uses
-        // accumulator elements 8s .. 8s+7, i.e. keys 16 s + 8 (t/4) + 4 lh + t%4
+        // O^T += V^T P^T over the 64 keys in four MFMA k-steps; step (hblk, sblk)
+        // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
+        // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8 pb;
+        for (int hblk = 0; hblk < 2; ++hblk)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) pb[t] = (__bf16)pv[8 * s + t];
+            for (int sblk = 0; sblk < 2; ++sblk)
 #pragma unroll
-            for (int t = 0; t < OT; ++t) {
-                // A = V^T rows dh = 32 t + lr, the same 8 keys in the same order
-                const bf16_t* vr = Vt + (32 * t + lr) * LDV + 16 * s + 4 * lh;
-                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-                const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
-                const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[t], 0, 0, 0);
-            }
-        }
+                for (int t = 0; t < OT; ++t) {
+                    // A = V^T rows dh = 32 t + lr, the same 8 keys in the same order
+                    const bf16_t* vr = Vt + (32 * t + lr) * LDV + 32 * hblk + 16 * sblk + 4 * lh;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                    const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
+                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
+                }
     }
     if (myq >= S) return;
     const float inv = 1.0f / l_run;
