@@ -587,7 +587,8 @@ template <int DH>
 __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H,
                                                               bf16_t* __restrict__ out)
 {
-    constexpr int BQ = 128, BKV = 64;
+    constexpr int BQ = 128, BKV = DH == 64 ? 64 : 32;
+    constexpr int NB = BKV / 32;  // 32-key blocks per tile
     constexpr int KS = DH / 16;   // MFMA k-steps over the head dim for S^T
     constexpr int OT = DH / 32;   // 32-row blocks of O^T
     constexpr int LDK = DH + 8;   // K tile row (bf16), padded
@@ -625,31 +626,56 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
     float m_run = -INFINITY, l_run = 0.f;  // in log2 units
 
     const int kv_end = min(S, q0 + BQ);  // causal: keys < last query of the block
-    for (int k0 = 0; k0 < kv_end; k0 += BKV) {
-        __syncthreads();
-        // K tile [BKV][DH] and V^T tile [DH][BKV]
-        for (int cc = tid; cc < BKV * DH / 8; cc += kThreads) {
-            const int kr = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
-            const int key = k0 + kr;
-            uint4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (key < S) {
-                kv = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
-                vv = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + voff + dc);
-            }
-            *reinterpret_cast<uint4*>(Ks + kr * LDK + dc) = kv;
-            const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+    // Each thread stages CH (key pair, 8-column) chunks of K and V per tile:
+    // keys 2 kp and 2 kp + 1, head-dim columns dc .. dc + 7.  The next tile's
+    // chunks are loaded into registers while the current tile is computed.
+    constexpr int CH = (BKV / 2) * (DH / 8) / kThreads;
+    static_assert(CH * kThreads == (BKV / 2) * (DH / 8), "tile / thread mismatch");
+    uint4 rk[CH][2], rv[CH][2];
+    auto load_kv = [&](int k0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                Vt[(dc + 2 * e) * LDV + kr] = (bf16_t)(w4[e] & 0xFFFFu);
-                Vt[(dc + 2 * e + 1) * LDV + kr] = (bf16_t)(w4[e] >> 16);
+        for (int j = 0; j < CH; ++j) {
+            const int cc = tid + j * kThreads;
+            const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int key = k0 + 2 * kp + e;
+                rk[j][e] = rv[j][e] = uint4{0u, 0u, 0u, 0u};
+                if (key < S) {
+                    rk[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
+                    rv[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + voff + dc);
+                }
             }
         }
-        __syncthreads();
-        if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
-        // S^T [64 keys][32 queries] as two 32x32 blocks
-        f32x16 st[2];
+    };
+    auto store_kv = [&]() {
 #pragma unroll
-        for (int hblk = 0; hblk < 2; ++hblk) {
+        for (int j = 0; j < CH; ++j) {
+            const int cc = tid + j * kThreads;
+            const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
+            *reinterpret_cast<uint4*>(Ks + (2 * kp) * LDK + dc) = rk[j][0];
+            *reinterpret_cast<uint4*>(Ks + (2 * kp + 1) * LDK + dc) = rk[j][1];
+            // V^T: column pair (2 kp, 2 kp + 1) of row dc + e, one 4-byte write each
+            const uint32_t a[4] = {rv[j][0].x, rv[j][0].y, rv[j][0].z, rv[j][0].w};
+            const uint32_t b4[4] = {rv[j][1].x, rv[j][1].y, rv[j][1].z, rv[j][1].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e) * LDV + 2 * kp) = (a[e] & 0xFFFFu) | (b4[e] << 16);
+                *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e + 1) * LDV + 2 * kp) = (a[e] >> 16) | (b4[e] & 0xFFFF0000u);
+            }
+        }
+    };
+    load_kv(0);
+    for (int k0 = 0; k0 < kv_end; k0 += BKV) {
+        __syncthreads();  // every wave is done with the previous tile
+        store_kv();
+        __syncthreads();
+        if (k0 + BKV < kv_end) load_kv(k0 + BKV);  // in flight during this tile's MFMAs
+        if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
+        // S^T [BKV keys][32 queries] as NB 32x32 blocks
+        f32x16 st[NB];
+#pragma unroll
+        for (int hblk = 0; hblk < NB; ++hblk) {
             st[hblk] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -659,48 +685,58 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
             }
         }
         // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
-        const bool diag = k0 + BKV - 1 > qw;  // some key of the tile may follow some query of the wave
+        if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
+            const int last = min(myq, S - 1);
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
+                }
+        }
+        // running max in log2 units: max(s c) = c max(s) for c > 0
         float tmax = -INFINITY;
 #pragma unroll
-        for (int hblk = 0; hblk < 2; ++hblk)
+        for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = st[hblk][r] * c;
-                if (diag) {
-                    const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    if (key > myq || key >= S) v = -INFINITY;
-                }
-                st[hblk][r] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         float psum = 0.f;
-        bf16x8 pb[2][2];
+        bf16x8 pb[NB][2];
 #pragma unroll
-        for (int hblk = 0; hblk < 2; ++hblk)
+        for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-            for (int sblk = 0; sblk < 2; ++sblk)
+            for (int sblk = 0; sblk < 2; ++sblk) {
+                uint32_t w4[4];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float e = __builtin_amdgcn_exp2f(st[hblk][8 * sblk + t] - m_new);  // exp2(-inf) = 0
-                    const __bf16 eb = (__bf16)e;
-                    pb[hblk][sblk][t] = eb;
-                    psum += (float)eb;
+                for (int t = 0; t < 8; t += 2) {
+                    // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
+                    psum += e0 + e1;
+                    w4[t >> 1] = pack2(e0, e1);
                 }
+                const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
+                pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
+            }
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        // rescale only when some query of the wave raised its max
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int t = 0; t < OT; ++t)
+            for (int t = 0; t < OT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        // O^T += V^T P^T over the 64 keys in four MFMA k-steps; step (hblk, sblk)
+                for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        }
+        // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
         // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
         // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4
 #pragma unroll
-        for (int hblk = 0; hblk < 2; ++hblk)
+        for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
             for (int sblk = 0; sblk < 2; ++sblk)
 #pragma unroll
