@@ -216,13 +216,13 @@ __device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erf
 
 // Linear tile index -> (tm, tn): consecutive workgroups land on consecutive
 // XCDs, so give each XCD a contiguous range of tiles, and walk tiles in
-// groups of 8 M-tiles so neighbours share A rows and W columns in L2.
+// groups of G M-tiles so neighbours share A rows and W columns in L2.
+template <int G = 8>
 __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& tn)
 {
     const int total = nbm * nbn;
     int t = b;
     if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
-    constexpr int G = 8;
     const int group = t / (G * nbn);
     const int first = group * G;
     const int gsize = min(nbm - first, G);
@@ -419,28 +419,37 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
 
 // The same product with the stage tiles written to LDS directly by the loads
 // (global_load_lds, 16 B per lane) for the stored-weight path: no register
-// staging, STAGES-deep ring of BK = 32 slices, prefetch distance STAGES - 1.
-// LDS rows are 64 B (4 chunks of 16 B) and unpadded; chunk c of row r sits at
-// position c ^ ((r >> 2) & 3), so the 32 rows a fragment read touches spread
-// over all banks.  Rows past M or N load a clamped (valid) row and are never
-// stored.  The barrier is a bare s_barrier after each wave has waited for its
-// own share of the stage (vmcnt), so the later stages stay in flight.
-template <int BM, int BN, int EPI, int STAGES>
+// staging.  Rows past M or N load a clamped (valid) row and are never stored.
+// Barriers are bare s_barrier after each wave has waited (vmcnt) for its own
+// share of a stage, so that later stages stay in flight across them.
+
+// vmcnt(n) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+#define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+
+// Large tiles: ring of 4 BK = 32 stages, prefetch distance 3.  LDS rows are
+// 64 B (4 chunks of 16 B), chunk c of row r at position c ^ ((r >> 2) & 3),
+// so the 32 rows a fragment read touches spread over all banks.  The two
+// k-halves of a stage are read into alternating register sets: the second
+// half's reads and the next stage's first half are issued while the MFMAs of
+// the previous half run.
+template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
 {
-    constexpr int BK = 32;
+    constexpr int BK = 32, STAGES = 4;
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int RB = WM / 32, CB = WN / 32;
     constexpr int A_INS = BM * 4 / kThreads, B_INS = BN * 4 / kThreads;
     constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(A_INS * kThreads == BM * 4 && B_INS * kThreads == BN * 4, "tile / thread mismatch");
+    static_assert(2 * INS < 64, "vmcnt range");
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     int tm, tn;
-    tile_of(blockIdx.x, nbm, nbn, tm, tn);
+    tile_of<4>(blockIdx.x, nbm, nbn, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
@@ -460,51 +469,148 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
             const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const int gm = min(m0 + row, M - 1);
-            const bf16_t* src = g.A + (size_t)gm * K + k0 + 8 * lc;
+            const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
             bf16_t* dst = sa + (j * kThreads + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < B_INS; ++j) {
             const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const int gn = min(n0 + row, N - 1);
-            const bf16_t* src = g.W + (size_t)gn * K + k0 + 8 * lc;
+            const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
             bf16_t* dst = sb + (j * kThreads + wave * 64) * 8;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
-    // vmcnt wait with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
-    auto wait_vm = [](int n) {
-        if (n >= 2 * INS) __builtin_amdgcn_s_waitcnt(((2 * INS) & 15) | (((2 * INS) >> 4) << 14) | (7 << 4) | (15 << 8));
-        else if (n >= INS) __builtin_amdgcn_s_waitcnt((INS & 15) | ((INS >> 4) << 14) | (7 << 4) | (15 << 8));
-        else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    auto wait_vm = [](int stages_in_flight) {
+        if (stages_in_flight >= 2) ZO_WAIT_VM(2 * INS);
+        else if (stages_in_flight == 1) ZO_WAIT_VM(INS);
+        else ZO_WAIT_VM(0);
     };
-    static_assert(2 * INS < 64, "vmcnt range");
-    static_assert(STAGES <= 4, "at most two stages may stay in flight at a wait");
+    // fragment offsets (elements) of this lane for k-half ks of a stage
+    int aoff[2][RB], boff[2][CB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int lc = 2 * ks + lh;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int row = wm * WM + i * 32 + lr;
+            aoff[ks][i] = (row * 4 + (lc ^ ((row >> 2) & 3))) * 8;
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int row = wn * WN + j * 32 + lr;
+            boff[ks][j] = BM * BK + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8;
+        }
+    }
+    bf16x8 fa[2][RB], fb[2][CB];
+    auto read = [&](int kt, int ks, int slot) {
+        const bf16_t* st = lds + (kt % STAGES) * STAGE;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks][j]);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks][i]);
+    };
+    auto mma = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    };
 
     for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
+    wait_vm(min(2, KT - 1));  // stage 0 landed
+    asm volatile("s_barrier" ::: "memory");
+    read(0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
-        // stages kt+1 .. min(kt+STAGES-2, KT-1) may remain outstanding
-        const int ahead = min(STAGES - 2, KT - 1 - kt);
-        wait_vm(ahead * INS);
+        read(kt, 1, 1);
+        mma(0);
+        if (kt + 1 < KT) {
+            // stage kt+1 landed (only kt+2 may remain in flight) and this
+            // wave's reads of stage kt are in registers; after the barrier
+            // every wave is done with stage kt-1's buffer, which is refilled
+            wait_vm(min(1, KT - 2 - kt));
+            ZO_WAIT_LGKM0();
+            asm volatile("s_barrier" ::: "memory");
+            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+            read(kt + 1, 0, 0);
+        }
+        mma(1);
+    }
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
+}
+
+// Small tiles: two BK = 64 stages.  LDS rows are 128 B (8 chunks of 16 B),
+// chunk c of row r at position c ^ ((r >> 1) & 7): the 32 rows of a fragment
+// read (16 B each, half the wave on one chunk column) cover every bank
+// evenly.  Stage k+1 loads while stage k's MFMAs run.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
+{
+    constexpr int BK = 64;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int A_INS = BM * 8 / kThreads, B_INS = BN * 8 / kThreads;
+    constexpr int STAGE = (BM + BN) * BK;
+    static_assert(A_INS * kThreads == BM * 8 && B_INS * kThreads == BN * 8, "tile / thread mismatch");
+    extern __shared__ __align__(16) bf16_t lds[];
+
+    const int M = g.M, N = g.N, K = g.K;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of<8>(blockIdx.x, nbm, nbn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+
+    const int KT = K / BK;
+    auto issue = [&](int kt) {
+        bf16_t* sa = lds + (kt & 1) * STAGE;
+        bf16_t* sb = sa + BM * BK;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < A_INS; ++j) {
+            const int p = j * kThreads + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
+            bf16_t* dst = sa + (j * kThreads + wave * 64) * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < B_INS; ++j) {
+            const int p = j * kThreads + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
+            bf16_t* dst = sb + (j * kThreads + wave * 64) * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+
+    issue(0);
+    for (int kt = 0; kt < KT; ++kt) {
+        ZO_WAIT_VM(0);
         asm volatile("s_barrier" ::: "memory");
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-        const bf16_t* sa = lds + (kt % STAGES) * STAGE;
+        if (kt + 1 < KT) issue(kt + 1);
+        const bf16_t* sa = lds + (kt & 1) * STAGE;
         const bf16_t* sb = sa + BM * BK;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
             const int lc = 2 * ks + lh;
             bf16x8 af[RB], bfr[CB];
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int row = wm * WM + i * 32 + lr;
-                af[i] = *reinterpret_cast<const bf16x8*>(sa + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8);
+                af[i] = *reinterpret_cast<const bf16x8*>(sa + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
             }
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int row = wn * WN + j * 32 + lr;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8);
+                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
             }
 #pragma unroll
             for (int i = 0; i < RB; ++i)
@@ -512,9 +618,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
                 for (int j = 0; j < CB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
+        // every wave is done reading this stage before the next issue refills it
+        asm volatile("s_barrier" ::: "memory");
     }
-    // the epilogue may reuse LDS (LM head): every wave must be done reading it
-    asm volatile("s_barrier" ::: "memory");
     gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
 }
 
@@ -782,9 +888,15 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         KernelTimer timer(fam, s);
         kern<<<blocks, kThreads, lds, s>>>(gp, p);
     } else {
-        constexpr int STAGES = 4;
-        const size_t lds = (size_t)STAGES * (BM + BN) * 32 * sizeof(bf16_t);
-        auto kern = gemm_bf16_dma_kernel<BM, BN, EPI, STAGES>;
+        // 256-wide tiles: 4-stage BK = 32 ring; 128-wide: 2-stage BK = 64
+        constexpr bool big = BM == 256;
+        constexpr size_t lds = big ? (size_t)4 * (BM + BN) * 32 * sizeof(bf16_t)
+                                   : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
+        void (*kern)(GemmParams);
+        if constexpr (big)
+            kern = gemm_bf16_dma_kernel<BM, BN, EPI>;
+        else
+            kern = gemm_bf16_k64_kernel<BM, BN, EPI>;
         static bool attr = false;
         if (!attr) {
             if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
