@@ -226,7 +226,8 @@ zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float
  * Single decoder kernels, for testing them in isolation (bf16 buffers, device):
  *  zo_debug_gemm_bf16: C[M][N] = epi(A[M][K] W[N][K]^T), fp32 accumulation,
  *    epi 0: bf16 store, 1: GELU then bf16, 2: ReLU then bf16,
- *    3: residual C = bf16(C + bf16(product)); K % 64 == 0.
+ *    3: residual C = bf16(C + bf16(product)); K % 64 == 0, N % 8 == 0,
+ *    buffers 16-byte aligned (ZO_ERR_UNSUPPORTED / ZO_ERR_INVALID otherwise).
  *  zo_debug_attention: out[B*S][H*dh] = causal softmax(Q K^T / sqrt(dh)) V per
  *    (sequence, head) from qkv[B*S][3*H*dh] (Q, K, V blocks of H*dh columns,
  *    head h at columns h*dh); dh in {64, 128}.

@@ -16,10 +16,13 @@
 // which is how the perturbed-tile (fused) mode evaluates W +- eps z without
 // writing W; with sigma = 0 and no direction the stored weights are used.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
 #include "zo_internal.hpp"
+#include "zo_math.hpp"
 #include "zo_models.hpp"
 #include "zo_rng.hpp"
 
@@ -212,7 +215,6 @@ struct GemmParams {
     int S;
 };
 
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
 // Linear tile index -> (tm, tn): consecutive workgroups land on consecutive
 // XCDs, so give each XCD a contiguous range of tiles, and walk tiles in
@@ -233,8 +235,18 @@ __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& t
 
 // Writes one block tile's accumulators (see the GEMM kernels below).
 // Accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr.
+// Stores go through LDS: the activated, bf16-rounded tile is written to
+// `smem` (rows padded by 8 bf16, so the two row groups of one write land on
+// different banks), then every thread moves 16-byte row chunks, for the
+// residual path reading the matching 16 bytes of h first: all global traffic
+// of the epilogue is coalesced 16-byte accesses.  Needs N % 8 == 0, C 16-byte
+// aligned and BM * (BN + 8) bf16 of LDS that no wave still reads.
+template <int BM, int BN>
+constexpr size_t epilogue_lds_bytes() { return (size_t)BM * (BN + 8) * sizeof(bf16_t); }
+
 template <int BM, int BN, int EPI, int RB, int CB>
-__device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn)
+__device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn,
+                                                   bf16_t* smem)
 {
     constexpr int WM = BM / 2, WN = BN / 2;
     const int M = g.M, N = g.N;
@@ -242,22 +254,39 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31, lh = lane >> 5;
     if constexpr (EPI != EPI_LMHEAD) {
+        constexpr int LDC = BN + 8;
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int j = 0; j < CB; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    const int col = n0 + wn * WN + j * 32 + lr;
-                    if (row >= M || col >= N) continue;
+                    const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = wn * WN + j * 32 + lr;
                     float v = acc[i][j][r];
-                    bf16_t* dst = g.C + (size_t)row * N + col;
-                    if constexpr (EPI == EPI_GELU) v = gelu_f(v);
+                    if constexpr (EPI == EPI_GELU) v = gelu_erf(v);
                     if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
-                    if constexpr (EPI == EPI_RESID) v = bf2f(*dst) + round_bf(v);
-                    *dst = f2bf(v);
+                    smem[row * LDC + col] = f2bf(v);
                 }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per row
+#pragma unroll 4
+        for (int p = tid; p < BM * CPR; p += kThreads) {
+            const int row = p / CPR, cc = p % CPR;
+            const int gr = m0 + row, gc = n0 + 8 * cc;
+            if (gr >= M || gc >= N) continue;
+            uint4 v = *reinterpret_cast<const uint4*>(smem + row * LDC + 8 * cc);
+            uint4* dst = reinterpret_cast<uint4*>(g.C + (size_t)gr * N + gc);
+            if constexpr (EPI == EPI_RESID) {
+                // h + bf16(product), rounded once more to bf16
+                const uint4 h = *dst;
+                auto add2 = [](uint32_t hw, uint32_t pw) {
+                    return pack2(bf2f(hw & 0xFFFF) + bf2f(pw & 0xFFFF), bf2f(hw >> 16) + bf2f(pw >> 16));
+                };
+                v = uint4{add2(h.x, v.x), add2(h.y, v.y), add2(h.z, v.z), add2(h.w, v.w)};
+            }
+            *dst = v;
+        }
     } else {
         // Fused cross-entropy partials over this tile's BN vocabulary columns:
         // per row the max and the sum of exp(logit - max), plus the target
@@ -314,9 +343,10 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
 }
 
 template <int BM, int BN, int EPI, int RB, int CB>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn)
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn,
+                                              bf16_t* smem)
 {
-    gemm_epilogue_impl<BM, BN, EPI, RB, CB>(g, acc, m0, n0, tn);
+    gemm_epilogue_impl<BM, BN, EPI, RB, CB>(g, acc, m0, n0, tn, smem);
 }
 
 template <int BM, int BN, int EPI, bool PERT>
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
         __syncthreads();
     }
 
-    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
 }
 
 // The same product with the stage tiles written to LDS directly by the loads
@@ -537,7 +567,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
         }
         mma(1);
     }
-    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
+    __syncthreads();  // every wave is done with the stage buffers
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
 }
 
 // Small tiles: two BK = 64 stages.  LDS rows are 128 B (8 chunks of 16 B),
@@ -621,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
         // every wave is done reading this stage before the next issue refills it
         asm volatile("s_barrier" ::: "memory");
     }
-    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn);
+    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
 }
 
 // Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1.
@@ -876,7 +907,8 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
     if constexpr (PERT) {
         // perturbed tiles pass through registers: z is applied before the LDS store
         constexpr int LDK = 64 + 8;
-        const size_t lds = (size_t)(2 * BM * LDK + 2 * BN * LDK) * sizeof(bf16_t);
+        const size_t lds = std::max((size_t)(2 * BM * LDK + 2 * BN * LDK) * sizeof(bf16_t),
+                                    epilogue_lds_bytes<BM, BN>());
         auto kern = gemm_bf16_kernel<BM, BN, EPI, true>;
         static bool attr = false;
         if (!attr) {
@@ -890,8 +922,9 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
     } else {
         // 256-wide tiles: 4-stage BK = 32 ring; 128-wide: 2-stage BK = 64
         constexpr bool big = BM == 256;
-        constexpr size_t lds = big ? (size_t)4 * (BM + BN) * 32 * sizeof(bf16_t)
-                                   : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
+        constexpr size_t stages = big ? (size_t)4 * (BM + BN) * 32 * sizeof(bf16_t)
+                                      : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
+        constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
         if constexpr (big)
             kern = gemm_bf16_dma_kernel<BM, BN, EPI>;
@@ -1064,6 +1097,8 @@ zo_status debug_gemm_bf16(const void* A, const void* W, void* C, int M, int N, i
 {
     if (!A || !W || !C || M <= 0 || N <= 0 || K <= 0) return fail(ZO_ERR_INVALID, "bad GEMM arguments");
     if (K % 64) return fail(ZO_ERR_UNSUPPORTED, "K must be a multiple of 64");
+    if (N % 8) return fail(ZO_ERR_UNSUPPORTED, "N must be a multiple of 8");
+    if (((uintptr_t)A | (uintptr_t)W | (uintptr_t)C) & 15) return fail(ZO_ERR_INVALID, "A, W, C must be 16-byte aligned");
     GemmParams g = {};
     g.A = (const bf16_t*)A; g.W = (const bf16_t*)W; g.C = (bf16_t*)C; g.M = M; g.N = N; g.K = K;
     Pert p = {};

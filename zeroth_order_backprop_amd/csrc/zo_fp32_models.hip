@@ -21,6 +21,7 @@
 #include <string.h>
 
 #include "zo_internal.hpp"
+#include "zo_math.hpp"
 #include "zo_models.hpp"
 #include "zo_rng.hpp"
 
@@ -65,7 +66,6 @@ __device__ __forceinline__ double wave_sum(double v)
 }
 
 // GELU with the exact (erf) form.
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
 enum { EPI_LSQ = 0, EPI_MLP = 1 };
 
