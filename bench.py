@@ -26,12 +26,18 @@ METRIC = "SPSA probe-evals/sec per model + perturb/update HBM GB/s (frac. of pea
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 BF16_PEAK_TFLOPS = 2500.0
+# VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz non-packed 32-bit lane operations per second
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# VALU instructions per generated Gaussian (Philox4x32-10 quarter plus half a
+# Box-Muller pair): the perturb_f32 loop issues 400 per 8 elements including
+# its fma and address arithmetic
+C_Z = 48
 # HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
 # taken on -- set to None when that kernel changes.
 TRAFFIC = {"gemm_f32:mlp:r2": 2 * 16190 * 1024 + 20480 * 1024}
-KERNEL_REV = {"mlp": "gemm_f32:mlp:r3", "lsq": None}
+KERNEL_REV = {"mlp": "sgemm:mlp:r1", "lsq": None}
 
 
 def parse():
@@ -65,7 +71,10 @@ def build_mlp(torch, zo, inputs):
         "params": int(total),
         # algorithmic flops of one evaluation: X W1^T and H W2^T
         "flops_per_eval": 2.0 * B * D * H + 2.0 * B * H * C,
-        "dtype": "f32", "kernel": "gemm_f32", "peak_tflops": FP32_PEAK_TFLOPS,
+        # the dominant kernel forms X Z_i^T for each probe direction (fp32
+        # through six bf16 MFMA products) and generates Z_i (and W2's part)
+        "split_bf16": {"direction_flops": 2.0 * B * D * H, "gaussians": H * D + C * H},
+        "dtype": "f32", "kernel": "gemm_f32", "peak_tflops": BF16_PEAK_TFLOPS,
         "oracle_desc": {"kind": "mlp", "batch": B, "d_in": D, "hidden": H, "classes": C},
         "oracle_batch": {"X": inp["X"], "labels": inp["labels"]}, "arena": arena,
     }
@@ -242,14 +251,27 @@ def main():
     evals_per_s = 2 * N * args.steps / (total_ms * 1e-3)
     k_ms, k_n = zo.timing_query(info["kernel"])
     k_avg_s = k_ms / k_n * 1e-3
+    extra = {}
     if info["kernel"] == "gemm_bf16":
         # layer GEMMs of all evaluations: algorithmic flops / summed launch time
         flops_per_launch = 2 * N * info["gemm_flops_per_eval"] * args.steps / k_n
+    elif "split_bf16" in info:
+        # one launch: N direction products X Z_i^T, each fp32 product taken as
+        # six bf16 MFMA products (priced against the bf16 peak), plus the
+        # generation of every direction element it uses
+        sp = info["split_bf16"]
+        flops_per_launch = 6 * N * sp["direction_flops"]
+        gauss = N * sp["gaussians"]
+        extra = {"fp32_equiv_tflops": round(N * sp["direction_flops"] / k_avg_s / 1e12, 2),
+                 "fp32_equiv_peak": round(BF16_PEAK_TFLOPS / 6, 1),
+                 "gaussians_per_s": round(gauss / k_avg_s, 1),
+                 "valu_frac_generation": round(gauss * C_Z / k_avg_s / VALU_PEAK_LANE_OPS, 4),
+                 "c_z": C_Z}
     else:
         flops_per_launch = 2 * N * info["flops_per_eval"]
     achieved = flops_per_launch / k_avg_s / 1e12
     kernels = {}
-    for fam in ("gemm_f32", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
+    for fam in ("gemm_f32", "gemm_f32_base", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
                 "perturb"):
         ms, n = zo.timing_query(fam)
         if n:
@@ -273,9 +295,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
                      "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
                      "traffic": TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
-                     "kernel": (f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch"
+                     "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), {2 * N} evaluations per launch"
+                                 if "split_bf16" in info else
+                                 f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch")
                                 if info["kernel"] == "gemm_f32" else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
-                     "avg_launch_us": round(k_avg_s * 1e6, 2)},
+                     "avg_launch_us": round(k_avg_s * 1e6, 2), **extra},
         "kernels": kernels,
         "last_losses_mean": float(final.mean()),
     }

@@ -65,6 +65,7 @@ def oracle_loss_at(arena, obatch, seed, probe, sigma):
 @pytest.mark.parametrize("setup,kw", [
     (lsq_setup, {}), (lsq_setup, dict(n=100, d_in=20, d_out=36)),
     (mlp_setup, dict(batch=64, d_in=64, hidden=256)), (mlp_setup, dict(batch=37, d_in=12, hidden=100, classes=3)),
+    (mlp_setup, dict(batch=37, d_in=96, hidden=100, classes=3)), (mlp_setup, dict(batch=300, d_in=160, hidden=388, classes=16)),
     (mlp_setup, {}),
 ])
 def test_forward_losses(setup, kw):

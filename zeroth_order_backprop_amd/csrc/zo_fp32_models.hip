@@ -17,6 +17,8 @@
 // Reductions are two-stage and fixed-order (fp64 partials), so results are
 // bitwise reproducible.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -24,6 +26,7 @@
 #include "zo_math.hpp"
 #include "zo_models.hpp"
 #include "zo_rng.hpp"
+
 
 namespace zo {
 namespace {
@@ -111,6 +114,7 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
 #pragma unroll
             for (int j = 0; j < CB; ++j) acc[v][i][j] = f32x16{};
 
+    static_assert(A_VEC % kThreads == 0 && B_VEC % kThreads == 0, "tile quads must divide evenly over the threads");
     float4 ra[A_PER], rb[B_PER], zb[B_PER];
     // LDS stage st: A tile at smem + st * STAGE, then NV B tiles
     constexpr int STAGE = BM * SA + NV * BN * SA;
@@ -122,49 +126,64 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
         gn = n0 + ln;
         gk = k0 + lk;
     };
+    // Branch-free tile loads: out-of-range quads read element 0 and are
+    // replaced by zeros, so a whole k-step stays one basic block and the
+    // scheduler can place the direction arithmetic between the MFMAs.
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int t = 0; t < A_PER; ++t) {
             const int i = tid + t * kThreads;
             const int r = i / (BK / 4), c4 = i % (BK / 4);
             const int gm = m0 + r, gk = k0 + 4 * c4;
-            ra[t] = (i < A_VEC && gm < M && gk < K) ? *reinterpret_cast<const float4*>(a.X + (size_t)gm * K + gk)
-                                                     : float4{0.f, 0.f, 0.f, 0.f};
+            const bool ok = gm < M && gk < K;
+            const float4 v = *reinterpret_cast<const float4*>(a.X + (ok ? (size_t)gm * K + gk : 0));
+            ra[t] = ok ? v : float4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int t = 0; t < B_PER; ++t) {
             const int i = tid + t * kThreads;
             int ln, lk, gn, gk;
             b_coords(i, k0, ln, lk, gn, gk);
-            const bool ok = i < B_VEC && gn < N && gk < K;
+            const bool ok = gn < N && gk < K;
             const size_t idx = B_KN ? (size_t)gk * N + gn : (size_t)gn * K + gk;
-            rb[t] = ok ? *reinterpret_cast<const float4*>(a.W + idx) : float4{0.f, 0.f, 0.f, 0.f};
+            const float4 v = *reinterpret_cast<const float4*>(a.W + (ok ? idx : 0));
+            rb[t] = ok ? v : float4{0.f, 0.f, 0.f, 0.f};
         }
     };
-    // direction values of B quad t of the tile at k0 (zero outside the matrix)
-    auto gen_z = [&](int t, int k0) {
-        const int i = tid + t * kThreads;
-        int ln, lk, gn, gk;
-        b_coords(i, k0, ln, lk, gn, gk);
-        zb[t] = float4{0.f, 0.f, 0.f, 0.f};
-        if (pert && i < B_VEC && gn < N && gk < K) {
+    // Direction values of B quad t of the tile at k0, as three pieces (the
+    // Philox block, then each Box-Muller pair) that are spread over the
+    // k-step's MFMA groups.  Zero outside the matrix and for the stored weights.
+    uint32_t wd[B_PER][4];
+    bool zok[B_PER];
+    auto z_piece = [&](int piece, int k0) {
+        const int t = piece / 3, part = piece % 3;
+        if (part == 0) {
+            const int i = tid + t * kThreads;
+            int ln, lk, gn, gk;
+            b_coords(i, k0, ln, lk, gn, gk);
+            zok[t] = pert & (gn < N) & (gk < K);
             const size_t idx = B_KN ? (size_t)gk * N + gn : (size_t)gn * K + gk;
-            zb[t] = gauss4(key, probe, (a.w_dir + idx) >> 2);
+            const uint64_t q = (a.w_dir + (zok[t] ? idx : 0)) >> 2;
+            uint32_t c0 = (uint32_t)q, c1 = (uint32_t)(q >> 32), c2 = probe, c3 = 0u;
+            philox4x32_10(c0, c1, c2, c3, key);
+            wd[t][0] = c0; wd[t][1] = c1; wd[t][2] = c2; wd[t][3] = c3;
+        } else {
+            float z0, z1;
+            box_muller(wd[t][2 * part - 2], wd[t][2 * part - 1], z0, z1);
+            if (part == 1) { zb[t].x = zok[t] ? z0 : 0.f; zb[t].y = zok[t] ? z1 : 0.f; }
+            else { zb[t].z = zok[t] ? z0 : 0.f; zb[t].w = zok[t] ? z1 : 0.f; }
         }
     };
     auto store_tiles = [&](int st, int k0) {
 #pragma unroll
         for (int t = 0; t < A_PER; ++t) {
             const int i = tid + t * kThreads;
-            if (i < A_VEC) {
-                const int r = i / (BK / 4), c4 = i % (BK / 4);
-                *reinterpret_cast<float4*>(As(st) + r * SA + 4 * c4) = ra[t];
-            }
+            const int r = i / (BK / 4), c4 = i % (BK / 4);
+            *reinterpret_cast<float4*>(As(st) + r * SA + 4 * c4) = ra[t];
         }
 #pragma unroll
         for (int t = 0; t < B_PER; ++t) {
             const int i = tid + t * kThreads;
-            if (i >= B_VEC) continue;
             int ln, lk, gn, gk;
             b_coords(i, k0, ln, lk, gn, gk);
             const float4 z = zb[t];
@@ -184,51 +203,54 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
             }
         }
     };
-
-    load_tiles(0);
+    // one k-substep of 8: lane (lr, lh) supplies k = kk + 4 lh + s in MFMA
+    // step s; the same permutation of k on both operands leaves the sum unchanged
+    auto mma_step = [&](int st, int kk) {
+        f32x4 af[RB], bf[NV][CB];
 #pragma unroll
-    for (int t = 0; t < B_PER; ++t) gen_z(t, 0);
-    store_tiles(0, 0);
-    __syncthreads();
-    int cur = 0;
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        const bool more = k0 + BK < K;
-        if (more) load_tiles(k0 + BK);  // in flight during the MFMAs
+        for (int i = 0; i < RB; ++i)
+            af[i] = *reinterpret_cast<const f32x4*>(As(st) + (wm * WM + i * 32 + lr) * SA + kk + 4 * lh);
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 8) {
-            // lane (lr, lh) supplies k = kk + 4 lh + s in MFMA step s: the
-            // same permutation of k on both operands leaves the sum unchanged
-            f32x4 af[RB], bf[NV][CB];
+        for (int v = 0; v < NV; ++v)
 #pragma unroll
-            for (int i = 0; i < RB; ++i)
-                af[i] = *reinterpret_cast<const f32x4*>(As(cur) + (wm * WM + i * 32 + lr) * SA + kk + 4 * lh);
+            for (int j = 0; j < CB; ++j)
+                bf[v][j] = *reinterpret_cast<const f32x4*>(Bs(st, v) + (wn * WN + j * 32 + lr) * SA + kk + 4 * lh);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int v = 0; v < NV; ++v)
 #pragma unroll
-                for (int j = 0; j < CB; ++j)
-                    bf[v][j] = *reinterpret_cast<const f32x4*>(Bs(cur, v) + (wn * WN + j * 32 + lr) * SA + kk + 4 * lh);
+                for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                    for (int j = 0; j < CB; ++j)
+                        acc[v][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[v][j][s], acc[v][i][j],
+                                                                            0, 0, 0);
+    };
+    constexpr int NKK = BK / 8, NPIECE = 3 * B_PER;
+
+    load_tiles(0);
 #pragma unroll
-                for (int v = 0; v < NV; ++v)
+    for (int pc = 0; pc < NPIECE; ++pc) z_piece(pc, 0);
+    store_tiles(0, 0);
+    __syncthreads();
+    int cur = 0;
+    const int KT = (K + BK - 1) / BK;
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const int kn = (kt + 1) * BK;
+        load_tiles(kn);  // in flight during the MFMAs
 #pragma unroll
-                    for (int i = 0; i < RB; ++i)
+        for (int kk = 0; kk < NKK; ++kk) {
+            mma_step(cur, 8 * kk);
 #pragma unroll
-                        for (int j = 0; j < CB; ++j)
-                            acc[v][i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[v][j][s], acc[v][i][j],
-                                                                                0, 0, 0);
-            // the next tile's direction values, spread over this tile's MFMA
-            // groups so the VALU work overlaps the matrix cores
-            if (more) {
-#pragma unroll
-                for (int t = 0; t < B_PER; ++t)
-                    if ((t * (BK / 8)) / B_PER == kk / 8) gen_z(t, k0 + BK);
-            }
+            for (int pc = 0; pc < NPIECE; ++pc)
+                if ((pc * NKK) / NPIECE == kk) z_piece(pc, kn);
         }
-        if (more) store_tiles(cur ^ 1, k0 + BK);
+        store_tiles(cur ^ 1, kn);
         __syncthreads();
         cur ^= 1;
     }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) mma_step(cur, 8 * kk);
 
     // accumulator element r of a 32x32 tile: row 8 (r/4) + 4 lh + r%4, col lr
     if constexpr (EPI == EPI_LSQ) {
@@ -392,6 +414,351 @@ __global__ __launch_bounds__(64) void mlp_ce_final(const double* __restrict__ ch
 // ---------------------------------------------------------------- host side
 // LSQ tiles: C[512 x 256] per eval in 128 x 64 tiles.  MLP: all 256 rows per
 // block so each W1 element's direction value is regenerated once per probe.
+// ============================================================ split-bf16 MLP GEMMs
+// fp32 products on the bf16 matrix cores.  Each fp32 operand value is split
+// exactly into three bf16 parts, x = x0 + x1 + x2 (8 + 8 + 8 significand
+// bits), and x w is taken as x0w0 + x0w1 + x1w0 + x0w2 + x1w1 + x2w0: the
+// three dropped products weigh at most 2^-24 relative to x0w0, bf16 products
+// are exact in fp32 and the MFMA accumulates in fp32, so the result carries
+// the error of an fp32 dot product.  On this chip fp32 MFMAs do not overlap
+// VALU work while bf16 MFMAs do, and the six bf16 products of a 16-deep k
+// step cost 12 cycles per k against 32 for fp32 MFMAs.
+//
+// The first layer is linear in W1, so for a perturbation sigma z,
+// X (W1 + sigma Z)^T = X W1^T + sigma X Z^T: the stored-weight product is
+// formed once per call and each evaluation group (one direction, NV signs)
+// needs one product with its direction tile, generated into LDS in the main
+// loop, instead of NV products with perturbed weights.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// q = p0 + p1 + p2 exactly (per element), bf16 pairs packed (low, high)
+__device__ __forceinline__ void split4(float4 q, uint2 (&p)[3])
+{
+    uint32_t a = bf16x2_rne(q.x, q.y), b = bf16x2_rne(q.z, q.w);
+    p[0] = uint2{a, b};
+    float r0 = q.x - bf16_lo(a), r1 = q.y - bf16_hi(a), r2 = q.z - bf16_lo(b), r3 = q.w - bf16_hi(b);
+    a = bf16x2_rne(r0, r1);
+    b = bf16x2_rne(r2, r3);
+    p[1] = uint2{a, b};
+    r0 -= bf16_lo(a); r1 -= bf16_hi(a); r2 -= bf16_lo(b); r3 -= bf16_hi(b);
+    p[2] = uint2{bf16x2_rne(r0, r1), bf16x2_rne(r2, r3)};
+}
+
+// x [n4 quads] -> three bf16 planes, plane k at planes + k * plane_stride
+__global__ __launch_bounds__(kThreads) void split_planes_kernel(const float* __restrict__ x, size_t n4,
+                                                                bf16_t* __restrict__ planes, size_t plane_stride)
+{
+    for (size_t q = (size_t)blockIdx.x * kThreads + threadIdx.x; q < n4; q += (size_t)gridDim.x * kThreads) {
+        uint2 p[3];
+        split4(reinterpret_cast<const float4*>(x)[q], p);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) reinterpret_cast<uint2*>(planes + k * plane_stride)[q] = p[k];
+    }
+}
+
+enum { SG_BASE_STORE = 0, SG_BASE_MLP = 1, SG_PROBE_MLP = 2 };
+
+struct SplitArgs {
+    const bf16_t* Xp;   // [3][M][K] bf16 planes of X
+    const float* W;     // [N][K] first-layer weights (base modes)
+    uint64_t w_dir;     // direction index of W[0][0]
+    int M, N, K;
+    float* H;           // [M][N] X W^T: written by SG_BASE_STORE, read by SG_PROBE_MLP
+    const float* W2;    // [C][N]
+    uint64_t w2_dir;
+    int C;
+    float* logit_part;  // [eval][n_tile][M][C]
+};
+
+// vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+#define ZO_WAIT_VM0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+
+// C = X B^T over one BM x BN tile with K % 32 == 0: B = W (base modes) or the
+// direction tile Z of group blockIdx.z (probe mode).  NT/64 waves in a
+// (NT/128) x 2 grid, each owning (BM/(NT/128)) x (BN/2) as 32x32 MFMA blocks.
+// LDS stage: the three X planes (BM rows of 32 bf16, written by direct-to-LDS
+// loads) then the three B planes (BN rows, written from registers after the
+// split); rows are 64 B with chunk c of row r at c ^ ((r >> 2) & 3).  One
+// barrier per k step: the next stage is filled while the current one feeds
+// the MFMAs.
+//   SG_BASE_STORE: H = acc.
+//   SG_BASE_MLP:   stored weights, logits of GELU(acc) against W2.
+//   SG_PROBE_MLP:  for each sign v, logits of GELU(H + sigma_v acc) against
+//                  W2 + sigma_v z2 (z2 the same direction's W2 part).
+template <int BM, int BN, int NT, int MODE, int NV>
+__global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
+{
+    constexpr int BK = 32;
+    constexpr int WAVES_M = NT / 128, WM = BM / WAVES_M, WN = BN / 2;
+    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int PA = BM * BK, PB = BN * BK;          // bf16 per plane
+    constexpr int STAGE = 3 * (PA + PB);
+    constexpr int A_INS = 3 * PA / 8 / NT;             // 16-byte loads per thread per stage
+    constexpr int B_Q = PB / 4 / NT;                   // B quads per thread per stage
+    static_assert(A_INS * NT * 8 == 3 * PA && B_Q * NT * 4 == PB, "tile / thread mismatch");
+    static_assert(RB >= 1 && CB >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    extern __shared__ __align__(16) bf16_t lds_bf[];
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int tn = blockIdx.x, m0 = blockIdx.y * BM, n0 = tn * BN;
+    const int g = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+    const Key key = make_key(ev.seed[g]);
+    const uint32_t probe = ev.probe[g];
+
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+
+    // ---- X planes: direct-to-LDS, rows past M clamped (never stored)
+    auto issue_a = [&](int st, int k0) {
+        bf16_t* base = lds_bf + st * STAGE;
+#pragma unroll
+        for (int j = 0; j < A_INS; ++j) {
+            const int p = j * NT + tid;
+            const int plane = p / (BM * 4), rem = p % (BM * 4), row = rem >> 2;
+            const int lc = (rem & 3) ^ ((row >> 2) & 3);
+            const bf16_t* src = a.Xp + (size_t)plane * M * K + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
+            bf16_t* dst = base + (j * NT + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+    // ---- B quads: t-th quad of this thread is row ln = i / 8, k = 4 (i % 8)
+    float4 bq[B_Q];
+    uint32_t wd[B_Q][4];
+    auto b_row = [&](int t) { return (t * NT + tid) >> 3; };
+    auto b_k = [&](int t) { return 4 * ((t * NT + tid) & 7); };
+    auto load_b = [&](int k0) {  // base modes: W quads (zero past N)
+#pragma unroll
+        for (int t = 0; t < B_Q; ++t) {
+            const int gn = n0 + b_row(t);
+            const bool ok = gn < N;
+            const float4 v = *reinterpret_cast<const float4*>(a.W + (ok ? (size_t)gn * K + k0 + b_k(t) : 0));
+            bq[t] = ok ? v : float4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    // probe mode: direction quads in three pieces (Philox block, then each
+    // Box-Muller pair) so the VALU work spreads between the MFMAs
+    auto z_piece = [&](int piece, int k0) {
+        const int t = piece / 3, part = piece % 3;
+        const int gn = n0 + b_row(t);
+        if (part == 0) {
+            const uint64_t q = (a.w_dir + (size_t)min(gn, N - 1) * K + k0 + b_k(t)) >> 2;
+            uint32_t c0 = (uint32_t)q, c1 = (uint32_t)(q >> 32), c2 = probe, c3 = 0u;
+            philox4x32_10(c0, c1, c2, c3, key);
+            wd[t][0] = c0; wd[t][1] = c1; wd[t][2] = c2; wd[t][3] = c3;
+        } else {
+            float z0, z1;
+            box_muller(wd[t][2 * part - 2], wd[t][2 * part - 1], z0, z1);
+            const bool ok = gn < N;
+            if (part == 1) { bq[t].x = ok ? z0 : 0.f; bq[t].y = ok ? z1 : 0.f; }
+            else { bq[t].z = ok ? z0 : 0.f; bq[t].w = ok ? z1 : 0.f; }
+        }
+    };
+    auto store_b = [&](int st) {
+        bf16_t* base = lds_bf + st * STAGE + 3 * PA;
+#pragma unroll
+        for (int t = 0; t < B_Q; ++t) {
+            uint2 p[3];
+            split4(bq[t], p);
+            const int row = b_row(t), k = b_k(t);
+            const int off = row * BK + ((((k >> 3) ^ ((row >> 2) & 3))) << 3) + (k & 4);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) *reinterpret_cast<uint2*>(base + pl * PB + off) = p[pl];
+        }
+    };
+    // ---- one 16-deep k step: six bf16 products per 32x32 block, smallest first
+    auto mma_step = [&](int st, int ks) {
+        const bf16_t* base = lds_bf + st * STAGE;
+        bf16x8 af[RB][3], bfr[CB][3];
+        const int lc = 2 * ks + lh;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int row = wm * WM + i * 32 + lr;
+            const int off = row * BK + ((lc ^ ((row >> 2) & 3)) << 3);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) af[i][pl] = *reinterpret_cast<const bf16x8*>(base + pl * PA + off);
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int row = wn * WN + j * 32 + lr;
+            const int off = row * BK + ((lc ^ ((row >> 2) & 3)) << 3);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+                bfr[j][pl] = *reinterpret_cast<const bf16x8*>(base + 3 * PA + pl * PB + off);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                f32x16 c = acc[i][j];
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][2], bfr[j][0], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][1], bfr[j][1], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][2], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][1], bfr[j][0], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][1], c, 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][0], c, 0, 0, 0);
+            }
+    };
+    constexpr int NPIECE = 3 * B_Q;
+    auto produce_b = [&](int k0) {
+        if constexpr (MODE == SG_PROBE_MLP) {
+#pragma unroll
+            for (int pc = 0; pc < NPIECE; ++pc) z_piece(pc, k0);
+        } else {
+            load_b(k0);
+        }
+    };
+
+    const int KT = K / BK;
+    issue_a(0, 0);
+    produce_b(0);
+    store_b(0);
+    ZO_WAIT_VM0();
+    __syncthreads();
+    int cur = 0;
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const int kn = (kt + 1) * BK;
+        issue_a(cur ^ 1, kn);
+        if constexpr (MODE != SG_PROBE_MLP) load_b(kn);
+        mma_step(cur, 0);
+        if constexpr (MODE == SG_PROBE_MLP) {
+#pragma unroll
+            for (int pc = 0; pc < NPIECE / 2; ++pc) z_piece(pc, kn);
+        }
+        mma_step(cur, 1);
+        if constexpr (MODE == SG_PROBE_MLP) {
+#pragma unroll
+            for (int pc = NPIECE / 2; pc < NPIECE; ++pc) z_piece(pc, kn);
+        }
+        store_b(cur ^ 1);
+        ZO_WAIT_VM0();
+        __syncthreads();
+        cur ^= 1;
+    }
+    mma_step(cur, 0);
+    mma_step(cur, 1);
+
+    // accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr
+    if constexpr (MODE == SG_BASE_STORE) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (row < M && col < N) a.H[(size_t)row * N + col] = acc[i][j][r];
+                }
+    } else {
+        // GELU(H tile) -> LDS, then partial logits over this tile's BN hidden
+        // units against the (perturbed) W2 columns n0 .. n0+BN.  Columns past
+        // N hold GELU(0) = 0 and meet zero W2 weights.
+        constexpr int SH = BN + 4;  // 16-byte rows; float4 row reads by consecutive rows are bank-even
+        constexpr int GROUPS = NT / BM, CPG = (kMaxClasses + GROUPS - 1) / GROUPS;
+        static_assert(GROUPS * BM == NT, "one thread per (row, class group)");
+        float* Hs = reinterpret_cast<float*>(lds_bf);    // BM x SH
+        float* W2s = Hs + BM * SH;                      // NV x C x BN
+        const int C = a.C;
+        const int cpg = (C + GROUPS - 1) / GROUPS;      // classes per thread group, balanced
+        const bool pert = MODE == SG_PROBE_MLP && ev.perturbed != 0;
+        float sig[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) sig[v] = MODE == SG_PROBE_MLP ? ev.sigma[g][v] : 0.f;
+        // the stored-weight product under this thread's accumulators, loaded
+        // first so its latency hides behind the W2 tile generation
+        float hb[RB][CB][16];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    hb[i][j][r] = 0.f;
+                    if constexpr (MODE == SG_PROBE_MLP) {
+                        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int col = n0 + wn * WN + j * 32 + lr;
+                        if (row < M && col < N) hb[i][j][r] = a.H[(size_t)row * N + col];
+                    }
+                }
+        __syncthreads();  // every wave is done with the stage buffers
+        for (int q = tid; q < C * (BN / 4); q += NT) {
+            const int c = q / (BN / 4), n4 = 4 * (q % (BN / 4));
+            const int gn = n0 + n4;
+            float4 w = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+            if (gn < N) {
+                const size_t idx = (size_t)c * N + gn;
+                w = *reinterpret_cast<const float4*>(a.W2 + idx);
+                if (pert) z = gauss4(key, probe, (a.w2_dir + idx) >> 2);
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                *reinterpret_cast<float4*>(W2s + (v * C + c) * BN + n4) =
+                    float4{fmaf(sig[v], z.x, w.x), fmaf(sig[v], z.y, w.y), fmaf(sig[v], z.z, w.z),
+                           fmaf(sig[v], z.w, w.w)};
+        }
+        const int row = tid % BM, grp = tid / BM;
+        const int gm = m0 + row;
+        const int c0 = grp * cpg, c1 = min(C, c0 + cpg);
+#pragma unroll 1
+        for (int v = 0; v < NV; ++v) {
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int lcol = wn * WN + j * 32 + lr;
+                        const float h = MODE == SG_PROBE_MLP ? fmaf(sig[v], acc[i][j][r], hb[i][j][r]) : acc[i][j][r];
+                        Hs[lrow * SH + lcol] = gelu_erf(h);
+                    }
+            __syncthreads();
+            float p[CPG];
+#pragma unroll
+            for (int cc = 0; cc < CPG; ++cc) p[cc] = 0.f;
+            const float* hrow = Hs + row * SH;
+            const float* w2v = W2s + v * C * BN;
+            for (int n = 0; n < BN; n += 4) {
+                const float4 h4 = *reinterpret_cast<const float4*>(hrow + n);
+#pragma unroll
+                for (int cc = 0; cc < CPG; ++cc) {
+                    if (c0 + cc < c1) {
+                        const float4 w4 = *reinterpret_cast<const float4*>(w2v + (c0 + cc) * BN + n);
+                        float t = p[cc];
+                        t = fmaf(h4.x, w4.x, t); t = fmaf(h4.y, w4.y, t);
+                        t = fmaf(h4.z, w4.z, t); t = fmaf(h4.w, w4.w, t);
+                        p[cc] = t;
+                    }
+                }
+            }
+            if (gm < M) {
+                float* dst = a.logit_part + (((size_t)ev.out[g][v] * gridDim.x + tn) * M + gm) * C;
+#pragma unroll
+                for (int cc = 0; cc < CPG; ++cc)
+                    if (c0 + cc < c1) dst[c0 + cc] = p[cc];
+            }
+            __syncthreads();  // Hs is rewritten for the next sign
+        }
+    }
+}
+
 constexpr int LSQ_BM = 128, LSQ_BN = 64, LSQ_BK = 32;
 constexpr int MLP_BM = 256, MLP_BN = 64, MLP_BK = 32;
 
@@ -444,6 +811,31 @@ zo_status launch_fgemm(const GemmArgs& a, const EvalList& ev, hipStream_t s)
     KernelTimer timer("gemm_f32", s);
     kern<<<grid, NT, lds, s>>>(a, ev);
     return check_launch("fp32 fused GEMM");
+}
+
+// Split-bf16 MLP GEMM tiles: probe groups 256 x 128 (8 waves), the stored-
+// weight product 64 x 64 (4 waves) so that one call still spreads over the CUs.
+constexpr int SP_BM = 256, SP_BN = 128, SP_NT = 512;
+constexpr int SB_BM = 64, SB_BN = 64, SB_NT = 256;
+
+template <int BM, int BN, int NT, int MODE, int NV>
+zo_status launch_sgemm(const SplitArgs& a, const EvalList& ev, int groups, hipStream_t s, const char* fam)
+{
+    constexpr size_t stages = (size_t)2 * 3 * (BM + BN) * 32 * sizeof(bf16_t);
+    constexpr size_t epi = MODE == SG_BASE_STORE ? 0 : (size_t)(BM * (BN + 4) + NV * kMaxClasses * BN) * sizeof(float);
+    constexpr size_t lds = stages > epi ? stages : epi;
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    auto kern = sgemm_kernel<BM, BN, NT, MODE, NV>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
+        attr_set = true;
+    }
+    dim3 grid(cdiv(a.N, BN), cdiv(a.M, BM), groups);
+    KernelTimer timer(fam, s);
+    kern<<<grid, NT, lds, s>>>(a, ev);
+    return check_launch("split-bf16 MLP GEMM");
 }
 
 }  // namespace
@@ -504,9 +896,17 @@ size_t mlp_part_bytes(const zo_model_desc& d)
     return (kMaxEvalsPerCall * tiles * d.batch * d.classes * sizeof(float) + 255) / 256 * 256;
 }
 
+// workspace: logit partials | per-chunk CE sums | X planes (3 M K bf16) | X W1^T (M N fp32)
+size_t mlp_chunk_bytes(const zo_model_desc& d)
+{
+    return (kMaxEvalsPerCall * (size_t)cdiv((int)d.batch, 64) * sizeof(double) + 255) / 256 * 256;
+}
+size_t mlp_planes_bytes(const zo_model_desc& d) { return (3 * (size_t)d.batch * d.d_in * 2 + 255) / 256 * 256; }
+size_t mlp_h_bytes(const zo_model_desc& d) { return ((size_t)d.batch * d.hidden * 4 + 255) / 256 * 256; }
+
 size_t mlp_workspace(const zo_model_desc& d)
 {
-    return mlp_part_bytes(d) + kMaxEvalsPerCall * (size_t)cdiv((int)d.batch, 64) * sizeof(double);
+    return mlp_part_bytes(d) + mlp_chunk_bytes(d) + mlp_planes_bytes(d) + mlp_h_bytes(d);
 }
 
 zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
@@ -515,27 +915,67 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
     const zo_model_desc& d = m.desc;
     EvalList ev;
     const int nv = make_evals(perts, n, ev);
-    GemmArgs a = {};
-    a.X = (const float*)b.x;
-    a.W = (const float*)m.params + m.offsets[0];
-    a.w_dir = m.offsets[0];
-    a.M = (int)b.batch;
-    a.N = (int)d.hidden;
-    a.K = (int)d.d_in;
-    a.W2 = (const float*)m.params + m.offsets[1];
-    a.w2_dir = m.offsets[1];
-    a.C = (int)d.classes;
-    a.logit_part = (float*)m.workspace;
-    zo_status st = nv == 2 ? launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 2, EPI_MLP, 512>(a, ev, s)
-                           : launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 1, EPI_MLP, 512>(a, ev, s);
+    const int M = (int)b.batch, N = (int)d.hidden, K = (int)d.d_in;
+    char* ws = (char*)m.workspace;
+    float* logit_part = (float*)ws;
+    double* chunk_sum = (double*)(ws + mlp_part_bytes(d));
+    int n_tiles;
+    zo_status st;
+    if (K % 32 == 0) {
+        // split-bf16 path: X planes, then X W1^T, then one product per group
+        bf16_t* planes = (bf16_t*)(ws + mlp_part_bytes(d) + mlp_chunk_bytes(d));
+        SplitArgs a = {};
+        a.Xp = planes;
+        a.W = (const float*)m.params + m.offsets[0];
+        a.w_dir = m.offsets[0];
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.H = (float*)((char*)planes + mlp_planes_bytes(d));
+        a.W2 = (const float*)m.params + m.offsets[1];
+        a.w2_dir = m.offsets[1];
+        a.C = (int)d.classes;
+        a.logit_part = logit_part;
+        {
+            const size_t n4 = (size_t)M * K / 4;
+            KernelTimer timer("gemm_f32_base", s);
+            split_planes_kernel<<<(int)std::min<size_t>((n4 + kThreads - 1) / kThreads, 2048), kThreads, 0, s>>>(
+                (const float*)b.x, n4, planes, (size_t)M * K);
+        }
+        if ((st = check_launch("X split"))) return st;
+        if (n == 0) {
+            st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1>(a, ev, 1, s, "gemm_f32");
+            n_tiles = cdiv(N, SB_BN);
+        } else {
+            st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_STORE, 1>(a, ev, 1, s, "gemm_f32_base");
+            if (st) return st;
+            st = nv == 2 ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 2>(a, ev, ev.n_groups, s, "gemm_f32")
+                         : launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 1>(a, ev, ev.n_groups, s, "gemm_f32");
+            n_tiles = cdiv(N, SP_BN);
+        }
+    } else {
+        GemmArgs a = {};
+        a.X = (const float*)b.x;
+        a.W = (const float*)m.params + m.offsets[0];
+        a.w_dir = m.offsets[0];
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.W2 = (const float*)m.params + m.offsets[1];
+        a.w2_dir = m.offsets[1];
+        a.C = (int)d.classes;
+        a.logit_part = logit_part;
+        st = nv == 2 ? launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 2, EPI_MLP, 512>(a, ev, s)
+                     : launch_fgemm<MLP_BM, MLP_BN, MLP_BK, false, 1, EPI_MLP, 512>(a, ev, s);
+        n_tiles = cdiv(N, MLP_BN);
+    }
     if (st) return st;
     const int n_evals = n == 0 ? 1 : n;
-    double* chunk_sum = (double*)((char*)m.workspace + mlp_part_bytes(d));
-    const int n_chunks = cdiv(a.M, 64);
+    const int n_chunks = cdiv(M, 64);
     KernelTimer timer("reduce", s);
-    mlp_ce_rows<<<dim3(n_chunks, n_evals), kThreads, 0, s>>>(a.logit_part, cdiv(a.N, MLP_BN), a.M, a.C, b.labels,
+    mlp_ce_rows<<<dim3(n_chunks, n_evals), kThreads, 0, s>>>(logit_part, n_tiles, M, (int)d.classes, b.labels,
                                                               chunk_sum);
-    mlp_ce_final<<<n_evals, 64, 0, s>>>(chunk_sum, n_chunks, a.M, loss);
+    mlp_ce_final<<<n_evals, 64, 0, s>>>(chunk_sum, n_chunks, M, loss);
     return check_launch("mlp cross-entropy");
 }
 
