@@ -44,8 +44,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
     for (int round = 0; round < 10; ++round) {
         const uint64_t pa = (uint64_t)c0 * kMulA;
         const uint64_t pb = (uint64_t)c2 * kMulB;
-        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        // three-way xor in one v_bitop3_b32 (truth table 0x96 = a ^ b ^ c)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c3, k1, 0x96);
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;
