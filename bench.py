@@ -36,7 +36,7 @@ C_Z = 48
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
 # taken on -- set to None when that kernel changes.
-TRAFFIC = {"gemm_f32:mlp:r2": 2 * 16190 * 1024 + 20480 * 1024}
+TRAFFIC = {"sgemm:mlp:r1": 2 * 8506 * 1024 + 10240 * 1024}
 KERNEL_REV = {"mlp": "sgemm:mlp:r1", "lsq": None}
 
 
