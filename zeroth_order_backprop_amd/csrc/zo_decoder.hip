@@ -35,6 +35,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;
 
 constexpr int kThreads = 256;
+constexpr int kDmaThreads = 512, kDmaWavesM = 4;  // 256 x 256 stored-weight GEMM
 
 // A perturbation applied while reading weights.
 struct Pert {
@@ -244,14 +245,16 @@ __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& t
 template <int BM, int BN>
 constexpr size_t epilogue_lds_bytes() { return (size_t)BM * (BN + 8) * sizeof(bf16_t); }
 
-template <int BM, int BN, int EPI, int RB, int CB>
+template <int BM, int BN, int EPI, int RB, int CB, int NT, int WGM>
 __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn,
                                                    bf16_t* smem)
 {
-    constexpr int WM = BM / 2, WN = BN / 2;
+    // NT threads as a WGM x WGN grid of waves, each owning WM x WN
+    constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
+    static_assert(WM == RB * 32 && WN == CB * 32, "wave tile mismatch");
     const int M = g.M, N = g.N;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int lr = lane & 31, lh = lane >> 5;
     if constexpr (EPI != EPI_LMHEAD) {
         constexpr int LDC = BN + 8;
@@ -271,7 +274,7 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
         __syncthreads();
         constexpr int CPR = BN / 8;  // 16-byte chunks per row
 #pragma unroll 4
-        for (int p = tid; p < BM * CPR; p += kThreads) {
+        for (int p = tid; p < BM * CPR; p += NT) {
             const int row = p / CPR, cc = p % CPR;
             const int gr = m0 + row, gc = n0 + 8 * cc;
             if (gr >= M || gc >= N) continue;
@@ -288,6 +291,7 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
             *dst = v;
         }
     } else {
+        static_assert(WGN == 2 && NT == kThreads, "LM-head partials assume two wave columns");
         // Fused cross-entropy partials over this tile's BN vocabulary columns:
         // per row the max and the sum of exp(logit - max), plus the target
         // logit when the target column lies in this tile.
@@ -342,11 +346,11 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
     }
 }
 
-template <int BM, int BN, int EPI, int RB, int CB>
+template <int BM, int BN, int EPI, int NT = kThreads, int WGM = 2, int RB, int CB>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& g, f32x16 (&acc)[RB][CB], int m0, int n0, int tn,
                                               bf16_t* smem)
 {
-    gemm_epilogue_impl<BM, BN, EPI, RB, CB>(g, acc, m0, n0, tn, smem);
+    gemm_epilogue_impl<BM, BN, EPI, RB, CB, NT, WGM>(g, acc, m0, n0, tn, smem);
 }
 
 template <int BM, int BN, int EPI, bool PERT>
@@ -457,22 +461,25 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
 #define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
-// Large tiles: ring of 4 BK = 32 stages, prefetch distance 3.  LDS rows are
+// Large tiles: 8 waves (two per SIMD, so one wave's MFMAs cover the other's
+// LDS and barrier waits) in a 4 x 2 grid of 64 x 128 wave tiles; a ring of 4
+// BK = 32 stages, prefetch distance 3.  LDS rows are
 // 64 B (4 chunks of 16 B), chunk c of row r at position c ^ ((r >> 2) & 3),
 // so the 32 rows a fragment read touches spread over all banks.  The two
 // k-halves of a stage are read into alternating register sets: the second
 // half's reads and the next stage's first half are issued while the MFMAs of
 // the previous half run.
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
+__global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g)
 {
     constexpr int BK = 32, STAGES = 4;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int NT = kDmaThreads, WGM = kDmaWavesM, WGN = NT / 64 / WGM;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int RB = WM / 32, CB = WN / 32;
-    constexpr int A_INS = BM * 4 / kThreads, B_INS = BN * 4 / kThreads;
+    constexpr int A_INS = BM * 4 / NT, B_INS = BN * 4 / NT;
     constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
     constexpr int STAGE = (BM + BN) * BK;
-    static_assert(A_INS * kThreads == BM * 4 && B_INS * kThreads == BN * 4, "tile / thread mismatch");
+    static_assert(A_INS * NT == BM * 4 && B_INS * NT == BN * 4, "tile / thread mismatch");
     static_assert(2 * INS < 64, "vmcnt range");
     extern __shared__ __align__(16) bf16_t lds[];
 
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
     tile_of<4>(blockIdx.x, nbm, nbn, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int lr = lane & 31, lh = lane >> 5;
 
     f32x16 acc[RB][CB];
@@ -498,16 +505,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
         const int k0 = kt * BK;
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
-            const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+            const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
             const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sa + (j * kThreads + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
+            bf16_t* dst = sa + (j * NT + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < B_INS; ++j) {
-            const int p = j * kThreads + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+            const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
             const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sb + (j * kThreads + wave * 64) * 8;
+            bf16_t* dst = sb + (j * NT + wave * 64) * 8;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams g)
         mma(1);
     }
     __syncthreads();  // every wave is done with the stage buffers
-    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
+    gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
 // Small tiles: two BK = 64 stages.  LDS rows are 128 B (8 chunks of 16 B),
@@ -938,7 +945,7 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
             attr = true;
         }
         KernelTimer timer(fam, s);
-        kern<<<blocks, kThreads, lds, s>>>(gp);
+        kern<<<blocks, big ? kDmaThreads : kThreads, lds, s>>>(gp);
     }
     return check_launch("bf16 GEMM");
 }
