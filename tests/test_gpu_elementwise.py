@@ -65,10 +65,11 @@ def test_box_muller_exhaustive_radius():
 
 
 def test_box_muller_exhaustive_angle():
-    """Every one of the 2^24 angle inputs at the largest radius (a = 0, r = 5.77)
-    and at a mid radius."""
+    """Every one of the 2^24 angle inputs at the largest radius (a = 0, r = 5.77),
+    at a mid radius, and at the two radius inputs where the hardware log2 errs
+    most (a = 225: largest effect on r; a = 64456: largest error in ulps)."""
     b = np.arange(1 << 24, dtype=np.uint64).astype(np.uint32) << np.uint32(8)
-    for a in (0, 1 << 23):
+    for a in (0, 225, 64456, 1 << 23):
         pairs = np.stack([np.full_like(b, a << 8), b], axis=1)
         got = _bm_gpu(pairs)
         want = oracle.box_muller_f64_array(pairs)

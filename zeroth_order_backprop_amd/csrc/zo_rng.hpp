@@ -14,10 +14,10 @@
 // Box-Muller: u_r = ((x_even >> 8) + 1) 2^-24, u_t = (x_odd >> 8) 2^-24,
 // r = sqrt(-2 ln u_r), (z_even, z_odd) = r (cos 2 pi u_t, sin 2 pi u_t).
 //
-// The fp32 evaluation here is this file's own: ln via exponent extraction and
-// the atanh series, sin/cos of a quarter turn via their Taylor series on
-// [-pi/4, pi/4] after an exact integer quadrant reduction, and sqrt carried as
-// a value plus its residual so the final product is rounded once.
+// The fp32 evaluation: ln u_r from the hardware log2 with the scaling carried
+// exactly, sin/cos of a quarter turn via their Taylor series on [-pi/4, pi/4]
+// after an exact integer quadrant reduction, and sqrt carried as a value plus
+// its residual so the final product is rounded once.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,39 +70,20 @@ constexpr float kS1 = (float)sin_coef(0), kS3 = (float)sin_coef(1), kS5 = (float
                 kS7 = (float)sin_coef(3), kS9 = (float)sin_coef(4);
 constexpr float kC2 = (float)cos_coef(1), kC4 = (float)cos_coef(2), kC6 = (float)cos_coef(3),
                 kC8 = (float)cos_coef(4), kC10 = (float)cos_coef(5);
-// ln(1+f) = 2 atanh(s), s = f / (2 + f): 2 (s + s^3/3 + s^5/5 + ...)
-constexpr float kA3 = (float)(2.0 / 3.0), kA5 = (float)(2.0 / 5.0), kA7 = (float)(2.0 / 7.0),
-                kA9 = (float)(2.0 / 9.0);
 constexpr double kLn2 = 0.693147180559945309417232121458176568;
-constexpr float kLn2Hi = (float)kLn2;
-constexpr float kLn2Lo = (float)(kLn2 - (double)(float)kLn2);
 
-// -2 ln(u_r) for u_r = (a + 1) 2^-24, a = x >> 8.
-__device__ __forceinline__ float minus_two_log_radius(uint32_t x)
+// -2 ln(u_r) for u_r = (a + 1) 2^-24, a = x >> 8, as L + L_lo.  u_r is exact
+// in fp32; the hardware log2 (v_log_f32) is within one ulp on every one of
+// these 2^24 inputs, and the factor -2 ln 2 is applied in two parts so that
+// L + L_lo carries no further rounding.
+constexpr float kM2Ln2Hi = (float)(-2.0 * kLn2);
+constexpr float kM2Ln2Lo = (float)(-2.0 * kLn2 - (double)kM2Ln2Hi);
+__device__ __forceinline__ void minus_two_log_radius(uint32_t x, float& L, float& L_lo)
 {
-    const uint32_t n = (x >> 8) + 1u;          // 1 .. 2^24, exact in fp32
-    const float nf = (float)n;
-    const uint32_t bits = __float_as_uint(nf);
-    int e = (int)(bits >> 23) - 127;           // nf = m 2^e, m in [1, 2)
-    float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u);
-    if (m > 1.41421356237f) {                  // move m into [sqrt(1/2), sqrt(2))
-        m *= 0.5f;
-        e += 1;
-    }
-    const float f = m - 1.0f;                  // exact
-    const float den = 2.0f + f;
-    const float rcp = __builtin_amdgcn_rcpf(den);
-    float s = f * rcp;
-    s = fmaf(fmaf(-s, den, f), rcp, s);        // one Newton correction of f / den
-    const float s2 = s * s;
-    float p = kA9;
-    p = fmaf(p, s2, kA7);
-    p = fmaf(p, s2, kA5);
-    p = fmaf(p, s2, kA3);
-    const float log1p_f = fmaf(s * s2, p, 2.0f * s);    // ln m
-    const float ef = (float)(e - 24);                   // u_r = m 2^(e - 24)
-    const float ln_u = fmaf(ef, kLn2Hi, fmaf(ef, kLn2Lo, log1p_f));
-    return -2.0f * ln_u;
+    const float u = (float)((x >> 8) + 1u) * 0x1p-24f;
+    const float l2 = __builtin_amdgcn_logf(u);
+    L = l2 * kM2Ln2Hi;
+    L_lo = fmaf(l2, kM2Ln2Lo, fmaf(l2, kM2Ln2Hi, -L));
 }
 
 // (cos, sin) of 2 pi u_t for u_t = (x >> 8) 2^-24.
@@ -136,10 +117,11 @@ __device__ __forceinline__ void unit_circle(uint32_t x, float& c, float& s)
 // Box-Muller pair from two words.
 __device__ __forceinline__ void box_muller(uint32_t x_even, uint32_t x_odd, float& z_even, float& z_odd)
 {
-    const float L = minus_two_log_radius(x_even);        // >= 0
+    float L, L_lo;
+    minus_two_log_radius(x_even, L, L_lo);               // L >= 0
     const float r = __builtin_amdgcn_sqrtf(L);
-    // r + r_lo = sqrt(L) to well below fp32 rounding; r_lo = (L - r^2) / (2 r)
-    const float res = fmaf(-r, r, L);
+    // r + r_lo = sqrt(L + L_lo) to well below fp32 rounding; r_lo = (L + L_lo - r^2) / (2 r)
+    const float res = fmaf(-r, r, L) + L_lo;
     const float r_lo = (L > 0.0f) ? res * (0.5f * __builtin_amdgcn_rcpf(r)) : 0.0f;
     float c, s;
     unit_circle(x_odd, c, s);
