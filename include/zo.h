@@ -251,9 +251,12 @@ zo_status zo_debug_layernorm(const void* h_dev, const void* g_dev, const void* b
  * "attention", "layernorm", "embed", "lm_head", "debug".  zo_timing_query
  * returns the summed elapsed milliseconds and the launch count of one family
  * since the last reset; it synchronises the recorded events, so call it after
- * the stream work is complete.  Not thread-safe across concurrent callers.
+ * the stream work is complete.  zo_timing_select restricts the bracketing to
+ * one family (NULL: every family), so that timing one kernel adds no events
+ * around the others.  Not thread-safe across concurrent callers.
  */
 zo_status zo_timing_enable(int32_t on);
+zo_status zo_timing_select(const char* family);
 zo_status zo_timing_reset(void);
 zo_status zo_timing_query(const char* family, double* total_ms, int64_t* launches);
 

@@ -45,6 +45,7 @@ struct TimedLaunch {
     hipEvent_t start, stop;
 };
 bool g_timing = false;
+std::string g_timing_family;  // empty: every family
 std::vector<TimedLaunch> g_timed;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -63,7 +64,7 @@ hipEvent_t take_event()
 
 KernelTimer::KernelTimer(const char* family, hipStream_t s) : slot_(-1), s_(s)
 {
-    if (!g_timing) return;
+    if (!g_timing || (!g_timing_family.empty() && g_timing_family != family)) return;
     TimedLaunch t{family, take_event(), take_event()};
     if (!t.start || !t.stop) return;
     hipEventRecord(t.start, s);
@@ -201,6 +202,12 @@ const char* zo_last_error(void) { return g_err; }
 zo_status zo_timing_enable(int32_t on)
 {
     g_timing = on != 0;
+    return ZO_OK;
+}
+
+zo_status zo_timing_select(const char* family)
+{
+    g_timing_family = family ? family : "";
     return ZO_OK;
 }
 

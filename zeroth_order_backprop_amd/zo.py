@@ -20,7 +20,7 @@ EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
     "zo_forward_loss", "zo_update", "zo_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
-    "zo_timing_enable", "zo_timing_reset", "zo_timing_query",
+    "zo_timing_enable", "zo_timing_select", "zo_timing_reset", "zo_timing_query",
     "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
 ]
 
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "zo_debug_attention": [P, P, I32, I32, I32, I32, P],
         "zo_debug_layernorm": [P, P, P, P, I32, I32, P],
         "zo_timing_enable": [I32],
+        "zo_timing_select": [ctypes.c_char_p],
         "zo_timing_reset": [],
         "zo_timing_query": [ctypes.c_char_p, P, P],
     }
@@ -158,6 +159,11 @@ def debug_layernorm(h, g, b, x, rows, d, stream=None):
 # ------------------------------------------------------------------ timing
 def timing_enable(on: bool = True) -> None:
     check(lib().zo_timing_enable(1 if on else 0), "zo_timing_enable")
+
+
+def timing_select(family=None) -> None:
+    """Restrict timing to one kernel family (None: every family)."""
+    check(lib().zo_timing_select(family.encode() if family else None), "zo_timing_select")
 
 
 def timing_reset() -> None:
