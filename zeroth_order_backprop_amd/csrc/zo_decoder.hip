@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restri
 // groups l, l + 64, ... of the row in registers (8-byte loads), the mean and
 // the variance come from wave reductions.
 constexpr int kLnMaxQuads = 32;  // d <= 64 lanes * 32 groups * 4 = 8192
+template <int NQ>
 __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __restrict__ h, int rows, int d,
                                                               const bf16_t* __restrict__ g, uint64_t g_dir,
                                                               const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
@@ -142,10 +143,10 @@ __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __res
     if (t >= rows) return;
     const int nq = d >> 2;
     const uint2* row = reinterpret_cast<const uint2*>(h + (size_t)t * d);
-    float v[kLnMaxQuads][4];
+    float v[NQ][4];
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < kLnMaxQuads; ++k) {
+    for (int k = 0; k < NQ; ++k) {
         const int q = lane + 64 * k;
         if (q < nq) {
             const uint2 u = row[q];
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __res
     const float mean = wave_sumf(s) / (float)d;
     float q2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < kLnMaxQuads; ++k) {
+    for (int k = 0; k < NQ; ++k) {
         if (lane + 64 * k < nq) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __res
     const float rstd = 1.0f / sqrtf(var + 1e-5f);
     uint2* out = reinterpret_cast<uint2*>(x + (size_t)t * d);
 #pragma unroll
-    for (int k = 0; k < kLnMaxQuads; ++k) {
+    for (int k = 0; k < NQ; ++k) {
         const int q = lane + 64 * k;
         if (q >= nq) continue;
         float o[4];
@@ -192,6 +193,92 @@ __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __res
         }
         out[q] = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
     }
+}
+
+// Wide rows (d > 2048): one 256-thread block per row, NQ groups of 4 per
+// thread (group q = tid + 256 k); the sums are combined across the 4 waves
+// through LDS in a fixed order.
+template <int NQ>
+__global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* __restrict__ h, int d,
+                                                                   const bf16_t* __restrict__ g, uint64_t g_dir,
+                                                                   const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
+                                                                   bf16_t* __restrict__ x)
+{
+    __shared__ float part[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t t = blockIdx.x;
+    const int nq = d >> 2;
+    const uint2* row = reinterpret_cast<const uint2*>(h + t * d);
+    float v[NQ][4];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = tid + kThreads * k;
+        if (q < nq) {
+            const uint2 u = row[q];
+            v[k][0] = bf2f(u.x & 0xFFFF); v[k][1] = bf2f(u.x >> 16);
+            v[k][2] = bf2f(u.y & 0xFFFF); v[k][3] = bf2f(u.y >> 16);
+        } else {
+            v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0.f;
+        }
+        s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+    }
+    s = wave_sumf(s);
+    if (lane == 0) part[0][wave] = s;
+    __syncthreads();
+    const float mean = (((part[0][0] + part[0][1]) + part[0][2]) + part[0][3]) / (float)d;
+    float q2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        if (tid + kThreads * k < nq) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dv = v[k][e] - mean;
+                q2 = fmaf(dv, dv, q2);
+            }
+        }
+    }
+    q2 = wave_sumf(q2);
+    if (lane == 0) part[1][wave] = q2;
+    __syncthreads();
+    const float var = (((part[1][0] + part[1][1]) + part[1][2]) + part[1][3]) / (float)d;
+    const float rstd = 1.0f / sqrtf(var + 1e-5f);
+    uint2* out = reinterpret_cast<uint2*>(x + t * d);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = tid + kThreads * k;
+        if (q >= nq) continue;
+        float o[4];
+        if (p.on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 4 * q + e;
+                o[e] = fmaf((v[k][e] - mean) * rstd, weight1(g, c, g_dir, p), weight1(b, c, b_dir, p));
+            }
+        } else {
+            const uint2 gg = reinterpret_cast<const uint2*>(g)[q];
+            const uint2 bb = reinterpret_cast<const uint2*>(b)[q];
+            const float gv[4] = {bf2f(gg.x & 0xFFFF), bf2f(gg.x >> 16), bf2f(gg.y & 0xFFFF), bf2f(gg.y >> 16)};
+            const float bv[4] = {bf2f(bb.x & 0xFFFF), bf2f(bb.x >> 16), bf2f(bb.y & 0xFFFF), bf2f(bb.y >> 16)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = fmaf((v[k][e] - mean) * rstd, gv[e], bv[e]);
+        }
+        out[q] = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+    }
+}
+
+// LayerNorm of `rows` rows of width d (d % 4 == 0, d <= 8192): one wave per
+// row with the smallest register footprint that holds it (NQ groups of 4 per
+// lane) up to d = 2048, one block per row beyond.
+void launch_layernorm(const bf16_t* h, int rows, int d, const bf16_t* g, uint64_t g_dir, const bf16_t* b,
+                      uint64_t b_dir, const Pert& p, bf16_t* x, hipStream_t s)
+{
+    const int nq = (d / 4 + 63) / 64;
+    const dim3 grid((rows + 3) / 4);
+    if (nq <= 1) layernorm_kernel<1><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
+    else if (nq <= 3) layernorm_kernel<3><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
+    else if (nq <= 8) layernorm_kernel<8><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
+    else layernorm_wide_kernel<kLnMaxQuads / 4><<<rows, kThreads, 0, s>>>(h, d, g, g_dir, b, b_dir, p, x);
 }
 
 // ============================================================ bf16 GEMM
@@ -1044,8 +1131,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             const int t0 = 2 + 8 * l;
             {
                 KernelTimer t("layernorm", s);
-                layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p,
-                                                         w.x);
+                launch_layernorm(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p, w.x, s);
                 if (zo_status st = check_launch("layernorm")) return st;
             }
             GemmParams gq = {};
@@ -1065,8 +1151,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
             {
                 KernelTimer t("layernorm", s);
-                layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5),
-                                                         off(t0 + 5), p, w.x);
+                launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s);
                 if (zo_status st = check_launch("layernorm")) return st;
             }
             GemmParams gu = {};
@@ -1081,7 +1166,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         const int tf = 2 + 8 * L;
         {
             KernelTimer t("layernorm", s);
-            layernorm_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x);
+            launch_layernorm(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x, s);
             if (zo_status st = check_launch("layernorm")) return st;
         }
         GemmParams gl = {};
@@ -1137,8 +1222,7 @@ zo_status debug_layernorm(const void* h, const void* g, const void* b, void* x, 
     if (d > 64 * 4 * kLnMaxQuads || d % 4) return fail(ZO_ERR_UNSUPPORTED, "row length must be a multiple of 4, <= 8192");
     Pert p = {};
     KernelTimer t("layernorm", s);
-    layernorm_kernel<<<cdiv(rows, 4), kThreads, 0, s>>>((const bf16_t*)h, rows, d, (const bf16_t*)g, 0,
-                                                        (const bf16_t*)b, 0, p, (bf16_t*)x);
+    launch_layernorm((const bf16_t*)h, rows, d, (const bf16_t*)g, 0, (const bf16_t*)b, 0, p, (bf16_t*)x, s);
     return check_launch("layernorm");
 }
 
