@@ -193,19 +193,24 @@ def test_fullwidth_forward_reduced_tokens(name, batch, seq):
 
 
 def test_gpt_full_batch_forward():
-    """GPT-small shape on its configured 8 x 512 batch, the whole forward."""
+    """GPT-small shape on its configured 8 x 512 batch, the whole forward: with
+    the stored weights (256-wide tiles, LM head included) and perturbed on the
+    fly (register-staged perturbed tiles)."""
     m = full("gpt")
     tokens = inputs.zipf_tokens(0, 8, 512, 32000)
     tok = torch.from_numpy(tokens).to(DEV)
     b = zo.make_batch(tokens=tok, batch=8, seq=512)
-    out = torch.zeros(1, dtype=torch.float64, device=DEV)
+    out = torch.zeros(2, dtype=torch.float64, device=DEV)
     eps = float(np.float32(1e-3))
-    m.model.forward_loss(b, out, perts=[(5, 0, eps)])  # perturbed on the fly, W untouched
+    m.model.forward_loss(b, out[:1])
+    m.model.forward_loss(b, out[1:], perts=[(5, 0, eps)])  # W untouched
     torch.cuda.synchronize()
     a = oracle.Arena(odesc_of(m.sh), m.fetch(0, m.total).copy())
+    want0 = oracle.model_loss(a, {"tokens": tokens})
     a.perturb(5, 0, eps)
-    want = oracle.model_loss(a, {"tokens": tokens})
-    assert out[0].item() == pytest.approx(want, rel=2e-3)
+    want1 = oracle.model_loss(a, {"tokens": tokens})
+    assert out[0].item() == pytest.approx(want0, rel=2e-3)
+    assert out[1].item() == pytest.approx(want1, rel=2e-3)
 
 
 @pytest.mark.parametrize("name", ["opt1.3b", "opt30b"])

@@ -378,7 +378,7 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
             *dst = v;
         }
     } else {
-        static_assert(WGN == 2 && NT == kThreads, "LM-head partials assume two wave columns");
+        static_assert(WGN == 2, "LM-head partials assume two wave columns");
         // Fused cross-entropy partials over this tile's BN vocabulary columns:
         // per row the max and the sum of exp(logit - max), plus the target
         // logit when the target column lies in this tile.
@@ -419,7 +419,7 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
                 }
             }
         __syncthreads();
-        for (int lrow = tid; lrow < BM; lrow += kThreads) {
+        for (int lrow = tid; lrow < BM; lrow += NT) {
             const int row = m0 + lrow;
             if (row >= M) continue;
             const float m1 = part_m[0][lrow], m2 = part_m[1][lrow];
@@ -1038,12 +1038,22 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
 }
 
 // Tile choice: 256x256 when the grid still fills the 256 CUs, else 128x128.
+// The register-staged perturbed kernel keeps the LM head at 128x128 (its
+// 256-wide cross-entropy epilogue would not fit the registers).
+template <int EPI, bool PERT>
+constexpr bool may_use_big_tiles() { return !(PERT && EPI == EPI_LMHEAD); }
+
+int gemm_tile_n(int M, int N, bool pert, int epi)
+{
+    const long big = (long)cdiv(M, 256) * cdiv(N, 256);
+    return (big >= 256 && !(pert && epi == EPI_LMHEAD)) ? 256 : 128;
+}
+
 template <int EPI, bool PERT>
 zo_status gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
-    if constexpr (EPI != EPI_LMHEAD) {
-        const long big = (long)cdiv(gp.M, 256) * cdiv(gp.N, 256);
-        if (big >= 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
+    if constexpr (may_use_big_tiles<EPI, PERT>()) {
+        if (gemm_tile_n(gp.M, gp.N, PERT, EPI) == 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
     }
     return launch_gemm<128, 128, EPI, PERT>(gp, p, s, fam);
 }
@@ -1061,7 +1071,7 @@ struct DecoderWs {
     size_t bytes;
 };
 
-constexpr int kLmTile = 128;
+constexpr int kLmTile = 128;  // narrowest LM-head tile: sizes the per-tile partials
 
 DecoderWs carve(const zo_model_desc& d, void* base)
 {
@@ -1176,7 +1186,8 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         {
             KernelTimer t("reduce", s);
             const int nb = cdiv(M, 64);
-            ce_rows_kernel<<<nb, kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, cdiv(V, kLmTile), M, S, w.ce_part);
+            const int lm_tiles = cdiv(V, gemm_tile_n(M, V, p.on != 0, EPI_LMHEAD));
+            ce_rows_kernel<<<nb, kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, lm_tiles, M, S, w.ce_part);
             ce_final_kernel<<<1, kThreads, 0, s>>>(w.ce_part, nb, M, S, loss + e);
             if (zo_status st = check_launch("ce reduce")) return st;
         }
