@@ -665,19 +665,20 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
     gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
-// Small tiles: two BK = 64 stages.  LDS rows are 128 B (8 chunks of 16 B),
+// Small tiles (128 x 128 or 128 x 64): two BK = 64 stages, NT/64 waves in a
+// WGM x (NT/64/WGM) grid.  LDS rows are 128 B (8 chunks of 16 B),
 // chunk c of row r at position c ^ ((r >> 1) & 7): the 32 rows of a fragment
 // read (16 B each, half the wave on one chunk column) cover every bank
 // evenly.  Stage k+1 loads while stage k's MFMAs run.
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
+template <int BM, int BN, int EPI, int NT, int WGM>
+__global__ __launch_bounds__(NT) void gemm_bf16_k64_kernel(GemmParams g)
 {
     constexpr int BK = 64;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
     constexpr int RB = WM / 32, CB = WN / 32;
-    constexpr int A_INS = BM * 8 / kThreads, B_INS = BN * 8 / kThreads;
+    constexpr int A_INS = BM * 8 / NT, B_INS = BN * 8 / NT;
     constexpr int STAGE = (BM + BN) * BK;
-    static_assert(A_INS * kThreads == BM * 8 && B_INS * kThreads == BN * 8, "tile / thread mismatch");
+    static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
     tile_of<8>(blockIdx.x, nbm, nbn, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int lr = lane & 31, lh = lane >> 5;
 
     f32x16 acc[RB][CB];
@@ -702,16 +703,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
         const int k0 = kt * BK;
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
-            const int p = j * kThreads + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
             const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sa + (j * kThreads + wave * 64) * 8;
+            bf16_t* dst = sa + (j * NT + wave * 64) * 8;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < B_INS; ++j) {
-            const int p = j * kThreads + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
             const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sb + (j * kThreads + wave * 64) * 8;
+            bf16_t* dst = sb + (j * NT + wave * 64) * 8;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
@@ -746,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_k64_kernel(GemmParams g)
         // every wave is done reading this stage before the next issue refills it
         asm volatile("s_barrier" ::: "memory");
     }
-    gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
+    gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
 // Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1.
@@ -1016,14 +1017,18 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
     } else {
         // 256-wide tiles: 4-stage BK = 32 ring; 128-wide: 2-stage BK = 64
         constexpr bool big = BM == 256;
+        // the LM head's cross-entropy epilogue needs two wave columns of 4 waves
+        constexpr bool eight = !big && EPI != EPI_LMHEAD;
         constexpr size_t stages = big ? (size_t)4 * (BM + BN) * 32 * sizeof(bf16_t)
                                       : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
         if constexpr (big)
             kern = gemm_bf16_dma_kernel<BM, BN, EPI>;
+        else if constexpr (eight)
+            kern = gemm_bf16_k64_kernel<BM, BN, EPI, 512, 4>;
         else
-            kern = gemm_bf16_k64_kernel<BM, BN, EPI>;
+            kern = gemm_bf16_k64_kernel<BM, BN, EPI, kThreads, 2>;
         static bool attr = false;
         if (!attr) {
             if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
@@ -1032,7 +1037,7 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
             attr = true;
         }
         KernelTimer timer(fam, s);
-        kern<<<blocks, big ? kDmaThreads : kThreads, lds, s>>>(gp);
+        kern<<<blocks, (big || eight) ? kDmaThreads : kThreads, lds, s>>>(gp);
     }
     return check_launch("bf16 GEMM");
 }
@@ -1054,6 +1059,10 @@ zo_status gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* f
 {
     if constexpr (may_use_big_tiles<EPI, PERT>()) {
         if (gemm_tile_n(gp.M, gp.N, PERT, EPI) == 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
+    }
+    if constexpr (!PERT && EPI != EPI_LMHEAD) {
+        // narrow outputs: 128 x 64 tiles when 128 x 128 would leave CUs idle
+        if ((long)cdiv(gp.M, 128) * cdiv(gp.N, 128) < 256) return launch_gemm<128, 64, EPI, PERT>(gp, p, s, fam);
     }
     return launch_gemm<128, 128, EPI, PERT>(gp, p, s, fam);
 }
