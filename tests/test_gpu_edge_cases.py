@@ -1,0 +1,105 @@
+"""GPU edge cases of the step's entry points, through the C ABI: empty
+ranges, zero scales (exact no-ops), a batch smaller than the model was sized
+for, and single-probe steps in both modes, each against the CPU oracle or an
+exact invariant."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from zeroth_order_backprop_amd import inputs, zo
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _arena(dtype, n, seed=0):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal(n).astype(np.float32)
+    if dtype == zo.ZO_F32:
+        return torch.from_numpy(w).to(DEV)
+    return torch.from_numpy(inputs.f32_to_bf16_bits(w).view(np.int16)).to(DEV)
+
+
+@pytest.mark.parametrize("dtype", [zo.ZO_F32, zo.ZO_BF16])
+def test_empty_ranges_are_noops(dtype):
+    w = _arena(dtype, 4096)
+    before = w.clone()
+    g = torch.ones(2, dtype=torch.float64, device=DEV)
+    zo.perturb_buffer(w, 0, 0, 7, 0, 1.0, dtype)
+    zo.update_buffer(w, 0, 0, 7, 2, g, 1.0, dtype)
+    z = torch.full((8,), 3.0, dtype=torch.float32, device=DEV)
+    zo.debug_rng(7, 0, 0, 0, z=z)
+    torch.cuda.synchronize()
+    assert torch.equal(w, before)
+    assert (z.cpu() == 3.0).all()
+
+
+@pytest.mark.parametrize("dtype", [zo.ZO_F32, zo.ZO_BF16])
+def test_zero_scale_is_exact_noop(dtype):
+    """sigma = 0 perturbs nothing and g = 0 updates nothing, bit for bit: every
+    direction value is finite, so fma(0, z, w) = w."""
+    n = (1 << 16) + 37
+    w = _arena(dtype, n, seed=1)
+    before = w.clone()
+    zo.perturb_buffer(w, n, 0, 3, 5, 0.0, dtype)
+    g = torch.zeros(4, dtype=torch.float64, device=DEV)
+    zo.update_buffer(w, n, 0, 3, 4, g, 1e-3, dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(w, before)
+
+
+def _mlp(batch_model, d_in=1024, hidden=4096, classes=10):
+    inp = inputs.mlp_inputs(0, batch=batch_model, d_in=d_in, hidden=hidden, classes=classes)
+    odesc = {"kind": "mlp", "batch": batch_model, "d_in": d_in, "hidden": hidden, "classes": classes}
+    desc = zo.make_desc(zo.ZO_MODEL_MLP, batch=batch_model, d_in=d_in, hidden=hidden, classes=classes)
+    layout, total = oracle.param_layout(odesc)
+    arena = np.zeros(total, np.float32)
+    for name, off, shape in layout:
+        arena[off:off + int(np.prod(shape))] = inp[name].ravel()
+    model = zo.Model(desc, torch.from_numpy(arena.copy()).to(DEV))
+    return model, inp, oracle.Arena(odesc, arena)
+
+
+def test_mlp_batch_smaller_than_model():
+    """A model sized for 256 rows evaluated on the first 100 (ragged against
+    the 256-row tiles); stored and paired perturbed evaluations."""
+    model, inp, arena = _mlp(256)
+    rows = 100
+    x = torch.from_numpy(inp["X"]).to(DEV)
+    lab = torch.from_numpy(inp["labels"]).to(DEV)
+    b = zo.make_batch(x=x, labels=lab, batch=rows)
+    obatch = {"X": inp["X"][:rows], "labels": inp["labels"][:rows]}
+    eps = float(np.float32(1e-3))
+    perts = [(9, 0, eps), (9, 0, -eps), (9, 1, eps), (9, 1, -eps)]
+    out = torch.zeros(1 + len(perts), dtype=torch.float64, device=DEV)
+    model.forward_loss(b, out[:1])
+    model.forward_loss(b, out[1:], perts=perts)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = [oracle.model_loss(arena, obatch)]
+    for s, i, sg in perts:
+        a = arena.copy()
+        a.perturb(s, i, sg)
+        want.append(oracle.model_loss(a, obatch))
+    np.testing.assert_allclose(got, want, rtol=1e-5)
+
+
+@pytest.mark.parametrize("mode", [zo.ZO_MODE_FUSED, zo.ZO_MODE_INPLACE])
+def test_single_probe_step(mode):
+    """N = 1: one direction, two evaluations, one update."""
+    model, inp, arena = _mlp(64, d_in=64, hidden=256)
+    x = torch.from_numpy(inp["X"]).to(DEV)
+    lab = torch.from_numpy(inp["labels"]).to(DEV)
+    b = zo.make_batch(x=x, labels=lab, batch=64)
+    obatch = {"X": inp["X"], "labels": inp["labels"]}
+    losses = torch.zeros(2, dtype=torch.float64, device=DEV)
+    g = torch.zeros(1, dtype=torch.float64, device=DEV)
+    model.step(b, 11, 1, 1e-3, 1e-3, mode, losses, g)
+    torch.cuda.synchronize()
+    ol, og = oracle.spsa_step(arena, obatch, seed=11, n_probes=1, eps=1e-3, lr=1e-3,
+                              mode="fused" if mode == zo.ZO_MODE_FUSED else "inplace")
+    np.testing.assert_allclose(losses.cpu().numpy(), ol, rtol=1e-5)
+    assert g.item() == pytest.approx(og[0], rel=1e-2, abs=1e-3)
+    w = model.arena.cpu().numpy().astype(np.float64)
+    assert np.abs(w - arena.values()).max() <= 1e-5
