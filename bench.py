@@ -206,7 +206,7 @@ def cpu_baseline(info):
             oracle.spsa_step(arena, info["oracle_batch"], seed=reps, n_probes=probes, eps=info["eps"],
                              lr=info["lr"], mode="fused")
             reps += 1
-            if time.perf_counter() - t0 > 8.0:
+            if time.perf_counter() - t0 > 12.0:
                 break
         t = time.perf_counter() - t0
     evals = 2 * probes * reps
