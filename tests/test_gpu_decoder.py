@@ -81,7 +81,7 @@ def test_gemm_bf16(M, N, K, epi):
 
 # ------------------------------------------------------------- attention
 @pytest.mark.parametrize("B,S,H,dh", [(2, 64, 2, 64), (1, 200, 3, 64), (2, 512, 2, 64), (1, 300, 2, 128),
-                                      (1, 128, 1, 128), (1, 1100, 2, 64), (1, 2048, 1, 64)])
+                                      (1, 128, 1, 128), (1, 1100, 2, 64), (1, 2048, 1, 64), (4, 1024, 32, 64)])
 def test_attention(B, S, H, dh):
     rng = np.random.default_rng(S + dh)
     d = H * dh
