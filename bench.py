@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--workload", default="mlp", choices=["mlp", "lsq", "gpt", "opt1.3b", "opt30b"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-passes", action="store_true", help="skip the perturb/update pass measurement")
+    p.add_argument("--precond", action="store_true",
+                   help="1.5-SPSA: one clean evaluation per step and probe-space preconditioning")
+    p.add_argument("--curv-floor", type=float, default=1.0, help="1.5-SPSA curvature floor")
     return p.parse_args()
 
 
@@ -230,11 +233,18 @@ def main():
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     N = info["probes"]
-    losses = torch.zeros(2 * N, dtype=torch.float64, device="cuda")
+    pc = 1 if args.precond else 0
+    evals_per_step = 2 * N + pc
+    losses = torch.zeros(evals_per_step, dtype=torch.float64, device="cuda")
     g = torch.zeros(N, dtype=torch.float64, device="cuda")
     mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
+
+    def step(seed):
+        model.step(batch, seed, N, info["eps"], info["lr"], mode, losses, g, precond=pc,
+                   curv_floor=args.curv_floor)
+
     for t in range(args.warmup):
-        model.step(batch, t, N, info["eps"], info["lr"], mode, losses, g)
+        step(t)
     torch.cuda.synchronize()
     # timed region: exactly K steps; HIP events bracket only the dominant
     # kernel's launches (on the library's stream) for the roofline
@@ -246,7 +256,7 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for t in range(args.steps):
-        model.step(batch, args.warmup + t, N, info["eps"], info["lr"], mode, losses, g)
+        step(args.warmup + t)
     stop.record()
     torch.cuda.synchronize()
     zo.timing_enable(False)
@@ -264,7 +274,7 @@ def main():
     i1 = torch.cuda.Event(enable_timing=True)
     i0.record()
     for t in range(args.steps):
-        model.step(batch, args.warmup + args.steps + t, N, info["eps"], info["lr"], mode, losses, g)
+        step(args.warmup + args.steps + t)
     i1.record()
     torch.cuda.synchronize()
     zo.timing_enable(False)
@@ -272,7 +282,7 @@ def main():
     extra = {}
     if info["kernel"] == "gemm_bf16":
         # layer GEMMs of all evaluations: algorithmic flops / summed launch time
-        flops_per_launch = 2 * N * info["gemm_flops_per_eval"] * args.steps / k_n
+        flops_per_launch = evals_per_step * info["gemm_flops_per_eval"] * args.steps / k_n
     elif "split_bf16" in info:
         # one launch: N direction products X Z_i^T, each fp32 product taken as
         # six bf16 MFMA products (priced against the bf16 peak), plus the
@@ -297,10 +307,10 @@ def main():
                             "ms_per_step": round(ms / args.steps, 3)}
     if "lm_head" in kernels:
         t = kernels["lm_head"]["ms_per_step"] * 1e-3
-        kernels["lm_head"]["TFLOP/s"] = round(2 * N * info["head_flops_per_eval"] / t / 1e12, 1)
+        kernels["lm_head"]["TFLOP/s"] = round(evals_per_step * info["head_flops_per_eval"] / t / 1e12, 1)
     if "attention" in kernels:
         t = kernels["attention"]["ms_per_step"] * 1e-3
-        kernels["attention"]["TFLOP/s"] = round(2 * N * info["attn_flops_per_eval"] / t / 1e12, 1)
+        kernels["attention"]["TFLOP/s"] = round(evals_per_step * info["attn_flops_per_eval"] / t / 1e12, 1)
     zo.timing_reset()
     final = losses.cpu().numpy()
     line = {
@@ -310,7 +320,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": info["dtype"],
         "data": "synthetic (seeded N(0,1) inputs, random-init weights; no dataset)",
         "config": {"workload": info["workload"], "probes": N, "batch": info["batch"], "params": info["params"],
-                   "mode": info["mode"], "parallelism": "none (1 GPU)"},
+                   "mode": info["mode"], "parallelism": "none (1 GPU)",
+                   **({"variant": "1.5-SPSA", "evals_per_step": evals_per_step, "curv_floor": args.curv_floor}
+                      if pc else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
                      "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
                      "traffic": TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),

@@ -126,6 +126,8 @@ typedef struct {
     float eps;         /* perturbation scale */
     float lr;          /* eta */
     int32_t mode;      /* zo_mode */
+    int32_t precond;   /* 0: plain SPSA; 1: 1.5-SPSA (one clean evaluation per step) */
+    float curv_floor;  /* 1.5-SPSA: lower bound of the curvature estimate, > 0 */
 } zo_step_cfg;
 
 typedef struct zo_model zo_model;
@@ -191,6 +193,11 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
  * losses_dev: device fp64 [2N] as (L+_0, L-_0, L+_1, ...); g_dev: device fp64
  * [N].  A non-finite loss leaves W unchanged by the update (in place: after
  * the restore passes); the caller sees it in losses_dev / g_dev.
+ * precond = 1 (1.5-SPSA: "1.5-SPSA" in the ZOO blog, section "첫 번째 논문:
+ * probe-space 사전조건화"): one more evaluation L0 at the stored weights, first,
+ * into losses_dev[2N] (losses_dev then holds 2N + 1 values); the probe-space
+ * curvature h_i = (L+_i + L-_i - 2 L0) / eps^2 and g_dev[i] =
+ * g_i / max(h_i, curv_floor), which the update uses in place of g_i.
  */
 zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev,
                   double* g_dev, zo_stream s);
@@ -247,7 +254,9 @@ zo_status zo_debug_layernorm(const void* h_dev, const void* g_dev, const void* b
 /*
  * Kernel timing, a measurement aid.  While enabled, every kernel launch of the
  * library is bracketed by HIP events recorded on the launch's own stream and
- * grouped by family: "perturb", "update", "gemm_f32", "reduce", "gemm_bf16",
+ * grouped by family: "perturb", "update", "gemm_f32" (fp32 GEMMs that carry
+ * directions), "gemm_f32_base" (fp32 work on the stored weights alone: input
+ * splitting, the stored product, clean evaluations), "reduce", "gemm_bf16",
  * "attention", "layernorm", "embed", "lm_head", "debug".  zo_timing_query
  * returns the summed elapsed milliseconds and the launch count of one family
  * since the last reset; it synchronises the recorded events, so call it after

@@ -357,8 +357,15 @@ def model_loss(arena: Arena, batch: dict, round_bf16: bool = True) -> float:
 
 
 # ==================================================================== step
+def probe_curvature(lp, lm, l0, sig):
+    """Central second difference along each probe direction:
+    (L(W + s z) + L(W - s z) - 2 L(W)) / s^2 = z^T H z + O(s^2)."""
+    return ((np.asarray(lp) + np.asarray(lm)) - 2.0 * l0) / (sig * sig)
+
+
 def spsa_step(arena: Arena, batch: dict, seed: int, n_probes: int, eps: float, lr: float,
-              mode: str = "inplace", round_bf16: bool = True):
+              mode: str = "inplace", round_bf16: bool = True, precond: bool = False,
+              curv_floor: float = 1.0):
     """One multi-probe SPSA step; updates ``arena`` in place.
 
     inplace: for each probe i, W += eps z_i; L+ ; W -= 2 eps z_i; L- ;
@@ -367,9 +374,19 @@ def spsa_step(arena: Arena, batch: dict, seed: int, n_probes: int, eps: float, l
     Then g_i = (L+_i - L-_i) / (2 eps) with eps taken at fp32 precision,
     c_i = -lr * g_i / N, and W <- round_storage(W + sum_i c_i z_i).
     Returns (losses [2N] as L+_0, L-_0, L+_1, ..., g [N]).
+
+    precond (1.5-SPSA, ZOO blog, section on the first paper, probe-space
+    preconditioning): one clean evaluation L0 at the stored weights, taken
+    before any probe, gives each direction a curvature estimate
+    h_i = (L+_i + L-_i - 2 L0) / eps^2 (the central second difference of
+    L along z_i, i.e. z_i^T H z_i up to O(eps^2)); the step then uses
+    g_i / max(h_i, curv_floor) in place of g_i (curv_floor at fp32 precision),
+    and the returned losses hold 2N + 1 values, L0 last.
     """
     sig = float(np.float32(eps))
-    losses = np.zeros(2 * n_probes)
+    losses = np.zeros(2 * n_probes + (1 if precond else 0))
+    if precond:
+        losses[2 * n_probes] = model_loss(arena, batch, round_bf16)
     for i in range(n_probes):
         if mode == "inplace":
             arena.perturb(seed, i, sig)
@@ -386,7 +403,12 @@ def spsa_step(arena: Arena, batch: dict, seed: int, n_probes: int, eps: float, l
             losses[2 * i + 1] = model_loss(a, batch, round_bf16)
         else:
             raise ValueError(mode)
-    g = (losses[0::2] - losses[1::2]) / (2.0 * sig)
+    lp, lm = losses[0:2 * n_probes:2], losses[1:2 * n_probes:2]
+    g = (lp - lm) / (2.0 * sig)
+    if precond:
+        h = probe_curvature(lp, lm, losses[2 * n_probes], sig)
+        with np.errstate(invalid="ignore"):
+            g = np.where(np.isfinite(h), g / np.maximum(h, float(np.float32(curv_floor))), h)
     c = -lr * g / n_probes
     if np.all(np.isfinite(losses)):
         arena.update(seed, c)

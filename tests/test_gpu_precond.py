@@ -1,0 +1,112 @@
+"""GPU parity of the 1.5-SPSA step (probe-space diagonal preconditioning from
+one clean evaluation per step) against the CPU oracle, through the C ABI.
+
+Checks: the 2N + 1 losses (clean loss last) within the fp32 loss bar; g' equal
+to the stated formula evaluated on the GPU's own losses (fp64 on both sides);
+g' against the oracle's own within what the loss error allows; the weights
+after the step against the oracle's trajectory; on least squares, the
+curvature estimate against its closed form ||X Z||^2 / n.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from zeroth_order_backprop_amd import zo
+
+from test_gpu_fp32_models import DEV, LOSS_RTOL, W_ATOL, lsq_setup, mlp_setup
+
+pytestmark = pytest.mark.gpu
+
+
+def _precond_from_losses(losses, n, sig, floor):
+    lp, lm, l0 = losses[0:2 * n:2], losses[1:2 * n:2], losses[2 * n]
+    g = (lp - lm) / (2.0 * sig)
+    h = ((lp + lm) - 2.0 * l0) / (sig * sig)
+    return g / np.maximum(h, floor), h
+
+
+def _step(model, batch, seed, n, eps, lr, mode, floor):
+    losses = torch.zeros(2 * n + 1, dtype=torch.float64, device=DEV)
+    g = torch.zeros(n, dtype=torch.float64, device=DEV)
+    model.step(batch, seed, n, eps, lr, mode, losses, g, precond=1, curv_floor=floor)
+    torch.cuda.synchronize()
+    return losses.cpu().numpy(), g.cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", [zo.ZO_MODE_FUSED, zo.ZO_MODE_INPLACE])
+def test_mlp_precond_steps(mode):
+    model, batch, keep, arena, obatch = mlp_setup(batch=64, d_in=64, hidden=256)
+    omode = "fused" if mode == zo.ZO_MODE_FUSED else "inplace"
+    n, eps, lr, floor = 4, 1e-2, 1e-2, 1e-3
+    sig = float(np.float32(eps))
+    for t in range(3):
+        gl, gg = _step(model, batch, 40 + t, n, eps, lr, mode, floor)
+        ol, og = oracle.spsa_step(arena, obatch, seed=40 + t, n_probes=n, eps=eps, lr=lr, mode=omode,
+                                  precond=True, curv_floor=floor)
+        np.testing.assert_allclose(gl, ol, rtol=LOSS_RTOL)
+        want, h = _precond_from_losses(gl, n, sig, float(np.float32(floor)))
+        np.testing.assert_allclose(gg, want, rtol=1e-12, atol=0)
+        assert (h > floor).all(), h  # the estimate, not the floor, decided this case
+        # a loss error d moves h by up to 4 d / sig^2 and g by d / sig
+        d = LOSS_RTOL * np.abs(ol).max()
+        _, oh = _precond_from_losses(ol, n, sig, floor)
+        tol = np.abs(og) * 4 * d / (sig * sig) / oh + d / sig / oh
+        assert (np.abs(gg - og) <= 1.01 * tol + 1e-12).all(), (gg, og, tol)
+        w = model.arena.cpu().numpy().astype(np.float64)
+        assert np.abs(w - arena.values()).max() <= W_ATOL, t
+
+
+def test_mlp_full_precond_step_fused():
+    """The 1024 -> 4096 -> 10 MLP, batch 256, N = 16, one fused 1.5-SPSA step."""
+    model, batch, keep, arena, obatch = mlp_setup()
+    n, eps, lr, floor = 16, 1e-2, 1e-3, 1e-2
+    gl, gg = _step(model, batch, 7, n, eps, lr, zo.ZO_MODE_FUSED, floor)
+    ol, og = oracle.spsa_step(arena, obatch, seed=7, n_probes=n, eps=eps, lr=lr, mode="fused",
+                              precond=True, curv_floor=floor)
+    np.testing.assert_allclose(gl, ol, rtol=LOSS_RTOL)
+    want, _ = _precond_from_losses(gl, n, float(np.float32(eps)), float(np.float32(floor)))
+    np.testing.assert_allclose(gg, want, rtol=1e-12, atol=0)
+    w = model.arena.cpu().numpy().astype(np.float64)
+    assert np.abs(w - arena.values()).max() <= W_ATOL
+
+
+def test_lsq_precond_curvature_closed_form():
+    model, batch, keep, arena, obatch = lsq_setup()
+    n, eps = 4, 0.05
+    sig = float(np.float32(eps))
+    gl, gg = _step(model, batch, 21, n, eps, 0.0, zo.ZO_MODE_FUSED, 1e-6)
+    _, h = _precond_from_losses(gl, n, sig, 1e-6)
+    X = obatch["X"].astype(np.float64)
+    want = np.array([np.sum((X @ oracle.gauss(21, i, 0, 256 * 256).astype(np.float64).reshape(256, 256)) ** 2)
+                     / X.shape[0] for i in range(n)])
+    np.testing.assert_allclose(h, want, rtol=2e-3)
+
+
+def test_precond_nonfinite_and_bad_config():
+    model, batch, (x, y), arena, obatch = lsq_setup(n=64, d_in=16, d_out=16)
+    losses = torch.zeros(5, dtype=torch.float64, device=DEV)
+    g = torch.zeros(2, dtype=torch.float64, device=DEV)
+    with pytest.raises(zo.ZoError):
+        model.step(batch, 0, 2, 1e-3, 1e-2, zo.ZO_MODE_FUSED, losses, g, precond=1, curv_floor=0.0)
+    with pytest.raises(zo.ZoError):
+        model.step(batch, 0, 2, 1e-3, 1e-2, zo.ZO_MODE_FUSED, losses, g, precond=2, curv_floor=1.0)
+    with pytest.raises(ValueError):  # the clean loss needs slot 2N
+        model.step(batch, 0, 2, 1e-3, 1e-2, zo.ZO_MODE_FUSED, losses[:4], g, precond=1, curv_floor=1.0)
+    x[3, 2] = float("nan")
+    bad = dict(obatch, X=obatch["X"].copy())
+    bad["X"][3, 2] = np.nan
+    before = model.arena.clone()
+    model.step(batch, 0, 2, 1e-3, 1e-2, zo.ZO_MODE_FUSED, losses, g, precond=1, curv_floor=1.0)
+    torch.cuda.synchronize()
+    assert not np.isfinite(g.cpu().numpy()).any()
+    assert torch.equal(model.arena, before)
+    # in place: the probes' restore passes still run (their rounding drift is
+    # the oracle's too), the update does not
+    model.step(batch, 0, 2, 1e-3, 1e-2, zo.ZO_MODE_INPLACE, losses, g, precond=1, curv_floor=1.0)
+    oracle.spsa_step(arena, bad, seed=0, n_probes=2, eps=1e-3, lr=1e-2, mode="inplace",
+                     precond=True, curv_floor=1.0)
+    torch.cuda.synchronize()
+    assert not np.isfinite(g.cpu().numpy()).any()
+    w = model.arena.cpu().numpy().astype(np.float64)
+    assert np.abs(w - arena.values()).max() <= W_ATOL

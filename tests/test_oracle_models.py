@@ -11,6 +11,9 @@ against the mathematics and independent libraries:
 * MLP and decoder losses equal torch (CPU, fp64) implementations built from
   library layers, and their central differences match torch autograd;
 * seed replay rebuilds the trained weights bitwise from (seed, c_i) alone;
+* 1.5-SPSA: on least squares the probe curvature is ||X Z||^2 / n in closed
+  form, one preconditioned probe at eta = 1 lands on the line minimum, and
+  the floor and non-finite cases behave as stated;
 * the OPT-30B-shaped parameter count at 2 bytes matches the ~60 GB figure.
 """
 import numpy as np
@@ -148,6 +151,68 @@ def test_spsa_converges_to_gradient_tiny_lsq():
     for n_, e in errs.items():
         assert e < 3.0 * np.sqrt(257 / n_), (n_, e)
     assert errs[20000] < errs[200]
+
+
+# ----------------------------------------------------------- 1.5-SPSA
+def test_precond_curvature_is_closed_form_on_lsq():
+    """For L = ||X W - Y||^2 / (2n) the second difference along Z is exact:
+    (L(W + sZ) + L(W - sZ) - 2 L(W)) / s^2 = ||X Z||_F^2 / n for every s."""
+    d, arena, batch = _lsq(seed=2)
+    N, eps = 3, 0.05
+    losses, g = oracle.spsa_step(arena.copy(), batch, seed=5, n_probes=N, eps=eps, lr=0.0,
+                                 mode="fused", precond=True, curv_floor=1e-6)
+    assert losses.shape == (2 * N + 1,)
+    assert losses[-1] == oracle.model_loss(arena, batch)
+    sig = float(np.float32(eps))
+    h = oracle.probe_curvature(losses[0:2 * N:2], losses[1:2 * N:2], losses[-1], sig)
+    X = batch["X"].astype(np.float64)
+    want = np.array([np.sum((X @ oracle.gauss(5, i, 0, 256 * 256).astype(np.float64).reshape(256, 256)) ** 2)
+                     / X.shape[0] for i in range(N)])
+    np.testing.assert_allclose(h, want, rtol=1e-4)
+    plain = (losses[0:2 * N:2] - losses[1:2 * N:2]) / (2 * sig)
+    np.testing.assert_allclose(g, plain / want, rtol=1e-4)
+
+
+@pytest.mark.parametrize("mode", ["fused", "inplace"])
+def test_precond_single_probe_lands_on_line_minimum(mode):
+    """N = 1, eta = 1: W - (g / h) z is the exact minimiser of the quadratic
+    along z, with value L(W) - g^2 / (2h) (g = <grad, z>, h = z^T H z)."""
+    d, arena, batch = _lsq(seed=4, n=128, d_in=32, d_out=16)
+    W0 = arena.values().reshape(32, 16)
+    X, Y = batch["X"].astype(np.float64), batch["Y"].astype(np.float64)
+    z = oracle.gauss(9, 0, 0, W0.size).astype(np.float64)
+    gz = oracle.lsq_grad(W0, X, Y).ravel() @ z
+    hz = np.sum((X @ z.reshape(32, 16)) ** 2) / X.shape[0]
+    L0 = oracle.lsq_loss(W0, X, Y)
+    losses, g = oracle.spsa_step(arena, batch, seed=9, n_probes=1, eps=0.05, lr=1.0, mode=mode,
+                                 precond=True, curv_floor=1e-6)
+    assert g[0] == pytest.approx(gz / hz, rel=1e-4)
+    W1 = arena.values().reshape(32, 16)
+    L1 = oracle.lsq_loss(W1, X, Y)
+    assert L1 == pytest.approx(L0 - gz * gz / (2 * hz), rel=1e-5)
+    # and it is the minimum along z: moving either way from W1 costs
+    for t in (-1e-2, 1e-2):
+        assert oracle.lsq_loss(W1 + t * z.reshape(32, 16), X, Y) > L1
+
+
+def test_precond_floor_and_nonfinite():
+    """Curvature below the floor divides by the floor; a non-finite clean loss
+    gives non-finite g and no update."""
+    d, arena, batch = _lsq(seed=1, n=64, d_in=16, d_out=16)
+    floor = 1e6
+    losses, g = oracle.spsa_step(arena.copy(), batch, seed=3, n_probes=2, eps=1e-2, lr=0.0,
+                                 mode="fused", precond=True, curv_floor=floor)
+    sig = float(np.float32(1e-2))
+    plain = (losses[0:4:2] - losses[1:4:2]) / (2 * sig)
+    assert (oracle.probe_curvature(losses[0:4:2], losses[1:4:2], losses[4], sig) < floor).all()
+    np.testing.assert_array_equal(g, plain / floor)
+    bad = dict(batch, X=batch["X"].copy())
+    bad["X"][0, 0] = np.nan
+    a = arena.copy()
+    losses, g = oracle.spsa_step(a, bad, seed=3, n_probes=2, eps=1e-2, lr=1.0, mode="fused",
+                                 precond=True, curv_floor=1.0)
+    assert not np.isfinite(g).any()
+    assert np.array_equal(a.values(), arena.values())
 
 
 # ------------------------------------------------------------------- MLP

@@ -361,10 +361,15 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
     if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
     if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
+    if (cfg->precond != 0 && cfg->precond != 1) return fail(ZO_ERR_INVALID, "precond must be 0 or 1");
+    if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
     hipStream_t st = (hipStream_t)s;
     const ModelView v = view_of(m);
     const float sig = cfg->eps;
     const float sig2 = -2.0f * cfg->eps;
+    // 1.5-SPSA: the clean evaluation at the stored weights, before any probe
+    if (cfg->precond)
+        if (zo_status r = model_forward(v, *b, nullptr, 0, losses_dev + 2 * N, st)) return r;
     if (cfg->mode == ZO_MODE_INPLACE) {
         for (uint32_t i = 0; i < N; ++i) {
             zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st);
@@ -390,7 +395,9 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
             if (zo_status r = model_forward(v, *b, perts.data() + k, cnt, losses_dev + k, st)) return r;
         }
     }
-    if (zo_status r = launch_gscalar(losses_dev, N, cfg->eps, g_dev, st)) return r;
+    zo_status r = cfg->precond ? launch_precond(losses_dev, N, cfg->eps, cfg->curv_floor, g_dev, st)
+                               : launch_gscalar(losses_dev, N, cfg->eps, g_dev, st);
+    if (r) return r;
     return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
 }
 

@@ -225,6 +225,24 @@ __global__ void gscalar_kernel(const double* __restrict__ losses, uint32_t n, do
     if (i < n) g[i] = (losses[2 * i] - losses[2 * i + 1]) / two_sigma;
 }
 
+// Probe-space diagonal preconditioning from one extra clean evaluation L0 =
+// losses[2n]: h_i = (L+_i + L-_i - 2 L0) / sigma^2 estimates z_i^T H z_i, and
+// g_i becomes ((L+_i - L-_i) / (2 sigma)) / max(h_i, floor), so directions of
+// large curvature move less.  A non-finite loss makes g non-finite, which
+// the update treats as a skipped step.
+__global__ void precond_kernel(const double* __restrict__ losses, uint32_t n, double sigma, double floor,
+                               double* __restrict__ g)
+{
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const double lp = losses[2 * i], lm = losses[2 * i + 1], l0 = losses[2 * n];
+    const double gi = (lp - lm) / (2.0 * sigma);
+    const double hi = ((lp + lm) - 2.0 * l0) / (sigma * sigma);
+    // fmax would drop a NaN curvature; a non-finite h must reach the update
+    // as a non-finite g so the step is skipped
+    g[i] = isfinite(hi) ? gi / fmax(hi, floor) : hi;
+}
+
 // ------------------------------------------------------------------ debug
 __global__ __launch_bounds__(kThreads) void debug_rng_kernel(Key key, uint32_t probe, uint64_t j0, uint64_t n,
                                                               uint32_t* __restrict__ words,
@@ -315,6 +333,13 @@ zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* 
     KernelTimer timer("reduce", s);
     gscalar_kernel<<<(n + 63) / 64, 64, 0, s>>>(losses, n, 2.0 * (double)sigma, g);
     return check_launch("gscalar");
+}
+
+zo_status launch_precond(const double* losses, uint32_t n, float sigma, float floor, double* g, hipStream_t s)
+{
+    KernelTimer timer("reduce", s);
+    precond_kernel<<<(n + 63) / 64, 64, 0, s>>>(losses, n, (double)sigma, (double)floor, g);
+    return check_launch("precond");
 }
 
 zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words, float* z,

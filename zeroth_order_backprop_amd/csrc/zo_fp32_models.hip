@@ -808,7 +808,7 @@ zo_status launch_fgemm(const GemmArgs& a, const EvalList& ev, hipStream_t s)
         attr_set = true;
     }
     dim3 grid(cdiv(a.N, BN), cdiv(a.M, BM), ev.n_groups);
-    KernelTimer timer("gemm_f32", s);
+    KernelTimer timer(ev.perturbed ? "gemm_f32" : "gemm_f32_base", s);
     kern<<<grid, NT, lds, s>>>(a, ev);
     return check_launch("fp32 fused GEMM");
 }
@@ -944,7 +944,7 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
         }
         if ((st = check_launch("X split"))) return st;
         if (n == 0) {
-            st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1>(a, ev, 1, s, "gemm_f32");
+            st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1>(a, ev, 1, s, "gemm_f32_base");
             n_tiles = cdiv(N, SB_BN);
         } else {
             st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_STORE, 1>(a, ev, 1, s, "gemm_f32_base");

@@ -39,5 +39,6 @@ zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t 
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);
 // g_i = (L[2i] - L[2i+1]) / (2 (double)sigma), i < n
 zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s);
+zo_status launch_precond(const double* losses, uint32_t n, float sigma, float floor, double* g, hipStream_t s);
 
 }  // namespace zo

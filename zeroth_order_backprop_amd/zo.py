@@ -56,7 +56,8 @@ class Pert(ctypes.Structure):
 
 class StepCfg(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("n_probes", ctypes.c_uint32), ("eps", ctypes.c_float),
-                ("lr", ctypes.c_float), ("mode", ctypes.c_int32)]
+                ("lr", ctypes.c_float), ("mode", ctypes.c_int32), ("precond", ctypes.c_int32),
+                ("curv_floor", ctypes.c_float)]
 
 
 _lib = None
@@ -247,8 +248,14 @@ class Model:
     def update(self, seed, n_probes, g_dev, lr, stream=None):
         check(lib().zo_update(self._h, seed, n_probes, _ptr(g_dev), float(lr), _stream(stream)), "zo_update")
 
-    def step(self, batch: Batch, seed, n_probes, eps, lr, mode, losses_dev, g_dev, stream=None):
-        cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode))
+    def step(self, batch: Batch, seed, n_probes, eps, lr, mode, losses_dev, g_dev, stream=None,
+             precond=0, curv_floor=0.0):
+        """One SPSA step; precond=1 selects 1.5-SPSA, and losses_dev then needs
+        2 * n_probes + 1 entries (the clean loss last)."""
+        need = 2 * int(n_probes) + (1 if precond else 0)
+        if losses_dev.numel() < need or g_dev.numel() < int(n_probes):
+            raise ValueError(f"zo_step: losses need {need} entries, g {int(n_probes)}")
+        cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), int(precond), float(curv_floor))
         check(lib().zo_step(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _ptr(g_dev),
                             _stream(stream)), "zo_step")
 
