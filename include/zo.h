@@ -202,6 +202,20 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
 zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev,
                   double* g_dev, zo_stream s);
 
+/*
+ * Seed replay of one recorded step (position paper summary, P5, and FedSPZO,
+ * "통신 프로토콜": a model is rebuilt from the shared seeds and the scalar
+ * gradients alone, no weights exchanged).  Applies to W exactly the weight
+ * changes zo_step made with this cfg, given the g_dev [N] (device fp64) that
+ * step produced: in place, the 3N perturb / restore passes in the step's order,
+ * then the update; fused, the update only.  No evaluation runs, so no batch is
+ * needed.  Starting from the same weights, replaying a step's records gives its
+ * weights bit for bit (every kernel involved is deterministic); a checkpoint is
+ * the initial weights plus (cfg, g) per step.  precond and curv_floor are not
+ * read: g_dev already holds the scalars the update used.
+ */
+zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_dev, zo_stream s);
+
 /* ------------------------------------------------- model-free buffer path */
 
 /*

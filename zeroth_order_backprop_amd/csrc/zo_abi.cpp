@@ -401,6 +401,25 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
 }
 
+zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_dev, zo_stream s)
+{
+    if (!m || !cfg || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
+    const uint32_t N = cfg->n_probes;
+    if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
+    if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
+    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
+    hipStream_t st = (hipStream_t)s;
+    if (cfg->mode == ZO_MODE_INPLACE) {
+        // the step's perturb / restore passes, in its order, without the evaluations
+        const float sig = cfg->eps, sig2 = -2.0f * cfg->eps;
+        for (uint32_t i = 0; i < N; ++i)
+            for (float sg : {sig, sig2, sig})
+                if (zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sg, st))
+                    return r;
+    }
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
+}
+
 static zo_status check_buffer(const void* w, int32_t dtype, uint64_t j0)
 {
     if (!w) return fail(ZO_ERR_INVALID, "null buffer");

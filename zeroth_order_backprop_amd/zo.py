@@ -18,7 +18,7 @@ ZO_MODE_INPLACE, ZO_MODE_FUSED = 0, 1
 
 EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
-    "zo_forward_loss", "zo_update", "zo_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
+    "zo_forward_loss", "zo_update", "zo_step", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
     "zo_timing_enable", "zo_timing_select", "zo_timing_reset", "zo_timing_query",
     "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "zo_forward_loss": [P, P, P, I32, P, P],
         "zo_update": [P, U64, U32, P, F, P],
         "zo_step": [P, P, P, P, P, P],
+        "zo_replay_step": [P, P, P, P],
         "zo_perturb_buffer": [P, I32, U64, U64, U64, U32, F, P],
         "zo_update_buffer": [P, I32, U64, U64, U64, U32, P, F, P],
         "zo_gscalar": [P, U32, F, P, P],
@@ -258,6 +259,13 @@ class Model:
         cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), int(precond), float(curv_floor))
         check(lib().zo_step(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _ptr(g_dev),
                             _stream(stream)), "zo_step")
+
+    def replay_step(self, seed, n_probes, eps, lr, mode, g_dev, stream=None):
+        """The weight changes of a recorded step, given the g it produced."""
+        if g_dev.numel() < int(n_probes):
+            raise ValueError(f"zo_replay_step: g needs {int(n_probes)} entries")
+        cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), 0, 0.0)
+        check(lib().zo_replay_step(self._h, ctypes.byref(cfg), _ptr(g_dev), _stream(stream)), "zo_replay_step")
 
 
 def make_batch(x=None, y=None, labels=None, tokens=None, batch=0, seq=0) -> Batch:
