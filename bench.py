@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--precond", action="store_true",
                    help="1.5-SPSA: one clean evaluation per step and probe-space preconditioning")
     p.add_argument("--curv-floor", type=float, default=1.0, help="1.5-SPSA curvature floor")
+    p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
+                   help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
     return p.parse_args()
 
 
@@ -114,10 +116,11 @@ DECODERS = {
 }
 
 
-def build_decoder(torch, zo, inputs, name):
+def build_decoder(torch, zo, inputs, name, dirs="gauss"):
     L, D, H, F, V, B, S, act, N = DECODERS[name]
     desc = zo.make_desc(zo.ZO_MODEL_DECODER, batch=B, seq=S, layers=L, d_model=D, heads=H, ffn=F, vocab=V,
-                        max_seq=S, act=zo.ZO_ACT_GELU if act == "gelu" else zo.ZO_ACT_RELU)
+                        max_seq=S, act=zo.ZO_ACT_GELU if act == "gelu" else zo.ZO_ACT_RELU,
+                        dirs=zo.ZO_DIRS_Q8 if dirs == "q8" else zo.ZO_DIRS_GAUSS)
     layout, total = zo.param_layout(desc)
     arena = torch.empty(total, dtype=torch.bfloat16, device="cuda")
     gen = torch.Generator(device="cuda")
@@ -152,22 +155,13 @@ def build_decoder(torch, zo, inputs, name):
 
 
 def measure_passes(torch, zo):
-    """Perturb and update passes over an OPT-1.3B-sized parameter count."""
+    """Perturb and update passes over an OPT-1.3B-sized parameter count, with
+    Gaussian and with 8-bit packed directions; the update also at N = 32."""
     n = 1_315_311_616
     out = {}
     for name, dtype, tdt, esz in (("bf16", zo.ZO_BF16, torch.bfloat16, 2), ("f32", zo.ZO_F32, torch.float32, 4)):
         w = torch.zeros(n, dtype=tdt, device="cuda")
-        g = torch.ones(1, dtype=torch.float64, device="cuda")
-        zo.perturb_buffer(w, n, 0, 1, 0, 1e-3, dtype)
-        zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype)
-        torch.cuda.synchronize()
-        zo.timing_reset()
-        zo.timing_enable(True)
-        for r in range(5):
-            zo.perturb_buffer(w, n, 0, 1, r, 1e-3, dtype)
-            zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype)
-        torch.cuda.synchronize()
-        zo.timing_enable(False)
+        g = torch.ones(32, dtype=torch.float64, device="cuda")
         # plain copy of the same size: the HBM reference for these passes
         c = torch.empty_like(w)
         c.copy_(w)
@@ -181,13 +175,35 @@ def measure_passes(torch, zo):
         out[f"copy_{name}"] = {"GB/s": round(2.0 * n * esz / tc / 1e9, 1), "ms": round(tc * 1e3, 4),
                                "elements": n, "kind": "torch copy_, reference"}
         del c
-        for fam in ("perturb", "update"):
-            ms, k = zo.timing_query(fam)
+        for dirs, suffix in ((zo.ZO_DIRS_GAUSS, ""), (zo.ZO_DIRS_Q8, "_q8")):
+            zo.perturb_buffer(w, n, 0, 1, 0, 1e-3, dtype, dirs=dirs)
+            zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype, dirs=dirs)
+            torch.cuda.synchronize()
+            zo.timing_reset()
+            zo.timing_enable(True)
+            for r in range(5):
+                zo.perturb_buffer(w, n, 0, 1, r, 1e-3, dtype, dirs=dirs)
+                zo.update_buffer(w, n, 0, 1, 1, g, 1e-3, dtype, dirs=dirs)
+            torch.cuda.synchronize()
+            zo.timing_enable(False)
+            for fam in ("perturb", "update"):
+                ms, k = zo.timing_query(fam)
+                t = ms / k * 1e-3
+                gbs = 2.0 * n * esz / t / 1e9
+                out[f"{fam}_{name}{suffix}"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                                "ms": round(t * 1e3, 4), "elements": n, "probes": 1}
+            # many probes: the update regenerates N directions per element
+            zo.timing_reset()
+            zo.timing_enable(True)
+            for r in range(2):
+                zo.update_buffer(w, n, 0, 1, 32, g, 1e-9, dtype, dirs=dirs)
+            torch.cuda.synchronize()
+            zo.timing_enable(False)
+            ms, k = zo.timing_query("update")
             t = ms / k * 1e-3
-            gbs = 2.0 * n * esz / t / 1e9
-            out[f"{fam}_{name}"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                    "ms": round(t * 1e3, 4), "elements": n, "probes": 1}
-        zo.timing_reset()
+            out[f"update_{name}{suffix}_N32"] = {"directions_per_s": round(32 * n / t, 1), "ms": round(t * 1e3, 3),
+                                                 "elements": n, "probes": 32}
+            zo.timing_reset()
         del w
         torch.cuda.empty_cache()
     return out
@@ -228,8 +244,12 @@ def main():
 
     from zeroth_order_backprop_amd import inputs, zo
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.dirs != "gauss" and args.workload not in DECODERS:
+        print("bench.py: 8-bit directions apply in place; use a decoder workload (the fp32 ones run fused)",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload in DECODERS:
-        model, batch, keep, info = build_decoder(torch, zo, inputs, args.workload)
+        model, batch, keep, info = build_decoder(torch, zo, inputs, args.workload, args.dirs)
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     N = info["probes"]
@@ -322,7 +342,8 @@ def main():
         "config": {"workload": info["workload"], "probes": N, "batch": info["batch"], "params": info["params"],
                    "mode": info["mode"], "parallelism": "none (1 GPU)",
                    **({"variant": "1.5-SPSA", "evals_per_step": evals_per_step, "curv_floor": args.curv_floor}
-                      if pc else {})},
+                      if pc else {}),
+                   **({"directions": "8-bit packed (256-level quantised Gaussian)"} if args.dirs == "q8" else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
                      "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
                      "traffic": TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),

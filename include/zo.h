@@ -63,6 +63,23 @@ typedef enum { ZO_ACT_GELU = 0, ZO_ACT_RELU = 1 } zo_act;
 typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1 } zo_mode;
 
 /*
+ * Direction distribution of a model (zo_model_desc.dirs).
+ *  ZO_DIRS_GAUSS: the Gaussian stream above.
+ *  ZO_DIRS_Q8: 8-bit packed directions (the ZOO blog's 1.5-SPSA section names
+ *    an 8-bit packing random generator with a fused unpack/apply kernel for
+ *    OPT-30B in place; it gives no format).  Element j of direction i is byte
+ *    j % 4 (least significant first) of word (j / 4) % 4 of
+ *    Philox4x32-10(counter = (q lo, q hi, i, 1), key = (s lo, s hi)), q = j / 16,
+ *    used as a code k into T[k] = Phi^-1((k + 1/2) / 256) / r, r^2 the mean of
+ *    the 256 squared quantiles, rounded once to fp32: a 256-level quantised
+ *    Gaussian with mean 0 and variance 1.  Perturb, update, replay and in-place
+ *    steps support it for every model; evaluations that apply directions
+ *    inside the GEMMs (zo_forward_loss with perturbations, fused steps) return
+ *    ZO_ERR_UNSUPPORTED for it.
+ */
+typedef enum { ZO_DIRS_GAUSS = 0, ZO_DIRS_Q8 = 1 } zo_dirs;
+
+/*
  * Model description.  Fields a kind does not use must be 0.
  *  LSQ:     loss = ||X W - Y||_F^2 / (2 batch); W [d_in][d_out] fp32.
  *  MLP:     loss = mean_b CE(GELU(X W1^T) W2^T, label_b); W1 [hidden][d_in],
@@ -85,7 +102,7 @@ typedef struct {
     int64_t hidden, classes;         /* MLP */
     int64_t layers, d_model, heads, ffn, vocab, max_seq; /* DECODER */
     int32_t act;                     /* zo_act, DECODER */
-    int32_t reserved;
+    int32_t dirs;                    /* zo_dirs: the direction distribution */
 } zo_model_desc;
 
 /* One parameter tensor inside the flat parameter arena. */
@@ -220,13 +237,14 @@ zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_de
 
 /*
  * The perturb and update passes on a raw buffer w (device, n elements of
- * `dtype`, 16-byte aligned) whose element 0 is direction element j0
- * (j0 % 4 == 0).  Same arithmetic as zo_perturb / zo_update.
+ * `dtype`, 16-byte aligned) whose element 0 is direction element j0, with
+ * directions of kind `dirs` (zo_dirs; j0 % 4 == 0 for ZO_DIRS_GAUSS,
+ * j0 % 16 == 0 for ZO_DIRS_Q8).  Same arithmetic as zo_perturb / zo_update.
  */
-zo_status zo_perturb_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
-                            float sigma, zo_stream s);
-zo_status zo_update_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                           const double* g_dev, float lr, zo_stream s);
+zo_status zo_perturb_buffer(void* w, int32_t dtype, int32_t dirs, uint64_t n, uint64_t j0, uint64_t seed,
+                            uint32_t probe, float sigma, zo_stream s);
+zo_status zo_update_buffer(void* w, int32_t dtype, int32_t dirs, uint64_t n, uint64_t j0, uint64_t seed,
+                           uint32_t n_probes, const double* g_dev, float lr, zo_stream s);
 
 /* g_dev[i] = (losses_dev[2i] - losses_dev[2i+1]) / (2 (double)eps), i < n. */
 zo_status zo_gscalar(const double* losses_dev, uint32_t n, float eps, double* g_dev, zo_stream s);

@@ -23,6 +23,13 @@ What is computed, and where the pages state it:
 * In-place, inference-mode training: the weights themselves are perturbed and
   restored, nothing else is kept (ZOO blog, "zero-order optimization이란" and
   the OPT-30B in-place paragraph of the 1.5-SPSA section).
+* 8-bit packed directions (ZOO blog, 1.5-SPSA section: an 8-bit packing random
+  generator with a fused unpack/apply kernel; no format given): read as one
+  byte code per element, sixteen per Philox block, each code standing for one
+  of 256 equal-probability Gaussian quantiles scaled to unit variance
+  (``q8_table``; arena desc key ``"dirs": "q8"``).
+* 1.5-SPSA (same section): one clean evaluation per step and a probe-space
+  diagonal preconditioner (``spsa_step(precond=True)``).
 
 Readings where the pages are silent are listed in the repository's design
 notes; the ones that fix arithmetic are repeated at each function.
@@ -80,6 +87,16 @@ def lib():
         L.oracle_round_bf16_array.argtypes = [P, U64]
         L.oracle_round_f32_array.argtypes = [P, U64]
         L.oracle_box_muller_f64_array.argtypes = [P, U64, P]
+        L.oracle_q8_values.argtypes = [U64, U32, U64, U64, P, P]
+        L.oracle_q8_values_at.argtypes = [U64, U32, P, U64, P, P]
+        for name in ("oracle_q8_perturb_f32", "oracle_q8_perturb_bf16"):
+            getattr(L, name).argtypes = [P, U64, U64, U64, U32, F, P]
+        for name in ("oracle_q8_update_f32", "oracle_q8_update_bf16"):
+            getattr(L, name).argtypes = [P, U64, U64, U64, U32, P, P]
+        for name in ("oracle_q8_perturb_f32_at", "oracle_q8_perturb_bf16_at"):
+            getattr(L, name).argtypes = [P, P, U64, U64, U32, F, P]
+        for name in ("oracle_q8_update_f32_at", "oracle_q8_update_bf16_at"):
+            getattr(L, name).argtypes = [P, P, U64, U64, U32, P, P]
         _lib = L
     return _lib
 
@@ -118,10 +135,42 @@ def box_muller_f64_array(pairs: np.ndarray) -> np.ndarray:
     return out
 
 
+def q8_table() -> np.ndarray:
+    """The 256 values of the 8-bit directions: x_k = Phi^-1((k + 1/2) / 256),
+    divided by r = sqrt(mean_k x_k^2) so the codes (uniform over 0..255) give
+    unit variance, rounded once to fp32.  Built from the upper half and
+    mirrored (Phi^-1(1 - p) = -Phi^-1(p)), so it is exactly antisymmetric."""
+    from scipy.special import ndtri
+    up = ndtri((np.arange(128, 256) + 0.5) / 256.0)
+    r = np.sqrt(2.0 * np.sum(up * up) / 256.0)
+    half = (up / r).astype(np.float32)
+    return np.concatenate([-half[::-1], half])
+
+
+_Q8 = None
+
+
+def _q8() -> np.ndarray:
+    global _Q8
+    if _Q8 is None:
+        _Q8 = np.ascontiguousarray(q8_table())
+    return _Q8
+
+
 def gauss(seed: int, probe: int, j0: int, n: int) -> np.ndarray:
     """Direction z_probe at elements j0..j0+n-1 (fp32, rounded once from fp64)."""
+    return directions("gauss", seed, probe, j0, n)
+
+
+def directions(kind: str, seed: int, probe: int, j0: int, n: int) -> np.ndarray:
+    """Direction values ('gauss' or 'q8') at elements j0..j0+n-1."""
     z = np.zeros(n, np.float32)
-    lib().oracle_gauss(seed, probe, j0, n, _ptr(z))
+    if kind == "gauss":
+        lib().oracle_gauss(seed, probe, j0, n, _ptr(z))
+    elif kind == "q8":
+        lib().oracle_q8_values(seed, probe, j0, n, _ptr(z), _ptr(_q8()))
+    else:
+        raise ValueError(kind)
     return z
 
 
@@ -334,16 +383,28 @@ class Arena:
             return bf16_bits_to_f64(self.data)
         return self.data.astype(np.float64)
 
+    @property
+    def dirs(self) -> str:
+        return self.desc.get("dirs", "gauss")
+
     def perturb(self, seed: int, probe: int, sigma: float) -> None:
         """w <- round_storage(w + sigma * z_probe), every element of the arena."""
-        fn = lib().oracle_perturb_bf16 if self.dtype == "bf16" else lib().oracle_perturb_f32
-        fn(_ptr(self.data), self.data.size, 0, seed, probe, float(np.float32(sigma)))
+        kind = "bf16" if self.dtype == "bf16" else "f32"
+        args = (_ptr(self.data), self.data.size, 0, seed, probe, float(np.float32(sigma)))
+        if self.dirs == "q8":
+            getattr(lib(), "oracle_q8_perturb_" + kind)(*args, _ptr(_q8()))
+        else:
+            getattr(lib(), "oracle_perturb_" + kind)(*args)
 
     def update(self, seed: int, coeffs: np.ndarray) -> None:
         """w <- round_storage(w + sum_i c_i z_i), every element of the arena."""
         c = np.ascontiguousarray(coeffs, dtype=np.float64)
-        fn = lib().oracle_update_bf16 if self.dtype == "bf16" else lib().oracle_update_f32
-        fn(_ptr(self.data), self.data.size, 0, seed, c.size, _ptr(c))
+        kind = "bf16" if self.dtype == "bf16" else "f32"
+        args = (_ptr(self.data), self.data.size, 0, seed, c.size, _ptr(c))
+        if self.dirs == "q8":
+            getattr(lib(), "oracle_q8_update_" + kind)(*args, _ptr(_q8()))
+        else:
+            getattr(lib(), "oracle_update_" + kind)(*args)
 
 
 def model_loss(arena: Arena, batch: dict, round_bf16: bool = True) -> float:

@@ -98,8 +98,30 @@ double oracle_box_muller_f64(uint32_t x_even, uint32_t x_odd, double* z_odd)
     return r * cos(two_pi * u_t);
 }
 
+/* ---- 8-bit packed directions -------------------------------------------
+ * Reading of the ZOO blog's 1.5-SPSA section (an 8-bit packing random
+ * generator with a fused unpack/apply kernel; no format given): element j of
+ * direction `probe` is byte j mod 4 (least significant first) of word
+ * (j / 4) mod 4 of the Philox block with counter (q lo, q hi, probe, 1),
+ * q = j / 16, and byte value k stands for table[k], the k-th of 256
+ * equal-probability Gaussian quantiles scaled to unit variance.  The table is
+ * supplied by the caller (oracle.py builds it from the normal quantile
+ * function); every routine below takes it as `q8`, NULL meaning Gaussian
+ * directions. */
+static float q8_value(uint64_t seed, uint32_t probe, uint64_t j, const float* q8)
+{
+    uint64_t q = j >> 4;
+    uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), probe, 1u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    uint32_t word = w[(j >> 2) & 3u];
+    unsigned byte = (word >> (8u * (unsigned)(j & 3u))) & 0xFFu;
+    return q8[byte];
+}
+
 /* Gaussian direction value of element j, fp64 definition rounded once to fp32. */
-static float direction_value(uint64_t seed, uint32_t probe, uint64_t j)
+static float gauss_value(uint64_t seed, uint32_t probe, uint64_t j)
 {
     uint32_t w[4];
     direction_block(seed, probe, j, w);
@@ -109,17 +131,22 @@ static float direction_value(uint64_t seed, uint32_t probe, uint64_t j)
     return (float)((j & 1u) ? zo : ze);
 }
 
-void oracle_gauss(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, float* z)
+static float dir_value(uint64_t seed, uint32_t probe, uint64_t j, const float* q8)
+{
+    return q8 ? q8_value(seed, probe, j, q8) : gauss_value(seed, probe, j);
+}
+
+static void gauss_impl(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, float* z, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t)
-        z[t] = direction_value(seed, probe, j0 + t);
+        z[t] = dir_value(seed, probe, j0 + t, q8);
 }
 
 /* Same, at strided element indices idx[0..n). */
-void oracle_gauss_at(uint64_t seed, uint32_t probe, const uint64_t* idx, uint64_t n, float* z)
+static void gauss_at_impl(uint64_t seed, uint32_t probe, const uint64_t* idx, uint64_t n, float* z, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t)
-        z[t] = direction_value(seed, probe, idx[t]);
+        z[t] = dir_value(seed, probe, idx[t], q8);
 }
 
 /* ---- bfloat16: round to nearest, ties to even ---------------------------- */
@@ -171,18 +198,18 @@ uint16_t oracle_bf16_from_f64(double x)
 
 /* ---- perturbation: w <- round_storage(w + sigma * z_j) ------------------- */
 
-void oracle_perturb_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma)
+static void perturb_f32_impl(float* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
-        float z = direction_value(seed, probe, j0 + t);
+        float z = dir_value(seed, probe, j0 + t, q8);
         w[t] = fmaf(sigma, z, w[t]); /* exact sigma*z + w, rounded once */
     }
 }
 
-void oracle_perturb_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma)
+static void perturb_bf16_impl(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
-        float z = direction_value(seed, probe, j0 + t);
+        float z = dir_value(seed, probe, j0 + t, q8);
         double v = (double)oracle_f32_from_bf16(w[t]) + (double)sigma * (double)z;
         w[t] = oracle_bf16_from_f64(v);
     }
@@ -190,64 +217,64 @@ void oracle_perturb_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed, ui
 
 /* ---- update: w <- round_storage(w + sum_i c_i z_i[j]) --------------------- */
 
-void oracle_update_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed,
-                       uint32_t n_probes, const double* c)
+static void update_f32_impl(float* w, uint64_t n, uint64_t j0, uint64_t seed,
+                       uint32_t n_probes, const double* c, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
         double acc = 0.0;
         for (uint32_t i = 0; i < n_probes; ++i)
-            acc += c[i] * (double)direction_value(seed, i, j0 + t);
+            acc += c[i] * (double)dir_value(seed, i, j0 + t, q8);
         w[t] = (float)((double)w[t] + acc);
     }
 }
 
-void oracle_update_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed,
-                        uint32_t n_probes, const double* c)
+static void update_bf16_impl(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed,
+                        uint32_t n_probes, const double* c, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
         double acc = 0.0;
         for (uint32_t i = 0; i < n_probes; ++i)
-            acc += c[i] * (double)direction_value(seed, i, j0 + t);
+            acc += c[i] * (double)dir_value(seed, i, j0 + t, q8);
         w[t] = oracle_bf16_from_f64((double)oracle_f32_from_bf16(w[t]) + acc);
     }
 }
 
 /* Same updates at strided element indices (for sampled checks on large
    parameter vectors): w[t] is element idx[t]. */
-void oracle_update_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
-                          uint32_t n_probes, const double* c)
+static void update_f32_at_impl(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                          uint32_t n_probes, const double* c, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
         double acc = 0.0;
         for (uint32_t i = 0; i < n_probes; ++i)
-            acc += c[i] * (double)direction_value(seed, i, idx[t]);
+            acc += c[i] * (double)dir_value(seed, i, idx[t], q8);
         w[t] = (float)((double)w[t] + acc);
     }
 }
 
-void oracle_update_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
-                           uint32_t n_probes, const double* c)
+static void update_bf16_at_impl(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t n_probes, const double* c, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
         double acc = 0.0;
         for (uint32_t i = 0; i < n_probes; ++i)
-            acc += c[i] * (double)direction_value(seed, i, idx[t]);
+            acc += c[i] * (double)dir_value(seed, i, idx[t], q8);
         w[t] = oracle_bf16_from_f64((double)oracle_f32_from_bf16(w[t]) + acc);
     }
 }
 
-void oracle_perturb_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
-                           uint32_t probe, float sigma)
+static void perturb_f32_at_impl(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t probe, float sigma, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t)
-        w[t] = fmaf(sigma, direction_value(seed, probe, idx[t]), w[t]);
+        w[t] = fmaf(sigma, dir_value(seed, probe, idx[t], q8), w[t]);
 }
 
-void oracle_perturb_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
-                            uint32_t probe, float sigma)
+static void perturb_bf16_at_impl(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                            uint32_t probe, float sigma, const float* q8)
 {
     for (uint64_t t = 0; t < n; ++t) {
-        float z = direction_value(seed, probe, idx[t]);
+        float z = dir_value(seed, probe, idx[t], q8);
         double v = (double)oracle_f32_from_bf16(w[t]) + (double)sigma * (double)z;
         w[t] = oracle_bf16_from_f64(v);
     }
@@ -298,4 +325,120 @@ void oracle_box_muller_f64_array(const uint32_t* pairs, uint64_t n_pairs, double
         out[2 * t] = oracle_box_muller_f64(pairs[2 * t], pairs[2 * t + 1], &zo);
         out[2 * t + 1] = zo;
     }
+}
+
+/* ---- public entry points: Gaussian directions, and the same routines with
+
+ * 8-bit directions from the 256-value table `q8` ------------------------- */
+
+void oracle_gauss(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, float* z)
+{
+    gauss_impl(seed, probe, j0, n, z, NULL);
+}
+
+void oracle_q8_values(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, float* z, const float* q8)
+{
+    gauss_impl(seed, probe, j0, n, z, q8);
+}
+
+void oracle_gauss_at(uint64_t seed, uint32_t probe, const uint64_t* idx, uint64_t n, float* z)
+{
+    gauss_at_impl(seed, probe, idx, n, z, NULL);
+}
+
+void oracle_q8_values_at(uint64_t seed, uint32_t probe, const uint64_t* idx, uint64_t n, float* z, const float* q8)
+{
+    gauss_at_impl(seed, probe, idx, n, z, q8);
+}
+
+void oracle_perturb_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma)
+{
+    perturb_f32_impl(w, n, j0, seed, probe, sigma, NULL);
+}
+
+void oracle_q8_perturb_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma, const float* q8)
+{
+    perturb_f32_impl(w, n, j0, seed, probe, sigma, q8);
+}
+
+void oracle_perturb_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma)
+{
+    perturb_bf16_impl(w, n, j0, seed, probe, sigma, NULL);
+}
+
+void oracle_q8_perturb_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe, float sigma, const float* q8)
+{
+    perturb_bf16_impl(w, n, j0, seed, probe, sigma, q8);
+}
+
+void oracle_update_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed,
+                       uint32_t n_probes, const double* c)
+{
+    update_f32_impl(w, n, j0, seed, n_probes, c, NULL);
+}
+
+void oracle_q8_update_f32(float* w, uint64_t n, uint64_t j0, uint64_t seed,
+                       uint32_t n_probes, const double* c, const float* q8)
+{
+    update_f32_impl(w, n, j0, seed, n_probes, c, q8);
+}
+
+void oracle_update_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed,
+                        uint32_t n_probes, const double* c)
+{
+    update_bf16_impl(w, n, j0, seed, n_probes, c, NULL);
+}
+
+void oracle_q8_update_bf16(uint16_t* w, uint64_t n, uint64_t j0, uint64_t seed,
+                        uint32_t n_probes, const double* c, const float* q8)
+{
+    update_bf16_impl(w, n, j0, seed, n_probes, c, q8);
+}
+
+void oracle_update_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                          uint32_t n_probes, const double* c)
+{
+    update_f32_at_impl(w, idx, n, seed, n_probes, c, NULL);
+}
+
+void oracle_q8_update_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                          uint32_t n_probes, const double* c, const float* q8)
+{
+    update_f32_at_impl(w, idx, n, seed, n_probes, c, q8);
+}
+
+void oracle_update_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t n_probes, const double* c)
+{
+    update_bf16_at_impl(w, idx, n, seed, n_probes, c, NULL);
+}
+
+void oracle_q8_update_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t n_probes, const double* c, const float* q8)
+{
+    update_bf16_at_impl(w, idx, n, seed, n_probes, c, q8);
+}
+
+void oracle_perturb_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t probe, float sigma)
+{
+    perturb_f32_at_impl(w, idx, n, seed, probe, sigma, NULL);
+}
+
+void oracle_q8_perturb_f32_at(float* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                           uint32_t probe, float sigma, const float* q8)
+{
+    perturb_f32_at_impl(w, idx, n, seed, probe, sigma, q8);
+}
+
+void oracle_perturb_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                            uint32_t probe, float sigma)
+{
+    perturb_bf16_at_impl(w, idx, n, seed, probe, sigma, NULL);
+}
+
+void oracle_q8_perturb_bf16_at(uint16_t* w, const uint64_t* idx, uint64_t n, uint64_t seed,
+                            uint32_t probe, float sigma, const float* q8)
+{
+    perturb_bf16_at_impl(w, idx, n, seed, probe, sigma, q8);
 }

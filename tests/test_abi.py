@@ -74,13 +74,18 @@ def test_parameter_counts():
 def test_validation_rejects_before_launch():
     L = zo.lib()
     s = ctypes.c_void_p(0)
-    assert L.zo_perturb_buffer(None, zo.ZO_F32, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
-    assert L.zo_perturb_buffer(ctypes.c_void_p(256), 7, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_UNSUPPORTED
-    assert L.zo_perturb_buffer(ctypes.c_void_p(258), zo.ZO_F32, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
-    assert L.zo_perturb_buffer(ctypes.c_void_p(256), zo.ZO_F32, 16, 2, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
-    assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_F32, 16, 0, 1, 0, ctypes.c_void_p(512), 1e-3,
+    G, Q = zo.ZO_DIRS_GAUSS, zo.ZO_DIRS_Q8
+    assert L.zo_perturb_buffer(None, zo.ZO_F32, G, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_perturb_buffer(ctypes.c_void_p(256), 7, G, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_UNSUPPORTED
+    assert L.zo_perturb_buffer(ctypes.c_void_p(258), zo.ZO_F32, G, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_perturb_buffer(ctypes.c_void_p(256), zo.ZO_F32, G, 16, 2, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_perturb_buffer(ctypes.c_void_p(256), zo.ZO_F32, 2, 16, 0, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_perturb_buffer(ctypes.c_void_p(256), zo.ZO_F32, Q, 16, 4, 1, 0, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_F32, G, 16, 0, 1, 0, ctypes.c_void_p(512), 1e-3,
                               s) == zo.ZO_ERR_INVALID
-    assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_F32, 16, 0, 1, 2, None, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_F32, G, 16, 0, 1, 2, None, 1e-3, s) == zo.ZO_ERR_INVALID
+    assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_BF16, Q, 16, 8, 1, 2, ctypes.c_void_p(512), 1e-3,
+                              s) == zo.ZO_ERR_INVALID
     assert L.zo_debug_rng(0, 0, 0, 16, None, None, s) == zo.ZO_ERR_INVALID
     # model creation: wrong arena size, misalignment, overlap, small workspace
     desc = zo.make_desc(**DESCS["lsq"][1])
@@ -97,6 +102,9 @@ def test_validation_rejects_before_launch():
                                  ws - 1, ctypes.byref(h)) == zo.ZO_ERR_WORKSPACE
         assert L.zo_model_create(ctypes.byref(desc), ctypes.c_void_p(base), total, ctypes.c_void_p(base + 256),
                                  ws, ctypes.byref(h)) == zo.ZO_ERR_INVALID
+    bad_dirs = zo.make_desc(**dict(DESCS["lsq"][1], dirs=3))
+    assert L.zo_model_create(ctypes.byref(bad_dirs), ctypes.c_void_p(base), total, ctypes.c_void_p(base << 1),
+                             ws, ctypes.byref(h)) == zo.ZO_ERR_INVALID
     bad = zo.make_desc(**dict(DESCS["gpt"][1], d_model=770))
     assert L.zo_workspace_bytes(ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == zo.ZO_ERR_INVALID
     bad = zo.make_desc(**dict(DESCS["gpt"][1], heads=24))  # head dim 32: unsupported

@@ -1,0 +1,188 @@
+"""GPU parity of the 8-bit packed directions against the CPU oracle, through
+the C ABI: the direction values bit for bit (which also pins the device copy
+of the quantile table), perturb and update on fp32 and bf16 arenas including
+ragged tails and the grid-stride loop, whole in-place steps, seed replay, and
+the entry points that refuse them."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from zeroth_order_backprop_amd import checkpoint, inputs, zo
+
+from test_gpu_decoder import decoder_setup
+from test_gpu_fp32_models import DEV, LOSS_RTOL, W_ATOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _ulp_bf16(x):
+    a = np.maximum(np.abs(x), 2.0**-126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def lsq_q8(n=64, d_in=256, d_out=256, seed=0, arena_values=None):
+    inp = inputs.lsq_inputs(seed, n=n, d_in=d_in, d_out=d_out)
+    odesc = {"kind": "lsq", "n": n, "d_in": d_in, "d_out": d_out, "dirs": "q8"}
+    desc = zo.make_desc(zo.ZO_MODEL_LSQ, batch=n, d_in=d_in, d_out=d_out, dirs=zo.ZO_DIRS_Q8)
+    _, total = oracle.param_layout(odesc)
+    arena = np.zeros(total, np.float32)
+    if arena_values is None:
+        arena[:d_in * d_out] = inp["W"].ravel()
+    model = zo.Model(desc, torch.from_numpy(arena.copy()).to(DEV))
+    x = torch.from_numpy(inp["X"]).to(DEV)
+    y = torch.from_numpy(inp["Y"]).to(DEV)
+    return model, zo.make_batch(x=x, y=y, batch=n), (x, y), oracle.Arena(odesc, arena), \
+        {"X": inp["X"], "Y": inp["Y"]}
+
+
+def mlp_q8(batch=64, d_in=64, hidden=256, classes=10, seed=0):
+    inp = inputs.mlp_inputs(seed, batch=batch, d_in=d_in, hidden=hidden, classes=classes)
+    odesc = {"kind": "mlp", "batch": batch, "d_in": d_in, "hidden": hidden, "classes": classes, "dirs": "q8"}
+    desc = zo.make_desc(zo.ZO_MODEL_MLP, batch=batch, d_in=d_in, hidden=hidden, classes=classes,
+                        dirs=zo.ZO_DIRS_Q8)
+    layout, total = oracle.param_layout(odesc)
+    arena = np.zeros(total, np.float32)
+    for name, off, shape in layout:
+        arena[off:off + int(np.prod(shape))] = inp[name].ravel()
+    model = zo.Model(desc, torch.from_numpy(arena.copy()).to(DEV))
+    x = torch.from_numpy(inp["X"]).to(DEV)
+    lab = torch.from_numpy(inp["labels"]).to(DEV)
+    return model, zo.make_batch(x=x, labels=lab, batch=batch), (x, lab), oracle.Arena(odesc, arena), \
+        {"X": inp["X"], "labels": inp["labels"]}
+
+
+@pytest.mark.parametrize("d_in,d_out", [(20, 36), (100, 44), (256, 256), (4096, 4100)])
+def test_values_bit_exact(d_in, d_out):
+    """Perturbing a zero fp32 arena by sigma = 1 stores fma(1, z, 0) = z: the
+    values for arenas that are all tail (768), one block iteration plus a tail
+    (4416), whole iterations (65,536) and more than one grid sweep (16.8 M)."""
+    model, *_ = lsq_q8(n=8, d_in=d_in, d_out=d_out, arena_values=0)
+    n = model.arena.numel()
+    model.perturb(77, 5, 1.0)
+    torch.cuda.synchronize()
+    got = model.arena.cpu().numpy()
+    want = oracle.directions("q8", 77, 5, 0, n)
+    assert got.tobytes() == want.tobytes()
+    if n >= 65536:
+        t = oracle.q8_table()
+        assert np.unique(np.searchsorted(t, got)).size == 256  # every table entry was read
+
+
+def decoder_q8():
+    """The tiny decoder of the decoder tests, as an 8-bit-direction model."""
+    model, batch, tok, arena, obatch = decoder_setup()
+    desc = zo.ModelDesc.from_buffer_copy(model.desc)
+    desc.dirs = zo.ZO_DIRS_Q8
+    arena.desc = dict(arena.desc, dirs="q8")
+    return zo.Model(desc, model.arena), batch, tok, arena, obatch
+
+
+def test_perturb_bf16_and_restore():
+    m8, batch, tok, arena, obatch = decoder_q8()
+    w0 = arena.values()
+    m8.perturb(12, 3, 1e-2)
+    arena.perturb(12, 3, 1e-2)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    want = arena.values()
+    bad = got != want
+    if bad.any():  # only fp32-then-bf16 double rounding at a bf16 midpoint
+        z = oracle.directions("q8", 12, 3, 0, w0.size).astype(np.float64)[bad]
+        exact = w0[bad] + np.float64(np.float32(1e-2)) * z
+        mid = 0.5 * (got[bad] + want[bad])
+        assert (np.abs(exact - mid) <= np.spacing(np.abs(exact).astype(np.float32))).all()
+    assert np.mean(bad) < 1e-4
+    m8.perturb(12, 3, -2e-2)
+    torch.cuda.synchronize()
+    wm = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    m8.perturb(12, 3, 1e-2)
+    torch.cuda.synchronize()
+    wr = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    # three roundings: within 1.5 ulp of the largest intermediate
+    mx = np.maximum(np.maximum(np.abs(w0), np.abs(got)), np.abs(wm))
+    assert (np.abs(wr - w0) <= 1.5 * _ulp_bf16(mx)).all()
+
+
+@pytest.mark.parametrize("N", [1, 16])
+def test_update_f32(N):
+    model, batch, keep, arena, obatch = lsq_q8(d_in=100, d_out=44)
+    g = np.random.default_rng(N).standard_normal(N) * 20.0
+    lr = 1e-2
+    model.update(31, N, torch.from_numpy(g).to(DEV), lr)
+    arena.update(31, -float(np.float32(lr)) * g / N)
+    torch.cuda.synchronize()
+    got = model.arena.cpu().numpy().astype(np.float64)
+    want = arena.values()
+    # fp32 c_i and fp32 accumulation on the GPU against the oracle's fp64 sum
+    c = np.abs(float(np.float32(lr)) * g / N)
+    tol = np.spacing(np.abs(want).astype(np.float32)) * 1.5 + c.sum() * 3.0 * N * 2.0**-23
+    assert (np.abs(got - want) <= tol).all()
+
+
+def test_update_bf16_decoder():
+    m8, batch, tok, arena, obatch = decoder_q8()
+    N = 8
+    g = np.random.default_rng(3).standard_normal(N) * 20.0
+    lr = 1e-3
+    m8.update(5, N, torch.from_numpy(g).to(DEV), lr)
+    arena.update(5, -float(np.float32(lr)) * g / N)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    want = arena.values()
+    bad = got != want
+    assert np.mean(bad) < 1e-3
+    assert (np.abs(got - want)[bad] <= _ulp_bf16(np.maximum(np.abs(got), np.abs(want)))[bad] * 1.0001).all()
+
+
+@pytest.mark.parametrize("precond", [0, 1])
+def test_inplace_steps_mlp(precond):
+    model, batch, keep, arena, obatch = mlp_q8()
+    n, eps, lr = 4, 1e-2, 1e-2
+    losses = torch.zeros(2 * n + 1, dtype=torch.float64, device=DEV)
+    g = torch.zeros(n, dtype=torch.float64, device=DEV)
+    for t in range(3):
+        model.step(batch, 60 + t, n, eps, lr, zo.ZO_MODE_INPLACE, losses, g, precond=precond, curv_floor=1e-3)
+        ol, og = oracle.spsa_step(arena, obatch, seed=60 + t, n_probes=n, eps=eps, lr=lr, mode="inplace",
+                                  precond=bool(precond), curv_floor=1e-3)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(losses.cpu().numpy()[:len(ol)], ol, rtol=LOSS_RTOL)
+        w = model.arena.cpu().numpy().astype(np.float64)
+        assert np.abs(w - arena.values()).max() <= W_ATOL, t
+
+
+def test_inplace_step_decoder_and_replay(tmp_path):
+    m8, batch, tok, arena, obatch = decoder_q8()
+    w0 = m8.arena.clone()
+    n, eps, lr = 2, 1e-3, 1e-2
+    losses = torch.zeros(2 * n, dtype=torch.float64, device=DEV)
+    g = torch.zeros(n, dtype=torch.float64, device=DEV)
+    log = checkpoint.StepLog()
+    for t in range(2):
+        m8.step(batch, 70 + t, n, eps, lr, zo.ZO_MODE_INPLACE, losses, g)
+        torch.cuda.synchronize()
+        log.record(70 + t, n, eps, lr, zo.ZO_MODE_INPLACE, g)
+        ol, og = oracle.spsa_step(arena, obatch, seed=70 + t, n_probes=n, eps=eps, lr=lr, mode="inplace")
+        np.testing.assert_allclose(losses.cpu().numpy(), ol, rtol=2e-3)
+    trained = m8.arena.clone()
+    m8.arena.copy_(w0)
+    log.save(tmp_path / "q8.npz")
+    checkpoint.replay(m8, checkpoint.StepLog.load(tmp_path / "q8.npz"))
+    torch.cuda.synchronize()
+    assert torch.equal(m8.arena, trained)
+
+
+def test_fused_evaluations_refused():
+    model, batch, keep, arena, obatch = mlp_q8()
+    before = model.arena.clone()
+    losses = torch.zeros(8, dtype=torch.float64, device=DEV)
+    g = torch.zeros(4, dtype=torch.float64, device=DEV)
+    with pytest.raises(zo.ZoError) as e:
+        model.step(batch, 0, 4, 1e-3, 1e-3, zo.ZO_MODE_FUSED, losses, g)
+    assert e.value.status == zo.ZO_ERR_UNSUPPORTED
+    with pytest.raises(zo.ZoError):
+        model.forward_loss(batch, losses, perts=[(0, 0, 1e-3)])
+    model.forward_loss(batch, losses[:1])  # the stored weights are fine
+    torch.cuda.synchronize()
+    assert losses[0].item() == pytest.approx(oracle.model_loss(arena, obatch), rel=LOSS_RTOL)
+    assert torch.equal(model.arena, before)

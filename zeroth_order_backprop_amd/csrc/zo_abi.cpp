@@ -157,6 +157,7 @@ static zo_status validate_desc(const zo_model_desc* d)
         default:
             return fail(ZO_ERR_INVALID, "unknown model kind %d", d->kind);
     }
+    if (d->dirs != ZO_DIRS_GAUSS && d->dirs != ZO_DIRS_Q8) return fail(ZO_ERR_INVALID, "bad direction kind %d", d->dirs);
     return model_check_shape(*d);
 }
 
@@ -312,7 +313,7 @@ static ModelView view_of(const zo_model* m)
 zo_status zo_perturb(zo_model* m, uint64_t seed, uint32_t probe, float sigma, zo_stream s)
 {
     if (!m) return fail(ZO_ERR_INVALID, "null model");
-    return launch_perturb(m->params, m->desc.dtype, m->n_params, 0, seed, probe, sigma, (hipStream_t)s);
+    return launch_perturb(m->params, m->desc.dtype, m->n_params, 0, seed, probe, sigma, (hipStream_t)s, m->desc.dirs);
 }
 
 static zo_status validate_batch(const zo_model* m, const zo_batch* b)
@@ -342,6 +343,8 @@ zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, 
     if (zo_status st = validate_batch(m, b)) return st;
     if (n_perts < 0 || (n_perts > 0 && !perts)) return fail(ZO_ERR_INVALID, "bad perturbation list");
     if (n_perts > kMaxEvalsPerCall) return fail(ZO_ERR_INVALID, "at most %d perturbations per call", kMaxEvalsPerCall);
+    if (n_perts > 0 && m->desc.dirs != ZO_DIRS_GAUSS)
+        return fail(ZO_ERR_UNSUPPORTED, "perturbed evaluations apply Gaussian directions only; use zo_perturb");
     return model_forward(view_of(m), *b, n_perts ? perts : nullptr, n_perts, loss_dev, (hipStream_t)s);
 }
 
@@ -349,7 +352,8 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
 {
     if (!m || !g_dev) return fail(ZO_ERR_INVALID, "null model or g");
     if (n_probes == 0) return fail(ZO_ERR_INVALID, "n_probes must be >= 1");
-    return launch_update(m->params, m->desc.dtype, m->n_params, 0, seed, n_probes, g_dev, lr, (hipStream_t)s);
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, seed, n_probes, g_dev, lr, (hipStream_t)s,
+                         m->desc.dirs);
 }
 
 zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev, double* g_dev,
@@ -363,6 +367,8 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
     if (cfg->precond != 0 && cfg->precond != 1) return fail(ZO_ERR_INVALID, "precond must be 0 or 1");
     if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
+    if (cfg->mode == ZO_MODE_FUSED && m->desc.dirs != ZO_DIRS_GAUSS)
+        return fail(ZO_ERR_UNSUPPORTED, "fused steps apply Gaussian directions only; use the in-place mode");
     hipStream_t st = (hipStream_t)s;
     const ModelView v = view_of(m);
     const float sig = cfg->eps;
@@ -372,13 +378,13 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
         if (zo_status r = model_forward(v, *b, nullptr, 0, losses_dev + 2 * N, st)) return r;
     if (cfg->mode == ZO_MODE_INPLACE) {
         for (uint32_t i = 0; i < N; ++i) {
-            zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st);
+            zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st, m->desc.dirs);
             if (r) return r;
             zo_status f1 = model_forward(v, *b, nullptr, 0, losses_dev + 2 * i, st);
             // the restore sequence always completes once a probe has started
-            zo_status r2 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig2, st);
+            zo_status r2 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig2, st, m->desc.dirs);
             zo_status f2 = f1 ? f1 : model_forward(v, *b, nullptr, 0, losses_dev + 2 * i + 1, st);
-            zo_status r3 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st);
+            zo_status r3 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st, m->desc.dirs);
             if (f1) return f1;
             if (r2) return r2;
             if (f2) return f2;
@@ -398,7 +404,7 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     zo_status r = cfg->precond ? launch_precond(losses_dev, N, cfg->eps, cfg->curv_floor, g_dev, st)
                                : launch_gscalar(losses_dev, N, cfg->eps, g_dev, st);
     if (r) return r;
-    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st, m->desc.dirs);
 }
 
 zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_dev, zo_stream s)
@@ -414,37 +420,38 @@ zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_de
         const float sig = cfg->eps, sig2 = -2.0f * cfg->eps;
         for (uint32_t i = 0; i < N; ++i)
             for (float sg : {sig, sig2, sig})
-                if (zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sg, st))
+                if (zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sg, st, m->desc.dirs))
                     return r;
     }
-    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st);
+    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st, m->desc.dirs);
 }
 
-static zo_status check_buffer(const void* w, int32_t dtype, uint64_t j0)
+static zo_status check_buffer(const void* w, int32_t dtype, int32_t dirs, uint64_t j0)
 {
     if (!w) return fail(ZO_ERR_INVALID, "null buffer");
     if (dtype != ZO_F32 && dtype != ZO_BF16) return fail(ZO_ERR_UNSUPPORTED, "dtype must be F32 or BF16");
+    if (dirs != ZO_DIRS_GAUSS && dirs != ZO_DIRS_Q8) return fail(ZO_ERR_INVALID, "bad direction kind %d", dirs);
     if ((uintptr_t)w % 16) return fail(ZO_ERR_INVALID, "buffer must be 16-byte aligned");
-    if (j0 % 4) return fail(ZO_ERR_INVALID, "j0 must be a multiple of 4");
+    if (j0 % (dirs == ZO_DIRS_Q8 ? 16 : 4)) return fail(ZO_ERR_INVALID, "j0 must be a multiple of 4 (16 for 8-bit)");
     return ZO_OK;
 }
 
-zo_status zo_perturb_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
-                            float sigma, zo_stream s)
+zo_status zo_perturb_buffer(void* w, int32_t dtype, int32_t dirs, uint64_t n, uint64_t j0, uint64_t seed,
+                            uint32_t probe, float sigma, zo_stream s)
 {
-    if (zo_status st = check_buffer(w, dtype, j0)) return st;
+    if (zo_status st = check_buffer(w, dtype, dirs, j0)) return st;
     if (n == 0) return ZO_OK;
-    return launch_perturb(w, dtype, n, j0, seed, probe, sigma, (hipStream_t)s);
+    return launch_perturb(w, dtype, n, j0, seed, probe, sigma, (hipStream_t)s, dirs);
 }
 
-zo_status zo_update_buffer(void* w, int32_t dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                           const double* g_dev, float lr, zo_stream s)
+zo_status zo_update_buffer(void* w, int32_t dtype, int32_t dirs, uint64_t n, uint64_t j0, uint64_t seed,
+                           uint32_t n_probes, const double* g_dev, float lr, zo_stream s)
 {
-    if (zo_status st = check_buffer(w, dtype, j0)) return st;
+    if (zo_status st = check_buffer(w, dtype, dirs, j0)) return st;
     if (!g_dev) return fail(ZO_ERR_INVALID, "null g");
     if (n_probes == 0) return fail(ZO_ERR_INVALID, "n_probes must be >= 1");
     if (n == 0) return ZO_OK;
-    return launch_update(w, dtype, n, j0, seed, n_probes, g_dev, lr, (hipStream_t)s);
+    return launch_update(w, dtype, n, j0, seed, n_probes, g_dev, lr, (hipStream_t)s, dirs);
 }
 
 zo_status zo_gscalar(const double* losses_dev, uint32_t n, float eps, double* g_dev, zo_stream s)

@@ -17,6 +17,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include "zo_dirs8.hpp"
 #include "zo_internal.hpp"
 #include "zo_rng.hpp"
 
@@ -217,6 +218,123 @@ __global__ __launch_bounds__(kThreads) void update_tail(T* __restrict__ w, uint6
     store_elem(w, i, load_elem(w, i) + acc);
 }
 
+// ------------------------------------------------ 8-bit packed directions
+// One Philox block gives the codes of 16 consecutive elements, so a thread
+// owns 16 elements per iteration (bf16: two 16-byte vectors; fp32: four) and
+// looks each code up in the LDS copy of the quantile table.  Requires
+// j0 % 16 == 0.
+constexpr int kQ8PerIter = kThreads * 16;
+
+template <typename T> struct Q8Io;
+template <> struct Q8Io<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* w, uint64_t e, float* f)
+    {
+        unpack8(*reinterpret_cast<const uint4*>(w + e), f);
+        unpack8(*reinterpret_cast<const uint4*>(w + e + 8), f + 8);
+    }
+    static __device__ __forceinline__ void store(uint16_t* w, uint64_t e, const float* f)
+    {
+        *reinterpret_cast<uint4*>(w + e) = pack8(f);
+        *reinterpret_cast<uint4*>(w + e + 8) = pack8(f + 8);
+    }
+};
+template <> struct Q8Io<float> {
+    static __device__ __forceinline__ void load(const float* w, uint64_t e, float* f)
+    {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float4 x = *reinterpret_cast<const float4*>(w + e + 4 * v);
+            f[4 * v] = x.x; f[4 * v + 1] = x.y; f[4 * v + 2] = x.z; f[4 * v + 3] = x.w;
+        }
+    }
+    static __device__ __forceinline__ void store(float* w, uint64_t e, const float* f)
+    {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<float4*>(w + e + 4 * v) = float4{f[4 * v], f[4 * v + 1], f[4 * v + 2], f[4 * v + 3]};
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64_t n_full, uint64_t j0, Key key,
+                                                        uint32_t probe, float sigma)
+{
+    __shared__ float tab[256];
+    dirs8::load_table(tab);
+    __syncthreads();
+    const uint64_t stride = (uint64_t)gridDim.x * kQ8PerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kQ8PerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 16 * threadIdx.x;
+        float f[16];
+        Q8Io<T>::load(w, e, f);
+        const uint4 c = dirs8::block(key, probe, (j0 + e) >> 4);
+        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) f[t] = fmaf(sigma, dirs8::code(tab, words[t >> 2], t & 3), f[t]);
+        Q8Io<T>::store(w, e, f);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_t n_full, uint64_t j0, Key key,
+                                                       uint32_t n_probes, const double* __restrict__ g, float lr)
+{
+    __shared__ float tab[256];
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    dirs8::load_table(tab);
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;  // its barriers also cover the table
+    const uint64_t stride = (uint64_t)gridDim.x * kQ8PerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kQ8PerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 16 * threadIdx.x;
+        float f[16];
+        Q8Io<T>::load(w, e, f);  // issued first, so the loads overlap the generation
+        float acc[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[t] = 0.0f;
+        for (uint32_t i = 0; i < n_probes; ++i) {
+            const float ci = c[i];
+            const uint4 cw = dirs8::block(key, i, (j0 + e) >> 4);
+            const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc[t] = fmaf(ci, dirs8::code(tab, words[t >> 2], t & 3), acc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) f[t] += acc[t];
+        Q8Io<T>::store(w, e, f);
+    }
+}
+
+// Elements [start, n) one thread each (ragged tail, < kQ8PerIter).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void perturb_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n,
+                                                             uint64_t j0, Key key, uint32_t probe, float sigma)
+{
+    __shared__ float tab[256];
+    dirs8::load_table(tab);
+    __syncthreads();
+    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    store_elem(w, i, fmaf(sigma, dirs8::value1(tab, key, probe, j0 + i), load_elem(w, i)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void update_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n,
+                                                            uint64_t j0, Key key, uint32_t n_probes,
+                                                            const double* __restrict__ g, float lr)
+{
+    __shared__ float tab[256];
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    dirs8::load_table(tab);
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
+    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n) return;
+    float acc = 0.f;
+    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], dirs8::value1(tab, key, p, j0 + i), acc);
+    store_elem(w, i, load_elem(w, i) + acc);
+}
+
 // ------------------------------------------------------------ g scalars
 __global__ void gscalar_kernel(const double* __restrict__ losses, uint32_t n, double two_sigma,
                                double* __restrict__ g)
@@ -272,20 +390,51 @@ __global__ __launch_bounds__(kThreads) void debug_box_muller_kernel(const uint32
     z[2 * t + 1] = b;
 }
 
-int grid_for(uint64_t n_full)
+int grid_for(uint64_t n_full, uint64_t per_iter = kElemsPerIter)
 {
     // enough blocks to fill 256 CUs several times over; the loop strides the rest
-    const uint64_t iters = n_full / kElemsPerIter;
+    const uint64_t iters = n_full / per_iter;
     const uint64_t cap = 256ull * 16ull;
     return (int)(iters < cap ? (iters ? iters : 1) : cap);
 }
 
 }  // namespace
 
+template <typename T>
+static zo_status launch_perturb_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32_t probe, float sigma,
+                                   hipStream_t s)
+{
+    if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
+    const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
+    KernelTimer timer("perturb", s);
+    if (n_full) perturb_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, probe, sigma);
+    if (n > n_full)
+        perturb_q8_tail<T><<<(int)((n - n_full + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, n_full, n, j0, key,
+                                                                                                probe, sigma);
+    return check_launch("perturb (8-bit directions)");
+}
+
+template <typename T>
+static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32_t n_probes, const double* g,
+                                  float lr, hipStream_t s)
+{
+    if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
+    const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
+    KernelTimer timer("update", s);
+    if (n_full) update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, n_probes, g, lr);
+    if (n > n_full)
+        update_q8_tail<T><<<(int)((n - n_full + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, n_full, n, j0, key,
+                                                                                               n_probes, g, lr);
+    return check_launch("update (8-bit directions)");
+}
+
 zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
-                         float sigma, hipStream_t s)
+                         float sigma, hipStream_t s, int dirs)
 {
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    if (dirs == ZO_DIRS_Q8)
+        return dtype == ZO_F32 ? launch_perturb_q8((float*)w, n, j0, key, probe, sigma, s)
+                               : launch_perturb_q8((uint16_t*)w, n, j0, key, probe, sigma, s);
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("perturb", s);
     if (n_full) {
@@ -305,11 +454,14 @@ zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t s
 }
 
 zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                        const double* g, float lr, hipStream_t s)
+                        const double* g, float lr, hipStream_t s, int dirs)
 {
     if (n_probes == 0 || n_probes > kMaxProbes)
         return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    if (dirs == ZO_DIRS_Q8)
+        return dtype == ZO_F32 ? launch_update_q8((float*)w, n, j0, key, n_probes, g, lr, s)
+                               : launch_update_q8((uint16_t*)w, n, j0, key, n_probes, g, lr, s);
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("update", s);
     if (n_full) {

@@ -28,12 +28,13 @@ private:
 
 // ---- element-wise kernels (zo_elementwise.hip) ----
 // w[0..n) is direction element j0 .. j0+n-1; j0 % 4 == 0, w 16-byte aligned.
+// dirs: zo_dirs (ZO_DIRS_Q8 needs j0 % 16 == 0).
 zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
-                         float sigma, hipStream_t s);
+                         float sigma, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 // w += sum_i c_i z_i, c_i = fp32(-lr * g_i / N) from fp64 g on the device;
 // nothing is written when any g_i is not finite.
 zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                        const double* g, float lr, hipStream_t s);
+                        const double* g, float lr, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words,
                            float* z, hipStream_t s);
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);

@@ -15,6 +15,7 @@ ZO_F32, ZO_BF16 = 0, 1
 ZO_MODEL_LSQ, ZO_MODEL_MLP, ZO_MODEL_DECODER = 0, 1, 2
 ZO_ACT_GELU, ZO_ACT_RELU = 0, 1
 ZO_MODE_INPLACE, ZO_MODE_FUSED = 0, 1
+ZO_DIRS_GAUSS, ZO_DIRS_Q8 = 0, 1
 
 EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
@@ -37,7 +38,7 @@ class ModelDesc(ctypes.Structure):
                 ("hidden", ctypes.c_int64), ("classes", ctypes.c_int64), ("layers", ctypes.c_int64),
                 ("d_model", ctypes.c_int64), ("heads", ctypes.c_int64), ("ffn", ctypes.c_int64),
                 ("vocab", ctypes.c_int64), ("max_seq", ctypes.c_int64), ("act", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("dirs", ctypes.c_int32)]
 
 
 class ParamInfo(ctypes.Structure):
@@ -81,8 +82,8 @@ def lib() -> ctypes.CDLL:
         "zo_update": [P, U64, U32, P, F, P],
         "zo_step": [P, P, P, P, P, P],
         "zo_replay_step": [P, P, P, P],
-        "zo_perturb_buffer": [P, I32, U64, U64, U64, U32, F, P],
-        "zo_update_buffer": [P, I32, U64, U64, U64, U32, P, F, P],
+        "zo_perturb_buffer": [P, I32, I32, U64, U64, U64, U32, F, P],
+        "zo_update_buffer": [P, I32, I32, U64, U64, U64, U32, P, F, P],
         "zo_gscalar": [P, U32, F, P, P],
         "zo_debug_rng": [U64, U32, U64, U64, P, P, P],
         "zo_debug_box_muller": [P, U64, P, P],
@@ -123,13 +124,13 @@ def _ptr(t):
 
 
 # ------------------------------------------------------------ raw buffers
-def perturb_buffer(w, n, j0, seed, probe, sigma, dtype, stream=None):
-    check(lib().zo_perturb_buffer(_ptr(w), dtype, n, j0, seed, probe, float(sigma), _stream(stream)),
+def perturb_buffer(w, n, j0, seed, probe, sigma, dtype, stream=None, dirs=ZO_DIRS_GAUSS):
+    check(lib().zo_perturb_buffer(_ptr(w), dtype, dirs, n, j0, seed, probe, float(sigma), _stream(stream)),
           "zo_perturb_buffer")
 
 
-def update_buffer(w, n, j0, seed, n_probes, g_dev, lr, dtype, stream=None):
-    check(lib().zo_update_buffer(_ptr(w), dtype, n, j0, seed, n_probes, _ptr(g_dev), float(lr),
+def update_buffer(w, n, j0, seed, n_probes, g_dev, lr, dtype, stream=None, dirs=ZO_DIRS_GAUSS):
+    check(lib().zo_update_buffer(_ptr(w), dtype, dirs, n, j0, seed, n_probes, _ptr(g_dev), float(lr),
                                  _stream(stream)), "zo_update_buffer")
 
 
