@@ -30,6 +30,8 @@ What is computed, and where the pages state it:
   (``q8_table``; arena desc key ``"dirs": "q8"``).
 * 1.5-SPSA (same section): one clean evaluation per step and a probe-space
   diagonal preconditioner (``spsa_step(precond=True)``).
+* Split perturbation with activation reuse (FedSPZO summary, section 2
+  "방법론"): ``fedspzo_step`` on the MLP.
 
 Readings where the pages are silent are listed in the repository's design
 notes; the ones that fix arithmetic are repeated at each function.
@@ -294,13 +296,16 @@ def lsq_grad(W, X, Y) -> np.ndarray:
     return X.T @ (X @ W - Y) / X.shape[0]
 
 
+def mean_ce(logits: np.ndarray, labels) -> float:
+    lse = logsumexp_rows(logits)
+    return float(np.mean(lse - logits[np.arange(logits.shape[0]), labels]))
+
+
 def mlp_loss(W1, W2, X, labels) -> float:
     """Mean cross-entropy of logits = GELU(X W1^T) W2^T (no biases)."""
     W1, W2, X = (np.asarray(a, np.float64) for a in (W1, W2, X))
     h = gelu_erf(X @ W1.T)
-    logits = h @ W2.T
-    lse = logsumexp_rows(logits)
-    return float(np.mean(lse - logits[np.arange(X.shape[0]), labels]))
+    return mean_ce(h @ W2.T, labels)
 
 
 def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5) -> np.ndarray:
@@ -396,6 +401,28 @@ class Arena:
         else:
             getattr(lib(), "oracle_perturb_" + kind)(*args)
 
+    def perturb_range(self, off: int, n: int, seed: int, probe: int, sigma: float) -> None:
+        """The same on arena elements off .. off+n-1 only (direction elements
+        off .. off+n-1)."""
+        kind = "bf16" if self.dtype == "bf16" else "f32"
+        view = self.data[off:off + n]
+        args = (_ptr(view), n, off, seed, probe, float(np.float32(sigma)))
+        if self.dirs == "q8":
+            getattr(lib(), "oracle_q8_perturb_" + kind)(*args, _ptr(_q8()))
+        else:
+            getattr(lib(), "oracle_perturb_" + kind)(*args)
+
+    def update_range(self, off: int, n: int, seed: int, coeffs: np.ndarray) -> None:
+        """w <- round_storage(w + sum_i c_i z_i) on elements off .. off+n-1."""
+        c = np.ascontiguousarray(coeffs, dtype=np.float64)
+        kind = "bf16" if self.dtype == "bf16" else "f32"
+        view = self.data[off:off + n]
+        args = (_ptr(view), n, off, seed, c.size, _ptr(c))
+        if self.dirs == "q8":
+            getattr(lib(), "oracle_q8_update_" + kind)(*args, _ptr(_q8()))
+        else:
+            getattr(lib(), "oracle_update_" + kind)(*args)
+
     def update(self, seed: int, coeffs: np.ndarray) -> None:
         """w <- round_storage(w + sum_i c_i z_i), every element of the arena."""
         c = np.ascontiguousarray(coeffs, dtype=np.float64)
@@ -405,6 +432,57 @@ class Arena:
             getattr(lib(), "oracle_q8_update_" + kind)(*args, _ptr(_q8()))
         else:
             getattr(lib(), "oracle_update_" + kind)(*args)
+
+
+def fedspzo_step(arena: Arena, batch: dict, seed: int, p1: int, ps: int, eps: float, lr: float):
+    """One split-perturbation step on the MLP (FedSPZO summary, section 2
+    "방법론"); updates ``arena`` in place.
+
+    The network is split into a first, larger block theta_1 = W1 (with the
+    GELU) and a second, smaller block theta_2 = W2.  For each of p1 directions
+    z1_i of theta_1 and each sign s: the block-1 output y_s = GELU(X D(W1 +
+    s eps z1_i)^T) is computed once and reused by ps directions z2_m of
+    theta_2, each evaluated at +eps and -eps: L(m, +-) = CE(y_s D(W2 +- eps
+    z2_m)^T), m = (2 i + v) ps + k for sign index v (0: +, 1: -) and k < ps.
+    So theta_2 gets p2 = 2 p1 ps directions.
+      g2_m = (L(m, +) - L(m, -)) / (2 eps)      (losses sharing one y_s)
+      g1_i = (Lbar(i, +) - Lbar(i, -)) / (2 eps), Lbar(i, s) the mean of the
+             2 ps losses of branch s (the average of the f2 perturbations'
+             loss differences)
+    then W1 <- D(W1 - (lr/p1) sum_i g1_i z1_i), W2 <- D(W2 - (lr/p2) sum_m
+    g2_m z2_m), nothing if any loss is not finite.  Directions: z1_i is probe
+    i of the step seed on W1's elements, z2_m is probe p1 + m on W2's (arena
+    element j uses direction element j); no other element is touched.
+    Returns (losses [4 p1 ps] as L(m, +), L(m, -) for m = 0, 1, ..., g1 [p1],
+    g2 [p2]).
+    """
+    assert arena.desc["kind"] == "mlp"
+    lay = {name: (off, shape) for name, off, shape in param_layout(arena.desc)[0]}
+    (o1, s1), (o2, s2) = lay["W1"], lay["W2"]
+    n1, n2 = int(np.prod(s1)), int(np.prod(s2))
+    sig = float(np.float32(eps))
+    X = np.asarray(batch["X"], np.float64)
+    labels = batch["labels"]
+    p2 = 2 * p1 * ps
+    losses = np.zeros(2 * p2)
+    for i in range(p1):
+        for v, s in enumerate((1.0, -1.0)):
+            a = arena.copy()
+            a.perturb_range(o1, n1, seed, i, s * sig)
+            y = gelu_erf(X @ a.values()[o1:o1 + n1].reshape(s1).T)  # block-1 output, reused below
+            for k in range(ps):
+                m = (2 * i + v) * ps + k
+                for t, u in enumerate((1.0, -1.0)):
+                    b = arena.copy()
+                    b.perturb_range(o2, n2, seed, p1 + m, u * sig)
+                    losses[2 * m + t] = mean_ce(y @ b.values()[o2:o2 + n2].reshape(s2).T, labels)
+    g2 = (losses[0::2] - losses[1::2]) / (2.0 * sig)
+    branch = losses.reshape(p1, 2, 2 * ps).mean(axis=2)
+    g1 = (branch[:, 0] - branch[:, 1]) / (2.0 * sig)
+    if np.all(np.isfinite(losses)):
+        arena.update_range(o1, n1, seed, -lr * g1 / p1)
+        arena.update_range(o2, n2, seed, np.concatenate([np.zeros(p1), -lr * g2 / p2]))
+    return losses, g1, g2
 
 
 def model_loss(arena: Arena, batch: dict, round_bf16: bool = True) -> float:
