@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--precond", action="store_true",
                    help="1.5-SPSA: one clean evaluation per step and probe-space preconditioning")
     p.add_argument("--curv-floor", type=float, default=1.0, help="1.5-SPSA curvature floor")
+    p.add_argument("--split", default=None, metavar="P1,PS",
+                   help="MLP: split-perturbation (FedSPZO) steps with P1 theta_1 directions and PS theta_2 "
+                        "directions per branch instead of SPSA steps")
     p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
                    help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
     return p.parse_args()
@@ -79,7 +82,8 @@ def build_mlp(torch, zo, inputs):
         "flops_per_eval": 2.0 * B * D * H + 2.0 * B * H * C,
         # the dominant kernel forms X Z_i^T for each probe direction (fp32
         # through six bf16 MFMA products) and generates Z_i (and W2's part)
-        "split_bf16": {"direction_flops": 2.0 * B * D * H, "gaussians": H * D + C * H},
+        "split_bf16": {"direction_flops": 2.0 * B * D * H, "gaussians": H * D + C * H, "w1_gaussians": H * D,
+                       "w2_gaussians": C * H},
         "dtype": "f32", "kernel": "gemm_f32", "peak_tflops": BF16_PEAK_TFLOPS,
         "oracle_desc": {"kind": "mlp", "batch": B, "d_in": D, "hidden": H, "classes": C},
         "oracle_batch": {"X": inp["X"], "labels": inp["labels"]}, "arena": arena,
@@ -254,14 +258,25 @@ def main():
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     N = info["probes"]
     pc = 1 if args.precond else 0
-    evals_per_step = 2 * N + pc
+    split = None
+    if args.split:
+        if args.workload != "mlp" or args.precond:
+            print("bench.py: --split applies to the MLP workload, without --precond", file=sys.stderr)
+            sys.exit(2)
+        split = tuple(int(x) for x in args.split.split(","))
+    evals_per_step = 4 * split[0] * split[1] if split else 2 * N + pc
+    probe_evals_per_step = evals_per_step if split else 2 * N
     losses = torch.zeros(evals_per_step, dtype=torch.float64, device="cuda")
-    g = torch.zeros(N, dtype=torch.float64, device="cuda")
+    g = torch.zeros(max(N, split[0] if split else 0), dtype=torch.float64, device="cuda")
+    g2 = torch.zeros(2 * split[0] * split[1] if split else 1, dtype=torch.float64, device="cuda")
     mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
 
     def step(seed):
-        model.step(batch, seed, N, info["eps"], info["lr"], mode, losses, g, precond=pc,
-                   curv_floor=args.curv_floor)
+        if split:
+            model.step_split(batch, seed, split[0], split[1], info["eps"], info["lr"], losses, g, g2)
+        else:
+            model.step(batch, seed, N, info["eps"], info["lr"], mode, losses, g, precond=pc,
+                       curv_floor=args.curv_floor)
 
     for t in range(args.warmup):
         step(t)
@@ -282,7 +297,7 @@ def main():
     zo.timing_enable(False)
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    evals_per_s = 2 * N * args.steps / (total_ms * 1e-3)
+    evals_per_s = probe_evals_per_step * args.steps / (total_ms * 1e-3)
     k_ms, k_n = zo.timing_query(info["kernel"])
     k_avg_s = k_ms / k_n * 1e-3
     # then the same number of steps again with events around every launch,
@@ -308,9 +323,11 @@ def main():
         # six bf16 MFMA products (priced against the bf16 peak), plus the
         # generation of every direction element it uses
         sp = info["split_bf16"]
-        flops_per_launch = 6 * N * sp["direction_flops"]
-        gauss = N * sp["gaussians"]
-        extra = {"fp32_equiv_tflops": round(N * sp["direction_flops"] / k_avg_s / 1e12, 2),
+        dirs_per_launch = split[0] * args.steps / k_n if split else N
+        flops_per_launch = 6 * dirs_per_launch * sp["direction_flops"]
+        # split perturbation: each theta_1 direction's launch also draws 2 ps theta_2 directions
+        gauss = dirs_per_launch * (sp["gaussians"] if not split else sp["w1_gaussians"] + 2 * split[1] * sp["w2_gaussians"])
+        extra = {"fp32_equiv_tflops": round(dirs_per_launch * sp["direction_flops"] / k_avg_s / 1e12, 2),
                  "fp32_equiv_peak": round(BF16_PEAK_TFLOPS / 6, 1),
                  "gaussians_per_s": round(gauss / k_avg_s, 1),
                  "valu_frac_generation": round(gauss * C_Z / k_avg_s / VALU_PEAK_LANE_OPS, 4),
@@ -343,11 +360,14 @@ def main():
                    "mode": info["mode"], "parallelism": "none (1 GPU)",
                    **({"variant": "1.5-SPSA", "evals_per_step": evals_per_step, "curv_floor": args.curv_floor}
                       if pc else {}),
-                   **({"directions": "8-bit packed (256-level quantised Gaussian)"} if args.dirs == "q8" else {})},
+                   **({"directions": "8-bit packed (256-level quantised Gaussian)"} if args.dirs == "q8" else {}),
+                   **({"variant": "split perturbation (FedSPZO), activation reuse", "p1": split[0], "ps": split[1],
+                       "p2": 2 * split[0] * split[1], "evals_per_step": evals_per_step} if split else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
                      "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
-                     "traffic": TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
-                     "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), {2 * N} evaluations per launch"
+                     "traffic": None if split else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
+                     "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), "
+                                 f"{evals_per_step if split else 2 * N} evaluations per step"
                                  if "split_bf16" in info else
                                  f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch")
                                 if info["kernel"] == "gemm_f32" else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
@@ -357,7 +377,7 @@ def main():
     }
     if not args.no_passes:
         line["perturb_update"] = measure_passes(torch, zo)
-    if not args.no_cpu_baseline and "oracle_desc" in info:
+    if not args.no_cpu_baseline and "oracle_desc" in info and not split:
         line["cpu_baseline"] = cpu_baseline(info)
     print(json.dumps(line), flush=True)
 

@@ -147,6 +147,15 @@ typedef struct {
     float curv_floor;  /* 1.5-SPSA: lower bound of the curvature estimate, > 0 */
 } zo_step_cfg;
 
+/* Split-perturbation step configuration (zo_step_split). */
+typedef struct {
+    uint64_t seed; /* this step's direction seed */
+    uint32_t p1;   /* theta_1 (W1) directions, >= 1 */
+    uint32_t ps;   /* theta_2 (W2) directions per theta_1 branch, 1..4 */
+    float eps;     /* perturbation scale of both blocks */
+    float lr;      /* eta */
+} zo_split_cfg;
+
 typedef struct zo_model zo_model;
 
 /* ---------------------------------------------------------------- layout */
@@ -218,6 +227,29 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
  */
 zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev,
                   double* g_dev, zo_stream s);
+
+/*
+ * One split-perturbation step with activation reuse (FedSPZO summary,
+ * section 2 "방법론"), for the MLP with d_in % 32 == 0 and Gaussian
+ * directions.  theta_1 = W1 (with the GELU), theta_2 = W2.  For each theta_1
+ * direction i < p1 and sign s (v = 0 for +, 1 for -) the block-1 output
+ * y = GELU(X (W1 + s eps z1_i)^T) is formed once and reused by ps theta_2
+ * directions z2_m, m = (2 i + v) ps + k, each evaluated at +eps and -eps:
+ * losses_dev[2m] = L(y, W2 + eps z2_m), losses_dev[2m + 1] = L(y, W2 - eps z2_m)
+ * (device fp64, 4 p1 ps values).  g2_dev[m] = (losses[2m] - losses[2m+1]) /
+ * (2 eps) (device fp64, p2 = 2 p1 ps values); g1_dev[i] = (mean of branch
+ * (i, +)'s 2 ps losses - mean of branch (i, -)'s) / (2 eps) (device, p1).
+ * Then W1 <- W1 - (lr / p1) sum_i g1_i z1_i with z1_i = direction i, and
+ * W2 <- W2 - (lr / p2) sum_m g2_m z2_m with z2_m = direction p1 + m, each on
+ * its own tensor's elements only; a non-finite loss skips both.  The
+ * evaluations use the linearity of both layers in their perturbation (W1's
+ * product with X formed once; logits at W2 +- eps z2 as A W2^T +- eps A z2^T),
+ * so they differ from products with rounded perturbed weights only by that
+ * rounding.  ZO_ERR_UNSUPPORTED for other models, 8-bit directions,
+ * d_in % 32 != 0, or (1 + ps) * classes > 56.
+ */
+zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg, double* losses_dev,
+                        double* g1_dev, double* g2_dev, zo_stream s);
 
 /*
  * Seed replay of one recorded step (position paper summary, P5, and FedSPZO,

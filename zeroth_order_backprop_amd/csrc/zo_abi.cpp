@@ -407,6 +407,18 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st, m->desc.dirs);
 }
 
+zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg, double* losses_dev,
+                        double* g1_dev, double* g2_dev, zo_stream s)
+{
+    if (!m || !cfg || !losses_dev || !g1_dev || !g2_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (zo_status st = validate_batch(m, b)) return st;
+    if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
+    if (m->desc.dirs != ZO_DIRS_GAUSS) return fail(ZO_ERR_UNSUPPORTED, "split perturbation uses Gaussian directions");
+    if (zo_status st = mlp_split_check(m->desc, (int)cfg->p1, (int)cfg->ps)) return st;
+    return mlp_split_step(view_of(m), *b, cfg->seed, (int)cfg->p1, (int)cfg->ps, cfg->eps, cfg->lr, losses_dev,
+                          g1_dev, g2_dev, (hipStream_t)s);
+}
+
 zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_dev, zo_stream s)
 {
     if (!m || !cfg || !g_dev) return fail(ZO_ERR_INVALID, "null argument");

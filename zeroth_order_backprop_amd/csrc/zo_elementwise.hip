@@ -145,7 +145,7 @@ __device__ __forceinline__ bool load_coeffs(const double* __restrict__ g, uint32
 constexpr uint32_t kMaxProbes = 1024;
 
 __global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, uint64_t n_full, uint64_t j0,
-                                                        Key key, uint32_t n_probes,
+                                                        Key key, uint32_t p0, uint32_t n_probes,
                                                         const double* __restrict__ g, float lr)
 {
     __shared__ float c[kMaxProbes];
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, ui
         float4 aa = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
         for (uint32_t i = 0; i < n_probes; ++i) {
             const float ci = c[i];
-            const float4 za = gauss4(key, i, (j0 + ea) >> 2);
-            const float4 zb = gauss4(key, i, (j0 + eb) >> 2);
+            const float4 za = gauss4(key, p0 + i, (j0 + ea) >> 2);
+            const float4 zb = gauss4(key, p0 + i, (j0 + eb) >> 2);
             aa.x = fmaf(ci, za.x, aa.x); aa.y = fmaf(ci, za.y, aa.y);
             aa.z = fmaf(ci, za.z, aa.z); aa.w = fmaf(ci, za.w, aa.w);
             ab.x = fmaf(ci, zb.x, ab.x); ab.y = fmaf(ci, zb.y, ab.y);
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, ui
 }
 
 __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w, uint64_t n_full,
-                                                         uint64_t j0, Key key, uint32_t n_probes,
+                                                         uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
                                                          const double* __restrict__ g, float lr)
 {
     __shared__ float c[kMaxProbes];
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (uint32_t i = 0; i < n_probes; ++i) {
             const float ci = c[i];
-            const float4 za = gauss4(key, i, (j0 + e) >> 2);
-            const float4 zb = gauss4(key, i, ((j0 + e) >> 2) + 1);
+            const float4 za = gauss4(key, p0 + i, (j0 + e) >> 2);
+            const float4 zb = gauss4(key, p0 + i, ((j0 + e) >> 2) + 1);
             acc[0] = fmaf(ci, za.x, acc[0]); acc[1] = fmaf(ci, za.y, acc[1]);
             acc[2] = fmaf(ci, za.z, acc[2]); acc[3] = fmaf(ci, za.w, acc[3]);
             acc[4] = fmaf(ci, zb.x, acc[4]); acc[5] = fmaf(ci, zb.y, acc[5]);
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void update_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                         uint64_t j0, Key key, uint32_t n_probes,
+                                                         uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
                                                          const double* __restrict__ g, float lr)
 {
     __shared__ float c[kMaxProbes];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void update_tail(T* __restrict__ w, uint6
     const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
     float acc = 0.f;
-    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p, j0 + i), acc);
+    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p0 + p, j0 + i), acc);
     store_elem(w, i, load_elem(w, i) + acc);
 }
 
@@ -277,7 +277,8 @@ __global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_t n_full, uint64_t j0, Key key,
-                                                       uint32_t n_probes, const double* __restrict__ g, float lr)
+                                                       uint32_t p0, uint32_t n_probes, const double* __restrict__ g,
+                                                       float lr)
 {
     __shared__ float tab[256];
     __shared__ float c[kMaxProbes];
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_
         for (int t = 0; t < 16; ++t) acc[t] = 0.0f;
         for (uint32_t i = 0; i < n_probes; ++i) {
             const float ci = c[i];
-            const uint4 cw = dirs8::block(key, i, (j0 + e) >> 4);
+            const uint4 cw = dirs8::block(key, p0 + i, (j0 + e) >> 4);
             const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
             for (int t = 0; t < 16; ++t) acc[t] = fmaf(ci, dirs8::code(tab, words[t >> 2], t & 3), acc[t]);
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void perturb_q8_tail(T* __restrict__ w, u
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void update_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                            uint64_t j0, Key key, uint32_t n_probes,
+                                                            uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
                                                             const double* __restrict__ g, float lr)
 {
     __shared__ float tab[256];
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void update_q8_tail(T* __restrict__ w, ui
     const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= n) return;
     float acc = 0.f;
-    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], dirs8::value1(tab, key, p, j0 + i), acc);
+    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], dirs8::value1(tab, key, p0 + p, j0 + i), acc);
     store_elem(w, i, load_elem(w, i) + acc);
 }
 
@@ -415,16 +416,17 @@ static zo_status launch_perturb_q8(T* w, uint64_t n, uint64_t j0, Key key, uint3
 }
 
 template <typename T>
-static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32_t n_probes, const double* g,
-                                  float lr, hipStream_t s)
+static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
+                                  const double* g, float lr, hipStream_t s)
 {
     if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
     const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
     KernelTimer timer("update", s);
-    if (n_full) update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, n_probes, g, lr);
+    if (n_full)
+        update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, p0, n_probes, g, lr);
     if (n > n_full)
         update_q8_tail<T><<<(int)((n - n_full + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, n_full, n, j0, key,
-                                                                                               n_probes, g, lr);
+                                                                                               p0, n_probes, g, lr);
     return check_launch("update (8-bit directions)");
 }
 
@@ -454,28 +456,29 @@ zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t s
 }
 
 zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                        const double* g, float lr, hipStream_t s, int dirs)
+                        const double* g, float lr, hipStream_t s, int dirs, uint32_t p0)
 {
     if (n_probes == 0 || n_probes > kMaxProbes)
         return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     if (dirs == ZO_DIRS_Q8)
-        return dtype == ZO_F32 ? launch_update_q8((float*)w, n, j0, key, n_probes, g, lr, s)
-                               : launch_update_q8((uint16_t*)w, n, j0, key, n_probes, g, lr, s);
+        return dtype == ZO_F32 ? launch_update_q8((float*)w, n, j0, key, p0, n_probes, g, lr, s)
+                               : launch_update_q8((uint16_t*)w, n, j0, key, p0, n_probes, g, lr, s);
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("update", s);
     if (n_full) {
         if (dtype == ZO_F32)
-            update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, n_probes, g, lr);
+            update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, p0, n_probes, g, lr);
         else
-            update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, n_probes, g, lr);
+            update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, p0, n_probes, g, lr);
     }
     if (n > n_full) {
         const int blocks = (int)((n - n_full + kThreads - 1) / kThreads);
         if (dtype == ZO_F32)
-            update_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, n_probes, g, lr);
+            update_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, p0, n_probes, g, lr);
         else
-            update_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, n_probes, g, lr);
+            update_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, p0, n_probes, g,
+                                                               lr);
     }
     return check_launch("update");
 }

@@ -59,6 +59,8 @@ struct GemmArgs {
     uint64_t w2_dir;
     int C;
     float* logit_part;  // [eval][n_tile][M][C]
+    int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
+    uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
 };
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -400,6 +402,100 @@ __global__ __launch_bounds__(kThreads) void mlp_ce_rows(const float* __restrict_
     if (lane == 0) chunk_sum[(size_t)e * gridDim.x + chunk] = v;
 }
 
+// Split perturbation: block (chunk, e2) with e2 = (2 d + v) ps + k covers rows
+// 64 chunk .. +63 of branch b = 2 d + v and its theta_2 direction k.  The
+// branch's partials are [tile][(1 + ps) C columns: slot * C + class][row].
+// The logits at W2 +- eps z2_k are base +- eps dir, base and dir the tile
+// sums of slot 0 and slot 1 + k (same fixed-order fp64 tile sums as
+// mlp_ce_rows); the block writes the row-loss sums of both signs as
+// evaluations 2 e2 and 2 e2 + 1.
+__global__ __launch_bounds__(kThreads) void split_ce_rows(const float* __restrict__ part, int n_tiles, int M, int C,
+                                                           int ps, double eps,
+                                                           const int32_t* __restrict__ labels,
+                                                           double* __restrict__ chunk_sum)
+{
+    __shared__ double lg_w[4][64][2 * kMaxClasses + 1];
+    const int e2 = blockIdx.y, chunk = blockIdx.x;
+    const int branch = e2 / ps, k = e2 % ps;
+    const int Q = (1 + ps) * C;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = chunk * 64 + lane;
+    double lb[kMaxClasses], ld[kMaxClasses];
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) lb[c] = ld[c] = 0.0;
+    if (m < M) {
+        for (int t = wave; t < n_tiles; t += 4) {
+            const float* pb = part + ((size_t)branch * n_tiles + t) * Q * M + m;
+            const float* pd = pb + (size_t)(1 + k) * C * M;
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c)
+                if (c < C) {
+                    lb[c] += (double)pb[(size_t)c * M];
+                    ld[c] += (double)pd[(size_t)c * M];
+                }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+        lg_w[wave][lane][c] = lb[c];
+        lg_w[wave][lane][kMaxClasses + c] = ld[c];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    double v[2] = {0.0, 0.0};
+    if (m < M) {
+        const int y = labels[m];
+#pragma unroll
+        for (int c = 0; c < kMaxClasses; ++c) {
+            lb[c] = ((lg_w[0][lane][c] + lg_w[1][lane][c]) + lg_w[2][lane][c]) + lg_w[3][lane][c];
+            const int cd = kMaxClasses + c;
+            ld[c] = ((lg_w[0][lane][cd] + lg_w[1][lane][cd]) + lg_w[2][lane][cd]) + lg_w[3][lane][cd];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const double se_ = t == 0 ? eps : -eps;
+            double mx = -INFINITY, picked = 0.0;
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c)
+                if (c < C) mx = fmax(mx, lb[c] + se_ * ld[c]);
+            double se = 0.0;
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c)
+                if (c < C) {
+                    const double l = lb[c] + se_ * ld[c];
+                    se += exp(l - mx);
+                    if (c == y) picked = l;
+                }
+            v[t] = (mx + log(se)) - picked;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const double w = wave_sum(v[t]);
+        if (lane == 0) chunk_sum[(size_t)(2 * e2 + t) * gridDim.x + chunk] = w;
+    }
+}
+
+// g2[m] = (L[2m] - L[2m+1]) / (2 eps) for m < 2 p1 ps; g1[d] = (mean of branch
+// (d, +)'s 2 ps losses - mean of branch (d, -)'s) / (2 eps) for d < p1.
+__global__ void split_g_kernel(const double* __restrict__ L, int p1, int ps, double eps, double* __restrict__ g1,
+                               double* __restrict__ g2)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int p2 = 2 * p1 * ps;
+    if (t < p2) {
+        g2[t] = (L[2 * t] - L[2 * t + 1]) / (2.0 * eps);
+    } else if (t < p2 + p1) {
+        const int d = t - p2;
+        double sp = 0.0, sm = 0.0;
+        for (int j = 0; j < 2 * ps; ++j) {
+            sp += L[(size_t)(2 * d) * 2 * ps + j];
+            sm += L[(size_t)(2 * d + 1) * 2 * ps + j];
+        }
+        g1[d] = (sp / (2 * ps) - sm / (2 * ps)) / (2.0 * eps);
+    }
+}
+
 // loss[e] = (sum of evaluation e's chunk sums, fixed order) / M
 __global__ __launch_bounds__(64) void mlp_ce_final(const double* __restrict__ chunk_sum, int n_chunks, int M,
                                                    double* __restrict__ loss)
@@ -467,7 +563,8 @@ __global__ __launch_bounds__(kThreads) void split_planes_kernel(const float* __r
     }
 }
 
-enum { SG_BASE_STORE = 0, SG_BASE_MLP = 1, SG_PROBE_MLP = 2 };
+enum { SG_BASE_STORE = 0, SG_BASE_MLP = 1, SG_PROBE_MLP = 2, SG_PROBE_SPLIT = 3 };
+constexpr int kSplitMaxPs = 4;  // theta_2 directions per branch in one split-perturbation launch
 
 struct SplitArgs {
     const bf16_t* Xp;   // [3][M][K] bf16 planes of X
@@ -479,6 +576,8 @@ struct SplitArgs {
     uint64_t w2_dir;
     int C;
     float* logit_part;  // [eval][n_tile][M][C]
+    int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
+    uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
 };
 
 // vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
@@ -496,9 +595,15 @@ struct SplitArgs {
 //   SG_BASE_MLP:   stored weights, logits of GELU(acc) against W2.
 //   SG_PROBE_MLP:  for each sign v, logits of GELU(H + sigma_v acc) against
 //                  W2 + sigma_v z2 (z2 the same direction's W2 part).
-template <int BM, int BN, int NT, int MODE, int NV>
+//   SG_PROBE_SPLIT: for each sign v of the theta_1 direction, the block-1
+//                  output A = GELU(H + sigma_v acc) is reused: partial logits
+//                  of A against W2 (slot 0) and against each of the branch's
+//                  ps theta_2 directions (slot 1 + k), so that the logits at
+//                  W2 +- eps z2_k are slot 0 +- eps slot (1 + k).
+template <int BM, int BN, int NT, int MODE, int NV, int QT = 0>
 __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
 {
+    constexpr bool PROBE = MODE == SG_PROBE_MLP || MODE == SG_PROBE_SPLIT;
     constexpr int BK = 32;
     constexpr int WAVES_M = NT / 128, WM = BM / WAVES_M, WN = BN / 2;
     constexpr int RB = WM / 32, CB = WN / 32;
@@ -617,7 +722,7 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
     };
     constexpr int NPIECE = 3 * B_Q;
     auto produce_b = [&](int k0) {
-        if constexpr (MODE == SG_PROBE_MLP) {
+        if constexpr (PROBE) {
 #pragma unroll
             for (int pc = 0; pc < NPIECE; ++pc) z_piece(pc, k0);
         } else {
@@ -635,14 +740,14 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
     for (int kt = 0; kt + 1 < KT; ++kt) {
         const int kn = (kt + 1) * BK;
         issue_a(cur ^ 1, kn);
-        if constexpr (MODE != SG_PROBE_MLP) load_b(kn);
+        if constexpr (!PROBE) load_b(kn);
         mma_step(cur, 0);
-        if constexpr (MODE == SG_PROBE_MLP) {
+        if constexpr (PROBE) {
 #pragma unroll
             for (int pc = 0; pc < NPIECE / 2; ++pc) z_piece(pc, kn);
         }
         mma_step(cur, 1);
-        if constexpr (MODE == SG_PROBE_MLP) {
+        if constexpr (PROBE) {
 #pragma unroll
             for (int pc = NPIECE / 2; pc < NPIECE; ++pc) z_piece(pc, kn);
         }
@@ -666,6 +771,98 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
                     const int col = n0 + wn * WN + j * 32 + lr;
                     if (row < M && col < N) a.H[(size_t)row * N + col] = acc[i][j][r];
                 }
+    } else if constexpr (MODE == SG_PROBE_SPLIT) {
+        // Columns q = slot * C + c of the (1 + ps) C partial logits (slot 0:
+        // W2, slot 1 + k: theta_2 direction k) are split between the two
+        // thread groups, QT per group; their weights sit in LDS as rows of BN,
+        // zero past (1 + ps) C, so the dot-product loop has no guards.
+        static_assert(NV == 2 && QT > 0, "both signs of the theta_1 direction");
+        constexpr int SH = BN + 4;
+        constexpr int GROUPS = NT / BM;
+        static_assert(GROUPS == 2, "two thread groups per row");
+        float* Hs = reinterpret_cast<float*>(lds_bf);    // BM x SH
+        float* Wz = Hs + BM * SH;                       // 2 QT rows of BN
+        const int C = a.C, ps = a.ps, Q = (1 + ps) * C;
+        __syncthreads();  // every wave is done with the stage buffers
+        // W2 rows (q < C) and the zero rows past Q, once
+        for (int t = tid; t < 2 * QT * (BN / 4); t += NT) {
+            const int q = t / (BN / 4), n4 = 4 * (t % (BN / 4));
+            const int gn = n0 + n4;
+            float4 w = {0.f, 0.f, 0.f, 0.f};
+            if (q < C && gn < N) w = *reinterpret_cast<const float4*>(a.W2 + (size_t)q * N + gn);
+            if (q < C || q >= Q) *reinterpret_cast<float4*>(Wz + q * BN + n4) = w;
+        }
+        const int row = tid % BM;
+        const int grp = __builtin_amdgcn_readfirstlane(tid / BM);  // wave-uniform
+        const int gm = m0 + row;
+        const float* wq = Wz + grp * QT * BN;
+        const int qlim = Q - grp * QT;  // this group's columns: qq < qlim
+#pragma unroll 1
+        for (int v = 0; v < 2; ++v) {
+            const float sg = ev.sigma[g][v];
+            // the stored-weight product under this thread's accumulators, read
+            // per sign (L2-resident) so it holds no registers through the dot
+            // products; issued before the direction rows are generated
+            float hb[RB][CB][16];
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int col = n0 + wn * WN + j * 32 + lr;
+                        hb[i][j][r] = (row < M && col < N) ? a.H[(size_t)row * N + col] : 0.f;
+                    }
+            // this branch's theta_2 directions on W2's elements: rows C .. Q-1
+            const uint32_t zp0 = a.z2_probe0 + (2 * probe + v) * (uint32_t)ps;
+            for (int t = tid; t < ps * C * (BN / 4); t += NT) {
+                const int q = C + t / (BN / 4), n4 = 4 * (t % (BN / 4));
+                const int k = q / C - 1, c = q % C;
+                const int gn = n0 + n4;
+                float4 z = {0.f, 0.f, 0.f, 0.f};
+                if (gn < N) z = gauss4(key, zp0 + k, (a.w2_dir + (size_t)c * N + gn) >> 2);
+                *reinterpret_cast<float4*>(Wz + q * BN + n4) = z;
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        const int lcol = wn * WN + j * 32 + lr;
+                        Hs[lrow * SH + lcol] = gelu_erf(fmaf(sg, acc[i][j][r], hb[i][j][r]));
+                    }
+            __syncthreads();
+            float p[QT];
+#pragma unroll
+            for (int qq = 0; qq < QT; ++qq) p[qq] = 0.f;
+            const float* hrow = Hs + row * SH;
+#pragma unroll 1
+            for (int n = 0; n < BN; n += 4) {
+                const float4 h4 = *reinterpret_cast<const float4*>(hrow + n);
+#pragma unroll
+                for (int qq = 0; qq < QT; ++qq) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(wq + qq * BN + n);
+                    float t = p[qq];
+                    t = fmaf(h4.x, w4.x, t); t = fmaf(h4.y, w4.y, t);
+                    t = fmaf(h4.z, w4.z, t); t = fmaf(h4.w, w4.w, t);
+                    p[qq] = t;
+                    // at most four rows' reads in flight: keeps the registers for the accumulators
+                    if (qq % 4 == 3) asm volatile("" ::: "memory");
+                }
+            }
+            if (gm < M) {
+                // branch (g, v): [tile][column q = slot * C + class][row], rows
+                // contiguous so that a wave's stores (and the reduction's loads) coalesce
+                float* dst = a.logit_part + (((size_t)(g * 2 + v) * gridDim.x + tn) * Q + grp * QT) * M + gm;
+#pragma unroll
+                for (int qq = 0; qq < QT; ++qq)
+                    if (qq < qlim) dst[(size_t)qq * M] = p[qq];
+            }
+            __syncthreads();  // Hs and the direction rows are rewritten for the next sign
+        }
     } else {
         // GELU(H tile) -> LDS, then partial logits over this tile's BN hidden
         // units against the (perturbed) W2 columns n0 .. n0+BN.  Columns past
@@ -691,7 +888,7 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     hb[i][j][r] = 0.f;
-                    if constexpr (MODE == SG_PROBE_MLP) {
+                    if constexpr (PROBE) {
                         const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
                         const int col = n0 + wn * WN + j * 32 + lr;
                         if (row < M && col < N) hb[i][j][r] = a.H[(size_t)row * N + col];
@@ -818,18 +1015,30 @@ zo_status launch_fgemm(const GemmArgs& a, const EvalList& ev, hipStream_t s)
 constexpr int SP_BM = 256, SP_BN = 128, SP_NT = 512;
 constexpr int SB_BM = 64, SB_BN = 64, SB_NT = 256;
 
-template <int BM, int BN, int NT, int MODE, int NV>
+template <int BM, int BN, int NT, int MODE, int NV, int QT = 0>
 zo_status launch_sgemm(const SplitArgs& a, const EvalList& ev, int groups, hipStream_t s, const char* fam)
 {
+    constexpr size_t kLdsMax = 160 * 1024;
     constexpr size_t stages = (size_t)2 * 3 * (BM + BN) * 32 * sizeof(bf16_t);
-    constexpr size_t epi = MODE == SG_BASE_STORE ? 0 : (size_t)(BM * (BN + 4) + NV * kMaxClasses * BN) * sizeof(float);
-    constexpr size_t lds = stages > epi ? stages : epi;
-    static_assert(lds <= 160 * 1024, "LDS budget");
-    auto kern = sgemm_kernel<BM, BN, NT, MODE, NV>;
+    constexpr size_t epi = MODE == SG_BASE_STORE || MODE == SG_PROBE_SPLIT
+                               ? 0
+                               : (size_t)(BM * (BN + 4) + NV * kMaxClasses * BN) * sizeof(float);
+    constexpr size_t lds_fixed = stages > epi ? stages : epi;
+    static_assert(lds_fixed <= kLdsMax, "LDS budget");
+    size_t lds = lds_fixed;
+    if constexpr (MODE == SG_PROBE_SPLIT) {
+        // GELU tile plus 2 QT weight rows of BN
+        const size_t e = (size_t)(BM * (BN + 4) + 2 * QT * BN) * sizeof(float);
+        if (e > kLdsMax || (1 + a.ps) * a.C > 2 * QT)
+            return fail(ZO_ERR_UNSUPPORTED, "split perturbation: (1 + ps) * classes too large");
+        lds = e > lds ? e : lds;
+    }
+    auto kern = sgemm_kernel<BM, BN, NT, MODE, NV, QT>;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", lds);
+        const size_t cap = MODE == SG_PROBE_SPLIT ? kLdsMax : lds_fixed;
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cap) != hipSuccess)
+            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", cap);
         attr_set = true;
     }
     dim3 grid(cdiv(a.N, BN), cdiv(a.M, BM), groups);
@@ -897,9 +1106,11 @@ size_t mlp_part_bytes(const zo_model_desc& d)
 }
 
 // workspace: logit partials | per-chunk CE sums | X planes (3 M K bf16) | X W1^T (M N fp32)
+constexpr int kSplitMaxEvalsPerCall = 256;  // theta_2 evaluations of one split-perturbation launch
 size_t mlp_chunk_bytes(const zo_model_desc& d)
 {
-    return (kMaxEvalsPerCall * (size_t)cdiv((int)d.batch, 64) * sizeof(double) + 255) / 256 * 256;
+    const size_t evals = kMaxEvalsPerCall > kSplitMaxEvalsPerCall ? kMaxEvalsPerCall : kSplitMaxEvalsPerCall;
+    return (evals * (size_t)cdiv((int)d.batch, 64) * sizeof(double) + 255) / 256 * 256;
 }
 size_t mlp_planes_bytes(const zo_model_desc& d) { return (3 * (size_t)d.batch * d.d_in * 2 + 255) / 256 * 256; }
 size_t mlp_h_bytes(const zo_model_desc& d) { return ((size_t)d.batch * d.hidden * 4 + 255) / 256 * 256; }
@@ -977,6 +1188,95 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
                                                               chunk_sum);
     mlp_ce_final<<<n_evals, 64, 0, s>>>(chunk_sum, n_chunks, M, loss);
     return check_launch("mlp cross-entropy");
+}
+
+zo_status mlp_split_check(const zo_model_desc& d, int p1, int ps)
+{
+    if (d.kind != ZO_MODEL_MLP) return fail(ZO_ERR_UNSUPPORTED, "split perturbation is defined for the MLP");
+    if (d.d_in % 32) return fail(ZO_ERR_UNSUPPORTED, "split perturbation needs d_in %% 32 == 0");
+    if (p1 < 1 || p1 > 1024) return fail(ZO_ERR_INVALID, "p1 must be in 1..1024");
+    if (ps < 1 || ps > kSplitMaxPs) return fail(ZO_ERR_INVALID, "ps must be in 1..%d", kSplitMaxPs);
+    if ((1 + ps) * d.classes > 56) return fail(ZO_ERR_UNSUPPORTED, "split perturbation: (1 + ps) * classes > 56");
+    if (2 * p1 * ps > 1024) return fail(ZO_ERR_INVALID, "2 p1 ps must be at most 1024");
+    return ZO_OK;
+}
+
+zo_status mlp_split_step(const ModelView& m, const zo_batch& b, uint64_t seed, int p1, int ps, float eps, float lr,
+                         double* losses, double* g1, double* g2, hipStream_t s)
+{
+    const zo_model_desc& d = m.desc;
+    const int M = (int)b.batch, N = (int)d.hidden, K = (int)d.d_in, C = (int)d.classes;
+    char* ws = (char*)m.workspace;
+    bf16_t* planes = (bf16_t*)(ws + mlp_part_bytes(d) + mlp_chunk_bytes(d));
+    double* chunk_sum = (double*)(ws + mlp_part_bytes(d));
+    SplitArgs a = {};
+    a.Xp = planes;
+    a.W = (const float*)m.params + m.offsets[0];
+    a.w_dir = m.offsets[0];
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.H = (float*)((char*)planes + mlp_planes_bytes(d));
+    a.W2 = (const float*)m.params + m.offsets[1];
+    a.w2_dir = m.offsets[1];
+    a.C = C;
+    a.logit_part = (float*)ws;
+    a.ps = ps;
+    a.z2_probe0 = (uint32_t)p1;
+    const int n_tiles = cdiv(N, SP_BN), n_chunks = cdiv(M, 64);
+    // directions per launch: partial slots, chunk sums and eval-list entries
+    const size_t slot_bytes = (size_t)n_tiles * M * C * sizeof(float);
+    const int by_slots = (int)(mlp_part_bytes(d) / slot_bytes) / (2 * (1 + ps));
+    const int by_evals = kSplitMaxEvalsPerCall / (4 * ps);
+    const int per_call = std::min(std::min(by_slots, by_evals), kMaxEvalsPerCall);
+    if (per_call < 1) return fail(ZO_ERR_WORKSPACE, "split perturbation: workspace too small");
+    zo_status st;
+    {
+        const size_t n4 = (size_t)M * K / 4;
+        KernelTimer timer("gemm_f32_base", s);
+        split_planes_kernel<<<(int)std::min<size_t>((n4 + kThreads - 1) / kThreads, 2048), kThreads, 0, s>>>(
+            (const float*)b.x, n4, planes, (size_t)M * K);
+    }
+    if ((st = check_launch("X split"))) return st;
+    EvalList base;
+    make_evals(nullptr, 0, base);
+    if ((st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_STORE, 1>(a, base, 1, s, "gemm_f32_base"))) return st;
+    for (int d0 = 0; d0 < p1; d0 += per_call) {
+        const int nd = std::min(per_call, p1 - d0);
+        EvalList ev;
+        memset(&ev, 0, sizeof ev);
+        ev.n_groups = nd;
+        ev.perturbed = 1;
+        for (int gi = 0; gi < nd; ++gi) {
+            ev.seed[gi] = seed;
+            ev.probe[gi] = (uint32_t)(d0 + gi);
+            ev.sigma[gi][0] = eps;
+            ev.sigma[gi][1] = -eps;
+        }
+        // columns per thread group: (1 + ps) C / 2, rounded up to an instantiated width
+        const int q2 = ((1 + ps) * C + 1) / 2;
+        st = q2 <= 8    ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_SPLIT, 2, 8>(a, ev, nd, s, "gemm_f32")
+             : q2 <= 16 ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_SPLIT, 2, 16>(a, ev, nd, s, "gemm_f32")
+                        : launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_SPLIT, 2, 28>(a, ev, nd, s, "gemm_f32");
+        if (st) return st;
+        const int n_e2 = nd * 2 * ps;
+        KernelTimer timer("reduce", s);
+        split_ce_rows<<<dim3(n_chunks, n_e2), kThreads, 0, s>>>(a.logit_part, n_tiles, M, C, ps, (double)eps,
+                                                                 b.labels, chunk_sum);
+        mlp_ce_final<<<2 * n_e2, 64, 0, s>>>(chunk_sum, n_chunks, M, losses + (size_t)4 * d0 * ps);
+        if ((st = check_launch("split cross-entropy"))) return st;
+    }
+    {
+        const int nt = 2 * p1 * ps + p1;
+        KernelTimer timer("reduce", s);
+        split_g_kernel<<<(nt + 63) / 64, 64, 0, s>>>(losses, p1, ps, (double)eps, g1, g2);
+        if ((st = check_launch("split g"))) return st;
+    }
+    const uint64_t n1 = (uint64_t)N * K, n2 = (uint64_t)C * N;
+    if ((st = launch_update((float*)m.params + m.offsets[0], ZO_F32, n1, m.offsets[0], seed, (uint32_t)p1, g1, lr, s)))
+        return st;
+    return launch_update((float*)m.params + m.offsets[1], ZO_F32, n2, m.offsets[1], seed, (uint32_t)(2 * p1 * ps), g2,
+                         lr, s, ZO_DIRS_GAUSS, (uint32_t)p1);
 }
 
 }  // namespace zo

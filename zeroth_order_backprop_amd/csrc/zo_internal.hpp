@@ -33,8 +33,9 @@ zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t s
                          float sigma, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 // w += sum_i c_i z_i, c_i = fp32(-lr * g_i / N) from fp64 g on the device;
 // nothing is written when any g_i is not finite.
+// Directions p0 .. p0 + n_probes - 1 (c_i pairs with direction p0 + i).
 zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
-                        const double* g, float lr, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
+                        const double* g, float lr, hipStream_t s, int dirs = ZO_DIRS_GAUSS, uint32_t p0 = 0);
 zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words,
                            float* z, hipStream_t s);
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);

@@ -36,6 +36,10 @@ zo_status mlp_check(const zo_model_desc& d);
 size_t mlp_workspace(const zo_model_desc& d);
 zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
                       hipStream_t s);
+// split-perturbation (FedSPZO) step of the MLP, fused
+zo_status mlp_split_check(const zo_model_desc& d, int p1, int ps);
+zo_status mlp_split_step(const ModelView& m, const zo_batch& b, uint64_t seed, int p1, int ps, float eps, float lr,
+                         double* losses, double* g1, double* g2, hipStream_t s);
 zo_status decoder_check(const zo_model_desc& d);
 size_t decoder_workspace(const zo_model_desc& d);
 zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,

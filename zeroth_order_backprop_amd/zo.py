@@ -19,7 +19,7 @@ ZO_DIRS_GAUSS, ZO_DIRS_Q8 = 0, 1
 
 EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
-    "zo_forward_loss", "zo_update", "zo_step", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
+    "zo_forward_loss", "zo_update", "zo_step", "zo_step_split", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
     "zo_timing_enable", "zo_timing_select", "zo_timing_reset", "zo_timing_query",
     "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
@@ -55,6 +55,11 @@ class Pert(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("probe", ctypes.c_uint32), ("sigma", ctypes.c_float)]
 
 
+class SplitCfg(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("p1", ctypes.c_uint32), ("ps", ctypes.c_uint32),
+                ("eps", ctypes.c_float), ("lr", ctypes.c_float)]
+
+
 class StepCfg(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("n_probes", ctypes.c_uint32), ("eps", ctypes.c_float),
                 ("lr", ctypes.c_float), ("mode", ctypes.c_int32), ("precond", ctypes.c_int32),
@@ -82,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "zo_update": [P, U64, U32, P, F, P],
         "zo_step": [P, P, P, P, P, P],
         "zo_replay_step": [P, P, P, P],
+        "zo_step_split": [P, P, P, P, P, P, P],
         "zo_perturb_buffer": [P, I32, I32, U64, U64, U64, U32, F, P],
         "zo_update_buffer": [P, I32, I32, U64, U64, U64, U32, P, F, P],
         "zo_gscalar": [P, U32, F, P, P],
@@ -260,6 +266,16 @@ class Model:
         cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), int(precond), float(curv_floor))
         check(lib().zo_step(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _ptr(g_dev),
                             _stream(stream)), "zo_step")
+
+    def step_split(self, batch: Batch, seed, p1, ps, eps, lr, losses_dev, g1_dev, g2_dev, stream=None):
+        """One split-perturbation (FedSPZO) step of the MLP: losses 4 p1 ps,
+        g1 p1, g2 2 p1 ps entries (device fp64)."""
+        p1, ps = int(p1), int(ps)
+        if losses_dev.numel() < 4 * p1 * ps or g1_dev.numel() < p1 or g2_dev.numel() < 2 * p1 * ps:
+            raise ValueError("zo_step_split: losses need 4 p1 ps entries, g1 p1, g2 2 p1 ps")
+        cfg = SplitCfg(int(seed), p1, ps, float(eps), float(lr))
+        check(lib().zo_step_split(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _ptr(g1_dev),
+                                  _ptr(g2_dev), _stream(stream)), "zo_step_split")
 
     def replay_step(self, seed, n_probes, eps, lr, mode, g_dev, stream=None):
         """The weight changes of a recorded step, given the g it produced."""
