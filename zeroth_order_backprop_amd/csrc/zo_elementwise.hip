@@ -73,7 +73,18 @@ __device__ __forceinline__ void store_elem(float* w, uint64_t i, float v) { w[i]
 __device__ __forceinline__ void store_elem(uint16_t* w, uint64_t i, float v) { w[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu); }
 
 // ---------------------------------------------------------------- perturb
-__global__ __launch_bounds__(kThreads) void perturb_f32(float* __restrict__ w, uint64_t n_full,
+// Elements [start, n) (the ragged tail, shorter than one block iteration),
+// taken by the grid's last block after its full iterations.
+template <typename T>
+__device__ __forceinline__ void perturb_tail(T* __restrict__ w, uint64_t start, uint64_t n, uint64_t j0, Key key,
+                                             uint32_t probe, float sigma)
+{
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t i = start + threadIdx.x; i < n; i += kThreads)
+        store_elem(w, i, fmaf(sigma, gauss1(key, probe, j0 + i), load_elem(w, i)));
+}
+
+__global__ __launch_bounds__(kThreads) void perturb_f32(float* __restrict__ w, uint64_t n_full, uint64_t n,
                                                          uint64_t j0, Key key, uint32_t probe,
                                                          float sigma)
 {
@@ -92,9 +103,10 @@ __global__ __launch_bounds__(kThreads) void perturb_f32(float* __restrict__ w, u
         *reinterpret_cast<float4*>(w + ea) = wa;
         *reinterpret_cast<float4*>(w + eb) = wb;
     }
+    perturb_tail(w, n_full, n, j0, key, probe, sigma);
 }
 
-__global__ __launch_bounds__(kThreads) void perturb_bf16(uint16_t* __restrict__ w, uint64_t n_full,
+__global__ __launch_bounds__(kThreads) void perturb_bf16(uint16_t* __restrict__ w, uint64_t n_full, uint64_t n,
                                                           uint64_t j0, Key key, uint32_t probe,
                                                           float sigma)
 {
@@ -112,18 +124,10 @@ __global__ __launch_bounds__(kThreads) void perturb_bf16(uint16_t* __restrict__ 
         f[6] = fmaf(sigma, zb.z, f[6]); f[7] = fmaf(sigma, zb.w, f[7]);
         *reinterpret_cast<uint4*>(w + e) = pack8(f);
     }
+    perturb_tail(w, n_full, n, j0, key, probe, sigma);
 }
 
-// Elements [start, n) one thread each (ragged tail, < kElemsPerIter).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void perturb_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                          uint64_t j0, Key key, uint32_t probe,
-                                                          float sigma)
-{
-    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    store_elem(w, i, fmaf(sigma, gauss1(key, probe, j0 + i), load_elem(w, i)));
-}
+
 
 // ----------------------------------------------------------------- update
 // Coefficients c_i = fp32(-lr * g_i / N) into LDS; returns false when any g_i
@@ -144,8 +148,21 @@ __device__ __forceinline__ bool load_coeffs(const double* __restrict__ g, uint32
 
 constexpr uint32_t kMaxProbes = 1024;
 
-__global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, uint64_t n_full, uint64_t j0,
-                                                        Key key, uint32_t p0, uint32_t n_probes,
+// The update's ragged tail (see perturb_tail); coefficients already in LDS.
+template <typename T>
+__device__ __forceinline__ void update_tail(T* __restrict__ w, uint64_t start, uint64_t n, uint64_t j0, Key key,
+                                            uint32_t p0, uint32_t n_probes, const float* c)
+{
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t i = start + threadIdx.x; i < n; i += kThreads) {
+        float acc = 0.f;
+        for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p0 + p, j0 + i), acc);
+        store_elem(w, i, load_elem(w, i) + acc);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, uint64_t n_full, uint64_t n,
+                                                        uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
                                                         const double* __restrict__ g, float lr)
 {
     __shared__ float c[kMaxProbes];
@@ -172,9 +189,10 @@ __global__ __launch_bounds__(kThreads) void update_f32(float* __restrict__ w, ui
         *reinterpret_cast<float4*>(w + ea) = wa;
         *reinterpret_cast<float4*>(w + eb) = wb;
     }
+    update_tail(w, n_full, n, j0, key, p0, n_probes, c);
 }
 
-__global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w, uint64_t n_full,
+__global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w, uint64_t n_full, uint64_t n,
                                                          uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
                                                          const double* __restrict__ g, float lr)
 {
@@ -201,22 +219,9 @@ __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w
         for (int t = 0; t < 8; ++t) f[t] += acc[t];
         *reinterpret_cast<uint4*>(w + e) = pack8(f);
     }
+    update_tail(w, n_full, n, j0, key, p0, n_probes, c);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void update_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                         uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
-                                                         const double* __restrict__ g, float lr)
-{
-    __shared__ float c[kMaxProbes];
-    __shared__ int bad;
-    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
-    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    float acc = 0.f;
-    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p0 + p, j0 + i), acc);
-    store_elem(w, i, load_elem(w, i) + acc);
-}
 
 // ------------------------------------------------ 8-bit packed directions
 // One Philox block gives the codes of 16 consecutive elements, so a thread
@@ -255,9 +260,32 @@ template <> struct Q8Io<float> {
     }
 };
 
+// The ragged tails of the 8-bit passes (see perturb_tail); table (and
+// coefficients) already in LDS.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64_t n_full, uint64_t j0, Key key,
-                                                        uint32_t probe, float sigma)
+__device__ __forceinline__ void perturb_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n, uint64_t j0,
+                                                Key key, uint32_t probe, float sigma, const float* tab)
+{
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t i = start + threadIdx.x; i < n; i += kThreads)
+        store_elem(w, i, fmaf(sigma, dirs8::value1(tab, key, probe, j0 + i), load_elem(w, i)));
+}
+
+template <typename T>
+__device__ __forceinline__ void update_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n, uint64_t j0, Key key,
+                                               uint32_t p0, uint32_t n_probes, const float* c, const float* tab)
+{
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t i = start + threadIdx.x; i < n; i += kThreads) {
+        float acc = 0.f;
+        for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], dirs8::value1(tab, key, p0 + p, j0 + i), acc);
+        store_elem(w, i, load_elem(w, i) + acc);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64_t n_full, uint64_t n, uint64_t j0,
+                                                        Key key, uint32_t probe, float sigma)
 {
     __shared__ float tab[256];
     dirs8::load_table(tab);
@@ -273,12 +301,13 @@ __global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64
         for (int t = 0; t < 16; ++t) f[t] = fmaf(sigma, dirs8::code(tab, words[t >> 2], t & 3), f[t]);
         Q8Io<T>::store(w, e, f);
     }
+    perturb_q8_tail(w, n_full, n, j0, key, probe, sigma, tab);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_t n_full, uint64_t j0, Key key,
-                                                       uint32_t p0, uint32_t n_probes, const double* __restrict__ g,
-                                                       float lr)
+__global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_t n_full, uint64_t n, uint64_t j0,
+                                                       Key key, uint32_t p0, uint32_t n_probes,
+                                                       const double* __restrict__ g, float lr)
 {
     __shared__ float tab[256];
     __shared__ float c[kMaxProbes];
@@ -304,36 +333,7 @@ __global__ __launch_bounds__(kThreads) void update_q8(T* __restrict__ w, uint64_
         for (int t = 0; t < 16; ++t) f[t] += acc[t];
         Q8Io<T>::store(w, e, f);
     }
-}
-
-// Elements [start, n) one thread each (ragged tail, < kQ8PerIter).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void perturb_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                             uint64_t j0, Key key, uint32_t probe, float sigma)
-{
-    __shared__ float tab[256];
-    dirs8::load_table(tab);
-    __syncthreads();
-    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    store_elem(w, i, fmaf(sigma, dirs8::value1(tab, key, probe, j0 + i), load_elem(w, i)));
-}
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void update_q8_tail(T* __restrict__ w, uint64_t start, uint64_t n,
-                                                            uint64_t j0, Key key, uint32_t p0, uint32_t n_probes,
-                                                            const double* __restrict__ g, float lr)
-{
-    __shared__ float tab[256];
-    __shared__ float c[kMaxProbes];
-    __shared__ int bad;
-    dirs8::load_table(tab);
-    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;
-    const uint64_t i = start + (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n) return;
-    float acc = 0.f;
-    for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], dirs8::value1(tab, key, p0 + p, j0 + i), acc);
-    store_elem(w, i, load_elem(w, i) + acc);
+    update_q8_tail(w, n_full, n, j0, key, p0, n_probes, c, tab);
 }
 
 // ------------------------------------------------------------ g scalars
@@ -408,10 +408,7 @@ static zo_status launch_perturb_q8(T* w, uint64_t n, uint64_t j0, Key key, uint3
     if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
     const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
     KernelTimer timer("perturb", s);
-    if (n_full) perturb_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, probe, sigma);
-    if (n > n_full)
-        perturb_q8_tail<T><<<(int)((n - n_full + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, n_full, n, j0, key,
-                                                                                                probe, sigma);
+    perturb_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, probe, sigma);
     return check_launch("perturb (8-bit directions)");
 }
 
@@ -422,36 +419,25 @@ static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32
     if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
     const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
     KernelTimer timer("update", s);
-    if (n_full)
-        update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, j0, key, p0, n_probes, g, lr);
-    if (n > n_full)
-        update_q8_tail<T><<<(int)((n - n_full + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, n_full, n, j0, key,
-                                                                                               p0, n_probes, g, lr);
+    update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, p0, n_probes, g, lr);
     return check_launch("update (8-bit directions)");
 }
 
+// Each pass is one launch; the grid's last block also takes the ragged tail.
 zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t probe,
                          float sigma, hipStream_t s, int dirs)
 {
+    if (n == 0) return ZO_OK;
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     if (dirs == ZO_DIRS_Q8)
         return dtype == ZO_F32 ? launch_perturb_q8((float*)w, n, j0, key, probe, sigma, s)
                                : launch_perturb_q8((uint16_t*)w, n, j0, key, probe, sigma, s);
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("perturb", s);
-    if (n_full) {
-        if (dtype == ZO_F32)
-            perturb_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, probe, sigma);
-        else
-            perturb_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, probe, sigma);
-    }
-    if (n > n_full) {
-        const int blocks = (int)((n - n_full + kThreads - 1) / kThreads);
-        if (dtype == ZO_F32)
-            perturb_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, probe, sigma);
-        else
-            perturb_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, probe, sigma);
-    }
+    if (dtype == ZO_F32)
+        perturb_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, n, j0, key, probe, sigma);
+    else
+        perturb_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, probe, sigma);
     return check_launch("perturb");
 }
 
@@ -460,26 +446,17 @@ zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t se
 {
     if (n_probes == 0 || n_probes > kMaxProbes)
         return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
+    if (n == 0) return ZO_OK;
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     if (dirs == ZO_DIRS_Q8)
         return dtype == ZO_F32 ? launch_update_q8((float*)w, n, j0, key, p0, n_probes, g, lr, s)
                                : launch_update_q8((uint16_t*)w, n, j0, key, p0, n_probes, g, lr, s);
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("update", s);
-    if (n_full) {
-        if (dtype == ZO_F32)
-            update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, j0, key, p0, n_probes, g, lr);
-        else
-            update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, j0, key, p0, n_probes, g, lr);
-    }
-    if (n > n_full) {
-        const int blocks = (int)((n - n_full + kThreads - 1) / kThreads);
-        if (dtype == ZO_F32)
-            update_tail<float><<<blocks, kThreads, 0, s>>>((float*)w, n_full, n, j0, key, p0, n_probes, g, lr);
-        else
-            update_tail<uint16_t><<<blocks, kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, p0, n_probes, g,
-                                                               lr);
-    }
+    if (dtype == ZO_F32)
+        update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, n, j0, key, p0, n_probes, g, lr);
+    else
+        update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, p0, n_probes, g, lr);
     return check_launch("update");
 }
 
