@@ -58,7 +58,7 @@ struct GemmArgs {
     const float* W2;  // [C][N]
     uint64_t w2_dir;
     int C;
-    float* logit_part;  // [eval][n_tile][M][C]
+    float* logit_part;  // [eval][n_tile][C][M] (split mode: [branch][n_tile][(1 + ps) C][M])
     int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
     uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
 };
@@ -253,6 +253,14 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) mma_step(cur, 8 * kk);
+    // every MFMA result lands before the epilogue's branches (as in sgemm_kernel)
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) asm volatile("" : "+a"(acc[v][i][j]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
     // accumulator element r of a 32x32 tile: row 8 (r/4) + 4 lh + r%4, col lr
     if constexpr (EPI == EPI_LSQ) {
@@ -325,13 +333,14 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
             for (int row = tid; row < BM; row += kThreads) {
                 const int gm = m0 + row;
                 if (gm >= M) continue;
-                float* dst = a.logit_part + (((size_t)ev.out[g][v] * gridDim.x + blockIdx.x) * M + gm) * C;
+                // [eval][tile][class][row]
+                float* dst = a.logit_part + ((size_t)ev.out[g][v] * gridDim.x + blockIdx.x) * C * M + gm;
                 for (int c = 0; c < C; ++c) {
                     const float* w2 = W2s + (v * C + c) * BN;
                     float p = 0.f;
 #pragma unroll 8
                     for (int n = 0; n < BN; ++n) p = fmaf(Hs[row * SH + n], w2[n], p);
-                    dst[c] = p;
+                    dst[(size_t)c * M] = p;
                 }
             }
             __syncthreads();
@@ -353,8 +362,8 @@ __global__ __launch_bounds__(kThreads) void lsq_reduce(const double* __restrict_
     if (threadIdx.x == 0) loss[e] = (((ws[0] + ws[1]) + ws[2]) + ws[3]) / (2.0 * (double)M);
 }
 
-// Cross-entropy of each row from the logit partials.  Block (chunk, e)
-// covers rows 64 chunk .. +63 of evaluation e; wave w sums the hidden tiles
+// Cross-entropy of each row from the logit partials ([eval][tile][class][row]).
+// Block (chunk, e) covers rows 64 chunk .. +63 of evaluation e; wave w sums the hidden tiles
 // t = w, w+4, ... in fp64, the four partial logits are added in fixed order,
 // and the block writes the fp64 sum of its rows' losses.
 __global__ __launch_bounds__(kThreads) void mlp_ce_rows(const float* __restrict__ part, int n_tiles, int M, int C,
@@ -370,10 +379,13 @@ __global__ __launch_bounds__(kThreads) void mlp_ce_rows(const float* __restrict_
     for (int c = 0; c < kMaxClasses; ++c) lg[c] = 0.0;
     if (m < M) {
         for (int t = wave; t < n_tiles; t += 4) {
-            const float* p = part + (((size_t)e * n_tiles + t) * M + m) * C;
+            const float* p = part + ((size_t)e * n_tiles + t) * C * M + m;
+            // unguarded loads (class index clamped) so they all issue at once
+            float v[kMaxClasses];
 #pragma unroll
-            for (int c = 0; c < kMaxClasses; ++c)
-                if (c < C) lg[c] += (double)p[c];
+            for (int c = 0; c < kMaxClasses; ++c) v[c] = p[(size_t)min(c, C - 1) * M];
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c) lg[c] += c < C ? (double)v[c] : 0.0;
         }
     }
 #pragma unroll
@@ -427,12 +439,17 @@ __global__ __launch_bounds__(kThreads) void split_ce_rows(const float* __restric
         for (int t = wave; t < n_tiles; t += 4) {
             const float* pb = part + ((size_t)branch * n_tiles + t) * Q * M + m;
             const float* pd = pb + (size_t)(1 + k) * C * M;
+            float vb[kMaxClasses], vd[kMaxClasses];
 #pragma unroll
-            for (int c = 0; c < kMaxClasses; ++c)
-                if (c < C) {
-                    lb[c] += (double)pb[(size_t)c * M];
-                    ld[c] += (double)pd[(size_t)c * M];
-                }
+            for (int c = 0; c < kMaxClasses; ++c) {
+                vb[c] = pb[(size_t)min(c, C - 1) * M];
+                vd[c] = pd[(size_t)min(c, C - 1) * M];
+            }
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c) {
+                lb[c] += c < C ? (double)vb[c] : 0.0;
+                ld[c] += c < C ? (double)vd[c] : 0.0;
+            }
         }
     }
 #pragma unroll
@@ -575,7 +592,7 @@ struct SplitArgs {
     const float* W2;    // [C][N]
     uint64_t w2_dir;
     int C;
-    float* logit_part;  // [eval][n_tile][M][C]
+    float* logit_part;  // [eval][n_tile][C][M] (split mode: [branch][n_tile][(1 + ps) C][M])
     int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
     uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
 };
@@ -758,6 +775,17 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
     }
     mma_step(cur, 0);
     mma_step(cur, 1);
+    // The epilogue can reach its first accumulator read through a branch that
+    // skips a whole wave's share of the W2 tile loads, and the compiler's
+    // wait-state count for the last MFMAs' results has been seen to miss that
+    // path (a stale last accumulator register in the waves that skip).  The
+    // empty statements name every accumulator, so they follow the last MFMA of
+    // each block; the wait states after them let every result land first.
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
     // accumulator element r of a 32x32 block: row 8 (r/4) + 4 lh + r%4, col lr
     if constexpr (MODE == SG_BASE_STORE) {
@@ -866,14 +894,18 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
     } else {
         // GELU(H tile) -> LDS, then partial logits over this tile's BN hidden
         // units against the (perturbed) W2 columns n0 .. n0+BN.  Columns past
-        // N hold GELU(0) = 0 and meet zero W2 weights.
+        // N hold GELU(0) = 0 and meet zero W2 weights.  Classes are split
+        // between the NT / BM thread groups of a row, QT each: group grp takes
+        // classes grp QT .. grp QT + QT - 1, whose (perturbed) W2 rows sit in
+        // LDS, zero past C, so the dot-product loop carries no per-class guards.
+        static_assert(QT > 0, "classes per thread group");
         constexpr int SH = BN + 4;  // 16-byte rows; float4 row reads by consecutive rows are bank-even
-        constexpr int GROUPS = NT / BM, CPG = (kMaxClasses + GROUPS - 1) / GROUPS;
-        static_assert(GROUPS * BM == NT, "one thread per (row, class group)");
+        constexpr int GROUPS = NT / BM;
+        static_assert(GROUPS * BM == NT, "whole thread groups per row");
+        constexpr int QR = GROUPS * QT;                 // W2 rows in LDS per sign
         float* Hs = reinterpret_cast<float*>(lds_bf);    // BM x SH
-        float* W2s = Hs + BM * SH;                      // NV x C x BN
+        float* W2s = Hs + BM * SH;                      // NV x QR x BN
         const int C = a.C;
-        const int cpg = (C + GROUPS - 1) / GROUPS;      // classes per thread group, balanced
         const bool pert = MODE == SG_PROBE_MLP && ev.perturbed != 0;
         float sig[NV];
 #pragma unroll
@@ -895,24 +927,25 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
                     }
                 }
         __syncthreads();  // every wave is done with the stage buffers
-        for (int q = tid; q < C * (BN / 4); q += NT) {
+        for (int q = tid; q < QR * (BN / 4); q += NT) {
             const int c = q / (BN / 4), n4 = 4 * (q % (BN / 4));
             const int gn = n0 + n4;
             float4 w = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-            if (gn < N) {
+            if (c < C && gn < N) {
                 const size_t idx = (size_t)c * N + gn;
                 w = *reinterpret_cast<const float4*>(a.W2 + idx);
                 if (pert) z = gauss4(key, probe, (a.w2_dir + idx) >> 2);
             }
 #pragma unroll
             for (int v = 0; v < NV; ++v)
-                *reinterpret_cast<float4*>(W2s + (v * C + c) * BN + n4) =
+                *reinterpret_cast<float4*>(W2s + (v * QR + c) * BN + n4) =
                     float4{fmaf(sig[v], z.x, w.x), fmaf(sig[v], z.y, w.y), fmaf(sig[v], z.z, w.z),
                            fmaf(sig[v], z.w, w.w)};
         }
-        const int row = tid % BM, grp = tid / BM;
+        const int row = tid % BM;
+        const int grp = __builtin_amdgcn_readfirstlane(tid / BM);  // wave-uniform
         const int gm = m0 + row;
-        const int c0 = grp * cpg, c1 = min(C, c0 + cpg);
+        const int qlim = C - grp * QT;  // this group's classes: qq < qlim
 #pragma unroll 1
         for (int v = 0; v < NV; ++v) {
 #pragma unroll
@@ -927,29 +960,29 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
                         Hs[lrow * SH + lcol] = gelu_erf(h);
                     }
             __syncthreads();
-            float p[CPG];
+            float p[QT];
 #pragma unroll
-            for (int cc = 0; cc < CPG; ++cc) p[cc] = 0.f;
+            for (int qq = 0; qq < QT; ++qq) p[qq] = 0.f;
             const float* hrow = Hs + row * SH;
-            const float* w2v = W2s + v * C * BN;
+            const float* wq = W2s + (v * QR + grp * QT) * BN;
+#pragma unroll 2
             for (int n = 0; n < BN; n += 4) {
                 const float4 h4 = *reinterpret_cast<const float4*>(hrow + n);
 #pragma unroll
-                for (int cc = 0; cc < CPG; ++cc) {
-                    if (c0 + cc < c1) {
-                        const float4 w4 = *reinterpret_cast<const float4*>(w2v + (c0 + cc) * BN + n);
-                        float t = p[cc];
-                        t = fmaf(h4.x, w4.x, t); t = fmaf(h4.y, w4.y, t);
-                        t = fmaf(h4.z, w4.z, t); t = fmaf(h4.w, w4.w, t);
-                        p[cc] = t;
-                    }
+                for (int qq = 0; qq < QT; ++qq) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(wq + qq * BN + n);
+                    float t = p[qq];
+                    t = fmaf(h4.x, w4.x, t); t = fmaf(h4.y, w4.y, t);
+                    t = fmaf(h4.z, w4.z, t); t = fmaf(h4.w, w4.w, t);
+                    p[qq] = t;
                 }
             }
             if (gm < M) {
-                float* dst = a.logit_part + (((size_t)ev.out[g][v] * gridDim.x + tn) * M + gm) * C;
+                // [eval][tile][class][row]: a wave's stores (and the reduction's loads) coalesce
+                float* dst = a.logit_part + (((size_t)ev.out[g][v] * gridDim.x + tn) * C + grp * QT) * M + gm;
 #pragma unroll
-                for (int cc = 0; cc < CPG; ++cc)
-                    if (c0 + cc < c1) dst[c0 + cc] = p[cc];
+                for (int qq = 0; qq < QT; ++qq)
+                    if (qq < qlim) dst[(size_t)qq * M] = p[qq];
             }
             __syncthreads();  // Hs is rewritten for the next sign
         }
@@ -1022,7 +1055,7 @@ zo_status launch_sgemm(const SplitArgs& a, const EvalList& ev, int groups, hipSt
     constexpr size_t stages = (size_t)2 * 3 * (BM + BN) * 32 * sizeof(bf16_t);
     constexpr size_t epi = MODE == SG_BASE_STORE || MODE == SG_PROBE_SPLIT
                                ? 0
-                               : (size_t)(BM * (BN + 4) + NV * kMaxClasses * BN) * sizeof(float);
+                               : (size_t)(BM * (BN + 4) + NV * (NT / BM) * QT * BN) * sizeof(float);
     constexpr size_t lds_fixed = stages > epi ? stages : epi;
     static_assert(lds_fixed <= kLdsMax, "LDS budget");
     size_t lds = lds_fixed;
@@ -1154,14 +1187,25 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
                 (const float*)b.x, n4, planes, (size_t)M * K);
         }
         if ((st = check_launch("X split"))) return st;
-        if (n == 0) {
-            st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1>(a, ev, 1, s, "gemm_f32_base");
+        // classes per thread group of the logit epilogue, rounded up to an instantiated width
+        const int half = ((int)d.classes + 1) / 2;  // two groups per row in the 256 x 128 tiles
+        if (n == 0) {  // four thread groups per row in the 64 x 64 tiles
+            const int quarter = ((int)d.classes + 3) / 4;
+            st = quarter <= 1   ? launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1, 1>(a, ev, 1, s, "gemm_f32_base")
+                 : quarter <= 3 ? launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1, 3>(a, ev, 1, s, "gemm_f32_base")
+                                : launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_MLP, 1, 4>(a, ev, 1, s, "gemm_f32_base");
             n_tiles = cdiv(N, SB_BN);
         } else {
             st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_STORE, 1>(a, ev, 1, s, "gemm_f32_base");
             if (st) return st;
-            st = nv == 2 ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 2>(a, ev, ev.n_groups, s, "gemm_f32")
-                         : launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 1>(a, ev, ev.n_groups, s, "gemm_f32");
+            if (nv == 2)
+                st = half <= 2   ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 2, 2>(a, ev, ev.n_groups, s, "gemm_f32")
+                     : half <= 5 ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 2, 5>(a, ev, ev.n_groups, s, "gemm_f32")
+                                 : launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 2, 8>(a, ev, ev.n_groups, s, "gemm_f32");
+            else
+                st = half <= 2   ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 1, 2>(a, ev, ev.n_groups, s, "gemm_f32")
+                     : half <= 5 ? launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 1, 5>(a, ev, ev.n_groups, s, "gemm_f32")
+                                 : launch_sgemm<SP_BM, SP_BN, SP_NT, SG_PROBE_MLP, 1, 8>(a, ev, ev.n_groups, s, "gemm_f32");
             n_tiles = cdiv(N, SP_BN);
         }
     } else {
