@@ -32,6 +32,8 @@ What is computed, and where the pages state it:
   diagonal preconditioner (``spsa_step(precond=True)``).
 * Split perturbation with activation reuse (FedSPZO summary, section 2
   "방법론"): ``fedspzo_step`` on the MLP.
+* Activation perturbation with per-token rewards (Dust review page):
+  ``dust_step`` on the MLP.
 
 Readings where the pages are silent are listed in the repository's design
 notes; the ones that fix arithmetic are repeated at each function.
@@ -89,6 +91,7 @@ def lib():
         L.oracle_round_bf16_array.argtypes = [P, U64]
         L.oracle_round_f32_array.argtypes = [P, U64]
         L.oracle_box_muller_f64_array.argtypes = [P, U64, P]
+        L.oracle_gauss_stream.argtypes = [U64, U32, U32, U64, U64, P]
         L.oracle_q8_values.argtypes = [U64, U32, U64, U64, P, P]
         L.oracle_q8_values_at.argtypes = [U64, U32, P, U64, P, P]
         for name in ("oracle_q8_perturb_f32", "oracle_q8_perturb_bf16"):
@@ -173,6 +176,14 @@ def directions(kind: str, seed: int, probe: int, j0: int, n: int) -> np.ndarray:
         lib().oracle_q8_values(seed, probe, j0, n, _ptr(z), _ptr(_q8()))
     else:
         raise ValueError(kind)
+    return z
+
+
+def gauss_stream(seed: int, probe: int, stream: int, j0: int, n: int) -> np.ndarray:
+    """Gaussian values of counter stream `stream` (stream 0 = the weight
+    directions of ``gauss``)."""
+    z = np.zeros(n, np.float32)
+    lib().oracle_gauss_stream(seed, probe, stream, j0, n, _ptr(z))
     return z
 
 
@@ -483,6 +494,82 @@ def fedspzo_step(arena: Arena, batch: dict, seed: int, p1: int, ps: int, eps: fl
         arena.update_range(o1, n1, seed, -lr * g1 / p1)
         arena.update_range(o2, n2, seed, np.concatenate([np.zeros(p1), -lr * g2 / p2]))
     return losses, g1, g2
+
+
+DUST_HIDDEN_STREAM, DUST_LOGIT_STREAM = 2, 3
+
+
+def ce_rows(logits: np.ndarray, labels) -> np.ndarray:
+    """Per-row cross-entropy."""
+    return logsumexp_rows(logits) - logits[np.arange(logits.shape[0]), labels]
+
+
+def dust_noise(seed: int, draw: int, stream: int, rows: int, width: int) -> np.ndarray:
+    """Noise a[t][w] of one draw: element t * width + w of the stream."""
+    return gauss_stream(seed, draw, stream, 0, rows * width).astype(np.float64).reshape(rows, width)
+
+
+def dust_step(arena: Arena, batch: dict, seed: int, k1: int, sigma1: float, k2: int, sigma2: float, lr: float):
+    """One Dust step on the MLP (Dust review page, "Dust: 역전파 없이
+    트랜스포머를 사전학습하다", sections "Dust의 해법: 가상 개체군" and "신용
+    할당(credit assignment): 보상에서 기울기까지", plus "간섭(interference)
+    줄이기" for the separate forward per layer type and the head perturbed on
+    cached logits); updates ``arena`` in place.
+
+    Every sample t of the batch is a token.  The clean forward is cached:
+    Y = X W1^T, A = GELU(Y), Z = A W2^T.
+    Hidden layer (output y_t of W1), k1 draws with noise a ~ N(0, I) from
+    stream 2 (draw i, element t * hidden + h):
+      l[i][t] = CE(GELU(Y_t + sigma1 a_t^(i)) W2^T, label_t)   (per token)
+      c = lbar_t - l[i][t], lbar_t the mean over the draws; the tokens are
+      independent, so the reward is r = c (no later tokens to credit);
+      ghat_t = -(1 / (k1 sigma1)) sum_i r a_t^(i),  G_W1 = sum_t ghat_t x_t^T.
+    Head (output of W2, the logits), k2 draws on the cached logits with noise
+    b ~ N(0, I) from stream 3 (element t * classes + c):
+      l2[i][t] = CE(Z_t + sigma2 b_t^(i)), the same rewards,
+      ghat2_t = -(1 / (k2 sigma2)) sum_i r2 b_t^(i),  G_W2 = sum_t ghat2_t A_t^T.
+    Then W1 <- D(W1 - lr G_W1), W2 <- D(W2 - lr G_W2) (sigma and lr at fp32
+    precision; both estimates from the same W), nothing if any loss is not
+    finite.  The sums over tokens estimate the gradient of the summed token
+    losses.  Returns (l [k1][M], l2 [k2][M], clean per-token losses [M],
+    ghat [M][hidden], ghat2 [M][classes]).
+    """
+    assert arena.desc["kind"] == "mlp"
+    lay = {name: (off, shape) for name, off, shape in param_layout(arena.desc)[0]}
+    (o1, s1), (o2, s2) = lay["W1"], lay["W2"]
+    n1, n2 = int(np.prod(s1)), int(np.prod(s2))
+    vals = arena.values()
+    W1 = vals[o1:o1 + n1].reshape(s1)
+    W2 = vals[o2:o2 + n2].reshape(s2)
+    X = np.asarray(batch["X"], np.float64)
+    labels = batch["labels"]
+    M, H, C = X.shape[0], s1[0], s2[0]
+    sg1, sg2 = float(np.float32(sigma1)), float(np.float32(sigma2))
+    Y = X @ W1.T
+    A = gelu_erf(Y)
+    Z = A @ W2.T
+    l0 = ce_rows(Z, labels)
+    # hidden layer: k1 draws, each a forward of the layers after W1
+    noise1 = [dust_noise(seed, i, DUST_HIDDEN_STREAM, M, H) for i in range(k1)]
+    l1 = np.stack([ce_rows(gelu_erf(Y + sg1 * a) @ W2.T, labels) for a in noise1])
+    r1 = l1.mean(axis=0)[None, :] - l1
+    ghat = -sum(r1[i][:, None] * noise1[i] for i in range(k1)) / (k1 * sg1)
+    G1 = ghat.T @ X
+    # head: k2 draws on the cached logits
+    noise2 = [dust_noise(seed, i, DUST_LOGIT_STREAM, M, C) for i in range(k2)]
+    l2 = np.stack([ce_rows(Z + sg2 * b, labels) for b in noise2])
+    r2 = l2.mean(axis=0)[None, :] - l2
+    ghat2 = -sum(r2[i][:, None] * noise2[i] for i in range(k2)) / (k2 * sg2)
+    G2 = ghat2.T @ A
+    if np.all(np.isfinite(l1)) and np.all(np.isfinite(l2)):
+        lr32 = float(np.float32(lr))
+        new = arena.data.copy()
+        if arena.dtype != "f32":
+            raise ValueError("the MLP arena is fp32")
+        new[o1:o1 + n1] = (W1 - lr32 * G1).ravel().astype(np.float32)
+        new[o2:o2 + n2] = (W2 - lr32 * G2).ravel().astype(np.float32)
+        arena.data[:] = new
+    return l1, l2, l0, ghat, ghat2
 
 
 def model_loss(arena: Arena, batch: dict, round_bf16: bool = True) -> float:

@@ -67,13 +67,19 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
     out[0] = c[0]; out[1] = c[1]; out[2] = c[2]; out[3] = c[3];
 }
 
-/* The four words that cover element j of direction `probe` under `seed`. */
-static void direction_block(uint64_t seed, uint32_t probe, uint64_t j, uint32_t w[4])
+/* The four words that cover element j of stream `stream` of direction
+   `probe` under `seed` (stream 0: weight directions). */
+static void stream_block(uint64_t seed, uint32_t probe, uint32_t stream, uint64_t j, uint32_t w[4])
 {
     uint64_t q = j >> 2;
-    uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), probe, 0u};
+    uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), probe, stream};
     uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     oracle_philox4x32_10(ctr, key, w);
+}
+
+static void direction_block(uint64_t seed, uint32_t probe, uint64_t j, uint32_t w[4])
+{
+    stream_block(seed, probe, 0u, j, w);
 }
 
 /* Raw words for elements j0 .. j0+n-1 (word j mod 4 of block j/4). */
@@ -129,6 +135,22 @@ static float gauss_value(uint64_t seed, uint32_t probe, uint64_t j)
     double zo;
     double ze = oracle_box_muller_f64(w[2 * pair], w[2 * pair + 1], &zo);
     return (float)((j & 1u) ? zo : ze);
+}
+
+/* Gaussian values of another counter stream (same Box-Muller map): the
+   activation noise of the Dust estimator uses streams 2 (hidden layer) and
+   3 (logits), element j = row * width + column. */
+void oracle_gauss_stream(uint64_t seed, uint32_t probe, uint32_t stream, uint64_t j0, uint64_t n, float* z)
+{
+    for (uint64_t t = 0; t < n; ++t) {
+        uint64_t j = j0 + t;
+        uint32_t w[4];
+        stream_block(seed, probe, stream, j, w);
+        unsigned pair = (unsigned)(j & 3u) >> 1;
+        double zo;
+        double ze = oracle_box_muller_f64(w[2 * pair], w[2 * pair + 1], &zo);
+        z[t] = (float)((j & 1u) ? zo : ze);
+    }
 }
 
 static float dir_value(uint64_t seed, uint32_t probe, uint64_t j, const float* q8)
