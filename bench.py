@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--split", default=None, metavar="P1,PS",
                    help="MLP: split-perturbation (FedSPZO) steps with P1 theta_1 directions and PS theta_2 "
                         "directions per branch instead of SPSA steps")
+    p.add_argument("--dust", default=None, metavar="K1,K2",
+                   help="MLP: Dust steps (activation noise) with K1 hidden-layer and K2 head draws")
     p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
                    help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
     return p.parse_args()
@@ -76,7 +78,7 @@ def build_mlp(torch, zo, inputs):
     info = {
         "workload": "2-layer MLP classifier fp32 1024->4096(GELU)->10, batch 256, cross-entropy; "
                     "N=16 probes, eps=1e-3, lr=1e-3; perturbed-tile (fused) mode",
-        "probes": 16, "eps": 1e-3, "lr": 1e-3, "mode": "fused", "batch": B,
+        "probes": 16, "eps": 1e-3, "lr": 1e-3, "mode": "fused", "batch": B, "hidden": H,
         "params": int(total),
         # algorithmic flops of one evaluation: X W1^T and H W2^T
         "flops_per_eval": 2.0 * B * D * H + 2.0 * B * H * C,
@@ -259,20 +261,34 @@ def main():
     N = info["probes"]
     pc = 1 if args.precond else 0
     split = None
+    dust = None
+    if args.dust:
+        if args.workload != "mlp" or args.precond or args.split:
+            print("bench.py: --dust applies to the MLP workload alone", file=sys.stderr)
+            sys.exit(2)
+        dust = tuple(int(x) for x in args.dust.split(","))
+        info["kernel"] = "dust"
     if args.split:
         if args.workload != "mlp" or args.precond:
             print("bench.py: --split applies to the MLP workload, without --precond", file=sys.stderr)
             sys.exit(2)
         split = tuple(int(x) for x in args.split.split(","))
-    evals_per_step = 4 * split[0] * split[1] if split else 2 * N + pc
-    probe_evals_per_step = evals_per_step if split else 2 * N
+    if dust:
+        evals_per_step = 1 + dust[0] + dust[1]          # clean + hidden draws + head draws
+        probe_evals_per_step = dust[0] + dust[1]        # the population members
+    else:
+        evals_per_step = 4 * split[0] * split[1] if split else 2 * N + pc
+        probe_evals_per_step = evals_per_step if split else 2 * N
+    dust_losses = torch.zeros(evals_per_step * info["batch"] if dust else 1, dtype=torch.float64, device="cuda")
     losses = torch.zeros(evals_per_step, dtype=torch.float64, device="cuda")
     g = torch.zeros(max(N, split[0] if split else 0), dtype=torch.float64, device="cuda")
     g2 = torch.zeros(2 * split[0] * split[1] if split else 1, dtype=torch.float64, device="cuda")
     mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
 
     def step(seed):
-        if split:
+        if dust:
+            model.step_dust(batch, seed, dust[0], dust[1], 0.05, 0.05, info["lr"], dust_losses)
+        elif split:
             model.step_split(batch, seed, split[0], split[1], info["eps"], info["lr"], losses, g, g2)
         else:
             model.step(batch, seed, N, info["eps"], info["lr"], mode, losses, g, precond=pc,
@@ -315,7 +331,15 @@ def main():
     zo.timing_enable(False)
     ms_step_instr = i0.elapsed_time(i1) / args.steps
     extra = {}
-    if info["kernel"] == "gemm_bf16":
+    bound, peak, unit = "mfma", info["peak_tflops"], "TFLOP/s"
+    if dust:
+        # hidden-layer draws and output errors: each regenerates k1 x M x hidden
+        # Gaussians (c_z VALU instructions each) -- priced against the VALU peak
+        gauss = 2.0 * dust[0] * info["batch"] * info["hidden"] * args.steps / k_n
+        flops_per_launch = gauss * C_Z / 1e0
+        bound, peak, unit = "alu", VALU_PEAK_LANE_OPS / 1e12, "T lane-op/s"
+        extra = {"gaussians_per_s": round(gauss / k_avg_s, 1), "c_z": C_Z}
+    elif info["kernel"] == "gemm_bf16":
         # layer GEMMs of all evaluations: algorithmic flops / summed launch time
         flops_per_launch = evals_per_step * info["gemm_flops_per_eval"] * args.steps / k_n
     elif "split_bf16" in info:
@@ -336,7 +360,7 @@ def main():
         flops_per_launch = 2 * N * info["flops_per_eval"]
     achieved = flops_per_launch / k_avg_s / 1e12
     kernels = {}
-    for fam in ("gemm_f32", "gemm_f32_base", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
+    for fam in ("gemm_f32", "gemm_f32_base", "dust", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
                 "perturb"):
         ms, n = zo.timing_query(fam)
         if n:
@@ -362,22 +386,27 @@ def main():
                       if pc else {}),
                    **({"directions": "8-bit packed (256-level quantised Gaussian)"} if args.dirs == "q8" else {}),
                    **({"variant": "split perturbation (FedSPZO), activation reuse", "p1": split[0], "ps": split[1],
-                       "p2": 2 * split[0] * split[1], "evals_per_step": evals_per_step} if split else {})},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": info["peak_tflops"],
-                     "unit": "TFLOP/s", "frac": round(achieved / info["peak_tflops"], 4),
-                     "traffic": None if split else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
+                       "p2": 2 * split[0] * split[1], "evals_per_step": evals_per_step} if split else {}),
+                   **({"variant": "Dust (activation noise, per-token rewards)", "k1": dust[0], "k2": dust[1],
+                       "sigma": 0.05, "evals_per_step": evals_per_step, "unit_note": "value counts draws (k1 + k2)"}
+                      if dust else {})},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None if (split or dust) else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
                      "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), "
                                  f"{evals_per_step if split else 2 * N} evaluations per step"
                                  if "split_bf16" in info else
                                  f"{info['kernel']} fused perturbed-tile GEMM, {2 * N} evaluations per launch")
-                                if info["kernel"] == "gemm_f32" else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
+                                if info["kernel"] == "gemm_f32" else
+                                "dust hidden-layer draws and output errors (Gaussian generation, GELU, logits)"
+                                if dust else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
                      "avg_launch_us": round(k_avg_s * 1e6, 2), **extra},
         "kernels": kernels,
         "last_losses_mean": float(final.mean()),
     }
     if not args.no_passes:
         line["perturb_update"] = measure_passes(torch, zo)
-    if not args.no_cpu_baseline and "oracle_desc" in info and not split:
+    if not args.no_cpu_baseline and "oracle_desc" in info and not split and not dust:
         line["cpu_baseline"] = cpu_baseline(info)
     print(json.dumps(line), flush=True)
 

@@ -156,6 +156,16 @@ typedef struct {
     float lr;      /* eta */
 } zo_split_cfg;
 
+/* Dust step configuration (zo_step_dust). */
+typedef struct {
+    uint64_t seed;  /* this step's noise seed */
+    uint32_t k1;    /* hidden-layer draws, 1..128 */
+    uint32_t k2;    /* head draws on the cached logits, 1..65536 */
+    float sigma1;   /* hidden-layer noise scale */
+    float sigma2;   /* logit noise scale */
+    float lr;       /* eta */
+} zo_dust_cfg;
+
 typedef struct zo_model zo_model;
 
 /* ---------------------------------------------------------------- layout */
@@ -250,6 +260,26 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
  */
 zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg, double* losses_dev,
                         double* g1_dev, double* g2_dev, zo_stream s);
+
+/*
+ * One Dust step (activation perturbation with per-token rewards; Dust review
+ * page "Dust: 역전파 없이 트랜스포머를 사전학습하다", sections "Dust의 해법:
+ * 가상 개체군", "신용 할당(credit assignment): 보상에서 기울기까지" and
+ * "간섭(interference) 줄이기"), for the MLP with d_in % 32 == 0 and
+ * batch % 32 == 0.  Every sample t is a token.  The clean forward is cached
+ * (Y = X W1^T, A = GELU(Y), Z = A W2^T).  Hidden layer: k1 draws of noise
+ * a ~ N(0, I) on Y (Philox counter stream 2, direction index = draw, element
+ * t * hidden + h), per-token losses l_i[t]; reward r = lbar[t] - l_i[t];
+ * output error ghat_t = -(1/(k1 sigma1)) sum_i r a_i[t]; W1 <- W1 - lr
+ * sum_t ghat_t x_t^T.  Head: k2 draws of noise b on the cached logits (stream 3,
+ * element t * classes + c), the same rewards, ghat2_t; W2 <- W2 - lr sum_t
+ * ghat2_t A_t^T.  Both estimates come from the same weights; a non-finite loss
+ * skips both updates.  losses_dev (device fp64, (1 + k1 + k2) * batch): the
+ * clean per-token losses, then the k1 hidden draws', then the k2 head draws',
+ * each [draw][token].  The step uses the model's workspace, which
+ * zo_workspace_bytes sizes for k1 up to 128 at the model's batch.
+ */
+zo_status zo_step_dust(zo_model* m, const zo_batch* b, const zo_dust_cfg* cfg, double* losses_dev, zo_stream s);
 
 /*
  * Seed replay of one recorded step (position paper summary, P5, and FedSPZO,

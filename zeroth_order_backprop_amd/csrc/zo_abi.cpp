@@ -419,6 +419,16 @@ zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg,
                           g1_dev, g2_dev, (hipStream_t)s);
 }
 
+zo_status zo_step_dust(zo_model* m, const zo_batch* b, const zo_dust_cfg* cfg, double* losses_dev, zo_stream s)
+{
+    if (!m || !cfg || !losses_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (zo_status st = validate_batch(m, b)) return st;
+    if (!(cfg->sigma1 > 0.0f) || !(cfg->sigma2 > 0.0f)) return fail(ZO_ERR_INVALID, "sigma1, sigma2 must be positive");
+    if (zo_status st = mlp_dust_check(m->desc, *b, (int)cfg->k1, (int)cfg->k2)) return st;
+    return mlp_dust_step(view_of(m), *b, cfg->seed, (int)cfg->k1, (int)cfg->k2, cfg->sigma1, cfg->sigma2, cfg->lr,
+                         losses_dev, (hipStream_t)s);
+}
+
 zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_dev, zo_stream s)
 {
     if (!m || !cfg || !g_dev) return fail(ZO_ERR_INVALID, "null argument");

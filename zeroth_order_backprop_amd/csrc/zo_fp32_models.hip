@@ -61,6 +61,8 @@ struct GemmArgs {
     float* logit_part;  // [eval][n_tile][C][M] (split mode: [branch][n_tile][(1 + ps) C][M])
     int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
     uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
+    float lr;           // SG_UPDATE: H[m][n] -= lr * acc
+    const int* skip;    // SG_UPDATE: nonzero -> write nothing
 };
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void split_planes_kernel(const float* __r
     }
 }
 
-enum { SG_BASE_STORE = 0, SG_BASE_MLP = 1, SG_PROBE_MLP = 2, SG_PROBE_SPLIT = 3 };
+enum { SG_BASE_STORE = 0, SG_BASE_MLP = 1, SG_PROBE_MLP = 2, SG_PROBE_SPLIT = 3, SG_UPDATE = 4 };
 constexpr int kSplitMaxPs = 4;  // theta_2 directions per branch in one split-perturbation launch
 
 struct SplitArgs {
@@ -595,6 +597,8 @@ struct SplitArgs {
     float* logit_part;  // [eval][n_tile][C][M] (split mode: [branch][n_tile][(1 + ps) C][M])
     int ps;             // SG_PROBE_SPLIT: theta_2 directions per branch
     uint32_t z2_probe0; // SG_PROBE_SPLIT: direction index of theta_2 direction 0
+    float lr;           // SG_UPDATE: H[m][n] -= lr * acc
+    const int* skip;    // SG_UPDATE: nonzero -> write nothing
 };
 
 // vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
@@ -798,6 +802,22 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
                     const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
                     const int col = n0 + wn * WN + j * 32 + lr;
                     if (row < M && col < N) a.H[(size_t)row * N + col] = acc[i][j][r];
+                }
+    } else if constexpr (MODE == SG_UPDATE) {
+        // H[m][n] <- fp32(H[m][n] - lr acc): a weight update from its gradient estimate
+        if (*a.skip) return;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    const int col = n0 + wn * WN + j * 32 + lr;
+                    if (row < M && col < N) {
+                        float* w = a.H + (size_t)row * N + col;
+                        *w = fmaf(-a.lr, acc[i][j][r], *w);
+                    }
                 }
     } else if constexpr (MODE == SG_PROBE_SPLIT) {
         // Columns q = slot * C + c of the (1 + ps) C partial logits (slot 0:
@@ -1053,7 +1073,7 @@ zo_status launch_sgemm(const SplitArgs& a, const EvalList& ev, int groups, hipSt
 {
     constexpr size_t kLdsMax = 160 * 1024;
     constexpr size_t stages = (size_t)2 * 3 * (BM + BN) * 32 * sizeof(bf16_t);
-    constexpr size_t epi = MODE == SG_BASE_STORE || MODE == SG_PROBE_SPLIT
+    constexpr size_t epi = MODE == SG_BASE_STORE || MODE == SG_PROBE_SPLIT || MODE == SG_UPDATE
                                ? 0
                                : (size_t)(BM * (BN + 4) + NV * (NT / BM) * QT * BN) * sizeof(float);
     constexpr size_t lds_fixed = stages > epi ? stages : epi;
@@ -1078,6 +1098,323 @@ zo_status launch_sgemm(const SplitArgs& a, const EvalList& ev, int groups, hipSt
     KernelTimer timer(fam, s);
     kern<<<grid, NT, lds, s>>>(a, ev);
     return check_launch("split-bf16 MLP GEMM");
+}
+
+// ================================================================== Dust
+// Activation-noise estimator on the MLP (per-token rewards, outer-product
+// weight estimates); the steps and their order are those of mlp_dust_step.
+
+// Hidden layer: block (tile tn of DH_BN hidden units, rows m0 .., draw d).
+// Draw 0 is the clean forward; draw d >= 1 adds sigma a^(d-1) (noise stream 2,
+// element row * N + h) to Y = X W1^T before the GELU.  The tile's partial
+// logits against W2 go to part[d][tn][class][row], as in the MLP epilogue:
+// QT classes per thread group, W2 rows in LDS zero past C.
+constexpr int DH_BM = 64, DH_BN = 128, DH_NT = 256;
+template <int QT>
+__global__ __launch_bounds__(DH_NT) void dust_hidden_kernel(const float* __restrict__ Y, const float* __restrict__ W2,
+                                                            int M, int N, int C, Key key, float sigma,
+                                                            float* __restrict__ part)
+{
+    constexpr int BM = DH_BM, BN = DH_BN, NT = DH_NT, SH = BN + 4;
+    constexpr int GROUPS = NT / BM, QR = GROUPS * QT;
+    __shared__ __align__(16) float Hs[BM * SH];
+    __shared__ __align__(16) float W2s[QR * BN];
+    const int tn = blockIdx.x, m0 = blockIdx.y * BM, d = blockIdx.z;
+    const int n0 = tn * BN, tid = threadIdx.x;
+    for (int q = tid; q < QR * (BN / 4); q += NT) {
+        const int c = q / (BN / 4), n4 = 4 * (q % (BN / 4));
+        const int gn = n0 + n4;
+        float4 w = {0.f, 0.f, 0.f, 0.f};
+        if (c < C && gn < N) w = *reinterpret_cast<const float4*>(W2 + (size_t)c * N + gn);
+        *reinterpret_cast<float4*>(W2s + c * BN + n4) = w;
+    }
+    const float sg = d == 0 ? 0.f : sigma;
+    for (int q = tid; q < BM * (BN / 4); q += NT) {
+        const int r = q / (BN / 4), n4 = 4 * (q % (BN / 4));
+        const int gm = m0 + r, gn = n0 + n4;
+        float4 h = {0.f, 0.f, 0.f, 0.f};
+        if (gm < M && gn < N) {
+            const size_t e = (size_t)gm * N + gn;
+            const float4 y = *reinterpret_cast<const float4*>(Y + e);
+            const float4 z = d > 0 ? gauss4s(key, (uint32_t)(d - 1), 2u, e >> 2) : float4{0.f, 0.f, 0.f, 0.f};
+            h = float4{gelu_erf(fmaf(sg, z.x, y.x)), gelu_erf(fmaf(sg, z.y, y.y)), gelu_erf(fmaf(sg, z.z, y.z)),
+                       gelu_erf(fmaf(sg, z.w, y.w))};
+        }
+        *reinterpret_cast<float4*>(Hs + r * SH + n4) = h;
+    }
+    __syncthreads();
+    const int row = tid % BM;
+    const int grp = __builtin_amdgcn_readfirstlane(tid / BM);
+    const int gm = m0 + row;
+    const int qlim = C - grp * QT;
+    float p[QT];
+#pragma unroll
+    for (int qq = 0; qq < QT; ++qq) p[qq] = 0.f;
+    const float* hrow = Hs + row * SH;
+    const float* wq = W2s + grp * QT * BN;
+#pragma unroll 2
+    for (int n = 0; n < BN; n += 4) {
+        const float4 h4 = *reinterpret_cast<const float4*>(hrow + n);
+#pragma unroll
+        for (int qq = 0; qq < QT; ++qq) {
+            const float4 w4 = *reinterpret_cast<const float4*>(wq + qq * BN + n);
+            float t = p[qq];
+            t = fmaf(h4.x, w4.x, t); t = fmaf(h4.y, w4.y, t);
+            t = fmaf(h4.z, w4.z, t); t = fmaf(h4.w, w4.w, t);
+            p[qq] = t;
+        }
+    }
+    if (gm < M) {
+        float* dst = part + (((size_t)d * gridDim.x + tn) * C + grp * QT) * M + gm;
+#pragma unroll
+        for (int qq = 0; qq < QT; ++qq)
+            if (qq < qlim) dst[(size_t)qq * M] = p[qq];
+    }
+}
+
+// Per-token cross-entropy of every draw from the partials (fixed-order fp64
+// tile sums as in mlp_ce_rows): loss[d][row]; draw 0's logits (the clean
+// ones) also go to Z[row][class].  Block (0, 0) clears the skip flag.
+__global__ __launch_bounds__(kThreads) void dust_rows_kernel(const float* __restrict__ part, int n_tiles, int M, int C,
+                                                              const int32_t* __restrict__ labels,
+                                                              double* __restrict__ loss, double* __restrict__ Z,
+                                                              int* __restrict__ skip)
+{
+    __shared__ double lg_w[4][64][kMaxClasses + 1];
+    const int e = blockIdx.y, chunk = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = chunk * 64 + lane;
+    if (e == 0 && chunk == 0 && threadIdx.x == 0) *skip = 0;
+    double lg[kMaxClasses];
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) lg[c] = 0.0;
+    if (m < M) {
+        for (int t = wave; t < n_tiles; t += 4) {
+            const float* p = part + ((size_t)e * n_tiles + t) * C * M + m;
+            float v[kMaxClasses];
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c) v[c] = p[(size_t)min(c, C - 1) * M];
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c) lg[c] += c < C ? (double)v[c] : 0.0;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) lg_w[wave][lane][c] = lg[c];
+    __syncthreads();
+    if (wave != 0 || m >= M) return;
+    const int y = labels[m];
+    double mx = -INFINITY, picked = 0.0;
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) {
+        lg[c] = ((lg_w[0][lane][c] + lg_w[1][lane][c]) + lg_w[2][lane][c]) + lg_w[3][lane][c];
+        if (c < C) mx = fmax(mx, lg[c]);
+    }
+    double se = 0.0;
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c)
+        if (c < C) {
+            se += exp(lg[c] - mx);
+            if (c == y) picked = lg[c];
+            if (e == 0) Z[(size_t)m * C + c] = lg[c];
+        }
+    loss[(size_t)e * M + m] = (mx + log(se)) - picked;
+}
+
+// The k2 head draws on the cached clean logits: thread per (draw i, token t),
+// loss2[i][t] = CE(Z_t + sigma2 b_i[t]), b from noise stream 3 (element
+// t * C + c).  A non-finite loss sets the skip flag.
+__device__ __forceinline__ void logit_draw(Key key, uint32_t i, int t, int C, float* b)
+{
+    const uint64_t j0 = (uint64_t)t * C;
+    const uint64_t q0 = j0 >> 2, q1 = (j0 + C - 1) >> 2;
+    for (uint64_t q = q0; q <= q1; ++q) {
+        const float4 z = gauss4s(key, i, 3u, q);
+        const float zz[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int64_t c = (int64_t)(4 * q + s) - (int64_t)j0;
+            if (c >= 0 && c < C) b[c] = zz[s];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void dust_head_loss_kernel(const double* __restrict__ Z,
+                                                                   const int32_t* __restrict__ labels, int M, int C,
+                                                                   int k2, float sigma2, Key key,
+                                                                   double* __restrict__ loss2, int* __restrict__ skip)
+{
+    const size_t n = (size_t)k2 * M;
+    for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (size_t)gridDim.x * kThreads) {
+        const int i = (int)(idx / M), t = (int)(idx % M);
+        float b[kMaxClasses];
+        logit_draw(key, (uint32_t)i, t, C, b);
+        const int y = labels[t];
+        double l[kMaxClasses], mx = -INFINITY, se = 0.0, picked = 0.0;
+        for (int c = 0; c < C; ++c) {
+            l[c] = Z[(size_t)t * C + c] + (double)sigma2 * (double)b[c];
+            mx = fmax(mx, l[c]);
+        }
+        for (int c = 0; c < C; ++c) {
+            se += exp(l[c] - mx);
+            if (c == y) picked = l[c];
+        }
+        const double v = (mx + log(se)) - picked;
+        loss2[(size_t)i * M + t] = v;
+        if (!isfinite(v)) atomicOr(skip, 1);
+    }
+}
+
+// Sum over the block's threads in a fixed order (LDS tree), result to all.
+__device__ __forceinline__ double block_sum(double v, double* red)
+{
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    const double r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// Block per token t.  Hidden layer: w[i][t] = (l_i - lbar) / (k1 sigma1), the
+// weight of draw i's noise in the token's output error (reward r = lbar - l_i,
+// ghat = -(1 / (k1 sigma1)) sum_i r a).  Head: ghat2[t][c] = -(1 / (k2 sigma2))
+// sum_i (l2bar - l2_i) b_i[c], the noise regenerated; draws split over the
+// threads, sums in a fixed order.
+__global__ __launch_bounds__(kThreads) void dust_reward_kernel(const double* __restrict__ loss,
+                                                                const double* __restrict__ loss2, int M, int C, int k1,
+                                                                int k2, float sigma1, float sigma2, Key key,
+                                                                float* __restrict__ w, float* __restrict__ ghat2,
+                                                                int* __restrict__ skip)
+{
+    __shared__ double red[kThreads];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    double s = 0.0;
+    bool bad = false;
+    for (int i = tid; i < k1; i += kThreads) {
+        const double v = loss[(size_t)(1 + i) * M + t];
+        s += v;
+        bad |= !isfinite(v);
+    }
+    const double lbar = block_sum(s, red) / k1;
+    const double s1 = (double)k1 * (double)sigma1;
+    for (int i = tid; i < k1; i += kThreads) w[(size_t)i * M + t] = (float)((loss[(size_t)(1 + i) * M + t] - lbar) / s1);
+    s = 0.0;
+    for (int i = tid; i < k2; i += kThreads) s += loss2[(size_t)i * M + t];
+    const double l2bar = block_sum(s, red) / k2;
+    double g[kMaxClasses];
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) g[c] = 0.0;
+    for (int i = tid; i < k2; i += kThreads) {
+        float b[kMaxClasses];
+        logit_draw(key, (uint32_t)i, t, C, b);
+        const double r = l2bar - loss2[(size_t)i * M + t];
+        for (int c = 0; c < C; ++c) g[c] += r * (double)b[c];
+    }
+    const double s2 = (double)k2 * (double)sigma2;
+    for (int c = 0; c < C; ++c) {
+        const double gc = block_sum(g[c], red);
+        if (tid == 0) ghat2[(size_t)t * C + c] = (float)(-gc / s2);
+    }
+    if (bad && tid == 0) atomicOr(skip, 1);
+}
+
+// The hidden layer's output errors G[t][h] = sum_i w[i][t] a_i[t][h] (noise
+// regenerated), written transposed as the three bf16 planes of the update
+// GEMM's A operand: planes[p][h][t], G^T = p0 + p1 + p2 exactly.  Block: 64
+// tokens x 64 hidden units, staged through LDS for the transpose.
+constexpr int DG_T = 64, DG_H = 64, DG_MAXK = 128;
+__global__ __launch_bounds__(kThreads) void dust_gy_kernel(const float* __restrict__ w, int M, int N, int k1, Key key,
+                                                            bf16_t* __restrict__ planes)
+{
+    __shared__ float wt[DG_MAXK][DG_T];
+    __shared__ float Gs[DG_H][DG_T + 4];
+    const int t0 = blockIdx.y * DG_T, h0 = blockIdx.x * DG_H, tid = threadIdx.x;
+    for (int q = tid; q < k1 * DG_T; q += kThreads) {
+        const int i = q / DG_T, tt = q % DG_T;
+        wt[i][tt] = t0 + tt < M ? w[(size_t)i * M + t0 + tt] : 0.f;
+    }
+    __syncthreads();
+    for (int q = tid; q < DG_T * (DG_H / 4); q += kThreads) {
+        const int tt = q / (DG_H / 4), hq = 4 * (q % (DG_H / 4));
+        const int t = t0 + tt, h = h0 + hq;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (t < M && h < N) {
+            const uint64_t qd = ((uint64_t)t * N + h) >> 2;
+            for (int i = 0; i < k1; ++i) {
+                const float c = wt[i][tt];
+                const float4 a = gauss4s(key, (uint32_t)i, 2u, qd);
+                acc.x = fmaf(c, a.x, acc.x); acc.y = fmaf(c, a.y, acc.y);
+                acc.z = fmaf(c, a.z, acc.z); acc.w = fmaf(c, a.w, acc.w);
+            }
+        }
+        Gs[hq][tt] = acc.x; Gs[hq + 1][tt] = acc.y; Gs[hq + 2][tt] = acc.z; Gs[hq + 3][tt] = acc.w;
+    }
+    __syncthreads();
+    for (int q = tid; q < DG_H * (DG_T / 4); q += kThreads) {
+        const int hh = q / (DG_T / 4), tq = 4 * (q % (DG_T / 4));
+        const int h = h0 + hh, t = t0 + tq;
+        if (h >= N || t >= M) continue;
+        uint2 pp[3];
+        split4(*reinterpret_cast<const float4*>(&Gs[hh][tq]), pp);
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+            *reinterpret_cast<uint2*>(planes + (size_t)pl * N * M + (size_t)h * M + t) = pp[pl];
+    }
+}
+
+// out[c][r] = in[r][c] (fp32), 32 x 32 tiles through LDS.
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const float* __restrict__ in, int R, int C,
+                                                              float* __restrict__ out)
+{
+    __shared__ float tile[32][33];
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    for (int q = threadIdx.x; q < 32 * 32; q += kThreads) {
+        const int rr = q / 32, cc = q % 32;
+        if (r0 + rr < R && c0 + cc < C) tile[rr][cc] = in[(size_t)(r0 + rr) * C + c0 + cc];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 32 * 32; q += kThreads) {
+        const int cc = q / 32, rr = q % 32;
+        if (r0 + rr < R && c0 + cc < C) out[(size_t)(c0 + cc) * R + r0 + rr] = tile[rr][cc];
+    }
+}
+
+// Head update: W2[c][h] <- fp32(W2[c][h] - lr sum_t ghat2[t][c] GELU(Y[t][h])).
+// Block: DW_H hidden units x DW_G token groups (group g takes tokens t with
+// t % DW_G == g); the groups' sums are added in a fixed order through LDS.
+constexpr int DW_H = 32, DW_G = kThreads / DW_H;
+__global__ __launch_bounds__(kThreads) void dust_w2_kernel(const float* __restrict__ Y, const float* __restrict__ ghat2,
+                                                            int M, int N, int C, float lr,
+                                                            const int* __restrict__ skip, float* __restrict__ W2)
+{
+    __shared__ float red[DW_G][DW_H][kMaxClasses + 1];
+    if (*skip) return;
+    const int hl = threadIdx.x % DW_H, g = threadIdx.x / DW_H;
+    const int h = blockIdx.x * DW_H + hl;
+    float acc[kMaxClasses];
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) acc[c] = 0.f;
+    if (h < N) {
+        for (int t = g; t < M; t += DW_G) {
+            const float a = gelu_erf(Y[(size_t)t * N + h]);
+            const float* gr = ghat2 + (size_t)t * C;
+#pragma unroll
+            for (int c = 0; c < kMaxClasses; ++c)
+                if (c < C) acc[c] = fmaf(gr[c], a, acc[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxClasses; ++c) red[g][hl][c] = acc[c];
+    __syncthreads();
+    if (g != 0 || h >= N) return;
+    for (int c = 0; c < C; ++c) {
+        float sum = 0.f;
+        for (int q = 0; q < DW_G; ++q) sum += red[q][hl][c];
+        W2[(size_t)c * N + h] = fmaf(-lr, sum, W2[(size_t)c * N + h]);
+    }
 }
 
 }  // namespace
@@ -1132,10 +1469,36 @@ zo_status mlp_check(const zo_model_desc& d)
     return ZO_OK;
 }
 
+// Workspace of the Dust step, inside the MLP's logit-partial region:
+// region A = the draws' partial logits, later (once reduced) the transposed
+// output-error planes and X^T; then Z, w, ghat2 and the skip flag.
+struct DustLayout {
+    size_t planes, xt, z, w, ghat2, skip, total;
+};
+static DustLayout dust_layout(const zo_model_desc& d, int M, int k1)
+{
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t N = d.hidden, D = d.d_in, C = d.classes;
+    const size_t part = (size_t)(k1 + 1) * cdiv((int)N, DH_BN) * C * M * sizeof(float);
+    const size_t gt = 3 * N * M * sizeof(bf16_t), xt = D * M * sizeof(float);
+    DustLayout L;
+    L.planes = 0;
+    L.xt = al(gt);
+    const size_t a = std::max(al(part), L.xt + al(xt));
+    L.z = a;
+    L.w = L.z + al(M * C * sizeof(double));
+    L.ghat2 = L.w + al((size_t)k1 * M * sizeof(float));
+    L.skip = L.ghat2 + al(M * C * sizeof(float));
+    L.total = L.skip + 256;
+    return L;
+}
+
 size_t mlp_part_bytes(const zo_model_desc& d)
 {
     const size_t tiles = cdiv((int)d.hidden, MLP_BN);
-    return (kMaxEvalsPerCall * tiles * d.batch * d.classes * sizeof(float) + 255) / 256 * 256;
+    const size_t probes = (kMaxEvalsPerCall * tiles * d.batch * d.classes * sizeof(float) + 255) / 256 * 256;
+    // large enough for a Dust step with the most hidden-layer draws
+    return std::max(probes, dust_layout(d, (int)d.batch, DG_MAXK).total);
 }
 
 // workspace: logit partials | per-chunk CE sums | X planes (3 M K bf16) | X W1^T (M N fp32)
@@ -1321,6 +1684,107 @@ zo_status mlp_split_step(const ModelView& m, const zo_batch& b, uint64_t seed, i
         return st;
     return launch_update((float*)m.params + m.offsets[1], ZO_F32, n2, m.offsets[1], seed, (uint32_t)(2 * p1 * ps), g2,
                          lr, s, ZO_DIRS_GAUSS, (uint32_t)p1);
+}
+
+zo_status mlp_dust_check(const zo_model_desc& d, const zo_batch& b, int k1, int k2)
+{
+    if (d.kind != ZO_MODEL_MLP) return fail(ZO_ERR_UNSUPPORTED, "the Dust step is defined for the MLP");
+    if (d.d_in % 32) return fail(ZO_ERR_UNSUPPORTED, "the Dust step needs d_in %% 32 == 0");
+    if (b.batch % 32) return fail(ZO_ERR_UNSUPPORTED, "the Dust step needs batch %% 32 == 0");
+    if (k1 < 1 || k1 > DG_MAXK) return fail(ZO_ERR_INVALID, "k1 must be in 1..%d", DG_MAXK);
+    if (k2 < 1 || k2 > (1 << 16)) return fail(ZO_ERR_INVALID, "k2 must be in 1..65536");
+    return ZO_OK;
+}
+
+zo_status mlp_dust_step(const ModelView& m, const zo_batch& b, uint64_t seed, int k1, int k2, float sigma1,
+                        float sigma2, float lr, double* losses, hipStream_t s)
+{
+    const zo_model_desc& d = m.desc;
+    const int M = (int)b.batch, N = (int)d.hidden, K = (int)d.d_in, C = (int)d.classes;
+    const DustLayout L = dust_layout(d, M, k1);
+    if (L.total > mlp_part_bytes(d)) return fail(ZO_ERR_WORKSPACE, "Dust step: the batch exceeds the model's");
+    char* ws = (char*)m.workspace;
+    char* region = ws;  // the logit-partial region
+    bf16_t* xplanes = (bf16_t*)(ws + mlp_part_bytes(d) + mlp_chunk_bytes(d));
+    float* Y = (float*)((char*)xplanes + mlp_planes_bytes(d));
+    float* part = (float*)region;
+    bf16_t* gplanes = (bf16_t*)(region + L.planes);
+    float* xt = (float*)(region + L.xt);
+    double* Z = (double*)(region + L.z);
+    float* w = (float*)(region + L.w);
+    float* ghat2 = (float*)(region + L.ghat2);
+    int* skip = (int*)(region + L.skip);
+    float* W1 = (float*)m.params + m.offsets[0];
+    float* W2 = (float*)m.params + m.offsets[1];
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    zo_status st;
+    // 1. the clean first layer Y = X W1^T (split-bf16), cached for every draw
+    SplitArgs a = {};
+    a.Xp = xplanes;
+    a.W = W1;
+    a.w_dir = m.offsets[0];
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.H = Y;
+    {
+        const size_t n4 = (size_t)M * K / 4;
+        KernelTimer timer("gemm_f32_base", s);
+        split_planes_kernel<<<(int)std::min<size_t>((n4 + kThreads - 1) / kThreads, 2048), kThreads, 0, s>>>(
+            (const float*)b.x, n4, xplanes, (size_t)M * K);
+    }
+    if ((st = check_launch("X split"))) return st;
+    EvalList base;
+    make_evals(nullptr, 0, base);
+    if ((st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_BASE_STORE, 1>(a, base, 1, s, "gemm_f32_base"))) return st;
+    // 2. the clean and k1 noisy forwards of the layers after W1
+    const int n_tiles = cdiv(N, DH_BN);
+    {
+        const dim3 grid(n_tiles, cdiv(M, DH_BM), k1 + 1);
+        const int q = (C + 3) / 4;  // four thread groups per row
+        KernelTimer timer("dust", s);
+        if (q <= 1)
+            dust_hidden_kernel<1><<<grid, DH_NT, 0, s>>>(Y, W2, M, N, C, key, sigma1, part);
+        else if (q <= 3)
+            dust_hidden_kernel<3><<<grid, DH_NT, 0, s>>>(Y, W2, M, N, C, key, sigma1, part);
+        else
+            dust_hidden_kernel<4><<<grid, DH_NT, 0, s>>>(Y, W2, M, N, C, key, sigma1, part);
+    }
+    if ((st = check_launch("dust hidden draws"))) return st;
+    // 3. per-token losses of every draw, clean logits; 4. rewards and the head
+    {
+        KernelTimer timer("reduce", s);
+        double* loss2 = losses + (size_t)(k1 + 1) * M;
+        dust_rows_kernel<<<dim3(cdiv(M, 64), k1 + 1), kThreads, 0, s>>>(part, n_tiles, M, C, b.labels, losses, Z, skip);
+        const size_t nh = (size_t)k2 * M;
+        dust_head_loss_kernel<<<(int)std::min<size_t>((nh + kThreads - 1) / kThreads, 4096), kThreads, 0, s>>>(
+            Z, b.labels, M, C, k2, sigma2, key, loss2, skip);
+        dust_reward_kernel<<<M, kThreads, 0, s>>>(losses, loss2, M, C, k1, k2, sigma1, sigma2, key, w, ghat2, skip);
+    }
+    if ((st = check_launch("dust rewards"))) return st;
+    // 5. hidden output errors (transposed planes), X^T, and W1 -= lr G^T X
+    {
+        KernelTimer timer("dust", s);
+        dust_gy_kernel<<<dim3(cdiv(N, DG_H), cdiv(M, DG_T)), kThreads, 0, s>>>(w, M, N, k1, key, gplanes);
+        transpose_kernel<<<dim3(cdiv(K, 32), cdiv(M, 32)), kThreads, 0, s>>>((const float*)b.x, M, K, xt);
+    }
+    if ((st = check_launch("dust output errors"))) return st;
+    SplitArgs u = {};
+    u.Xp = gplanes;
+    u.W = xt;
+    u.M = N;
+    u.N = K;
+    u.K = M;
+    u.H = W1;
+    u.lr = lr;
+    u.skip = skip;
+    if ((st = launch_sgemm<SB_BM, SB_BN, SB_NT, SG_UPDATE, 1>(u, base, 1, s, "update"))) return st;
+    // 6. W2 -= lr sum_t ghat2_t GELU(Y_t)^T
+    {
+        KernelTimer timer("update", s);
+        dust_w2_kernel<<<cdiv(N, DW_H), kThreads, 0, s>>>(Y, ghat2, M, N, C, lr, skip, W2);
+    }
+    return check_launch("dust head update");
 }
 
 }  // namespace zo

@@ -40,6 +40,10 @@ zo_status mlp_forward(const ModelView& m, const zo_batch& b, const zo_pert* pert
 zo_status mlp_split_check(const zo_model_desc& d, int p1, int ps);
 zo_status mlp_split_step(const ModelView& m, const zo_batch& b, uint64_t seed, int p1, int ps, float eps, float lr,
                          double* losses, double* g1, double* g2, hipStream_t s);
+// Dust (activation noise) step of the MLP
+zo_status mlp_dust_check(const zo_model_desc& d, const zo_batch& b, int k1, int k2);
+zo_status mlp_dust_step(const ModelView& m, const zo_batch& b, uint64_t seed, int k1, int k2, float sigma1,
+                        float sigma2, float lr, double* losses, hipStream_t s);
 zo_status decoder_check(const zo_model_desc& d);
 size_t decoder_workspace(const zo_model_desc& d);
 zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,

@@ -129,6 +129,19 @@ __device__ __forceinline__ void box_muller(uint32_t x_even, uint32_t x_odd, floa
     z_odd = fmaf(s, r, s * r_lo);
 }
 
+// Four Gaussians for elements 4q .. 4q+3 of counter stream `stream` of
+// direction `probe` (stream 0: the weight directions; the Dust estimator's
+// activation noise uses streams 2 and 3).
+__device__ __forceinline__ float4 gauss4s(Key key, uint32_t probe, uint32_t stream, uint64_t q)
+{
+    uint32_t c0 = (uint32_t)q, c1 = (uint32_t)(q >> 32), c2 = probe, c3 = stream;
+    philox4x32_10(c0, c1, c2, c3, key);
+    float4 z;
+    box_muller(c0, c1, z.x, z.y);
+    box_muller(c2, c3, z.z, z.w);
+    return z;
+}
+
 // Four Gaussians for elements 4q .. 4q+3 of direction `probe`.
 __device__ __forceinline__ float4 gauss4(Key key, uint32_t probe, uint64_t q)
 {

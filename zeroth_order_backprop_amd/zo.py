@@ -19,7 +19,7 @@ ZO_DIRS_GAUSS, ZO_DIRS_Q8 = 0, 1
 
 EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
-    "zo_forward_loss", "zo_update", "zo_step", "zo_step_split", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
+    "zo_forward_loss", "zo_update", "zo_step", "zo_step_split", "zo_step_dust", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
     "zo_timing_enable", "zo_timing_select", "zo_timing_reset", "zo_timing_query",
     "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
@@ -60,6 +60,11 @@ class SplitCfg(ctypes.Structure):
                 ("eps", ctypes.c_float), ("lr", ctypes.c_float)]
 
 
+class DustCfg(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("k1", ctypes.c_uint32), ("k2", ctypes.c_uint32),
+                ("sigma1", ctypes.c_float), ("sigma2", ctypes.c_float), ("lr", ctypes.c_float)]
+
+
 class StepCfg(ctypes.Structure):
     _fields_ = [("seed", ctypes.c_uint64), ("n_probes", ctypes.c_uint32), ("eps", ctypes.c_float),
                 ("lr", ctypes.c_float), ("mode", ctypes.c_int32), ("precond", ctypes.c_int32),
@@ -88,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "zo_step": [P, P, P, P, P, P],
         "zo_replay_step": [P, P, P, P],
         "zo_step_split": [P, P, P, P, P, P, P],
+        "zo_step_dust": [P, P, P, P, P],
         "zo_perturb_buffer": [P, I32, I32, U64, U64, U64, U32, F, P],
         "zo_update_buffer": [P, I32, I32, U64, U64, U64, U32, P, F, P],
         "zo_gscalar": [P, U32, F, P, P],
@@ -276,6 +282,16 @@ class Model:
         cfg = SplitCfg(int(seed), p1, ps, float(eps), float(lr))
         check(lib().zo_step_split(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _ptr(g1_dev),
                                   _ptr(g2_dev), _stream(stream)), "zo_step_split")
+
+    def step_dust(self, batch: Batch, seed, k1, k2, sigma1, sigma2, lr, losses_dev, stream=None):
+        """One Dust step of the MLP; losses_dev (device fp64) needs
+        (1 + k1 + k2) * batch entries: clean, hidden draws, head draws."""
+        need = (1 + int(k1) + int(k2)) * int(batch.batch)
+        if losses_dev.numel() < need:
+            raise ValueError(f"zo_step_dust: losses need {need} entries")
+        cfg = DustCfg(int(seed), int(k1), int(k2), float(sigma1), float(sigma2), float(lr))
+        check(lib().zo_step_dust(self._h, ctypes.byref(batch), ctypes.byref(cfg), _ptr(losses_dev), _stream(stream)),
+              "zo_step_dust")
 
     def replay_step(self, seed, n_probes, eps, lr, mode, g_dev, stream=None):
         """The weight changes of a recorded step, given the g it produced."""
