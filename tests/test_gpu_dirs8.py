@@ -186,3 +186,50 @@ def test_fused_evaluations_refused():
     torch.cuda.synchronize()
     assert losses[0].item() == pytest.approx(oracle.model_loss(arena, obatch), rel=LOSS_RTOL)
     assert torch.equal(model.arena, before)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_passes_larger_than_last_level_cache(dtype):
+    """Passes over 288 MB (more than the 256 MB last-level cache take the
+    non-temporal loads and stores): a perturbation of zeros by sigma = 1 gives
+    the directions, and an N = 1 update of zeros gives fp32(c z), on slices at
+    the start, the middle and the end (ragged tail included)."""
+    n = (72_000_000 if dtype == "f32" else 144_000_000) + 1234
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    zdt = zo.ZO_F32 if dtype == "f32" else zo.ZO_BF16
+    mid = n // 2 // 16 * 16
+    slices = [(0, 1 << 20), (mid, 1 << 16), (n - 70_000, 70_000)]
+
+    def check(w, scale):
+        for j0, cnt in slices:
+            z = oracle.directions("q8", 91, 4, j0, cnt).astype(np.float32)
+            want = (np.float32(scale) * z).astype(np.float64)
+            if dtype == "f32":
+                got = w[j0:j0 + cnt].cpu().numpy().astype(np.float64)
+            else:
+                got = oracle.bf16_bits_to_f64(w[j0:j0 + cnt].view(torch.int16).cpu().numpy().view(np.uint16))
+                want = oracle.bf16_round(want)
+            assert np.array_equal(got, want), (j0, cnt)
+
+    w = torch.zeros(n, dtype=tdt, device=DEV)
+    zo.perturb_buffer(w, n, 0, 91, 4, 1.0, zdt, dirs=zo.ZO_DIRS_Q8)
+    torch.cuda.synchronize()
+    check(w, 1.0)
+    w.zero_()
+    g = torch.tensor([2.5], dtype=torch.float64, device=DEV)
+    lr = 1e-2
+    zo.update_buffer(w, n, 0, 91, 1, g, lr, zdt, dirs=zo.ZO_DIRS_Q8)
+    torch.cuda.synchronize()
+    # c = fp32(-lr g / N); the update adds fma(c, z, 0) to zero; its probe is 0..N-1 = 0
+    c = np.float32(-np.float64(np.float32(lr)) * 2.5)
+    for j0, cnt in slices:
+        z = oracle.directions("q8", 91, 0, j0, cnt).astype(np.float32)
+        want = (c * z).astype(np.float64)
+        if dtype == "f32":
+            got = w[j0:j0 + cnt].cpu().numpy().astype(np.float64)
+        else:
+            got = oracle.bf16_bits_to_f64(w[j0:j0 + cnt].view(torch.int16).cpu().numpy().view(np.uint16))
+            want = oracle.bf16_round(want)
+        assert np.array_equal(got, want), (j0, cnt)
+    del w
+    torch.cuda.empty_cache()

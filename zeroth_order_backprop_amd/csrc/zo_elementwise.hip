@@ -55,6 +55,64 @@ __device__ __forceinline__ uint4 pack8(const float* f)
                  pack_bf16(f[6], f[7])};
 }
 
+// ---- streaming passes over the weights --------------------------------------
+// The 8-bit-direction passes that touch each weight once (perturbation;
+// updates with one or two directions) are HBM-bound.  They use the access
+// pattern that streams fastest here: one 16-byte vector per thread per
+// iteration, contiguous across the wave, the next iteration's vector loaded
+// before this one is worked on, and four blocks of 256 threads per CU.  Over a
+// 2.6 GB buffer that moves 5.3-5.5 TB/s, and 5.9 with non-temporal loads and
+// stores, against 4.9 for a thread owning 16 consecutive elements.  The
+// non-temporal form keeps the written weights out of the 256 MB last-level
+// cache, from which the forward evaluation right after a perturbation reads a
+// model that fits (GPT-small shape: its GEMMs 18% slower), so it is used only
+// for passes larger than that cache.  (The Gaussian passes are bound by the
+// direction generation and measured no faster in this pattern.)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T, bool NT> struct Vec16;
+template <bool NT> struct Vec16<uint16_t, NT> {
+    static constexpr int L = 8;  // elements per vector
+    typedef u32x4_t raw_t;
+    static __device__ __forceinline__ raw_t load(const uint16_t* p)
+    {
+        const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+        if constexpr (NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    }
+    static __device__ __forceinline__ void unpack(raw_t v, float* f) { unpack8(uint4{v.x, v.y, v.z, v.w}, f); }
+    static __device__ __forceinline__ void store(uint16_t* p, const float* f)
+    {
+        const uint4 v = pack8(f);
+        u32x4_t* q = reinterpret_cast<u32x4_t*>(p);
+        if constexpr (NT) __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, q);
+        else *q = u32x4_t{v.x, v.y, v.z, v.w};
+    }
+};
+template <bool NT> struct Vec16<float, NT> {
+    static constexpr int L = 4;
+    typedef f32x4_t raw_t;
+    static __device__ __forceinline__ raw_t load(const float* p)
+    {
+        const f32x4_t* q = reinterpret_cast<const f32x4_t*>(p);
+        if constexpr (NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    }
+    static __device__ __forceinline__ void unpack(raw_t v, float* f)
+    {
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float* f)
+    {
+        f32x4_t* q = reinterpret_cast<f32x4_t*>(p);
+        if constexpr (NT) __builtin_nontemporal_store(f32x4_t{f[0], f[1], f[2], f[3]}, q);
+        else *q = f32x4_t{f[0], f[1], f[2], f[3]};
+    }
+};
+constexpr int kStreamBlocks = 1024;
+constexpr uint64_t kLastLevelCacheBytes = 256ull << 20;
+constexpr uint32_t kStreamMaxProbes = 2;  // updates with more directions are VALU-bound
+
 // Gaussian for one element j (slow path for ragged tails and debug).
 __device__ __forceinline__ float gauss1(Key key, uint32_t probe, uint64_t j)
 {
@@ -224,10 +282,12 @@ __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w
 
 
 // ------------------------------------------------ 8-bit packed directions
-// One Philox block gives the codes of 16 consecutive elements, so a thread
-// owns 16 elements per iteration (bf16: two 16-byte vectors; fp32: four) and
-// looks each code up in the LDS copy of the quantile table.  Requires
-// j0 % 16 == 0.
+// One Philox block gives the codes of 16 consecutive elements; each code is
+// looked up in the LDS copy of the quantile table.  Requires j0 % 16 == 0.
+// The perturbation and the update with one or two directions stream the
+// weights (see above); the update with more directions, VALU-bound, gives a
+// thread the 16 elements of one block per iteration (bf16: two 16-byte
+// vectors; fp32: four) so that each block is generated once.
 constexpr int kQ8PerIter = kThreads * 16;
 
 template <typename T> struct Q8Io;
@@ -283,25 +343,87 @@ __device__ __forceinline__ void update_q8_tail(T* __restrict__ w, uint64_t start
     }
 }
 
-template <typename T>
+// The perturbation pass in the streaming pattern: a vector holds half (bf16)
+// or a quarter (fp32) of a Philox block's 16 elements; the lanes that share a
+// block each generate it (the pass has VALU to spare).
+template <typename T, bool NT>
 __global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64_t n_full, uint64_t n, uint64_t j0,
                                                         Key key, uint32_t probe, float sigma)
 {
+    typedef Vec16<T, NT> V;
+    constexpr int L = V::L, PER = kThreads * L;
     __shared__ float tab[256];
     dirs8::load_table(tab);
     __syncthreads();
-    const uint64_t stride = (uint64_t)gridDim.x * kQ8PerIter;
-    for (uint64_t base = (uint64_t)blockIdx.x * kQ8PerIter; base < n_full; base += stride) {
-        const uint64_t e = base + 16 * threadIdx.x;
-        float f[16];
-        Q8Io<T>::load(w, e, f);
+    const uint64_t stride = (uint64_t)gridDim.x * PER;
+    // the next iteration's vector is loaded (raw, unconditionally: the last
+    // iteration reloads its own) before this one's codes are made
+    typename V::raw_t nx = {};
+    if ((uint64_t)blockIdx.x * PER < n_full) nx = V::load(w + (uint64_t)blockIdx.x * PER + L * threadIdx.x);
+    for (uint64_t base = (uint64_t)blockIdx.x * PER; base < n_full; base += stride) {
+        const uint64_t e = base + L * threadIdx.x;
+        float f[L];
+        V::unpack(nx, f);
+        nx = V::load(w + e + (base + stride < n_full ? stride : 0));
         const uint4 c = dirs8::block(key, probe, (j0 + e) >> 4);
-        const uint32_t words[4] = {c.x, c.y, c.z, c.w};
+        const int w0 = (int)((j0 + e) >> 2) & 3;  // the block's first word for this vector
 #pragma unroll
-        for (int t = 0; t < 16; ++t) f[t] = fmaf(sigma, dirs8::code(tab, words[t >> 2], t & 3), f[t]);
-        Q8Io<T>::store(w, e, f);
+        for (int t = 0; t < L; ++t) {
+            const int k = w0 + (t >> 2);
+            const uint32_t word = k == 0 ? c.x : k == 1 ? c.y : k == 2 ? c.z : c.w;
+            f[t] = fmaf(sigma, dirs8::code(tab, word, t & 3), f[t]);
+        }
+        V::store(w + e, f);
     }
     perturb_q8_tail(w, n_full, n, j0, key, probe, sigma, tab);
+}
+
+// The update for few directions (HBM-bound) in the streaming pattern; more
+// directions make it VALU-bound, and update_q8 below generates each block once
+// per thread instead.
+template <typename T, uint32_t NP, bool NT>
+__global__ __launch_bounds__(kThreads) void update_q8_vec(T* __restrict__ w, uint64_t n_full, uint64_t n,
+                                                           uint64_t j0, Key key, uint32_t p0,
+                                                           const double* __restrict__ g, float lr)
+{
+    typedef Vec16<T, NT> V;
+    constexpr uint32_t n_probes = NP;
+    constexpr int L = V::L, PER = kThreads * L;
+    __shared__ float tab[256];
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    dirs8::load_table(tab);
+    if (!load_coeffs(g, n_probes, lr, c, &bad)) return;  // its barriers also cover the table
+    const uint64_t stride = (uint64_t)gridDim.x * PER;
+    // the next iteration's vector is loaded (raw, unconditionally: the last
+    // iteration reloads its own) before this one's sum is made
+    typename V::raw_t nx = {};
+    if ((uint64_t)blockIdx.x * PER < n_full) nx = V::load(w + (uint64_t)blockIdx.x * PER + L * threadIdx.x);
+    for (uint64_t base = (uint64_t)blockIdx.x * PER; base < n_full; base += stride) {
+        const uint64_t e = base + L * threadIdx.x;
+        float f[L];
+        V::unpack(nx, f);
+        nx = V::load(w + e + (base + stride < n_full ? stride : 0));
+        const int w0 = (int)((j0 + e) >> 2) & 3;
+        float acc[L];
+#pragma unroll
+        for (int t = 0; t < L; ++t) acc[t] = 0.0f;
+#pragma unroll
+        for (uint32_t i = 0; i < n_probes; ++i) {
+            const float ci = c[i];
+            const uint4 cw = dirs8::block(key, p0 + i, (j0 + e) >> 4);
+#pragma unroll
+            for (int t = 0; t < L; ++t) {
+                const int k = w0 + (t >> 2);
+                const uint32_t word = k == 0 ? cw.x : k == 1 ? cw.y : k == 2 ? cw.z : cw.w;
+                acc[t] = fmaf(ci, dirs8::code(tab, word, t & 3), acc[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t) f[t] += acc[t];
+        V::store(w + e, f);
+    }
+    update_q8_tail(w, n_full, n, j0, key, p0, n_probes, c, tab);
 }
 
 template <typename T>
@@ -391,11 +513,11 @@ __global__ __launch_bounds__(kThreads) void debug_box_muller_kernel(const uint32
     z[2 * t + 1] = b;
 }
 
-int grid_for(uint64_t n_full, uint64_t per_iter = kElemsPerIter)
+int grid_for(uint64_t n_full, uint64_t per_iter = kElemsPerIter, uint64_t cap = 256ull * 16ull)
 {
-    // enough blocks to fill 256 CUs several times over; the loop strides the rest
+    // enough blocks to fill 256 CUs (several times over by default); the loop
+    // strides the rest
     const uint64_t iters = n_full / per_iter;
-    const uint64_t cap = 256ull * 16ull;
     return (int)(iters < cap ? (iters ? iters : 1) : cap);
 }
 
@@ -406,9 +528,14 @@ static zo_status launch_perturb_q8(T* w, uint64_t n, uint64_t j0, Key key, uint3
                                    hipStream_t s)
 {
     if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
-    const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
+    constexpr uint64_t per = (uint64_t)kThreads * Vec16<T, false>::L;
+    const uint64_t n_full = n / per * per;
+    const int grid = grid_for(n_full, per, kStreamBlocks);
     KernelTimer timer("perturb", s);
-    perturb_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, probe, sigma);
+    if (n * sizeof(T) > kLastLevelCacheBytes)
+        perturb_q8<T, true><<<grid, kThreads, 0, s>>>(w, n_full, n, j0, key, probe, sigma);
+    else
+        perturb_q8<T, false><<<grid, kThreads, 0, s>>>(w, n_full, n, j0, key, probe, sigma);
     return check_launch("perturb (8-bit directions)");
 }
 
@@ -417,9 +544,20 @@ static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32
                                   const double* g, float lr, hipStream_t s)
 {
     if (j0 % 16) return fail(ZO_ERR_INVALID, "8-bit directions need j0 %% 16 == 0");
-    const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
     KernelTimer timer("update", s);
-    update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, p0, n_probes, g, lr);
+    if (n_probes <= kStreamMaxProbes) {
+        constexpr uint64_t per = (uint64_t)kThreads * Vec16<T, false>::L;
+        const uint64_t n_full = n / per * per;
+        const int grid = grid_for(n_full, per, kStreamBlocks);
+        const bool nt = n * sizeof(T) > kLastLevelCacheBytes;
+        static_assert(kStreamMaxProbes == 2, "instances below");
+        auto k = n_probes == 1 ? (nt ? update_q8_vec<T, 1, true> : update_q8_vec<T, 1, false>)
+                               : (nt ? update_q8_vec<T, 2, true> : update_q8_vec<T, 2, false>);
+        k<<<grid, kThreads, 0, s>>>(w, n_full, n, j0, key, p0, g, lr);
+    } else {
+        const uint64_t n_full = n / kQ8PerIter * kQ8PerIter;
+        update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, p0, n_probes, g, lr);
+    }
     return check_launch("update (8-bit directions)");
 }
 
