@@ -246,6 +246,7 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the step shards by probes, see the design notes", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
 
     from zeroth_order_backprop_amd import inputs, zo
@@ -304,14 +305,18 @@ def main():
     zo.timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]  # after each step, for percentiles
     torch.cuda.synchronize()
     start.record()
     for t in range(args.steps):
         step(args.warmup + t)
+        marks[t].record()
     stop.record()
     torch.cuda.synchronize()
     zo.timing_enable(False)
     total_ms = start.elapsed_time(stop)
+    per_step = np.array([start.elapsed_time(marks[0])] +
+                        [marks[t - 1].elapsed_time(marks[t]) for t in range(1, args.steps)])
     ms_step = total_ms / args.steps
     evals_per_s = probe_evals_per_step * args.steps / (total_ms * 1e-3)
     k_ms, k_n = zo.timing_query(info["kernel"])
@@ -360,12 +365,21 @@ def main():
         flops_per_launch = 2 * N * info["flops_per_eval"]
     achieved = flops_per_launch / k_avg_s / 1e12
     kernels = {}
+    fwd_ms = 0.0  # per step, summed over the kernels that evaluate (all but perturb and update)
     for fam in ("gemm_f32", "gemm_f32_base", "dust", "gemm_bf16", "lm_head", "attention", "layernorm", "embed", "reduce", "update",
                 "perturb"):
         ms, n = zo.timing_query(fam)
+        if n and fam not in ("perturb", "update"):
+            fwd_ms += ms / args.steps
         if n:
             kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / args.steps,
                             "ms_per_step": round(ms / args.steps, 3)}
+    # forward-only rate: the evaluations of a step over the summed time of the
+    # kernels that evaluate (everything but the perturbation and update passes)
+    rates = {"step_evals_per_s": round(evals_per_s, 2),
+             "forward_only_evals_per_s": round(probe_evals_per_step / (fwd_ms * 1e-3), 2) if fwd_ms else None,
+             "probe_pairs_per_s": None if (split or dust) else round(evals_per_s / 2, 2),
+             "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)]}
     if "lm_head" in kernels:
         t = kernels["lm_head"]["ms_per_step"] * 1e-3
         kernels["lm_head"]["TFLOP/s"] = round(evals_per_step * info["head_flops_per_eval"] / t / 1e12, 1)
@@ -401,6 +415,7 @@ def main():
                                 "dust hidden-layer draws and output errors (Gaussian generation, GELU, logits)"
                                 if dust else "gemm_bf16 layer GEMMs (QKV, O, up, down)"),
                      "avg_launch_us": round(k_avg_s * 1e6, 2), **extra},
+        "rates": rates,
         "kernels": kernels,
         "last_losses_mean": float(final.mean()),
     }
