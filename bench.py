@@ -215,6 +215,38 @@ def measure_passes(torch, zo):
     return out
 
 
+def _oracle_probe_worker(job):
+    """One host core: single-probe oracle steps of the workload for a fixed
+    time; returns (steps, seconds)."""
+    desc, arena, batch, eps, lr, seed0, seconds = job
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oracle
+    a = oracle.Arena(desc, arena.copy())
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < seconds:
+            oracle.spsa_step(a, batch, seed=seed0 + reps, n_probes=1, eps=eps, lr=lr, mode="fused")
+            reps += 1
+        return reps, time.perf_counter() - t0
+
+
+def cpu_baseline_probe_parallel(info, seconds=8.0):
+    """Probes are independent: one single-threaded oracle process per host
+    core (at most 16), each evaluating its own probe's pair and update."""
+    import multiprocessing
+    procs = max(1, min(16, os.cpu_count() or 1))
+    jobs = [(info["oracle_desc"], info["arena"], info["oracle_batch"], info["eps"], info["lr"], 1000 * i, seconds)
+            for i in range(procs)]
+    with multiprocessing.get_context("spawn").Pool(procs) as pool:
+        res = pool.map(_oracle_probe_worker, jobs)
+    rate = sum(2 * r / t for r, t in res)
+    return {"value": round(rate, 3), "unit": "probe-evals/s", "cores": procs, "kind": "oracle",
+            "sample": f"{procs} processes x {seconds:.0f} s of single-probe oracle steps "
+                      f"({sum(r for r, _ in res)} steps in all)"}
+
+
 def cpu_baseline(info):
     """The oracle as it stands, single-threaded, on a bounded sample: one
     fused-mode step of the same workload with fewer probes."""
@@ -237,7 +269,8 @@ def cpu_baseline(info):
     evals = 2 * probes * reps
     return {"value": round(evals / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} oracle SPSA step(s) of the same workload with N={probes} probes "
-                      f"({evals} evaluations + update), single-threaded, {t:.1f} s"}
+                      f"({evals} evaluations + update), single-threaded, {t:.1f} s",
+            "probe_parallel": cpu_baseline_probe_parallel(info)}
 
 
 def main():
