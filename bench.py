@@ -247,6 +247,36 @@ def cpu_baseline_probe_parallel(info, seconds=8.0):
                       f"({sum(r for r, _ in res)} steps in all)"}
 
 
+def cpu_baseline_variant(info, split=None, dust=None, seconds=12.0):
+    """The oracle's split-perturbation or Dust step on the same workload,
+    single-threaded, with smaller populations, counted in the bench line's
+    unit (split: f2-evaluations 4 p1 ps; Dust: draws k1 + k2)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oracle
+    arena = oracle.Arena(info["oracle_desc"], info["arena"].copy())
+    if split:
+        p1, ps = 2, min(split[1], 2)
+        run = lambda r: oracle.fedspzo_step(arena, info["oracle_batch"], seed=r, p1=p1, ps=ps, eps=info["eps"],
+                                            lr=info["lr"])
+        per, what = 4 * p1 * ps, f"split-perturbation step(s) with p1={p1}, ps={ps}"
+    else:
+        k1, k2 = 4, 16
+        run = lambda r: oracle.dust_step(arena, info["oracle_batch"], seed=r, k1=k1, sigma1=0.05, k2=k2,
+                                         sigma2=0.05, lr=info["lr"])
+        per, what = k1 + k2, f"Dust step(s) with k1={k1}, k2={k2}"
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < seconds:
+            run(reps)
+            reps += 1
+        t = time.perf_counter() - t0
+    counted = "f2-evaluations (4 p1 ps per step)" if split else "draws (k1 + k2 per step)"
+    return {"value": round(per * reps / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} oracle {what} of the same workload, single-threaded, {t:.1f} s; counts {counted}"}
+
+
 def cpu_baseline(info):
     """The oracle as it stands, single-threaded, on a bounded sample: one
     fused-mode step of the same workload with fewer probes."""
@@ -454,8 +484,8 @@ def main():
     }
     if not args.no_passes:
         line["perturb_update"] = measure_passes(torch, zo)
-    if not args.no_cpu_baseline and "oracle_desc" in info and not split and not dust:
-        line["cpu_baseline"] = cpu_baseline(info)
+    if not args.no_cpu_baseline and "oracle_desc" in info:
+        line["cpu_baseline"] = cpu_baseline_variant(info, split, dust) if (split or dust) else cpu_baseline(info)
     print(json.dumps(line), flush=True)
 
 
