@@ -156,6 +156,7 @@ def build_decoder(torch, zo, inputs, name, dirs="gauss"):
         "flops_per_eval": gemm_flops + attn_flops + head_flops, "gemm_flops_per_eval": gemm_flops,
         "head_flops_per_eval": head_flops, "attn_flops_per_eval": attn_flops,
         "dtype": "bf16", "kernel": "gemm_bf16", "peak_tflops": BF16_PEAK_TFLOPS,
+        "decoder_shape": {"layers": L, "d": D, "heads": H, "ffn": F, "vocab": V, "act": act, "batch": B, "seq": S},
     }
     return model, batch, (tok,), info
 
@@ -275,6 +276,47 @@ def cpu_baseline_variant(info, split=None, dust=None, seconds=12.0):
     counted = "f2-evaluations (4 p1 ps per step)" if split else "draws (k1 + k2 per step)"
     return {"value": round(per * reps / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} oracle {what} of the same workload, single-threaded, {t:.1f} s; counts {counted}"}
+
+
+def cpu_baseline_decoder(info):
+    """The oracle's decoder forward is far too slow for a whole evaluation
+    (OPT-30B shape: about 1e15 flops per evaluation in fp64 numpy), so its
+    cost is extrapolated: one forward on one sequence of S' tokens with 1 and
+    with 2 layers (full width and vocabulary, constant weights; the fastest of
+    three runs each) gives the
+    per-layer and the embedding + LM-head times, scaled linearly to L layers
+    and B x S tokens.  The causal attention's S^2 term is scaled linearly too,
+    which favours the CPU; the small products of S' tokens run below the
+    CPU's large-matrix rate, which disfavours it."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oracle
+    sh = info["decoder_shape"]
+    s_small = 16 if sh["d"] >= 4096 else 64
+    tokens = (np.arange(s_small, dtype=np.int64) * 7919 % sh["vocab"])[None, :]
+    times = []
+    with threadpool_limits(limits=1):
+        for layers in (1, 2):
+            desc = {"kind": "decoder", "layers": layers, "d": sh["d"], "heads": sh["heads"], "ffn": sh["ffn"],
+                    "vocab": sh["vocab"], "max_seq": s_small, "act": sh["act"]}
+            params = {name: np.full(shape, 0.01 if not name.endswith("_g") else 1.0)
+                      for name, shape in oracle.param_shapes(desc)}
+            best = float("inf")
+            for _ in range(3):  # the first call also pays one-time costs; keep the fastest
+                t0 = time.perf_counter()
+                oracle.decoder_loss(desc, params, tokens)
+                best = min(best, time.perf_counter() - t0)
+            times.append(best)
+            del params
+    per_layer = max(times[1] - times[0], 0.0)
+    rest = max(times[0] - per_layer, 0.0)
+    scale = sh["batch"] * sh["seq"] / s_small
+    t_eval = scale * (sh["layers"] * per_layer + rest)
+    return {"value": round(1.0 / t_eval, 6), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "sample": f"extrapolated (forward evaluations only): one forward on 1 x {s_small} tokens with 1 and 2 "
+                      f"layers ({times[0]:.2f} s, {times[1]:.2f} s), scaled to {sh['layers']} layers and "
+                      f"{sh['batch']} x {sh['seq']} tokens = {t_eval:.0f} s per evaluation, single-threaded"}
 
 
 def cpu_baseline(info):
@@ -486,6 +528,8 @@ def main():
         line["perturb_update"] = measure_passes(torch, zo)
     if not args.no_cpu_baseline and "oracle_desc" in info:
         line["cpu_baseline"] = cpu_baseline_variant(info, split, dust) if (split or dust) else cpu_baseline(info)
+    elif not args.no_cpu_baseline and "decoder_shape" in info:
+        line["cpu_baseline"] = cpu_baseline_decoder(info)
     print(json.dumps(line), flush=True)
 
 
