@@ -549,17 +549,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 // Large tiles: 8 waves (two per SIMD, so one wave's MFMAs cover the other's
-// LDS and barrier waits) in a 4 x 2 grid of 64 x 128 wave tiles; a ring of 4
-// BK = 32 stages, prefetch distance 3.  LDS rows are
-// 64 B (4 chunks of 16 B), chunk c of row r at position c ^ ((r >> 2) & 3),
-// so the 32 rows a fragment read touches spread over all banks.  The two
-// k-halves of a stage are read into alternating register sets: the second
-// half's reads and the next stage's first half are issued while the MFMAs of
-// the previous half run.
+// LDS and barrier waits) in a 4 x 2 grid of 64 x 128 wave tiles; a ring of 5
+// BK = 32 stages (all 160 KB of LDS), prefetch distance 4: the loads' latency
+// is what the waves wait on (measured 2-10% faster than a ring of 4).  The LM
+// head keeps a ring of 4: its epilogue's cross-entropy partials take 4 KB of
+// static LDS besides.  LDS rows are 64 B (4 chunks of 16 B), chunk c of row r
+// at position c ^ ((r >> 2) & 3), so the 32 rows a fragment read touches
+// spread over all banks.  The two k-halves of a stage are read into
+// alternating register sets: the second half's reads and the next stage's
+// first half are issued while the MFMAs of the previous half run.
+template <int EPI>
+constexpr int dma_stages() { return EPI == EPI_LMHEAD ? 4 : 5; }
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g)
 {
-    constexpr int BK = 32, STAGES = 4;
+    constexpr int BK = 32, STAGES = dma_stages<EPI>();
     constexpr int NT = kDmaThreads, WGM = kDmaWavesM, WGN = NT / 64 / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int RB = WM / 32, CB = WN / 32;
@@ -567,7 +572,7 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
     constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(A_INS * NT == BM * 4 && B_INS * NT == BN * 4, "tile / thread mismatch");
-    static_assert(2 * INS < 64, "vmcnt range");
+    static_assert((STAGES - 2) * INS < 64, "vmcnt range");
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
@@ -605,8 +610,10 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
+    static_assert(STAGES >= 3 && STAGES <= 5, "wait_vm covers up to three stages in flight");
     auto wait_vm = [](int stages_in_flight) {
-        if (stages_in_flight >= 2) ZO_WAIT_VM(2 * INS);
+        if (stages_in_flight >= 3) ZO_WAIT_VM(3 * INS);
+        else if (stages_in_flight >= 2) ZO_WAIT_VM(2 * INS);
         else if (stages_in_flight == 1) ZO_WAIT_VM(INS);
         else ZO_WAIT_VM(0);
     };
@@ -643,17 +650,18 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
     };
 
     for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
-    wait_vm(min(2, KT - 1));  // stage 0 landed
+    wait_vm(min(STAGES - 2, KT - 1));  // stage 0 landed; the next ones may be in flight
     asm volatile("s_barrier" ::: "memory");
     read(0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
         read(kt, 1, 1);
         mma(0);
         if (kt + 1 < KT) {
-            // stage kt+1 landed (only kt+2 may remain in flight) and this
-            // wave's reads of stage kt are in registers; after the barrier
-            // every wave is done with stage kt-1's buffer, which is refilled
-            wait_vm(min(1, KT - 2 - kt));
+            // stage kt+1 landed (kt+2 .. kt+STAGES-2 may remain in flight)
+            // and this wave's reads of stage kt are in registers; after the
+            // barrier every wave is done with stage kt-1's buffer, which is
+            // refilled
+            wait_vm(min(STAGES - 3, KT - 2 - kt));
             ZO_WAIT_LGKM0();
             asm volatile("s_barrier" ::: "memory");
             if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
@@ -1015,11 +1023,11 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         KernelTimer timer(fam, s);
         kern<<<blocks, kThreads, lds, s>>>(gp, p);
     } else {
-        // 256-wide tiles: 4-stage BK = 32 ring; 128-wide: 2-stage BK = 64
+        // 256-wide tiles: a ring of dma_stages<EPI>() BK = 32 stages; 128-wide: 2-stage BK = 64
         constexpr bool big = BM == 256;
         // the LM head's cross-entropy epilogue needs two wave columns of 4 waves
         constexpr bool eight = !big && EPI != EPI_LMHEAD;
-        constexpr size_t stages = big ? (size_t)4 * (BM + BN) * 32 * sizeof(bf16_t)
+        constexpr size_t stages = big ? (size_t)dma_stages<EPI>() * (BM + BN) * 32 * sizeof(bf16_t)
                                       : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
