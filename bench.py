@@ -59,6 +59,9 @@ def parse():
                    help="MLP: Dust steps (activation noise) with K1 hidden-layer and K2 head draws")
     p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
                    help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
+    p.add_argument("--gemm", default=None, metavar="M,N,K",
+                   help="instead of a step: time one stored-weight bf16 GEMM C = A W^T of this shape "
+                        "(--steps calls after --warmup), for kernel measurements")
     return p.parse_args()
 
 
@@ -248,6 +251,30 @@ def cpu_baseline_probe_parallel(info, seconds=8.0):
                       f"({sum(r for r, _ in res)} steps in all)"}
 
 
+def gemm_only(torch, zo, shape, steps, warmup):
+    """One layer GEMM of the decoders, C = A W^T in bf16 (fp32 accumulate,
+    plain store), through the C ABI's debug entry; prints its time and rate."""
+    M, N, K = shape
+    g = torch.Generator(device="cuda").manual_seed(0)
+    A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    W = (torch.randn(N, K, device="cuda", generator=g) * 0.05).to(torch.bfloat16).view(torch.int16)
+    C = torch.zeros(M * N, dtype=torch.int16, device="cuda")
+    for _ in range(max(warmup, 1)):
+        zo.debug_gemm_bf16(A, W, C, M, N, K, 0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        zo.debug_gemm_bf16(A, W, C, M, N, K, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm_bf16": {"M": M, "N": N, "K": K}, "calls": steps, "ms": round(ms, 4),
+                      "TFLOP/s": round(tflops, 1), "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
+
+
 def cpu_baseline_variant(info, split=None, dust=None, seconds=12.0):
     """The oracle's split-perturbation or Dust step on the same workload,
     single-threaded, with smaller populations, counted in the bench line's
@@ -356,6 +383,9 @@ def main():
 
     from zeroth_order_backprop_amd import inputs, zo
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.gemm:
+        gemm_only(torch, zo, [int(x) for x in args.gemm.split(",")], args.steps, args.warmup)
+        return
     if args.dirs != "gauss" and args.workload not in DECODERS:
         print("bench.py: 8-bit directions apply in place; use a decoder workload (the fp32 ones run fused)",
               file=sys.stderr)
