@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--gemm", default=None, metavar="M,N,K",
                    help="instead of a step: time one stored-weight bf16 GEMM C = A W^T of this shape "
                         "(--steps calls after --warmup), for kernel measurements")
+    p.add_argument("--attention", default=None, metavar="B,S,H,DH",
+                   help="instead of a step: time the decoders' causal attention kernel on a bf16 QKV of this "
+                        "shape (--steps calls after --warmup), for kernel measurements")
     return p.parse_args()
 
 
@@ -275,6 +278,30 @@ def gemm_only(torch, zo, shape, steps, warmup):
           flush=True)
 
 
+def attention_only(torch, zo, shape, steps, warmup):
+    """The decoders' causal attention softmax(Q K^T / sqrt(dh)) V on a bf16
+    QKV buffer [B S][3 H dh] of N(0,1) values, through the C ABI's debug entry;
+    prints its time and rate (causal flops 2 B H S^2 dh)."""
+    B, S, H, dh = shape
+    g = torch.Generator(device="cuda").manual_seed(0)
+    qkv = torch.randn(B * S, 3 * H * dh, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    out = torch.zeros(B * S * H * dh, dtype=torch.int16, device="cuda")
+    for _ in range(max(warmup, 1)):
+        zo.debug_attention(qkv, out, B, S, H, dh)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        zo.debug_attention(qkv, out, B, S, H, dh)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 2.0 * B * H * S * S * dh / (ms * 1e-3) / 1e12
+    print(json.dumps({"attention": {"B": B, "S": S, "H": H, "dh": dh}, "calls": steps, "ms": round(ms, 4),
+                      "TFLOP/s": round(tflops, 1), "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
+
+
 def cpu_baseline_variant(info, split=None, dust=None, seconds=12.0):
     """The oracle's split-perturbation or Dust step on the same workload,
     single-threaded, with smaller populations, counted in the bench line's
@@ -385,6 +412,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.gemm:
         gemm_only(torch, zo, [int(x) for x in args.gemm.split(",")], args.steps, args.warmup)
+        return
+    if args.attention:
+        attention_only(torch, zo, [int(x) for x in args.attention.split(",")], args.steps, args.warmup)
         return
     if args.dirs != "gauss" and args.workload not in DECODERS:
         print("bench.py: 8-bit directions apply in place; use a decoder workload (the fp32 ones run fused)",

@@ -832,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
     constexpr int KS = DH / 16;   // MFMA k-steps over the head dim for S^T
     constexpr int OT = DH / 32;   // 32-row blocks of O^T
     constexpr int LDK = DH + 8;   // K tile row (bf16), padded
-    constexpr int LDV = BKV + 8;  // V^T tile row (bf16), padded
+    constexpr int LDV = BKV + 4;  // V^T tile row (bf16): 8 rows apart = 16 banks apart
     __shared__ __align__(16) bf16_t Ks[BKV * LDK];
     __shared__ __align__(16) bf16_t Vt[DH * LDV];
 
@@ -869,6 +869,10 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
     // Each thread stages CH (key pair, 8-column) chunks of K and V per tile:
     // keys 2 kp and 2 kp + 1, head-dim columns dc .. dc + 7.  The next tile's
     // chunks are loaded into registers while the current tile is computed.
+    // K chunks go to LDS as 16-byte row pieces, so dc runs fastest across the
+    // lanes (one row's bytes contiguous); V goes in transposed as 4-byte key
+    // pairs, so there kp runs fastest (consecutive lanes, consecutive words:
+    // with dc fastest the lanes of one key pair hit one bank).
     constexpr int CH = (BKV / 2) * (DH / 8) / kThreads;
     static_assert(CH * kThreads == (BKV / 2) * (DH / 8), "tile / thread mismatch");
     uint4 rk[CH][2], rv[CH][2];
@@ -877,14 +881,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
         for (int j = 0; j < CH; ++j) {
             const int cc = tid + j * kThreads;
             const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
+            const int kpv = cc % (BKV / 2), dcv = 8 * (cc / (BKV / 2));
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int key = k0 + 2 * kp + e;
+                const int key = k0 + 2 * kp + e, keyv = k0 + 2 * kpv + e;
                 rk[j][e] = rv[j][e] = uint4{0u, 0u, 0u, 0u};
-                if (key < S) {
-                    rk[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
-                    rv[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + voff + dc);
-                }
+                if (key < S) rk[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
+                if (keyv < S) rv[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)keyv * row_stride + voff + dcv);
             }
         }
     };
@@ -893,15 +896,17 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
         for (int j = 0; j < CH; ++j) {
             const int cc = tid + j * kThreads;
             const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
+            const int kpv = cc % (BKV / 2), dcv = 8 * (cc / (BKV / 2));
             *reinterpret_cast<uint4*>(Ks + (2 * kp) * LDK + dc) = rk[j][0];
             *reinterpret_cast<uint4*>(Ks + (2 * kp + 1) * LDK + dc) = rk[j][1];
-            // V^T: column pair (2 kp, 2 kp + 1) of row dc + e, one 4-byte write each
+            // V^T: column pair (2 kpv, 2 kpv + 1) of row dcv + e, one 4-byte write each
             const uint32_t a[4] = {rv[j][0].x, rv[j][0].y, rv[j][0].z, rv[j][0].w};
             const uint32_t b4[4] = {rv[j][1].x, rv[j][1].y, rv[j][1].z, rv[j][1].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e) * LDV + 2 * kp) = (a[e] & 0xFFFFu) | (b4[e] << 16);
-                *reinterpret_cast<uint32_t*>(Vt + (dc + 2 * e + 1) * LDV + 2 * kp) = (a[e] >> 16) | (b4[e] & 0xFFFF0000u);
+                *reinterpret_cast<uint32_t*>(Vt + (dcv + 2 * e) * LDV + 2 * kpv) = (a[e] & 0xFFFFu) | (b4[e] << 16);
+                *reinterpret_cast<uint32_t*>(Vt + (dcv + 2 * e + 1) * LDV + 2 * kpv) =
+                    (a[e] >> 16) | (b4[e] & 0xFFFF0000u);
             }
         }
     };
