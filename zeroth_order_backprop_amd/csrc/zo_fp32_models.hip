@@ -124,9 +124,15 @@ __global__ __launch_bounds__(NT) void fgemm_kernel(GemmArgs a, EvalList ev)
     constexpr int STAGE = BM * SA + NV * BN * SA;
     auto As = [&](int st) { return smem + st * STAGE; };
     auto Bs = [&](int st, int v) { return smem + st * STAGE + BM * SA + v * BN * SA; };
+    // B quad i: four consecutive k of one column (W [N][K]) or four consecutive
+    // columns at one k (W [K][N]).  The latter are stored transposed as single
+    // floats, so there k runs fastest across the lanes: consecutive lanes write
+    // consecutive words of an LDS row (columns fastest put the 16 lanes of one
+    // k on two banks).  Their 16-byte global loads then come from different
+    // rows of W, which stays in L2.
     auto b_coords = [&](int i, int k0, int& ln, int& lk, int& gn, int& gk) {
         if (!B_KN) { ln = i / (BK / 4); lk = 4 * (i % (BK / 4)); }
-        else { lk = i / (BN / 4); ln = 4 * (i % (BN / 4)); }
+        else { lk = i % BK; ln = 4 * (i / BK); }
         gn = n0 + ln;
         gk = k0 + lk;
     };
