@@ -1343,8 +1343,11 @@ __global__ __launch_bounds__(kThreads) void dust_gy_kernel(const float* __restri
         wt[i][tt] = t0 + tt < M ? w[(size_t)i * M + t0 + tt] : 0.f;
     }
     __syncthreads();
+    // tokens run fastest across the lanes: the four column writes of a lane
+    // go to consecutive words of four Gs rows (hidden units fastest would put
+    // the 16 lanes of one token on two banks)
     for (int q = tid; q < DG_T * (DG_H / 4); q += kThreads) {
-        const int tt = q / (DG_H / 4), hq = 4 * (q % (DG_H / 4));
+        const int tt = q % DG_T, hq = 4 * (q / DG_T);
         const int t = t0 + tt, h = h0 + hq;
         float4 acc = {0.f, 0.f, 0.f, 0.f};
         if (t < M && h < N) {
