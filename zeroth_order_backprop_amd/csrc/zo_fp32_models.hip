@@ -714,38 +714,65 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
             for (int pl = 0; pl < 3; ++pl) *reinterpret_cast<uint2*>(base + pl * PB + off) = p[pl];
         }
     };
-    // ---- one 16-deep k step: six bf16 products per 32x32 block, smallest first
-    auto mma_step = [&](int st, int ks) {
+    // ---- 16-deep k steps: fragments in two register sets (one per k half of
+    // the stage), six bf16 products per 32x32 block, smallest first
+    bf16x8 fa[2][RB][3], fb[2][CB][3];
+    auto read_a = [&](int st, int ks, int set) {
         const bf16_t* base = lds_bf + st * STAGE;
-        bf16x8 af[RB][3], bfr[CB][3];
         const int lc = 2 * ks + lh;
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int row = wm * WM + i * 32 + lr;
             const int off = row * BK + ((lc ^ ((row >> 2) & 3)) << 3);
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl) af[i][pl] = *reinterpret_cast<const bf16x8*>(base + pl * PA + off);
+            for (int pl = 0; pl < 3; ++pl) fa[set][i][pl] = *reinterpret_cast<const bf16x8*>(base + pl * PA + off);
         }
+    };
+    auto read_b = [&](int st, int ks, int set) {
+        const bf16_t* base = lds_bf + st * STAGE;
+        const int lc = 2 * ks + lh;
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
             const int row = wn * WN + j * 32 + lr;
             const int off = row * BK + ((lc ^ ((row >> 2) & 3)) << 3);
 #pragma unroll
             for (int pl = 0; pl < 3; ++pl)
-                bfr[j][pl] = *reinterpret_cast<const bf16x8*>(base + 3 * PA + pl * PB + off);
+                fb[set][j][pl] = *reinterpret_cast<const bf16x8*>(base + 3 * PA + pl * PB + off);
         }
+    };
+    auto mma_row = [&](int set, int i) {
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+        for (int j = 0; j < CB; ++j) {
+            const bf16x8* af = fa[set][i];
+            const bf16x8* bfr = fb[set][j];
+            f32x16 c = acc[i][j];
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[2], bfr[0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bfr[1], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[2], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bfr[0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[1], c, 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[0], c, 0, 0, 0);
+        }
+    };
+    // The first k half's rows of blocks.  The second half's fragments are read
+    // right behind the first row's MFMAs, so those reads land while the other
+    // rows compute and the second half starts without waiting on LDS (the
+    // scheduling barriers keep the compiler from moving the reads back down).
+    auto first_half = [&](int st) {
+        read_a(st, 0, 0);
+        read_b(st, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                f32x16 c = acc[i][j];
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][2], bfr[j][0], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][1], bfr[j][1], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][2], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][1], bfr[j][0], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][1], c, 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][0], bfr[j][0], c, 0, 0, 0);
-            }
+        for (int i = 0; i < RB; ++i) {
+            mma_row(0, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i == 0) { read_a(st, 1, 1); read_b(st, 1, 1); }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto second_half = [&]() {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) mma_row(1, i);
     };
     constexpr int NPIECE = 3 * B_Q;
     auto produce_b = [&](int k0) {
@@ -768,12 +795,12 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
         const int kn = (kt + 1) * BK;
         issue_a(cur ^ 1, kn);
         if constexpr (!PROBE) load_b(kn);
-        mma_step(cur, 0);
+        first_half(cur);
         if constexpr (PROBE) {
 #pragma unroll
             for (int pc = 0; pc < NPIECE / 2; ++pc) z_piece(pc, kn);
         }
-        mma_step(cur, 1);
+        second_half();
         if constexpr (PROBE) {
 #pragma unroll
             for (int pc = NPIECE / 2; pc < NPIECE; ++pc) z_piece(pc, kn);
@@ -783,8 +810,8 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
         __syncthreads();
         cur ^= 1;
     }
-    mma_step(cur, 0);
-    mma_step(cur, 1);
+    first_half(cur);
+    second_half();
     // The epilogue can reach its first accumulator read through a branch that
     // skips a whole wave's share of the W2 tile loads, and the compiler's
     // wait-state count for the last MFMAs' results has been seen to miss that
