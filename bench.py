@@ -37,8 +37,8 @@ C_Z = 37
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
 # taken on -- set to None when that kernel changes.
-TRAFFIC = {"sgemm:mlp:r3": 2 * 8492.5 * 1024 + 10240 * 1024}
-KERNEL_REV = {"mlp": "sgemm:mlp:r3", "lsq": None}
+TRAFFIC = {"sgemm:mlp:r4": 2 * 8495.5 * 1024 + 10240 * 1024}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None}
 
 
 def parse():
