@@ -732,25 +732,47 @@ __global__ __launch_bounds__(NT) void gemm_bf16_k64_kernel(GemmParams g)
         if (kt + 1 < KT) issue(kt + 1);
         const bf16_t* sa = lds + (kt & 1) * STAGE;
         const bf16_t* sb = sa + BM * BK;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        // Fragments of the four 16-deep steps.  With a fused epilogue (GELU,
+        // residual) all of them are read first and the MFMAs follow, the
+        // scheduling barriers keeping the compiler from moving each read down
+        // next to its MFMA (where it waits before every MFMA); with the plain
+        // store epilogue the reads stay per step, which measured faster there.
+        constexpr bool HOIST = EPI != EPI_STORE;
+        constexpr int NF = HOIST ? 4 : 1;
+        bf16x8 af[NF][RB], bfr[NF][CB];
+        auto read_step = [&](int ks, int f) {
             const int lc = 2 * ks + lh;
-            bf16x8 af[RB], bfr[CB];
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int row = wm * WM + i * 32 + lr;
-                af[i] = *reinterpret_cast<const bf16x8*>(sa + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
+                af[f][i] = *reinterpret_cast<const bf16x8*>(sa + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
             }
 #pragma unroll
             for (int j = 0; j < CB; ++j) {
                 const int row = wn * WN + j * 32 + lr;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
+                bfr[f][j] = *reinterpret_cast<const bf16x8*>(sb + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
             }
+        };
+        auto mma_step = [&](int f) {
 #pragma unroll
             for (int i = 0; i < RB; ++i)
 #pragma unroll
                 for (int j = 0; j < CB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
+        };
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) read_step(ks, ks);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) mma_step(ks);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                read_step(ks, 0);
+                mma_step(0);
+            }
         }
         // every wave is done reading this stage before the next issue refills it
         asm volatile("s_barrier" ::: "memory");
