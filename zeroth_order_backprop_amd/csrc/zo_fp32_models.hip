@@ -756,7 +756,7 @@ __global__ __launch_bounds__(NT) void sgemm_kernel(SplitArgs a, EvalList ev)
     };
     // The first k half's rows of blocks.  The second half's fragments are read
     // right behind the first row's MFMAs, so those reads land while the other
-    // rows compute and the second half starts without waiting on LDS (the
+    // rows compute and the second half's single wait rarely stalls (the
     // scheduling barriers keep the compiler from moving the reads back down).
     auto first_half = [&](int st) {
         read_a(st, 0, 0);
