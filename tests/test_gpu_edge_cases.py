@@ -103,3 +103,79 @@ def test_single_probe_step(mode):
     assert g.item() == pytest.approx(og[0], rel=1e-2, abs=1e-3)
     w = model.arena.cpu().numpy().astype(np.float64)
     assert np.abs(w - arena.values()).max() <= 1e-5
+
+
+@pytest.mark.parametrize("pos,val", [(0, -1), (17, 500), (63, 1 << 30), (64 + 5, 999)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_decoder_token_out_of_range_gives_nan(pos, val, fused):
+    """A token id outside [0, vocab) reads nothing out of bounds; the loss of
+    every evaluation that sees it is NaN (first, middle and last position of
+    a sequence; negative and too-large ids), and a step then leaves the
+    weights unchanged."""
+    from test_gpu_decoder import decoder_setup
+    model, b, tok, arena, obatch = decoder_setup()
+    bad = tok.clone()
+    bad.view(-1)[pos] = val
+    bb = zo.make_batch(tokens=bad, batch=2, seq=64)
+    eps = float(np.float32(1e-3))
+    out = torch.zeros(2, dtype=torch.float64, device=DEV)
+    model.forward_loss(bb, out, perts=[(3, 0, eps), (3, 0, -eps)] if fused else None)
+    torch.cuda.synchronize()
+    vals = out.cpu().numpy()[:2 if fused else 1]
+    assert np.isnan(vals).all(), vals
+    before = model.arena.clone()
+    losses = torch.zeros(2, dtype=torch.float64, device=DEV)
+    g = torch.zeros(1, dtype=torch.float64, device=DEV)
+    model.step(bb, 5, 1, 1e-3, 1e-3, zo.ZO_MODE_FUSED if fused else zo.ZO_MODE_INPLACE, losses, g)
+    torch.cuda.synchronize()
+    assert not np.isfinite(g.cpu().numpy()).any()
+    if fused:
+        assert torch.equal(model.arena, before)
+    else:
+        # in place the perturb / restore passes ran and no update followed:
+        # the same three passes on a copy give the same bits
+        ref = before.clone()
+        for sg in (eps, -2 * eps, eps):
+            zo.perturb_buffer(ref, ref.numel(), 0, 5, 0, sg, zo.ZO_BF16)
+        torch.cuda.synchronize()
+        assert torch.equal(model.arena, ref)
+    # the good batch still evaluates to the oracle's loss afterwards
+    good = torch.zeros(1, dtype=torch.float64, device=DEV)
+    model2, b2, _, arena2, obatch2 = decoder_setup()
+    model2.forward_loss(b2, good)
+    torch.cuda.synchronize()
+    assert good.item() == pytest.approx(oracle.model_loss(arena2, obatch2), rel=2e-3)
+
+
+@pytest.mark.parametrize("val", [-1, 10, 77])
+def test_mlp_label_out_of_range_gives_nan(val):
+    """A label outside [0, classes) makes the loss NaN in the stored and the
+    fused evaluations (and so the step skips its update)."""
+    model, inp, arena = _mlp(64, d_in=64, hidden=256)
+    x = torch.from_numpy(inp["X"]).to(DEV)
+    lab = torch.from_numpy(inp["labels"]).to(DEV)
+    lab[13] = val
+    b = zo.make_batch(x=x, labels=lab, batch=64)
+    out = torch.zeros(3, dtype=torch.float64, device=DEV)
+    eps = float(np.float32(1e-3))
+    model.forward_loss(b, out[:1])
+    model.forward_loss(b, out[1:], perts=[(2, 0, eps), (2, 0, -eps)])
+    before = model.arena.clone()
+    losses = torch.zeros(4, dtype=torch.float64, device=DEV)
+    g = torch.zeros(2, dtype=torch.float64, device=DEV)
+    model.step(b, 3, 2, 1e-3, 1e-3, zo.ZO_MODE_FUSED, losses, g)
+    torch.cuda.synchronize()
+    assert np.isnan(out.cpu().numpy()).all()
+    assert torch.equal(model.arena, before)
+
+
+def test_make_batch_rejects_wrong_tensors():
+    x = torch.zeros(8, 4, dtype=torch.float64, device=DEV)
+    with pytest.raises(ValueError):
+        zo.make_batch(x=x, batch=8)
+    tok = torch.zeros(2, 8, dtype=torch.int64, device=DEV)
+    with pytest.raises(ValueError):
+        zo.make_batch(tokens=tok, batch=2, seq=8)
+    tok32 = torch.zeros(8, 2, dtype=torch.int32, device=DEV).t()
+    with pytest.raises(ValueError):
+        zo.make_batch(tokens=tok32, batch=2, seq=8)

@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -79,9 +81,62 @@ KernelTimer::~KernelTimer()
 
 static uint64_t align64(uint64_t x) { return (x + 63) / 64 * 64; }
 
-// Tensors of a model in declaration order (the arena layout).
+// Element count of every tensor of a model, in declaration order; returns the
+// count (no allocation).  Tensor t of a decoder: 0 tok_emb, 1 pos_emb, then per
+// layer ln1_g, ln1_b, w_qkv, w_o, ln2_g, ln2_b, w_up, w_down, then lnf_g, lnf_b.
+static int tensor_sizes(const zo_model_desc* d, uint64_t* sizes, int cap)
+{
+    int n = 0;
+    auto add = [&](uint64_t r, uint64_t c) {
+        if (n < cap) sizes[n] = r * (c ? c : 1);
+        ++n;
+    };
+    switch (d->kind) {
+        case ZO_MODEL_LSQ:
+            add(d->d_in, d->d_out);
+            break;
+        case ZO_MODEL_MLP:
+            add(d->hidden, d->d_in);
+            add(d->classes, d->hidden);
+            break;
+        case ZO_MODEL_DECODER: {
+            const uint64_t D = d->d_model, F = d->ffn;
+            add(d->vocab, D);
+            add(d->max_seq, D);
+            for (int64_t l = 0; l < d->layers; ++l) {
+                add(D, 0); add(D, 0); add(3 * D, D); add(D, D);
+                add(D, 0); add(D, 0); add(F, D); add(D, F);
+            }
+            add(D, 0);
+            add(D, 0);
+            break;
+        }
+    }
+    return n;
+}
+
+// Arena offsets of the tensors (each at a multiple of 64 elements) and the
+// arena length; `offs` holds kMaxTensors entries.  No allocation.
+static int layout_offsets(const zo_model_desc* d, uint64_t* offs, uint64_t& total)
+{
+    const int n = tensor_sizes(d, offs, kMaxTensors);
+    uint64_t off = 0;
+    for (int t = 0; t < n && t < kMaxTensors; ++t) {
+        off = align64(off);
+        const uint64_t sz = offs[t];
+        offs[t] = off;
+        off += sz;
+    }
+    total = align64(off);
+    return n;
+}
+
+// Tensors of a model in declaration order (the arena layout), with names.
 static zo_status build_layout(const zo_model_desc* d, std::vector<zo_param_info>& out, uint64_t& total)
 {
+    uint64_t offs[kMaxTensors];
+    const int n = layout_offsets(d, offs, total);
+    if (n > kMaxTensors) return fail(ZO_ERR_UNSUPPORTED, "too many tensors");
     out.clear();
     auto add = [&](const std::string& name, int64_t r, int64_t c) {
         zo_param_info p;
@@ -90,6 +145,7 @@ static zo_status build_layout(const zo_model_desc* d, std::vector<zo_param_info>
         p.shape[0] = r;
         p.shape[1] = c;
         p.ndim = c > 0 ? 2 : 1;
+        p.offset = offs[out.size()];
         out.push_back(p);
     };
     switch (d->kind) {
@@ -122,13 +178,6 @@ static zo_status build_layout(const zo_model_desc* d, std::vector<zo_param_info>
         default:
             return fail(ZO_ERR_INVALID, "unknown model kind %d", d->kind);
     }
-    uint64_t off = 0;
-    for (auto& p : out) {
-        off = align64(off);
-        p.offset = off;
-        off += (uint64_t)p.shape[0] * (uint64_t)(p.ndim == 2 ? p.shape[1] : 1);
-    }
-    total = align64(off);
     return ZO_OK;
 }
 
@@ -152,6 +201,7 @@ static zo_status validate_desc(const zo_model_desc* d)
                 d->max_seq <= 0 || d->seq <= 0 || d->seq > d->max_seq)
                 return fail(ZO_ERR_INVALID, "decoder sizes must be positive and seq <= max_seq");
             if (d->d_model % d->heads) return fail(ZO_ERR_INVALID, "d_model must divide into heads");
+            if (d->layers > kMaxLayers) return fail(ZO_ERR_UNSUPPORTED, "at most %d layers", kMaxLayers);
             if (d->act != ZO_ACT_GELU && d->act != ZO_ACT_RELU) return fail(ZO_ERR_INVALID, "bad activation");
             break;
         default:
@@ -159,6 +209,38 @@ static zo_status validate_desc(const zo_model_desc* d)
     }
     if (d->dirs != ZO_DIRS_GAUSS && d->dirs != ZO_DIRS_Q8) return fail(ZO_ERR_INVALID, "bad direction kind %d", d->dirs);
     return model_check_shape(*d);
+}
+
+// ------------------------------------------------- model-family dispatch
+zo_status model_check_shape(const zo_model_desc& d)
+{
+    switch (d.kind) {
+        case ZO_MODEL_LSQ: return lsq_check(d);
+        case ZO_MODEL_MLP: return mlp_check(d);
+        case ZO_MODEL_DECODER: return decoder_check(d);
+    }
+    return fail(ZO_ERR_INVALID, "unknown model kind");
+}
+
+size_t model_workspace_bytes(const zo_model_desc& d)
+{
+    switch (d.kind) {
+        case ZO_MODEL_LSQ: return lsq_workspace(d);
+        case ZO_MODEL_MLP: return mlp_workspace(d);
+        case ZO_MODEL_DECODER: return decoder_workspace(d);
+    }
+    return 0;
+}
+
+zo_status model_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n_perts, double* loss,
+                        hipStream_t s)
+{
+    switch (m.desc.kind) {
+        case ZO_MODEL_LSQ: return lsq_forward(m, b, perts, n_perts, loss, s);
+        case ZO_MODEL_MLP: return mlp_forward(m, b, perts, n_perts, loss, s);
+        case ZO_MODEL_DECODER: return decoder_forward(m, b, perts, n_perts, loss, s);
+    }
+    return fail(ZO_ERR_INVALID, "unknown model kind");
 }
 
 static size_t dtype_size(int dtype) { return dtype == ZO_F32 ? 4 : 2; }
@@ -181,6 +263,7 @@ struct zo_model {
     void* workspace;
     size_t ws_bytes;
     std::vector<zo_param_info> layout;
+    std::vector<uint64_t> offsets;
 };
 
 extern "C" {
@@ -288,6 +371,7 @@ zo_status zo_model_create(const zo_model_desc* desc, void* params, uint64_t n_pa
     m->workspace = workspace;
     m->ws_bytes = ws_bytes;
     m->layout = v;
+    for (const auto& p : v) m->offsets.push_back(p.offset);
     *out = m;
     return ZO_OK;
 }
@@ -305,8 +389,7 @@ static ModelView view_of(const zo_model* m)
     v.params = m->params;
     v.workspace = m->workspace;
     v.ws_bytes = m->ws_bytes;
-    v.offsets.reserve(m->layout.size());
-    for (const auto& p : m->layout) v.offsets.push_back(p.offset);
+    v.offsets = m->offsets.data();
     return v;
 }
 
@@ -316,10 +399,9 @@ zo_status zo_perturb(zo_model* m, uint64_t seed, uint32_t probe, float sigma, zo
     return launch_perturb(m->params, m->desc.dtype, m->n_params, 0, seed, probe, sigma, (hipStream_t)s, m->desc.dirs);
 }
 
-static zo_status validate_batch(const zo_model* m, const zo_batch* b)
+static zo_status validate_batch(const zo_model_desc& d, const zo_batch* b)
 {
     if (!b) return fail(ZO_ERR_INVALID, "null batch");
-    const zo_model_desc& d = m->desc;
     if (b->batch <= 0 || b->batch > d.batch) return fail(ZO_ERR_INVALID, "batch size out of range");
     switch (d.kind) {
         case ZO_MODEL_LSQ:
@@ -333,14 +415,19 @@ static zo_status validate_batch(const zo_model* m, const zo_batch* b)
             if (b->seq < 2 || b->seq > d.seq) return fail(ZO_ERR_INVALID, "seq must be in 2..desc.seq");
             break;
     }
-    return model_check_batch(d, *b);
+    // ids live in device memory and are not read here: an id out of range
+    // makes the evaluation's loss NaN on the device instead
+    if (((uintptr_t)b->labels | (uintptr_t)b->tokens) % 4)
+        return fail(ZO_ERR_INVALID, "labels and tokens must be 4-byte aligned int32");
+    if (((uintptr_t)b->x | (uintptr_t)b->y) % 4) return fail(ZO_ERR_INVALID, "x and y must be 4-byte aligned fp32");
+    return ZO_OK;
 }
 
 zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, int32_t n_perts,
                           double* loss_dev, zo_stream s)
 {
     if (!m || !loss_dev) return fail(ZO_ERR_INVALID, "null model or loss buffer");
-    if (zo_status st = validate_batch(m, b)) return st;
+    if (zo_status st = validate_batch(m->desc, b)) return st;
     if (n_perts < 0 || (n_perts > 0 && !perts)) return fail(ZO_ERR_INVALID, "bad perturbation list");
     if (n_perts > kMaxEvalsPerCall) return fail(ZO_ERR_INVALID, "at most %d perturbations per call", kMaxEvalsPerCall);
     if (n_perts > 0 && m->desc.dirs != ZO_DIRS_GAUSS)
@@ -356,62 +443,76 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
                          m->desc.dirs);
 }
 
-zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev, double* g_dev,
-                  zo_stream s)
+static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cfg)
 {
-    if (!m || !cfg || !losses_dev || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
-    if (zo_status st = validate_batch(m, b)) return st;
     const uint32_t N = cfg->n_probes;
     if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
     if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
     if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
     if (cfg->precond != 0 && cfg->precond != 1) return fail(ZO_ERR_INVALID, "precond must be 0 or 1");
     if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
-    if (cfg->mode == ZO_MODE_FUSED && m->desc.dirs != ZO_DIRS_GAUSS)
+    if (cfg->mode == ZO_MODE_FUSED && d.dirs != ZO_DIRS_GAUSS)
         return fail(ZO_ERR_UNSUPPORTED, "fused steps apply Gaussian directions only; use the in-place mode");
-    hipStream_t st = (hipStream_t)s;
-    const ModelView v = view_of(m);
-    const float sig = cfg->eps;
-    const float sig2 = -2.0f * cfg->eps;
+    return ZO_OK;
+}
+
+// The step's launches, after validation (allocates nothing).
+static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch& b, const zo_step_cfg& cfg,
+                          double* losses_dev, double* g_dev, hipStream_t st)
+{
+    const zo_model_desc& d = v.desc;
+    const uint32_t N = cfg.n_probes;
+    const float sig = cfg.eps;
+    const float sig2 = -2.0f * cfg.eps;
     // 1.5-SPSA: the clean evaluation at the stored weights, before any probe
-    if (cfg->precond)
-        if (zo_status r = model_forward(v, *b, nullptr, 0, losses_dev + 2 * N, st)) return r;
-    if (cfg->mode == ZO_MODE_INPLACE) {
+    if (cfg.precond)
+        if (zo_status r = model_forward(v, b, nullptr, 0, losses_dev + 2 * N, st)) return r;
+    if (cfg.mode == ZO_MODE_INPLACE) {
         for (uint32_t i = 0; i < N; ++i) {
-            zo_status r = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st, m->desc.dirs);
+            zo_status r = launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig, st, d.dirs);
             if (r) return r;
-            zo_status f1 = model_forward(v, *b, nullptr, 0, losses_dev + 2 * i, st);
+            zo_status f1 = model_forward(v, b, nullptr, 0, losses_dev + 2 * i, st);
             // the restore sequence always completes once a probe has started
-            zo_status r2 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig2, st, m->desc.dirs);
-            zo_status f2 = f1 ? f1 : model_forward(v, *b, nullptr, 0, losses_dev + 2 * i + 1, st);
-            zo_status r3 = launch_perturb(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, i, sig, st, m->desc.dirs);
+            zo_status r2 = launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig2, st, d.dirs);
+            zo_status f2 = f1 ? f1 : model_forward(v, b, nullptr, 0, losses_dev + 2 * i + 1, st);
+            zo_status r3 = launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig, st, d.dirs);
             if (f1) return f1;
             if (r2) return r2;
             if (f2) return f2;
             if (r3) return r3;
         }
     } else {
-        std::vector<zo_pert> perts(2 * (size_t)N);
-        for (uint32_t i = 0; i < N; ++i) {
-            perts[2 * i] = zo_pert{cfg->seed, i, sig};
-            perts[2 * i + 1] = zo_pert{cfg->seed, i, -sig};
-        }
+        // evaluations (L+_0, L-_0, L+_1, ...) in launches of at most kMaxEvalsPerCall
+        zo_pert perts[kMaxEvalsPerCall];
         for (uint32_t k = 0; k < 2 * N; k += kMaxEvalsPerCall) {
             const int32_t cnt = (int32_t)std::min<uint32_t>(kMaxEvalsPerCall, 2 * N - k);
-            if (zo_status r = model_forward(v, *b, perts.data() + k, cnt, losses_dev + k, st)) return r;
+            for (int32_t e = 0; e < cnt; ++e) {
+                const uint32_t q = k + (uint32_t)e;
+                perts[e] = zo_pert{cfg.seed, q / 2, (q & 1) ? -sig : sig};
+            }
+            if (zo_status r = model_forward(v, b, perts, cnt, losses_dev + k, st)) return r;
         }
     }
-    zo_status r = cfg->precond ? launch_precond(losses_dev, N, cfg->eps, cfg->curv_floor, g_dev, st)
-                               : launch_gscalar(losses_dev, N, cfg->eps, g_dev, st);
+    zo_status r = cfg.precond ? launch_precond(losses_dev, N, cfg.eps, cfg.curv_floor, g_dev, st)
+                              : launch_gscalar(losses_dev, N, cfg.eps, g_dev, st);
     if (r) return r;
-    return launch_update(m->params, m->desc.dtype, m->n_params, 0, cfg->seed, N, g_dev, cfg->lr, st, m->desc.dirs);
+    return launch_update(v.params, d.dtype, n_params, 0, cfg.seed, N, g_dev, cfg.lr, st, d.dirs);
+}
+
+zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double* losses_dev, double* g_dev,
+                  zo_stream s)
+{
+    if (!m || !cfg || !losses_dev || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (zo_status st = validate_batch(m->desc, b)) return st;
+    if (zo_status st = validate_step_cfg(m->desc, cfg)) return st;
+    return run_step(view_of(m), m->n_params, *b, *cfg, losses_dev, g_dev, (hipStream_t)s);
 }
 
 zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg, double* losses_dev,
                         double* g1_dev, double* g2_dev, zo_stream s)
 {
     if (!m || !cfg || !losses_dev || !g1_dev || !g2_dev) return fail(ZO_ERR_INVALID, "null argument");
-    if (zo_status st = validate_batch(m, b)) return st;
+    if (zo_status st = validate_batch(m->desc, b)) return st;
     if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
     if (m->desc.dirs != ZO_DIRS_GAUSS) return fail(ZO_ERR_UNSUPPORTED, "split perturbation uses Gaussian directions");
     if (zo_status st = mlp_split_check(m->desc, (int)cfg->p1, (int)cfg->ps)) return st;
@@ -422,7 +523,7 @@ zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg,
 zo_status zo_step_dust(zo_model* m, const zo_batch* b, const zo_dust_cfg* cfg, double* losses_dev, zo_stream s)
 {
     if (!m || !cfg || !losses_dev) return fail(ZO_ERR_INVALID, "null argument");
-    if (zo_status st = validate_batch(m, b)) return st;
+    if (zo_status st = validate_batch(m->desc, b)) return st;
     if (!(cfg->sigma1 > 0.0f) || !(cfg->sigma2 > 0.0f)) return fail(ZO_ERR_INVALID, "sigma1, sigma2 must be positive");
     if (zo_status st = mlp_dust_check(m->desc, *b, (int)cfg->k1, (int)cfg->k2)) return st;
     return mlp_dust_step(view_of(m), *b, cfg->seed, (int)cfg->k1, (int)cfg->k2, cfg->sigma1, cfg->sigma2, cfg->lr,

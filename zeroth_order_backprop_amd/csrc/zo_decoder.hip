@@ -110,7 +110,9 @@ __device__ __forceinline__ double wave_sumd(double v)
 
 // ============================================================ embedding
 // h[t][c] = bf16(tok_emb[tok[t]][c] + pos_emb[t % S][c]); one block per token.
-__global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restrict__ tokens, int S, int d,
+// A token id outside [0, V) reads nothing and gives its row NaN, so the loss
+// of the evaluation comes out NaN (and a step skips its update).
+__global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restrict__ tokens, int S, int d, int V,
                                                           const bf16_t* __restrict__ tok_emb, uint64_t tok_dir,
                                                           const bf16_t* __restrict__ pos_emb, uint64_t pos_dir,
                                                           Pert p, bf16_t* __restrict__ h)
@@ -118,6 +120,10 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restri
     const int t = blockIdx.x;
     const int tok = tokens[t];
     const int s = t % S;
+    if ((unsigned)tok >= (unsigned)V) {
+        for (int c = threadIdx.x; c < d; c += kThreads) h[(size_t)t * d + c] = (bf16_t)0x7FC0u;
+        return;
+    }
     const uint64_t te = (uint64_t)tok * d, pe = (uint64_t)s * d;
     for (int c = threadIdx.x; c < d; c += kThreads) {
         const float a = weight1(tok_emb, te + c, tok_dir, p);
@@ -416,6 +422,9 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& g, f32x16 (
                         const int col = n0 + wn * WN + j * 32 + lr;
                         if (col == target) g.lm_pick[row] = acc[i][j][r];
                     }
+                    // a target outside the vocabulary gives the row a NaN loss
+                    if ((unsigned)target >= (unsigned)N && tn == 0 && wn == 0 && lr == 0)
+                        g.lm_pick[row] = __builtin_nanf("");
                 }
             }
         __syncthreads();
@@ -1178,7 +1187,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         }
         {
             KernelTimer t("embed", s);
-            embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, P + off(0), off(0), P + off(1), off(1), p, w.h);
+            embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, V, P + off(0), off(0), P + off(1), off(1), p, w.h);
             if (zo_status st = check_launch("embed")) return st;
         }
         for (int l = 0; l < L; ++l) {

@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void mlp_ce_rows(const float* __restrict_
     double v = 0.0;
     if (m < M) {
         const int y = labels[m];
-        double mx = -INFINITY, picked = 0.0;
+        double mx = -INFINITY, picked = (unsigned)y < (unsigned)C ? 0.0 : (double)NAN;  // bad label: NaN loss
 #pragma unroll
         for (int c = 0; c < kMaxClasses; ++c) {
             lg[c] = ((lg_w[0][lane][c] + lg_w[1][lane][c]) + lg_w[2][lane][c]) + lg_w[3][lane][c];
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void split_ce_rows(const float* __restric
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const double se_ = t == 0 ? eps : -eps;
-            double mx = -INFINITY, picked = 0.0;
+            double mx = -INFINITY, picked = (unsigned)y < (unsigned)C ? 0.0 : (double)NAN;  // bad label: NaN loss
 #pragma unroll
             for (int c = 0; c < kMaxClasses; ++c)
                 if (c < C) mx = fmax(mx, lb[c] + se_ * ld[c]);
@@ -1236,7 +1236,7 @@ __global__ __launch_bounds__(kThreads) void dust_rows_kernel(const float* __rest
     __syncthreads();
     if (wave != 0 || m >= M) return;
     const int y = labels[m];
-    double mx = -INFINITY, picked = 0.0;
+    double mx = -INFINITY, picked = (unsigned)y < (unsigned)C ? 0.0 : (double)NAN;  // bad label: NaN loss
 #pragma unroll
     for (int c = 0; c < kMaxClasses; ++c) {
         lg[c] = ((lg_w[0][lane][c] + lg_w[1][lane][c]) + lg_w[2][lane][c]) + lg_w[3][lane][c];
@@ -1282,7 +1282,8 @@ __global__ __launch_bounds__(kThreads) void dust_head_loss_kernel(const double* 
         float b[kMaxClasses];
         logit_draw(key, (uint32_t)i, t, C, b);
         const int y = labels[t];
-        double l[kMaxClasses], mx = -INFINITY, se = 0.0, picked = 0.0;
+        double l[kMaxClasses], mx = -INFINITY, se = 0.0;
+        double picked = (unsigned)y < (unsigned)C ? 0.0 : (double)NAN;  // bad label: NaN loss
         for (int c = 0; c < C; ++c) {
             l[c] = Z[(size_t)t * C + c] + (double)sigma2 * (double)b[c];
             mx = fmax(mx, l[c]);

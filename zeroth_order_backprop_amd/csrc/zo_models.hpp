@@ -12,16 +12,19 @@ namespace zo {
 // Most losses one forward_loss call evaluates (probe-batched fused mode).
 constexpr int kMaxEvalsPerCall = 64;
 
+// Most tensors a model may have: a decoder of up to 255 layers.
+constexpr int kMaxLayers = 255;
+constexpr int kMaxTensors = 4 + 8 * kMaxLayers;
+
 struct ModelView {
     zo_model_desc desc;
     void* params;
     void* workspace;
     size_t ws_bytes;
-    std::vector<uint64_t> offsets;  // arena offset of each tensor, layout order
+    const uint64_t* offsets;  // arena offset of each tensor, layout order (not owned)
 };
 
 zo_status model_check_shape(const zo_model_desc& d);
-zo_status model_check_batch(const zo_model_desc& d, const zo_batch& b);
 size_t model_workspace_bytes(const zo_model_desc& d);
 // perts == nullptr: one loss at the stored weights into loss[0].
 zo_status model_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n_perts,

@@ -302,11 +302,21 @@ class Model:
 
 
 def make_batch(x=None, y=None, labels=None, tokens=None, batch=0, seq=0) -> Batch:
+    """A zo_batch over device tensors: x, y fp32, labels and tokens int32, all
+    contiguous on a GPU.  The returned structure keeps references to the
+    tensors, so they live as long as it does."""
+    import torch
     b = Batch()
-    b.x = None if x is None else x.data_ptr()
-    b.y = None if y is None else y.data_ptr()
-    b.labels = None if labels is None else labels.data_ptr()
-    b.tokens = None if tokens is None else tokens.data_ptr()
+    for name, t, dt in (("x", x, torch.float32), ("y", y, torch.float32), ("labels", labels, torch.int32),
+                        ("tokens", tokens, torch.int32)):
+        if t is None:
+            setattr(b, name, None)
+            continue
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"make_batch: {name} must be a contiguous {dt} tensor on a GPU "
+                             f"(got {t.dtype}, device {t.device}, contiguous={t.is_contiguous()})")
+        setattr(b, name, t.data_ptr())
     b.batch = batch
     b.seq = seq
+    b._keep = (x, y, labels, tokens)
     return b
