@@ -110,3 +110,37 @@ def test_precond_nonfinite_and_bad_config():
     assert not np.isfinite(g.cpu().numpy()).any()
     w = model.arena.cpu().numpy().astype(np.float64)
     assert np.abs(w - arena.values()).max() <= W_ATOL
+
+
+@pytest.mark.parametrize("mode", [zo.ZO_MODE_FUSED, zo.ZO_MODE_INPLACE])
+def test_decoder_precond_step(mode):
+    """1.5-SPSA on the bf16 decoder (ZOO blog, 1.5-SPSA section): the clean
+    loss and the 2N probe losses against the oracle's at the bf16 loss bar;
+    g' equal to the stated formula on the GPU's own losses; and the weights
+    after the update against the oracle's update fed the GPU's g' (the
+    decoder's losses carry bf16 rounding noise, so g' itself is compared
+    through the formula rather than against the oracle's g')."""
+    from test_gpu_decoder import LOSS_RTOL as BF16_RTOL, decoder_setup, from_bf16_dev, ulp_bf16
+    model, batch, keep, arena, obatch = decoder_setup()
+    omode = "fused" if mode == zo.ZO_MODE_FUSED else "inplace"
+    n, eps, lr, floor = 2, 1e-2, 1e-3, 50.0
+    sig = float(np.float32(eps))
+    before = arena.copy()
+    gl, gg = _step(model, batch, 61, n, eps, lr, mode, floor)
+    ol, og = oracle.spsa_step(arena, obatch, seed=61, n_probes=n, eps=eps, lr=lr, mode=omode,
+                              precond=True, curv_floor=floor)
+    np.testing.assert_allclose(gl, ol, rtol=BF16_RTOL)
+    want, h = _precond_from_losses(gl, n, sig, float(np.float32(floor)))
+    np.testing.assert_allclose(gg, want, rtol=1e-12, atol=0)
+    # the update the GPU applied, replayed by the oracle with the GPU's g'
+    ref = before.copy()
+    if mode == zo.ZO_MODE_INPLACE:
+        for i in range(n):
+            for sg in (sig, -2.0 * sig, sig):
+                ref.perturb(61, i, sg)
+    ref.update(61, -float(np.float32(lr)) * gg / n)
+    w = from_bf16_dev(model.arena)
+    wo = ref.values()
+    ulp = ulp_bf16(np.maximum(np.abs(w), np.abs(wo)))
+    assert (np.abs(w - wo) <= 2 * ulp * 1.0001).all()
+    assert np.mean(w == wo) >= 0.999

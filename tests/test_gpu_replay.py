@@ -1,11 +1,20 @@
 """Seed replay on the GPU, through the C ABI: a model trained for a few steps
 is rebuilt bit for bit from its initial weights and the recorded (seed, g_i)
 of each step, with the log written to and read back from disk.  Fused and
-in-place steps, plain and 1.5-SPSA, fp32 (MLP) and bf16 (decoder) arenas."""
+in-place steps, plain and 1.5-SPSA, fp32 (MLP) and bf16 (decoder) arenas.
+
+The same log is also replayed by the CPU oracle from the same initial weights
+(FedSPZO summary, "통신 프로토콜": the server rebuilds the client's model from
+the seeds and the scalar gradients alone): in place the step's 3N perturb /
+restore passes in order, then the update with c_i = -lr g_i / N.  The oracle's
+weights must match the GPU-trained ones to 1e-5 absolute (fp32) or, for bf16,
+bit for bit except at rounding boundaries (GPU directions are within 1e-6 of
+the oracle's, which can move a value that sits at a boundary by one ulp)."""
 import numpy as np
 import pytest
 import torch
 
+from oracle import oracle
 from zeroth_order_backprop_amd import checkpoint, zo
 
 from test_gpu_decoder import decoder_setup
@@ -32,6 +41,31 @@ def _train_and_replay(setup, tmp_path, schedule, n=4, eps=1e-2, lr=1e-3):
     checkpoint.replay(model, checkpoint.StepLog.load(path))
     torch.cuda.synchronize()
     assert torch.equal(model.arena, trained)
+    # the oracle rebuilds the same weights from the log alone
+    rebuilt = oracle_replay(arena.copy(), checkpoint.StepLog.load(path))
+    if rebuilt.dtype == "f32":
+        got = trained.cpu().numpy().astype(np.float64)
+        assert np.abs(got - rebuilt.values()).max() <= 1e-5
+    else:
+        got = oracle.bf16_bits_to_f64(trained.cpu().numpy().view(np.uint16))
+        want = rebuilt.values()
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(got), np.abs(want)), 2.0**-126))) - 7)
+        assert (np.abs(got - want) <= 2 * ulp * 1.0001).all()
+        assert np.mean(got == want) >= 0.999
+
+
+def oracle_replay(arena, log):
+    """The oracle's own replay of a step log: for each step, in place its
+    perturb / restore passes (+eps, -2 eps, +eps per probe, in probe order),
+    then W <- D(W + sum_i c_i z_i) with c_i = -lr g_i / N."""
+    for st in log.steps:
+        n, eps = st["n_probes"], st["eps"]
+        if st["mode"] == zo.ZO_MODE_INPLACE:
+            for i in range(n):
+                for sg in (eps, -2.0 * eps, eps):
+                    arena.perturb(st["seed"], i, sg)
+        arena.update(st["seed"], -st["lr"] * np.asarray(st["g"], np.float64) / n)
+    return arena
 
 
 @pytest.mark.parametrize("mode", [zo.ZO_MODE_FUSED, zo.ZO_MODE_INPLACE])
