@@ -1,15 +1,19 @@
 """Benchmark of the multi-probe SPSA step on one MI355X.
 
-Default workload: the 2-layer MLP classifier in fp32 (1024 -> 4096 GELU -> 10,
-batch 256 synthetic N(0,1) inputs, labels from a fixed random teacher
-projection), N = 16 probes, eps = 1e-3, lr = 1e-3, perturbed-tile (fused)
-mode: every step evaluates 2N = 32 losses and applies one fused update.
+Default workload: the OPT-30B-shaped decoder (48 layers, d = 7168, 56 heads,
+FFN 28672, vocabulary 50272, bf16 random-init weights, 59.94 GB held in place
+in HBM), batch 8 x seq 2048 Zipf(1.1) tokens, causal-LM loss, one SPSA pair
+per step (N = 1, +-eps) in place: perturb +eps, L+, perturb -2 eps, L-,
+perturb +eps, then the fused update -- the in-place, inference-mode OPT-30B
+training step of the ZOO blog ("backprop의 메모리 세금": batch 8, sequence
+2048, about 60 GB).  Other workloads: --workload mlp | lsq | gpt | opt1.3b.
 
 Prints one JSON line: probe-evals/s of the whole step, the dominant kernel's
 roofline (live HIP-event timing of its launches, and only its, over the timed
-region), a per-kernel table from a second instrumented pass, the
-perturb / update passes' HBM GB/s on a 1.3e9-element parameter buffer (the
-OPT-1.3B-shaped count), and the CPU oracle timed on a bounded sample.
+region), a per-kernel table from a second instrumented pass, the step's own
+perturb / update passes in GB/s, the same passes on a 1.3e9-element buffer
+(the OPT-1.3B-shaped count), and the CPU oracle timed on a bounded sample.
+Every timed loss must be finite, else the run fails.
 """
 from __future__ import annotations
 
@@ -46,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="mlp", choices=["mlp", "lsq", "gpt", "opt1.3b", "opt30b"])
+    p.add_argument("--workload", default="opt30b", choices=["mlp", "lsq", "gpt", "opt1.3b", "opt30b"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-passes", action="store_true", help="skip the perturb/update pass measurement")
     p.add_argument("--precond", action="store_true",
@@ -121,15 +125,19 @@ def build_lsq(torch, zo, inputs):
 
 
 DECODERS = {
-    # name: layers, d, heads, ffn, vocab, batch, seq, act, probes
-    "gpt": (12, 768, 12, 3072, 32000, 8, 512, "gelu", 32),
-    "opt1.3b": (24, 2048, 32, 8192, 50272, 8, 2048, "relu", 1),
-    "opt30b": (48, 7168, 56, 28672, 50272, 8, 2048, "relu", 1),
+    # name: layers, d, heads, ffn, vocab, batch, seq, act, probes, lr
+    # lr (the configs give none for the decoders): sized so that one step's
+    # weight change stays about 1e-3 of the weights' norm,
+    # ||dW|| / ||W|| ~ lr ||grad L|| / (0.02 sqrt(N)) with ||grad L|| ~ 10 at
+    # initialisation (the measured spread of g_i), i.e. lr ~ 2e-6 sqrt(N)
+    "gpt": (12, 768, 12, 3072, 32000, 8, 512, "gelu", 32, 1e-5),
+    "opt1.3b": (24, 2048, 32, 8192, 50272, 8, 2048, "relu", 1, 1e-6),
+    "opt30b": (48, 7168, 56, 28672, 50272, 8, 2048, "relu", 1, 1e-6),
 }
 
 
 def build_decoder(torch, zo, inputs, name, dirs="gauss"):
-    L, D, H, F, V, B, S, act, N = DECODERS[name]
+    L, D, H, F, V, B, S, act, N, lr = DECODERS[name]
     desc = zo.make_desc(zo.ZO_MODEL_DECODER, batch=B, seq=S, layers=L, d_model=D, heads=H, ffn=F, vocab=V,
                         max_seq=S, act=zo.ZO_ACT_GELU if act == "gelu" else zo.ZO_ACT_RELU,
                         dirs=zo.ZO_DIRS_Q8 if dirs == "q8" else zo.ZO_DIRS_GAUSS)
@@ -156,9 +164,10 @@ def build_decoder(torch, zo, inputs, name, dirs="gauss"):
     attn_flops = L * 2.0 * B * H * S * S * (D // H)  # causal half of 4 B H S^2 dh
     head_flops = 2.0 * M * D * V
     info = {
-        "workload": f"decoder {name}: {L} layers, d={D}, {H} heads, FFN {F}, vocab {V}, bf16; batch {B} x seq {S} "
-                    f"Zipf(1.1) tokens; N={N} probes, eps=1e-3, lr=1e-3; in-place mode",
-        "probes": N, "eps": 1e-3, "lr": 1e-3, "mode": "inplace", "batch": B, "params": int(total),
+        "workload": f"decoder {name}: {L} layers, d={D}, {H} heads, FFN {F}, vocab {V}, bf16 "
+                    f"({total * 2 / 1e9:.2f} GB of weights in place); batch {B} x seq {S} "
+                    f"Zipf(1.1) tokens; N={N} probes, eps=1e-3, lr={lr:g}; in-place mode",
+        "probes": N, "eps": 1e-3, "lr": lr, "mode": "inplace", "batch": B, "params": int(total),
         "flops_per_eval": gemm_flops + attn_flops + head_flops, "gemm_flops_per_eval": gemm_flops,
         "head_flops_per_eval": head_flops, "attn_flops_per_eval": attn_flops,
         "dtype": "bf16", "kernel": "gemm_bf16", "peak_tflops": BF16_PEAK_TFLOPS,
@@ -249,7 +258,7 @@ def cpu_baseline_probe_parallel(info, seconds=8.0):
     with multiprocessing.get_context("spawn").Pool(procs) as pool:
         res = pool.map(_oracle_probe_worker, jobs)
     rate = sum(2 * r / t for r, t in res)
-    return {"value": round(rate, 3), "unit": "probe-evals/s", "cores": procs, "kind": "oracle",
+    return {"value": round(rate, 3), "unit": "probe-evals/s", "cores": procs, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{procs} processes x {seconds:.0f} s of single-probe oracle steps "
                       f"({sum(r for r, _ in res)} steps in all)"}
 
@@ -329,7 +338,20 @@ def cpu_baseline_variant(info, split=None, dust=None, seconds=12.0):
         t = time.perf_counter() - t0
     counted = "f2-evaluations (4 p1 ps per step)" if split else "draws (k1 + k2 per step)"
     return {"value": round(per * reps / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{reps} oracle {what} of the same workload, single-threaded, {t:.1f} s; counts {counted}"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_decoder(info):
@@ -367,7 +389,8 @@ def cpu_baseline_decoder(info):
     rest = max(times[0] - per_layer, 0.0)
     scale = sh["batch"] * sh["seq"] / s_small
     t_eval = scale * (sh["layers"] * per_layer + rest)
-    return {"value": round(1.0 / t_eval, 6), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+    return {"value": float(f"{1.0 / t_eval:.4g}"), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(), "extrapolated": True,
             "sample": f"extrapolated (forward evaluations only): one forward on 1 x {s_small} tokens with 1 and 2 "
                       f"layers ({times[0]:.2f} s, {times[1]:.2f} s), scaled to {sh['layers']} layers and "
                       f"{sh['batch']} x {sh['seq']} tokens = {t_eval:.0f} s per evaluation, single-threaded"}
@@ -394,6 +417,7 @@ def cpu_baseline(info):
         t = time.perf_counter() - t0
     evals = 2 * probes * reps
     return {"value": round(evals / t, 3), "unit": "probe-evals/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{reps} oracle SPSA step(s) of the same workload with N={probes} probes "
                       f"({evals} evaluations + update), single-threaded, {t:.1f} s",
             "probe_parallel": cpu_baseline_probe_parallel(info)}
@@ -445,15 +469,22 @@ def main():
     else:
         evals_per_step = 4 * split[0] * split[1] if split else 2 * N + pc
         probe_evals_per_step = evals_per_step if split else 2 * N
-    dust_losses = torch.zeros(evals_per_step * info["batch"] if dust else 1, dtype=torch.float64, device="cuda")
-    losses = torch.zeros(evals_per_step, dtype=torch.float64, device="cuda")
-    g = torch.zeros(max(N, split[0] if split else 0), dtype=torch.float64, device="cuda")
+    # every step (warm-up, timed, instrumented) writes its losses and scalars
+    # into its own row, so that all of them can be checked for finiteness
+    # afterwards without adding work to the timed region
+    instr_steps = min(args.steps, 3) if "decoder_shape" in info and info["params"] > 10**10 else args.steps
+    total_steps = args.warmup + args.steps + instr_steps
+    n_loss = evals_per_step * info["batch"] if dust else evals_per_step
+    n_g = max(N, split[0] if split else 0)
+    losses_all = torch.zeros(total_steps, n_loss, dtype=torch.float64, device="cuda")
+    g_all = torch.zeros(total_steps, n_g, dtype=torch.float64, device="cuda")
     g2 = torch.zeros(2 * split[0] * split[1] if split else 1, dtype=torch.float64, device="cuda")
     mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
 
     def step(seed):
+        losses, g = losses_all[seed], g_all[seed]
         if dust:
-            model.step_dust(batch, seed, dust[0], dust[1], 0.05, 0.05, info["lr"], dust_losses)
+            model.step_dust(batch, seed, dust[0], dust[1], 0.05, 0.05, info["lr"], losses)
         elif split:
             model.step_split(batch, seed, split[0], split[1], info["eps"], info["lr"], losses, g, g2)
         else:
@@ -494,12 +525,21 @@ def main():
     i0 = torch.cuda.Event(enable_timing=True)
     i1 = torch.cuda.Event(enable_timing=True)
     i0.record()
-    for t in range(args.steps):
+    for t in range(instr_steps):
         step(args.warmup + args.steps + t)
     i1.record()
     torch.cuda.synchronize()
     zo.timing_enable(False)
-    ms_step_instr = i0.elapsed_time(i1) / args.steps
+    ms_step_instr = i0.elapsed_time(i1) / instr_steps
+    # a non-finite loss would make the update write nothing (and the step
+    # lighter than the method's): fail rather than report such a run
+    all_losses = losses_all.cpu().numpy()
+    all_g = g_all.cpu().numpy()
+    if not (np.isfinite(all_losses).all() and np.isfinite(all_g).all()):
+        bad = [int(t) for t in range(total_steps) if not np.isfinite(all_losses[t]).all()]
+        print(f"bench.py: non-finite losses or scalars at steps {bad}: the run is not a valid measurement",
+              file=sys.stderr)
+        sys.exit(3)
     extra = {}
     bound, peak, unit = "mfma", info["peak_tflops"], "TFLOP/s"
     if dust:
@@ -513,16 +553,20 @@ def main():
         # layer GEMMs of all evaluations: algorithmic flops / summed launch time
         flops_per_launch = evals_per_step * info["gemm_flops_per_eval"] * args.steps / k_n
     elif "split_bf16" in info:
-        # one launch: N direction products X Z_i^T, each fp32 product taken as
-        # six bf16 MFMA products (priced against the bf16 peak), plus the
-        # generation of every direction element it uses
+        # one launch forms the N direction products X Z_i^T (the +- evaluations
+        # of a probe share one, by the first layer's linearity): the method's
+        # fp32 work is 2 M K H flops per direction, priced against the fp32
+        # peak.  The kernel computes each fp32 product as six bf16 MFMA
+        # products; that emulation rate against the bf16 peak is reported
+        # beside it, with the generation of every direction element it uses.
         sp = info["split_bf16"]
         dirs_per_launch = split[0] * args.steps / k_n if split else N
-        flops_per_launch = 6 * dirs_per_launch * sp["direction_flops"]
+        flops_per_launch = dirs_per_launch * sp["direction_flops"]
+        bound, peak, unit = "mfma", FP32_PEAK_TFLOPS, "TFLOP/s"
         # split perturbation: each theta_1 direction's launch also draws 2 ps theta_2 directions
         gauss = dirs_per_launch * (sp["gaussians"] if not split else sp["w1_gaussians"] + 2 * split[1] * sp["w2_gaussians"])
-        extra = {"fp32_equiv_tflops": round(dirs_per_launch * sp["direction_flops"] / k_avg_s / 1e12, 2),
-                 "fp32_equiv_peak": round(BF16_PEAK_TFLOPS / 6, 1),
+        six = 6 * flops_per_launch / k_avg_s / 1e12
+        extra = {"split_bf16_tflops": round(six, 2), "split_bf16_frac_of_bf16_peak": round(six / BF16_PEAK_TFLOPS, 4),
                  "gaussians_per_s": round(gauss / k_avg_s, 1),
                  "valu_frac_generation": round(gauss * C_Z / k_avg_s / VALU_PEAK_LANE_OPS, 4),
                  "c_z": C_Z}
@@ -535,10 +579,22 @@ def main():
                 "perturb"):
         ms, n = zo.timing_query(fam)
         if n and fam not in ("perturb", "update"):
-            fwd_ms += ms / args.steps
+            fwd_ms += ms / instr_steps
         if n:
-            kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / args.steps,
-                            "ms_per_step": round(ms / args.steps, 3)}
+            kernels[fam] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / instr_steps,
+                            "ms_per_step": round(ms / instr_steps, 3)}
+    # the step's own perturbation and update passes over the whole arena
+    # (2 P b bytes each: one read and one write of every parameter)
+    step_passes = {}
+    arena_bytes = info["params"] * (2 if info["dtype"] == "bf16" else 4)
+    for fam in ("perturb", "update"):
+        if fam in kernels:
+            gbs = 2.0 * arena_bytes / (kernels[fam]["avg_us"] * 1e-6) / 1e9
+            step_passes[fam] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                "avg_us": kernels[fam]["avg_us"], "bytes": 2 * arena_bytes,
+                                **({"probes": N} if fam == "update" else {}),
+                                **({"note": "arena resident in the last-level cache (not an HBM figure)"}
+                                   if arena_bytes < 256e6 else {})}
     # forward-only rate: the evaluations of a step over the summed time of the
     # kernels that evaluate (everything but the perturbation and update passes)
     rates = {"step_evals_per_s": round(evals_per_s, 2),
@@ -552,7 +608,7 @@ def main():
         t = kernels["attention"]["ms_per_step"] * 1e-3
         kernels["attention"]["TFLOP/s"] = round(evals_per_step * info["attn_flops_per_eval"] / t / 1e12, 1)
     zo.timing_reset()
-    final = losses.cpu().numpy()
+    timed = all_losses[args.warmup:args.warmup + args.steps]
     line = {
         "metric": METRIC, "value": round(evals_per_s, 2), "unit": "probe-evals/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -582,7 +638,9 @@ def main():
                      "avg_launch_us": round(k_avg_s * 1e6, 2), **extra},
         "rates": rates,
         "kernels": kernels,
-        "last_losses_mean": float(final.mean()),
+        "step_passes": step_passes,
+        "losses": {"first_timed_step_mean": float(timed[0].mean()), "last_timed_step_mean": float(timed[-1].mean()),
+                   "all_finite": True, "steps_checked": total_steps},
     }
     if not args.no_passes:
         line["perturb_update"] = measure_passes(torch, zo)
