@@ -48,7 +48,8 @@ def assert_bf16_close(got, want, frac_exact=0.9, ulps=1.0, abs_tol=0.0):
 
 
 # ------------------------------------------------------------------ GEMM
-@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (300, 200, 128), (4096, 2304, 768), (4096, 4096, 256)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (300, 200, 128), (4096, 2304, 768), (4096, 4096, 256),
+                                   (4100, 4200, 192), (8192, 8192, 1024)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 def test_gemm_bf16(M, N, K, epi):
     rng = np.random.default_rng(M + N + K + epi)

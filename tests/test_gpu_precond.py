@@ -141,6 +141,8 @@ def test_decoder_precond_step(mode):
     ref.update(61, -float(np.float32(lr)) * gg / n)
     w = from_bf16_dev(model.arena)
     wo = ref.values()
-    ulp = ulp_bf16(np.maximum(np.abs(w), np.abs(wo)))
-    assert (np.abs(w - wo) <= 2 * ulp * 1.0001).all()
+    # boundary cases move a value by one ulp of the largest intermediate
+    # (|w| + 2 eps |z| in place, |z| <= 5.8)
+    ulp = ulp_bf16(np.maximum(np.abs(w), np.abs(wo)) + 12.0 * sig)
+    assert (np.abs(w - wo) <= 3 * ulp * 1.0001).all()
     assert np.mean(w == wo) >= 0.999

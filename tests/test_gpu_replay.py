@@ -42,30 +42,42 @@ def _train_and_replay(setup, tmp_path, schedule, n=4, eps=1e-2, lr=1e-3):
     torch.cuda.synchronize()
     assert torch.equal(model.arena, trained)
     # the oracle rebuilds the same weights from the log alone
-    rebuilt = oracle_replay(arena.copy(), checkpoint.StepLog.load(path))
+    log = checkpoint.StepLog.load(path)
+    rebuilt, peak = oracle_replay(arena.copy(), log)
     if rebuilt.dtype == "f32":
         got = trained.cpu().numpy().astype(np.float64)
         assert np.abs(got - rebuilt.values()).max() <= 1e-5
     else:
         got = oracle.bf16_bits_to_f64(trained.cpu().numpy().view(np.uint16))
         want = rebuilt.values()
-        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.maximum(np.abs(got), np.abs(want)), 2.0**-126))) - 7)
-        assert (np.abs(got - want) <= 2 * ulp * 1.0001).all()
+        # GPU directions are within 1e-6 of the oracle's and the GPU rounds
+        # through fp32: a value at a rounding boundary can land one ulp away,
+        # an ulp of the magnitude the value had then (the largest along the
+        # trajectory), which its final magnitude's ulp does not bound
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(peak, 2.0**-126))) - 7)
+        r = np.abs(got - want) / ulp
+        bad = r > 3.0001
+        print(f"bf16 replay: {np.mean(got != want):.2e} of elements differ, max {r.max():.2f} ulp of the peak")
+        assert not bad.any(), (np.nonzero(bad)[0][:8], got[bad][:8], want[bad][:8], peak[bad][:8])
         assert np.mean(got == want) >= 0.999
 
 
 def oracle_replay(arena, log):
     """The oracle's own replay of a step log: for each step, in place its
     perturb / restore passes (+eps, -2 eps, +eps per probe, in probe order),
-    then W <- D(W + sum_i c_i z_i) with c_i = -lr g_i / N."""
+    then W <- D(W + sum_i c_i z_i) with c_i = -lr g_i / N.  Returns the arena
+    and each element's largest magnitude along the way."""
+    peak = np.abs(arena.values())
     for st in log.steps:
         n, eps = st["n_probes"], st["eps"]
         if st["mode"] == zo.ZO_MODE_INPLACE:
             for i in range(n):
                 for sg in (eps, -2.0 * eps, eps):
                     arena.perturb(st["seed"], i, sg)
+                    peak = np.maximum(peak, np.abs(arena.values()))
         arena.update(st["seed"], -st["lr"] * np.asarray(st["g"], np.float64) / n)
-    return arena
+        peak = np.maximum(peak, np.abs(arena.values()))
+    return arena, peak
 
 
 @pytest.mark.parametrize("mode", [zo.ZO_MODE_FUSED, zo.ZO_MODE_INPLACE])

@@ -240,3 +240,25 @@ def test_value_at_equals_range(dirs):
             oracle.lib().oracle_q8_values_at(2**63 + 1, 7, oracle._ptr(np.ascontiguousarray(idx)), n,
                                              oracle._ptr(b), oracle._ptr(oracle._q8()))
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("sigma", [1e-3, -2e-3, 0.37])
+def test_perturb_is_nearest_even_of_exact_value(sigma):
+    """w <- D(w + sigma z) rounded once from the exact value (fp32: the fma;
+    bf16: nearest even of the exact sum), sigma taken at fp32 precision."""
+    rng = np.random.default_rng(31)
+    n, seed, probe, j0 = 3000, 12, 5, 2**35 + 8
+    s32 = float(np.float32(sigma))
+    z = oracle.gauss(seed, probe, j0, n)
+    w = oracle.bf16_round(rng.standard_normal(n) * 0.05)
+    bits = (w.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = bits.copy()
+    oracle.lib().oracle_perturb_bf16(oracle._ptr(got), n, j0, seed, probe, s32)
+    w32 = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    got32 = w32.copy()
+    oracle.lib().oracle_perturb_f32(oracle._ptr(got32), n, j0, seed, probe, s32)
+    sf = Fraction(s32)
+    for t in range(n):
+        zt = Fraction(float(z[t]))
+        assert int(got[t]) == _nearest_even_bf16(Fraction(float(w[t])) + sf * zt), t
+        assert _f32_bits(float(got32[t])) == _nearest_even_f32(Fraction(float(w32[t])) + sf * zt), t
