@@ -239,6 +239,27 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
                   double* g_dev, zo_stream s);
 
 /*
+ * zo_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * validation, kernels and results as zo_step on a model created from `desc`
+ * and `params` (params: the arena, n_params elements of desc->dtype, 256-byte
+ * aligned, exactly the layout's total; device, caller-owned), but no
+ * zo_model, no caller workspace and no allocation of any kind: the model's
+ * workspace is a static 64 MiB device array inside the library, one per GPU,
+ * held until the process ends (its address is looked up once per device, on
+ * the first call with that device current).  Models whose workspace
+ * (zo_workspace_bytes) exceeds 64 MiB are refused with ZO_ERR_WORKSPACE
+ * (e.g. the least-squares and MLP workloads fit; a 12 x 768 decoder at
+ * 8 x 512 tokens does not).  Every call on one GPU uses the same array:
+ * calls that overlap on one GPU (concurrent streams or threads) race and give
+ * undefined results; serialise them.  Nothing in the array needs to start at
+ * zero.  With zo_timing_enable on, the timing bookkeeping allocates host
+ * memory; leave it off here.
+ */
+zo_status zo_step_noalloc(const zo_model_desc* desc, void* params, uint64_t n_params, const zo_batch* b,
+                          const zo_step_cfg* cfg, double* losses_dev, double* g_dev, zo_stream s);
+
+/*
  * One split-perturbation step with activation reuse (FedSPZO summary,
  * section 2 "방법론"), for the MLP with d_in % 32 == 0 and Gaussian
  * directions.  theta_1 = W1 (with the GELU), theta_2 = W2.  For each theta_1

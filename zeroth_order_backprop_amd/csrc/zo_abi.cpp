@@ -252,6 +252,35 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb)
     return pa < pb + nb && pb < pa + na;
 }
 
+// ---------------------------------------------- scratch of zo_step_noalloc
+// Device memory for the workspace of zo_step_noalloc, for callers that cannot
+// allocate: a file-scope array, one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself (on the host that name is only a
+// stand-in); it takes each device's address from hipGetSymbolAddress once,
+// with that device current, and passes that pointer to the kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static zo_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(ZO_ERR_HIP, "hipGetDevice failed");
+    if (dev >= kMaxDevices) return fail(ZO_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail(ZO_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZO_OK;
+}
+
 }  // namespace zo
 
 using namespace zo;
@@ -456,7 +485,8 @@ static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cf
     return ZO_OK;
 }
 
-// The step's launches, after validation (allocates nothing).
+// The step's launches, after validation (shared by zo_step and
+// zo_step_noalloc; allocates nothing).
 static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch& b, const zo_step_cfg& cfg,
                           double* losses_dev, double* g_dev, hipStream_t st)
 {
@@ -506,6 +536,37 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
     if (zo_status st = validate_batch(m->desc, b)) return st;
     if (zo_status st = validate_step_cfg(m->desc, cfg)) return st;
     return run_step(view_of(m), m->n_params, *b, *cfg, losses_dev, g_dev, (hipStream_t)s);
+}
+
+zo_status zo_step_noalloc(const zo_model_desc* desc, void* params, uint64_t n_params, const zo_batch* b,
+                          const zo_step_cfg* cfg, double* losses_dev, double* g_dev, zo_stream s)
+{
+    if (!desc || !params || !cfg || !losses_dev || !g_dev) return fail(ZO_ERR_INVALID, "null argument");
+    if (zo_status st = validate_desc(desc)) return st;
+    uint64_t offs[kMaxTensors];
+    uint64_t total = 0;
+    if (layout_offsets(desc, offs, total) > kMaxTensors) return fail(ZO_ERR_UNSUPPORTED, "too many tensors");
+    if (n_params != total)
+        return fail(ZO_ERR_INVALID, "arena has %llu elements, layout needs %llu", (unsigned long long)n_params,
+                    (unsigned long long)total);
+    if ((uintptr_t)params % 256) return fail(ZO_ERR_INVALID, "params must be 256-byte aligned");
+    const size_t need = model_workspace_bytes(*desc);
+    if (need > kScratchBytes)
+        return fail(ZO_ERR_WORKSPACE, "this model needs %zu bytes of scratch; zo_step_noalloc holds %zu", need,
+                    (size_t)kScratchBytes);
+    if (zo_status st = validate_batch(*desc, b)) return st;
+    if (zo_status st = validate_step_cfg(*desc, cfg)) return st;
+    void* scratch_dev = nullptr;
+    if (zo_status st = scratch_of_current_device(&scratch_dev)) return st;
+    if (overlap(params, n_params * dtype_size(desc->dtype), scratch_dev, kScratchBytes))
+        return fail(ZO_ERR_INVALID, "params overlap the library's scratch");
+    ModelView v;
+    v.desc = *desc;
+    v.params = params;
+    v.workspace = scratch_dev;
+    v.ws_bytes = kScratchBytes;
+    v.offsets = offs;
+    return run_step(v, n_params, *b, *cfg, losses_dev, g_dev, (hipStream_t)s);
 }
 
 zo_status zo_step_split(zo_model* m, const zo_batch* b, const zo_split_cfg* cfg, double* losses_dev,

@@ -19,7 +19,7 @@ ZO_DIRS_GAUSS, ZO_DIRS_Q8 = 0, 1
 
 EXPORTS = [
     "zo_param_layout", "zo_workspace_bytes", "zo_model_create", "zo_model_destroy", "zo_perturb",
-    "zo_forward_loss", "zo_update", "zo_step", "zo_step_split", "zo_step_dust", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
+    "zo_forward_loss", "zo_update", "zo_step", "zo_step_noalloc", "zo_step_split", "zo_step_dust", "zo_replay_step", "zo_perturb_buffer", "zo_update_buffer", "zo_gscalar",
     "zo_debug_rng", "zo_debug_box_muller", "zo_status_str", "zo_last_error",
     "zo_timing_enable", "zo_timing_select", "zo_timing_reset", "zo_timing_query",
     "zo_debug_gemm_bf16", "zo_debug_attention", "zo_debug_layernorm",
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
         "zo_forward_loss": [P, P, P, I32, P, P],
         "zo_update": [P, U64, U32, P, F, P],
         "zo_step": [P, P, P, P, P, P],
+        "zo_step_noalloc": [P, P, U64, P, P, P, P, P],
         "zo_replay_step": [P, P, P, P],
         "zo_step_split": [P, P, P, P, P, P, P],
         "zo_step_dust": [P, P, P, P, P],
@@ -299,6 +300,16 @@ class Model:
             raise ValueError(f"zo_replay_step: g needs {int(n_probes)} entries")
         cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), 0, 0.0)
         check(lib().zo_replay_step(self._h, ctypes.byref(cfg), _ptr(g_dev), _stream(stream)), "zo_replay_step")
+
+
+def step_noalloc(desc: ModelDesc, arena, batch: Batch, seed, n_probes, eps, lr, mode, losses_dev, g_dev,
+                 stream=None, precond=0, curv_floor=0.0):
+    """zo_step_noalloc: one SPSA step on `arena` (device tensor) with the
+    library's static scratch as the workspace; no allocation."""
+    cfg = StepCfg(int(seed), int(n_probes), float(eps), float(lr), int(mode), int(precond), float(curv_floor))
+    check(lib().zo_step_noalloc(ctypes.byref(desc), _ptr(arena), arena.numel(), ctypes.byref(batch),
+                                ctypes.byref(cfg), _ptr(losses_dev), _ptr(g_dev), _stream(stream)),
+          "zo_step_noalloc")
 
 
 def make_batch(x=None, y=None, labels=None, tokens=None, batch=0, seq=0) -> Batch:
