@@ -26,6 +26,12 @@
 #include "zo_models.hpp"
 #include "zo_rng.hpp"
 
+// The buffer-resource direct-to-LDS load (llvm.amdgcn.raw.buffer.load.lds).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void zo_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                       int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace zo {
 namespace {
 
@@ -201,10 +207,10 @@ __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __res
     }
 }
 
-// Wide rows (d > 2048): one 256-thread block per row, NQ groups of 4 per
-// thread (group q = tid + 256 k); the sums are combined across the 4 waves
-// through LDS in a fixed order.
-template <int NQ>
+// Wide rows (d > 2048, d % 8 == 0): one 256-thread block per row, NO groups
+// of 8 per thread (group q = tid + 256 k, one 16-byte load each); the sums
+// are combined across the 4 waves through LDS in a fixed order.
+template <int NO>
 __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* __restrict__ h, int d,
                                                                    const bf16_t* __restrict__ g, uint64_t g_dir,
                                                                    const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
@@ -213,21 +219,26 @@ __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* 
     __shared__ float part[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t t = blockIdx.x;
-    const int nq = d >> 2;
-    const uint2* row = reinterpret_cast<const uint2*>(h + t * d);
-    float v[NQ][4];
+    const int no = d >> 3;
+    const uint4* row = reinterpret_cast<const uint4*>(h + t * d);
+    float v[NO][8];
     float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
+    for (int k = 0; k < NO; ++k) {
         const int q = tid + kThreads * k;
-        if (q < nq) {
-            const uint2 u = row[q];
-            v[k][0] = bf2f(u.x & 0xFFFF); v[k][1] = bf2f(u.x >> 16);
-            v[k][2] = bf2f(u.y & 0xFFFF); v[k][3] = bf2f(u.y >> 16);
+        if (q < no) {
+            const uint4 u = row[q];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[k][2 * e] = bf2f(w[e] & 0xFFFF);
+                v[k][2 * e + 1] = bf2f(w[e] >> 16);
+            }
         } else {
-            v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[k][e] = 0.f;
         }
-        s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+        s += ((v[k][0] + v[k][1]) + (v[k][2] + v[k][3])) + ((v[k][4] + v[k][5]) + (v[k][6] + v[k][7]));
     }
     s = wave_sumf(s);
     if (lane == 0) part[0][wave] = s;
@@ -235,10 +246,10 @@ __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* 
     const float mean = (((part[0][0] + part[0][1]) + part[0][2]) + part[0][3]) / (float)d;
     float q2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-        if (tid + kThreads * k < nq) {
+    for (int k = 0; k < NO; ++k) {
+        if (tid + kThreads * k < no) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 8; ++e) {
                 const float dv = v[k][e] - mean;
                 q2 = fmaf(dv, dv, q2);
             }
@@ -249,31 +260,34 @@ __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* 
     __syncthreads();
     const float var = (((part[1][0] + part[1][1]) + part[1][2]) + part[1][3]) / (float)d;
     const float rstd = 1.0f / sqrtf(var + 1e-5f);
-    uint2* out = reinterpret_cast<uint2*>(x + t * d);
+    uint4* out = reinterpret_cast<uint4*>(x + t * d);
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
+    for (int k = 0; k < NO; ++k) {
         const int q = tid + kThreads * k;
-        if (q >= nq) continue;
-        float o[4];
+        if (q >= no) continue;
+        float o[8];
         if (p.on) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = 4 * q + e;
+            for (int e = 0; e < 8; ++e) {
+                const int c = 8 * q + e;
                 o[e] = fmaf((v[k][e] - mean) * rstd, weight1(g, c, g_dir, p), weight1(b, c, b_dir, p));
             }
         } else {
-            const uint2 gg = reinterpret_cast<const uint2*>(g)[q];
-            const uint2 bb = reinterpret_cast<const uint2*>(b)[q];
-            const float gv[4] = {bf2f(gg.x & 0xFFFF), bf2f(gg.x >> 16), bf2f(gg.y & 0xFFFF), bf2f(gg.y >> 16)};
-            const float bv[4] = {bf2f(bb.x & 0xFFFF), bf2f(bb.x >> 16), bf2f(bb.y & 0xFFFF), bf2f(bb.y >> 16)};
+            const uint4 gg = reinterpret_cast<const uint4*>(g)[q];
+            const uint4 bb = reinterpret_cast<const uint4*>(b)[q];
+            const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w}, bw[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = fmaf((v[k][e] - mean) * rstd, gv[e], bv[e]);
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = fmaf((v[k][2 * e] - mean) * rstd, bf2f(gw[e] & 0xFFFF), bf2f(bw[e] & 0xFFFF));
+                o[2 * e + 1] = fmaf((v[k][2 * e + 1] - mean) * rstd, bf2f(gw[e] >> 16), bf2f(bw[e] >> 16));
+            }
         }
-        out[q] = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+        out[q] = uint4{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
     }
 }
 
-// LayerNorm of `rows` rows of width d (d % 4 == 0, d <= 8192): one wave per
+// LayerNorm of `rows` rows of width d (d % 4 == 0, and d % 8 == 0 above 2048;
+// d <= 8192): one wave per
 // row with the smallest register footprint that holds it (NQ groups of 4 per
 // lane) up to d = 2048, one block per row beyond.
 void launch_layernorm(const bf16_t* h, int rows, int d, const bf16_t* g, uint64_t g_dir, const bf16_t* b,
@@ -284,7 +298,7 @@ void launch_layernorm(const bf16_t* h, int rows, int d, const bf16_t* g, uint64_
     if (nq <= 1) layernorm_kernel<1><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
     else if (nq <= 3) layernorm_kernel<3><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
     else if (nq <= 8) layernorm_kernel<8><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
-    else layernorm_wide_kernel<kLnMaxQuads / 4><<<rows, kThreads, 0, s>>>(h, d, g, g_dir, b, b_dir, p, x);
+    else layernorm_wide_kernel<kLnMaxQuads / 8><<<rows, kThreads, 0, s>>>(h, d, g, g_dir, b, b_dir, p, x);
 }
 
 // ============================================================ bf16 GEMM
@@ -553,9 +567,29 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
 // Barriers are bare s_barrier after each wave has waited (vmcnt) for its own
 // share of a stage, so that later stages stay in flight across them.
 
+// Direct-to-LDS loads through a buffer resource (MUBUF "buffer_load ... lds"):
+// 16 bytes per lane land at the wave-uniform LDS address + 16 x lane.  Unlike
+// the flat-encoded global_load_lds, the compiler counts these on vmcnt alone,
+// so its waits for LDS fragment reads (lgkmcnt) can stay partial.  The
+// resource covers `bytes` bytes from `base` (no stride; loads beyond return
+// zeros) with the raw-buffer configuration word of the gfx9 family.
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)(uint32_t)(a >> 32);  // stride 0
+    r.z = (int)bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
 // vmcnt(n) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
 #define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+// lgkmcnt(n) with vmcnt / expcnt left at their maxima
+#define ZO_WAIT_LGKM(n) __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | ((n) << 8))
 
 // Large tiles: 8 waves (two per SIMD, so one wave's MFMAs cover the other's
 // LDS and barrier waits) in a 4 x 2 grid of 64 x 128 wave tiles; a ring of 5
@@ -570,11 +604,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
 template <int EPI>
 constexpr int dma_stages() { return EPI == EPI_LMHEAD ? 4 : 5; }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g)
+template <int BM, int BN, int EPI, int NT, int WGM>
+__device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 {
     constexpr int BK = 32, STAGES = dma_stages<EPI>();
-    constexpr int NT = kDmaThreads, WGM = kDmaWavesM, WGN = NT / 64 / WGM;
+    constexpr int WGN = NT / 64 / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int RB = WM / 32, CB = WN / 32;
     constexpr int A_INS = BM * 4 / NT, B_INS = BN * 4 / NT;
@@ -585,6 +619,10 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
+    // Load every argument the epilogue reads now: a scalar load still in
+    // flight inside the main loop would force the compiler's fragment-read
+    // waits there to drain every outstanding LDS read (lgkmcnt(0)).
+    asm volatile("" ::"s"(g.C), "s"(g.lm_max), "s"(g.lm_sum), "s"(g.lm_pick), "s"(g.tokens), "s"(g.S));
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     int tm, tn;
     tile_of<4>(blockIdx.x, nbm, nbn, tm, tn);
@@ -600,32 +638,34 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
         for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
 
     const int KT = K / BK;
+    // Stage kt goes to ring slot kt % STAGES.  Stages past the last one
+    // reload the last k range into a slot no wave reads again, so that every
+    // iteration issues the same loads and waits for the same count (a
+    // conditional issue makes the compiler's own wait at the loop's merge
+    // point drain the next stage's fragment reads too).
+    // byte offsets fit in 31 bits (the host refuses larger operands)
+    const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
+    const i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
     auto issue = [&](int kt) {
         bf16_t* sa = lds + (kt % STAGES) * STAGE;
         bf16_t* sb = sa + BM * BK;
-        const int k0 = kt * BK;
+        const int k0 = min(kt, KT - 1) * BK;
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
             const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
+            const int off = (min(m0 + row, M - 1) * K + k0 + 8 * lc) * 2;
             bf16_t* dst = sa + (j * NT + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
-            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            zo_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < B_INS; ++j) {
             const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
+            const int off = (min(n0 + row, N - 1) * K + k0 + 8 * lc) * 2;
             bf16_t* dst = sb + (j * NT + wave * 64) * 8;
-            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
         }
     };
-    static_assert(STAGES >= 3 && STAGES <= 5, "wait_vm covers up to three stages in flight");
-    auto wait_vm = [](int stages_in_flight) {
-        if (stages_in_flight >= 3) ZO_WAIT_VM(3 * INS);
-        else if (stages_in_flight >= 2) ZO_WAIT_VM(2 * INS);
-        else if (stages_in_flight == 1) ZO_WAIT_VM(INS);
-        else ZO_WAIT_VM(0);
-    };
+    static_assert(STAGES >= 3 && STAGES <= 5, "prefetch distance");
     // fragment offsets (elements) of this lane for k-half ks of a stage
     int aoff[2][RB], boff[2][CB];
 #pragma unroll
@@ -658,29 +698,45 @@ __global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
     };
 
-    for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
-    wait_vm(min(STAGES - 2, KT - 1));  // stage 0 landed; the next ones may be in flight
+    for (int st = 0; st < STAGES - 1; ++st) issue(st);
+    ZO_WAIT_VM((STAGES - 2) * INS);  // stage 0 landed; the next ones may be in flight
     asm volatile("s_barrier" ::: "memory");
     read(0, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
+    ZO_WAIT_LGKM0();  // nothing but these reads is outstanding on lgkm at the loop's entry
+    // the scheduling barriers keep each half's fragment reads ahead of the
+    // other half's MFMAs (the compiler would otherwise sink them next to
+    // their first use and wait for them there)
+    for (int kt = 0; kt < KT - 1; ++kt) {
         read(kt, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         mma(0);
-        if (kt + 1 < KT) {
-            // stage kt+1 landed (kt+2 .. kt+STAGES-2 may remain in flight)
-            // and this wave's reads of stage kt are in registers; after the
-            // barrier every wave is done with stage kt-1's buffer, which is
-            // refilled
-            wait_vm(min(STAGES - 3, KT - 2 - kt));
-            ZO_WAIT_LGKM0();
-            asm volatile("s_barrier" ::: "memory");
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-            read(kt + 1, 0, 0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt+1 landed (kt+2 .. kt+STAGES-2 may remain in flight) and
+        // this wave's reads of stage kt are in registers; after the barrier
+        // every wave is done with stage kt-1's slot, which is refilled
+        ZO_WAIT_VM((STAGES - 3) * INS);
+        ZO_WAIT_LGKM0();
+        asm volatile("s_barrier" ::: "memory");
+        issue(kt + STAGES - 1);
+        read(kt + 1, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         mma(1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    read(KT - 1, 1, 1);
+    mma(0);
+    mma(1);
+    ZO_WAIT_VM(0);    // the trailing reloads have landed before the slots are reused
     __syncthreads();  // every wave is done with the stage buffers
     gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g)
+{
+    gemm_dma_body<BM, BN, EPI, kDmaThreads, kDmaWavesM>(g);
+}
+
 
 // Small tiles (128 x 128 or 128 x 64): two BK = 64 stages, NT/64 waves in a
 // WGM x (NT/64/WGM) grid.  LDS rows are 128 B (8 chunks of 16 B),
@@ -855,8 +911,8 @@ __global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __rest
 // of scores pre-scaled by log2(e) / sqrt(dh).
 // Block: 4 waves x 32 queries = 128 queries; keys in tiles of 64.
 template <int DH>
-__global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H,
-                                                              bf16_t* __restrict__ out)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2)))
+void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_t* __restrict__ out)
 {
     constexpr int BQ = 128, BKV = DH == 64 ? 64 : 32;
     constexpr int NB = BKV / 32;  // 32-key blocks per tile
@@ -948,18 +1004,24 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
         __syncthreads();
         if (k0 + BKV < kv_end) load_kv(k0 + BKV);  // in flight during this tile's MFMAs
         if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
-        // S^T [BKV keys][32 queries] as NB 32x32 blocks
-        f32x16 st[NB];
+        // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
+        // head-dim steps in two interleaved chains (even and odd steps), so
+        // that consecutive MFMAs do not wait on each other's results.
+        f32x16 st[NB], sx[NB];
 #pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk) {
-            st[hblk] = f32x16{};
+        for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 kf =
-                    *reinterpret_cast<const bf16x8*>(Ks + (32 * hblk + lr) * LDK + 16 * ks + 8 * lh);
-                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[hblk], 0, 0, 0);
+        for (int ks = 0; ks < KS; ks += 2)
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk) {
+                const bf16_t* kr = Ks + (32 * hblk + lr) * LDK + 16 * ks + 8 * lh;
+                const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr);
+                const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 16);
+                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], st[hblk], 0, 0, 0);
+                sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks + 1], sx[hblk], 0, 0, 0);
             }
-        }
+#pragma unroll
+        for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
         // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
         if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
             const int last = min(myq, S - 1);
@@ -1039,6 +1101,15 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const bf16_t* __res
 // ============================================================ host side
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+void launch_attention(const bf16_t* qkv, int B, int S, int d, int H, int dh, bf16_t* out, hipStream_t s)
+{
+    const int blocks = B * H * cdiv(S, 128);
+    if (dh == 64)
+        attention_kernel<64><<<blocks, kThreads, 0, s>>>(qkv, S, d, H, out);
+    else
+        attention_kernel<128><<<blocks, kThreads, 0, s>>>(qkv, S, d, H, out);
+}
+
 template <int BM, int BN, int EPI, bool PERT>
 zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
@@ -1067,6 +1138,7 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
                                       : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
+        int threads = (big || eight) ? kDmaThreads : kThreads;
         if constexpr (big)
             kern = gemm_bf16_dma_kernel<BM, BN, EPI>;
         else if constexpr (eight)
@@ -1081,7 +1153,7 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
             attr = true;
         }
         KernelTimer timer(fam, s);
-        kern<<<blocks, (big || eight) ? kDmaThreads : kThreads, lds, s>>>(gp);
+        kern<<<blocks, threads, lds, s>>>(gp);
     }
     return check_launch("bf16 GEMM");
 }
@@ -1160,6 +1232,12 @@ zo_status decoder_check(const zo_model_desc& d)
     if (d.d_model % 64 || d.ffn % 64) return fail(ZO_ERR_UNSUPPORTED, "d_model and ffn must be multiples of 64");
     if (d.d_model > 64 * 4 * kLnMaxQuads) return fail(ZO_ERR_UNSUPPORTED, "d_model too large for LayerNorm");
     if (d.batch * d.seq > (1 << 24) || d.vocab > (1 << 24)) return fail(ZO_ERR_UNSUPPORTED, "shape too large");
+    // GEMM operands are addressed with 31-bit byte offsets: activations
+    // [M][D], [M][3D], [M][F]; weights [3D][D], [F][D], [D][F], [V][D]
+    const int64_t M = d.batch * d.seq, D = d.d_model, F = d.ffn;
+    const int64_t widest = std::max(std::max(3 * D, F), (int64_t)d.vocab);
+    if (M * std::max(3 * D, F) * 2 >= (1ll << 31) || widest * D * 2 >= (1ll << 31))
+        return fail(ZO_ERR_UNSUPPORTED, "a GEMM operand exceeds 2 GiB");
     return ZO_OK;
 }
 
@@ -1202,11 +1280,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
             {
                 KernelTimer t("attention", s);
-                const int blocks = B * H * cdiv(S, 128);
-                if (dh == 64)
-                    attention_kernel<64><<<blocks, kThreads, 0, s>>>(w.qkv, S, D, H, w.att);
-                else
-                    attention_kernel<128><<<blocks, kThreads, 0, s>>>(w.qkv, S, D, H, w.att);
+                launch_attention(w.qkv, B, S, D, H, dh, w.att, s);
                 if (zo_status st = check_launch("attention")) return st;
             }
             GemmParams go = {};
@@ -1255,6 +1329,8 @@ zo_status debug_gemm_bf16(const void* A, const void* W, void* C, int M, int N, i
     if (K % 64) return fail(ZO_ERR_UNSUPPORTED, "K must be a multiple of 64");
     if (N % 8) return fail(ZO_ERR_UNSUPPORTED, "N must be a multiple of 8");
     if (((uintptr_t)A | (uintptr_t)W | (uintptr_t)C) & 15) return fail(ZO_ERR_INVALID, "A, W, C must be 16-byte aligned");
+    if ((int64_t)M * K * 2 >= (1ll << 31) || (int64_t)N * K * 2 >= (1ll << 31))
+        return fail(ZO_ERR_UNSUPPORTED, "A and W must each be under 2 GiB");
     GemmParams g = {};
     g.A = (const bf16_t*)A; g.W = (const bf16_t*)W; g.C = (bf16_t*)C; g.M = M; g.N = N; g.K = K;
     Pert p = {};
@@ -1271,19 +1347,19 @@ zo_status debug_attention(const void* qkv, void* out, int B, int S, int H, int d
 {
     if (!qkv || !out || B <= 0 || S <= 0 || H <= 0) return fail(ZO_ERR_INVALID, "bad attention arguments");
     if (dh != 64 && dh != 128) return fail(ZO_ERR_UNSUPPORTED, "head dim must be 64 or 128");
-    const int blocks = B * H * cdiv(S, 128);
+    if ((int64_t)B * S * 3 * H * dh * 2 >= (1ll << 31)) return fail(ZO_ERR_UNSUPPORTED, "qkv must be under 2 GiB");
     KernelTimer t("attention", s);
-    if (dh == 64)
-        attention_kernel<64><<<blocks, kThreads, 0, s>>>((const bf16_t*)qkv, S, H * dh, H, (bf16_t*)out);
-    else
-        attention_kernel<128><<<blocks, kThreads, 0, s>>>((const bf16_t*)qkv, S, H * dh, H, (bf16_t*)out);
+    launch_attention((const bf16_t*)qkv, B, S, H * dh, H, dh, (bf16_t*)out, s);
     return check_launch("attention");
 }
 
 zo_status debug_layernorm(const void* h, const void* g, const void* b, void* x, int rows, int d, hipStream_t s)
 {
     if (!h || !g || !b || !x || rows <= 0 || d <= 0) return fail(ZO_ERR_INVALID, "bad LayerNorm arguments");
-    if (d > 64 * 4 * kLnMaxQuads || d % 4) return fail(ZO_ERR_UNSUPPORTED, "row length must be a multiple of 4, <= 8192");
+    if (d > 64 * 4 * kLnMaxQuads || d % 4 || (d > 2048 && d % 8))
+        return fail(ZO_ERR_UNSUPPORTED, "row length must be a multiple of 4 (of 8 above 2048), <= 8192");
+    if (((uintptr_t)h | (uintptr_t)g | (uintptr_t)b | (uintptr_t)x) & 15)
+        return fail(ZO_ERR_INVALID, "LayerNorm buffers must be 16-byte aligned");
     Pert p = {};
     KernelTimer t("layernorm", s);
     launch_layernorm((const bf16_t*)h, rows, d, (const bf16_t*)g, 0, (const bf16_t*)b, 0, p, (bf16_t*)x, s);
