@@ -505,7 +505,9 @@ static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch&
             // the restore sequence always completes once a probe has started
             zo_status r2 = launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig2, st, d.dirs);
             zo_status f2 = f1 ? f1 : model_forward(v, b, nullptr, 0, losses_dev + 2 * i + 1, st);
-            zo_status r3 = launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig, st, d.dirs);
+            // the last probe's restore is applied together with the update below
+            const bool defer = i + 1 == N && !f1 && !r2 && !f2;
+            zo_status r3 = defer ? ZO_OK : launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, i, sig, st, d.dirs);
             if (f1) return f1;
             if (r2) return r2;
             if (f2) return f2;
@@ -525,6 +527,15 @@ static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch&
     }
     zo_status r = cfg.precond ? launch_precond(losses_dev, N, cfg.eps, cfg.curv_floor, g_dev, st)
                               : launch_gscalar(losses_dev, N, cfg.eps, g_dev, st);
+    if (cfg.mode == ZO_MODE_INPLACE) {
+        // the last probe's restore (+eps) and the update, in one pass; the
+        // restore is written even if the scalars could not be formed
+        if (r) {
+            launch_perturb(v.params, d.dtype, n_params, 0, cfg.seed, N - 1, sig, st, d.dirs);
+            return r;
+        }
+        return launch_restore_update(v.params, d.dtype, n_params, cfg.seed, N, g_dev, cfg.lr, sig, st, d.dirs);
+    }
     if (r) return r;
     return launch_update(v.params, d.dtype, n_params, 0, cfg.seed, N, g_dev, cfg.lr, st, d.dirs);
 }

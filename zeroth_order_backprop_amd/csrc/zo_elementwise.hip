@@ -280,6 +280,126 @@ __global__ __launch_bounds__(kThreads) void update_bf16(uint16_t* __restrict__ w
     update_tail(w, n_full, n, j0, key, p0, n_probes, c);
 }
 
+// ------------------------------------------------- restore fused with update
+// The in-place step ends with the last probe's restore w1 = D(fma(sigma,
+// z_last, w)) followed by the update w2 = D(w1 + sum_i c_i z_i); nothing reads
+// the weights between the two, so one pass applies both: the same two
+// roundings in the same order (bit-identical to the two passes), one read and
+// one write of every weight instead of two each, and z_last generated once
+// (it is one of the update's directions).  When any g_i is not finite only the
+// restore is written, as the two separate passes would leave it.
+template <typename T>
+__device__ __forceinline__ void restore_update_tail(T* __restrict__ w, uint64_t start, uint64_t n, uint64_t j0,
+                                                    Key key, uint32_t n_probes, const float* c, bool ok,
+                                                    float sigma)
+{
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t i = start + threadIdx.x; i < n; i += kThreads) {
+        store_elem(w, i, fmaf(sigma, gauss1(key, n_probes - 1, j0 + i), load_elem(w, i)));
+        if (!ok) continue;
+        float acc = 0.f;
+        for (uint32_t p = 0; p < n_probes; ++p) acc = fmaf(c[p], gauss1(key, p, j0 + i), acc);
+        store_elem(w, i, load_elem(w, i) + acc);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void restore_update_f32(float* __restrict__ w, uint64_t n_full, uint64_t n,
+                                                                uint64_t j0, Key key, uint32_t n_probes,
+                                                                const double* __restrict__ g, float lr, float sigma)
+{
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    const bool ok = load_coeffs(g, n_probes, lr, c, &bad);
+    const uint32_t last = n_probes - 1;
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t ea = base + 4 * threadIdx.x;
+        const uint64_t eb = ea + kElemsPerIter / 2;
+        float4 aa = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+        float4 ra, rb;
+        if (ok) {
+            for (uint32_t i = 0; i < n_probes; ++i) {
+                const float ci = c[i];
+                const float4 za = gauss4(key, i, (j0 + ea) >> 2);
+                const float4 zb = gauss4(key, i, (j0 + eb) >> 2);
+                if (i == last) {
+                    ra = za;
+                    rb = zb;
+                }
+                aa.x = fmaf(ci, za.x, aa.x); aa.y = fmaf(ci, za.y, aa.y);
+                aa.z = fmaf(ci, za.z, aa.z); aa.w = fmaf(ci, za.w, aa.w);
+                ab.x = fmaf(ci, zb.x, ab.x); ab.y = fmaf(ci, zb.y, ab.y);
+                ab.z = fmaf(ci, zb.z, ab.z); ab.w = fmaf(ci, zb.w, ab.w);
+            }
+        } else {
+            ra = gauss4(key, last, (j0 + ea) >> 2);
+            rb = gauss4(key, last, (j0 + eb) >> 2);
+        }
+        float4 wa = *reinterpret_cast<const float4*>(w + ea);
+        float4 wb = *reinterpret_cast<const float4*>(w + eb);
+        wa.x = fmaf(sigma, ra.x, wa.x); wa.y = fmaf(sigma, ra.y, wa.y);
+        wa.z = fmaf(sigma, ra.z, wa.z); wa.w = fmaf(sigma, ra.w, wa.w);
+        wb.x = fmaf(sigma, rb.x, wb.x); wb.y = fmaf(sigma, rb.y, wb.y);
+        wb.z = fmaf(sigma, rb.z, wb.z); wb.w = fmaf(sigma, rb.w, wb.w);
+        if (ok) {
+            wa.x += aa.x; wa.y += aa.y; wa.z += aa.z; wa.w += aa.w;
+            wb.x += ab.x; wb.y += ab.y; wb.z += ab.z; wb.w += ab.w;
+        }
+        *reinterpret_cast<float4*>(w + ea) = wa;
+        *reinterpret_cast<float4*>(w + eb) = wb;
+    }
+    restore_update_tail(w, n_full, n, j0, key, n_probes, c, ok, sigma);
+}
+
+__global__ __launch_bounds__(kThreads) void restore_update_bf16(uint16_t* __restrict__ w, uint64_t n_full,
+                                                                 uint64_t n, uint64_t j0, Key key, uint32_t n_probes,
+                                                                 const double* __restrict__ g, float lr, float sigma)
+{
+    __shared__ float c[kMaxProbes];
+    __shared__ int bad;
+    const bool ok = load_coeffs(g, n_probes, lr, c, &bad);
+    const uint32_t last = n_probes - 1;
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 8 * threadIdx.x;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float4 ra, rb;
+        if (ok) {
+            for (uint32_t i = 0; i < n_probes; ++i) {
+                const float ci = c[i];
+                const float4 za = gauss4(key, i, (j0 + e) >> 2);
+                const float4 zb = gauss4(key, i, ((j0 + e) >> 2) + 1);
+                if (i == last) {
+                    ra = za;
+                    rb = zb;
+                }
+                acc[0] = fmaf(ci, za.x, acc[0]); acc[1] = fmaf(ci, za.y, acc[1]);
+                acc[2] = fmaf(ci, za.z, acc[2]); acc[3] = fmaf(ci, za.w, acc[3]);
+                acc[4] = fmaf(ci, zb.x, acc[4]); acc[5] = fmaf(ci, zb.y, acc[5]);
+                acc[6] = fmaf(ci, zb.z, acc[6]); acc[7] = fmaf(ci, zb.w, acc[7]);
+            }
+        } else {
+            ra = gauss4(key, last, (j0 + e) >> 2);
+            rb = gauss4(key, last, ((j0 + e) >> 2) + 1);
+        }
+        const uint4 v = *reinterpret_cast<const uint4*>(w + e);
+        float f[8];
+        unpack8(v, f);
+        const float zr[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] = fmaf(sigma, zr[t], f[t]);
+        if (ok) {
+            // the restored weights as stored (bf16), then the update
+            const uint4 mid = pack8(f);
+            unpack8(mid, f);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) f[t] += acc[t];
+        }
+        *reinterpret_cast<uint4*>(w + e) = pack8(f);
+    }
+    restore_update_tail(w, n_full, n, j0, key, n_probes, c, ok, sigma);
+}
+
 
 // ------------------------------------------------ 8-bit packed directions
 // One Philox block gives the codes of 16 consecutive elements; each code is
@@ -596,6 +716,28 @@ zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t se
     else
         update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, n, j0, key, p0, n_probes, g, lr);
     return check_launch("update");
+}
+
+zo_status launch_restore_update(void* w, int dtype, uint64_t n, uint64_t seed, uint32_t n_probes, const double* g,
+                                float lr, float sigma, hipStream_t s, int dirs)
+{
+    if (n_probes == 0 || n_probes > kMaxProbes)
+        return fail(ZO_ERR_INVALID, "update: n_probes must be in 1..%u", kMaxProbes);
+    if (dirs != ZO_DIRS_GAUSS) {
+        // 8-bit directions: the two passes
+        if (zo_status st = launch_perturb(w, dtype, n, 0, seed, n_probes - 1, sigma, s, dirs)) return st;
+        return launch_update(w, dtype, n, 0, seed, n_probes, g, lr, s, dirs, 0);
+    }
+    if (n == 0) return ZO_OK;
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    KernelTimer timer("update", s);
+    if (dtype == ZO_F32)
+        restore_update_f32<<<grid_for(n_full), kThreads, 0, s>>>((float*)w, n_full, n, 0, key, n_probes, g, lr, sigma);
+    else
+        restore_update_bf16<<<grid_for(n_full), kThreads, 0, s>>>((uint16_t*)w, n_full, n, 0, key, n_probes, g, lr,
+                                                                  sigma);
+    return check_launch("restore + update");
 }
 
 zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s)

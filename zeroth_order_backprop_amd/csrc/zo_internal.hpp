@@ -36,6 +36,12 @@ zo_status launch_perturb(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t s
 // Directions p0 .. p0 + n_probes - 1 (c_i pairs with direction p0 + i).
 zo_status launch_update(void* w, int dtype, uint64_t n, uint64_t j0, uint64_t seed, uint32_t n_probes,
                         const double* g, float lr, hipStream_t s, int dirs = ZO_DIRS_GAUSS, uint32_t p0 = 0);
+// The in-place step's last restore and its update in one pass over w[0..n)
+// (direction elements 0 .. n-1): w <- D(D(fma(sigma, z_{N-1}, w)) + sum_i c_i
+// z_i), bit-identical to launch_perturb followed by launch_update; when any
+// g_i is not finite only the restore is written.
+zo_status launch_restore_update(void* w, int dtype, uint64_t n, uint64_t seed, uint32_t n_probes, const double* g,
+                                float lr, float sigma, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words,
                            float* z, hipStream_t s);
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);
