@@ -41,8 +41,14 @@ C_Z = 37
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
 # taken on -- set to None when that kernel changes.
-TRAFFIC = {"sgemm:mlp:r4": 2 * 8495.5 * 1024 + 10240 * 1024}
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None}
+TRAFFIC = {
+    "sgemm:mlp:r4": 2 * 8495.5 * 1024 + 10240 * 1024,
+    # the OPT-30B shape's four layer GEMMs (QKV, O, up, down), mean per launch:
+    # FETCH_SIZE x 2 + WRITE_SIZE summed over one of each, divided by four
+    "gemm_bf16:opt30b:r2": (2 * (3.5013 + 1.2040 + 4.5940 + 4.8140) + (0.6563 + 0.2188 + 0.8750 + 0.2188))
+                           * 2**30 / 4,
+}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r2"}
 
 
 def parse():
@@ -61,6 +67,8 @@ def parse():
                         "directions per branch instead of SPSA steps")
     p.add_argument("--dust", default=None, metavar="K1,K2",
                    help="MLP: Dust steps (activation noise) with K1 hidden-layer and K2 head draws")
+    p.add_argument("--mode", default=None, choices=["inplace", "fused"],
+                   help="step mode (default: in place for the decoders, fused for the fp32 models)")
     p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
                    help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
     p.add_argument("--gemm", default=None, metavar="M,N,K",
@@ -448,6 +456,13 @@ def main():
         model, batch, keep, info = build_decoder(torch, zo, inputs, args.workload, args.dirs)
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
+    if args.mode:
+        if args.mode == "fused" and args.dirs != "gauss":
+            print("bench.py: fused steps apply Gaussian directions only", file=sys.stderr)
+            sys.exit(2)
+        info["mode"] = args.mode
+        info["workload"] = info["workload"].rsplit(";", 1)[0] + (
+            "; in-place mode" if args.mode == "inplace" else "; perturbed-tile (fused) mode")
     N = info["probes"]
     pc = 1 if args.precond else 0
     split = None
@@ -627,7 +642,8 @@ def main():
                       if dust else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None if (split or dust) else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
+                     "traffic": None if (split or dust or args.dirs != "gauss" or args.mode == "fused")
+                     else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
                      "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), "
                                  f"{evals_per_step if split else 2 * N} evaluations per step"
                                  if "split_bf16" in info else
