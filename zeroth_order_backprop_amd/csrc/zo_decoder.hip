@@ -703,13 +703,25 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     asm volatile("s_barrier" ::: "memory");
     read(0, 0, 0);
     ZO_WAIT_LGKM0();  // nothing but these reads is outstanding on lgkm at the loop's entry
-    // the scheduling barriers keep each half's fragment reads ahead of the
-    // other half's MFMAs (the compiler would otherwise sink them next to
-    // their first use and wait for them there)
+    // Each half's fragment reads and stage loads are spread one per MFMA
+    // over the other half's MFMAs (scheduling groups: 0x008 MFMA, 0x100 LDS
+    // read, 0x020 global read), so that the wave keeps issuing MFMAs while
+    // they go out; the scheduling barriers fence each half.  Left to itself
+    // the compiler sinks the reads next to their first use and waits there.
+    constexpr int NR = RB + CB, NM = RB * CB;  // fragment reads, MFMAs per half
+    constexpr int PA = NR < NM ? NR : NM;
+    constexpr int PV = INS < NM ? INS : NM;
+    constexpr int PD = NR < NM - PV ? NR : NM - PV;
     for (int kt = 0; kt < KT - 1; ++kt) {
-        read(kt, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
+        read(kt, 1, 1);
         mma(0);
+#pragma unroll
+        for (int i = 0; i < PA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, 0);
         __builtin_amdgcn_sched_barrier(0);
         // stage kt+1 landed (kt+2 .. kt+STAGES-2 may remain in flight) and
         // this wave's reads of stage kt are in registers; after the barrier
@@ -717,10 +729,21 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         ZO_WAIT_VM((STAGES - 3) * INS);
         ZO_WAIT_LGKM0();
         asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         issue(kt + STAGES - 1);
         read(kt + 1, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
         mma(1);
+#pragma unroll
+        for (int i = 0; i < PV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - PV - PD, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     read(KT - 1, 1, 1);
