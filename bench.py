@@ -48,7 +48,7 @@ TRAFFIC = {
     "gemm_bf16:opt30b:r2": (2 * (3.5013 + 1.2040 + 4.5940 + 4.8140) + (0.6563 + 0.2188 + 0.8750 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r3"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r4"}
 
 
 def parse():

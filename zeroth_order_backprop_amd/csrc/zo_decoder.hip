@@ -588,40 +588,34 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 // vmcnt(n) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
 #define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
-// lgkmcnt(n) with vmcnt / expcnt left at their maxima
-#define ZO_WAIT_LGKM(n) __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | ((n) << 8))
 
-// Large tiles: 8 waves (two per SIMD, so one wave's MFMAs cover the other's
-// LDS and barrier waits) in a 4 x 2 grid of 64 x 128 wave tiles; a ring of 5
-// BK = 32 stages (all 160 KB of LDS), prefetch distance 4: the loads' latency
-// is what the waves wait on (measured 2-10% faster than a ring of 4).  The LM
-// head keeps a ring of 4: its epilogue's cross-entropy partials take 4 KB of
-// static LDS besides.  LDS rows are 64 B (4 chunks of 16 B), chunk c of row r
-// at position c ^ ((r >> 2) & 3), so the 32 rows a fragment read touches
-// spread over all banks.  The two k-halves of a stage are read into
-// alternating register sets: the second half's reads and the next stage's
-// first half are issued while the MFMAs of the previous half run.
-template <int EPI>
-constexpr int dma_stages() { return EPI == EPI_LMHEAD ? 4 : 5; }
-
+// Large tiles (256 x 256): 8 waves, two per SIMD so that one wave's MFMAs
+// cover the other's LDS and barrier waits, in a 4 x 2 grid of 64 x 128 wave
+// tiles.  Two BK = 64 stages of (BM + BN) x 64 bf16 fill 128 KB of LDS; every
+// row of a stage is one whole 128-byte line of A or W, so each direct-to-LDS
+// load brings in full lines (BK = 32 stages fetch half lines: twice the
+// requests for the same bytes, measured 4-7 % slower even with a deeper ring).
+// Rows are 8 chunks of 16 B, chunk c of row r at position c ^ ((r >> 1) & 7),
+// so the 32 rows a fragment read touches spread over all banks.  The four
+// k-steps of a stage are read into alternating register sets, each while the
+// previous k-step's MFMAs run; stage kt+2 is loaded into stage kt's buffer
+// right after the barrier that ends every wave's reads of stage kt, so it has
+// one stage of MFMAs to land.
 template <int BM, int BN, int EPI, int NT, int WGM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 {
-    constexpr int BK = 32, STAGES = dma_stages<EPI>();
+    constexpr int BK = 64;
     constexpr int WGN = NT / 64 / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int RB = WM / 32, CB = WN / 32;
-    constexpr int A_INS = BM * 4 / NT, B_INS = BN * 4 / NT;
+    constexpr int A_INS = BM * 8 / NT, B_INS = BN * 8 / NT;
     constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
     constexpr int STAGE = (BM + BN) * BK;
-    static_assert(A_INS * NT == BM * 4 && B_INS * NT == BN * 4, "tile / thread mismatch");
-    static_assert((STAGES - 2) * INS < 64, "vmcnt range");
+    static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
+    static_assert(INS < 64, "vmcnt range");
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
-    // Load every argument the epilogue reads now: a scalar load still in
-    // flight inside the main loop would force the compiler's fragment-read
-    // waits there to drain every outstanding LDS read (lgkmcnt(0)).
     asm volatile("" ::"s"(g.C), "s"(g.lm_max), "s"(g.lm_sum), "s"(g.lm_pick), "s"(g.tokens), "s"(g.S));
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     int tm, tn;
@@ -638,57 +632,54 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
 
     const int KT = K / BK;
-    // Stage kt goes to ring slot kt % STAGES.  Stages past the last one
-    // reload the last k range into a slot no wave reads again, so that every
-    // iteration issues the same loads and waits for the same count (a
-    // conditional issue makes the compiler's own wait at the loop's merge
-    // point drain the next stage's fragment reads too).
-    // byte offsets fit in 31 bits (the host refuses larger operands)
     const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
     const i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int voa[A_INS], vob[B_INS];
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+        const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+        voa[j] = (min(m0 + row, M - 1) * K + 8 * lc) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+        const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+        vob[j] = (min(n0 + row, N - 1) * K + 8 * lc) * 2;
+    }
+    // Stages past the last reload the last k range into the buffer no wave
+    // reads again, so that every iteration issues the same loads.
     auto issue = [&](int kt) {
-        bf16_t* sa = lds + (kt % STAGES) * STAGE;
+        bf16_t* sa = lds + (kt & 1) * STAGE;
         bf16_t* sb = sa + BM * BK;
-        const int k0 = min(kt, KT - 1) * BK;
+        const int koff = min(kt, KT - 1) * BK * 2;
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
-            const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const int off = (min(m0 + row, M - 1) * K + k0 + 8 * lc) * 2;
-            bf16_t* dst = sa + (j * NT + wave * 64) * 8;  // wave-uniform: lane l lands at +16 l bytes
-            zo_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+            bf16_t* dst = sa + (j * NT + wave_u * 64) * 8;  // lane l lands at +16 l bytes
+            zo_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, voa[j], koff, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < B_INS; ++j) {
-            const int p = j * NT + tid, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
-            const int off = (min(n0 + row, N - 1) * K + k0 + 8 * lc) * 2;
-            bf16_t* dst = sb + (j * NT + wave * 64) * 8;
-            zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+            bf16_t* dst = sb + (j * NT + wave_u * 64) * 8;
+            zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, vob[j], koff, 0, 0);
         }
     };
-    static_assert(STAGES >= 3 && STAGES <= 5, "prefetch distance");
-    // fragment offsets (elements) of this lane for k-half ks of a stage
-    int aoff[2][RB], boff[2][CB];
+    // fragment offsets (elements) of this lane for k-step ks of a stage; the
+    // swizzle depends on lr only, so fragments i > 0 sit at fixed offsets
+    int aoff[4], boff[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
         const int lc = 2 * ks + lh;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const int row = wm * WM + i * 32 + lr;
-            aoff[ks][i] = (row * 4 + (lc ^ ((row >> 2) & 3))) * 8;
-        }
-#pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const int row = wn * WN + j * 32 + lr;
-            boff[ks][j] = BM * BK + (row * 4 + (lc ^ ((row >> 2) & 3))) * 8;
-        }
+        const int ra_ = wm * WM + lr, rb_ = wn * WN + lr;
+        aoff[ks] = ra_ * BK + (lc ^ ((ra_ >> 1) & 7)) * 8;
+        boff[ks] = BM * BK + rb_ * BK + (lc ^ ((rb_ >> 1) & 7)) * 8;
     }
     bf16x8 fa[2][RB], fb[2][CB];
     auto read = [&](int kt, int ks, int slot) {
-        const bf16_t* st = lds + (kt % STAGES) * STAGE;
+        const bf16_t* st = lds + (kt & 1) * STAGE;
 #pragma unroll
-        for (int j = 0; j < CB; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks][j]);
+        for (int j = 0; j < CB; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks] + j * 32 * BK);
 #pragma unroll
-        for (int i = 0; i < RB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks][i]);
+        for (int i = 0; i < RB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks] + i * 32 * BK);
     };
     auto mma = [&](int slot) {
 #pragma unroll
@@ -697,68 +688,80 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             for (int j = 0; j < CB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
     };
-
-    for (int st = 0; st < STAGES - 1; ++st) issue(st);
-    ZO_WAIT_VM((STAGES - 2) * INS);  // stage 0 landed; the next ones may be in flight
-    asm volatile("s_barrier" ::: "memory");
-    read(0, 0, 0);
-    ZO_WAIT_LGKM0();  // nothing but these reads is outstanding on lgkm at the loop's entry
-    // Each half's fragment reads and stage loads are spread one per MFMA
-    // over the other half's MFMAs (scheduling groups: 0x008 MFMA, 0x100 LDS
-    // read, 0x020 global read), so that the wave keeps issuing MFMAs while
-    // they go out; the scheduling barriers fence each half.  Left to itself
-    // the compiler sinks the reads next to their first use and waits there.
-    constexpr int NR = RB + CB, NM = RB * CB;  // fragment reads, MFMAs per half
+    // One k-step's MFMAs with the next k-step's fragment reads spread one per
+    // MFMA (scheduling groups: 0x008 MFMA, 0x100 LDS read, 0x020 global read).
+    constexpr int NR = RB + CB, NM = RB * CB;
     constexpr int PA = NR < NM ? NR : NM;
-    constexpr int PV = INS < NM ? INS : NM;
-    constexpr int PD = NR < NM - PV ? NR : NM - PV;
-    for (int kt = 0; kt < KT - 1; ++kt) {
-        __builtin_amdgcn_sched_barrier(0);
-        read(kt, 1, 1);
-        mma(0);
+    constexpr int NV = NM - PA;                              // MFMAs left for the loads
+    constexpr int VPER = NV > 0 ? (INS + NV - 1) / NV : 0;  // loads per such MFMA
+    auto spread_reads = [&]() {
 #pragma unroll
         for (int i = 0; i < PA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, 0);
+    };
+
+    issue(0);
+    ZO_WAIT_VM(0);
+    asm volatile("s_barrier" ::: "memory");
+    read(0, 0, 0);
+    issue(1);
+    ZO_WAIT_LGKM0();
+    for (int kt = 0; kt < KT - 1; ++kt) {
         __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 landed (kt+2 .. kt+STAGES-2 may remain in flight) and
-        // this wave's reads of stage kt are in registers; after the barrier
-        // every wave is done with stage kt-1's slot, which is refilled
-        ZO_WAIT_VM((STAGES - 3) * INS);
+        read(kt, 1, 1);
+        mma(0);
+        spread_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        read(kt, 2, 0);
+        mma(1);
+        spread_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        read(kt, 3, 1);
+        mma(0);
+        spread_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt+1 landed and this wave's reads of stage kt are in
+        // registers; after the barrier no wave reads stage kt's buffer
+        ZO_WAIT_VM(0);
         ZO_WAIT_LGKM0();
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        issue(kt + STAGES - 1);
         read(kt + 1, 0, 0);
+        issue(kt + 2);
         mma(1);
 #pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < PD; ++i) {
+        for (int i = 0; i < PA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - PV - PD, 0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, VPER, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
     read(KT - 1, 1, 1);
     mma(0);
+    read(KT - 1, 2, 0);
     mma(1);
-    ZO_WAIT_VM(0);    // the trailing reloads have landed before the slots are reused
+    read(KT - 1, 3, 1);
+    mma(0);
+    mma(1);
+    ZO_WAIT_VM(0);    // the trailing reload has landed before the buffers are reused
     __syncthreads();  // every wave is done with the stage buffers
     gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kDmaThreads) void gemm_bf16_dma_kernel(GemmParams g)
+template <int BM, int BN, int EPI, int NT, int WGM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 256, NT / 256))) void gemm_bf16_dma_kernel(GemmParams g)
 {
-    gemm_dma_body<BM, BN, EPI, kDmaThreads, kDmaWavesM>(g);
+    gemm_dma_body<BM, BN, EPI, NT, WGM>(g);
 }
+
 
 
 // Small tiles (128 x 128 or 128 x 64): two BK = 64 stages, NT/64 waves in a
@@ -1153,17 +1156,17 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         KernelTimer timer(fam, s);
         kern<<<blocks, kThreads, lds, s>>>(gp, p);
     } else {
-        // 256-wide tiles: a ring of dma_stages<EPI>() BK = 32 stages; 128-wide: 2-stage BK = 64
+        // 256-wide tiles: 8 waves of 64 x 128; 128-wide: 8 waves of 32 x 64,
+        // or 4 of 64 x 64 for the LM head (its cross-entropy epilogue needs
+        // two wave columns); two BK = 64 stages throughout (K % 64 == 0)
         constexpr bool big = BM == 256;
-        // the LM head's cross-entropy epilogue needs two wave columns of 4 waves
         constexpr bool eight = !big && EPI != EPI_LMHEAD;
-        constexpr size_t stages = big ? (size_t)dma_stages<EPI>() * (BM + BN) * 32 * sizeof(bf16_t)
-                                      : (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
+        constexpr size_t stages = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
         int threads = (big || eight) ? kDmaThreads : kThreads;
         if constexpr (big)
-            kern = gemm_bf16_dma_kernel<BM, BN, EPI>;
+            kern = gemm_bf16_dma_kernel<BM, BN, EPI, kDmaThreads, kDmaWavesM>;
         else if constexpr (eight)
             kern = gemm_bf16_k64_kernel<BM, BN, EPI, 512, 4>;
         else
