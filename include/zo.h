@@ -352,7 +352,8 @@ zo_status zo_debug_box_muller(const uint32_t* pairs_dev, uint64_t n_pairs, float
  *    buffers 16-byte aligned (ZO_ERR_UNSUPPORTED / ZO_ERR_INVALID otherwise).
  *  zo_debug_attention: out[B*S][H*dh] = causal softmax(Q K^T / sqrt(dh)) V per
  *    (sequence, head) from qkv[B*S][3*H*dh] (Q, K, V blocks of H*dh columns,
- *    head h at columns h*dh); dh in {64, 128}.
+ *    head h at columns h*dh); dh in {64, 128}; qkv and out 16-byte aligned
+ *    (ZO_ERR_INVALID otherwise), qkv under 2 GiB (ZO_ERR_UNSUPPORTED).
  *  zo_debug_layernorm: x[r] = bf16((h[r] - mean) / sqrt(var + 1e-5) * g + b).
  * The causal attention follows the decoder's definition (scale 1/sqrt(dh),
  * keys at positions <= the query's).

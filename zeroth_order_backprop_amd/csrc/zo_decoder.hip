@@ -331,8 +331,9 @@ template <int G = 8>
 __device__ __forceinline__ void tile_of(int b, int nbm, int nbn, int& tm, int& tn)
 {
     const int total = nbm * nbn;
-    int t = b;
-    if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
+    // blocks go round-robin to the 8 XCDs: each XCD takes a contiguous range
+    const int nx = total / 8, rx = total % 8, xcd = b % 8;
+    const int t = xcd * nx + min(xcd, rx) + b / 8;
     const int group = t / (G * nbn);
     const int first = group * G;
     const int gsize = min(nbm - first, G);
@@ -935,7 +936,45 @@ __global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __rest
 // order over keys is the same permutation on both operands).  P is rounded to
 // bf16 for the MFMA; max, sums and rescaling are fp32, exponentials are exp2
 // of scores pre-scaled by log2(e) / sqrt(dh).
-// Block: 4 waves x 32 queries = 128 queries; keys in tiles of 64.
+// Block: 4 waves x 32 queries = 128 queries; keys in tiles of BKV.  K and V
+// tiles go straight from global memory into a ring of NSLOT LDS slots
+// (buffer-resource direct-to-LDS loads, NSLOT - 1 tiles ahead, one barrier
+// per tile), both key-major as in qkv; the V^T operand is read with the
+// transposing LDS read ds_read_b64_tr_b16: within each 16-lane group, lane
+// 4 q + r receives element r of the 8 bytes read by lanes q, 4 + q, 8 + q and
+// 12 + q (lane 4 e + q reads key e, head-dim columns 4 q .. 4 q + 3, so lane
+// 4 q + r gets keys 0..3 of column 4 q + r).  Rows are 16-byte chunks, chunk
+// c of row r at position c ^ (2 (r & 3) + ((r >> 2) & 1)): a K fragment read
+// (8 consecutive rows, one chunk) and a V^T read (4 consecutive rows, two
+// chunks) each touch every bank once.
+__device__ __forceinline__ int att_swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// Eight transposing LDS reads and the wait for them in one asm statement, so
+// that no register they write is reused before its data lands.  (Through the
+// builtin, the compiler waits for every direct-to-LDS load in flight, the
+// next tiles' included, before each such read.)
+__device__ __forceinline__ void ds_read_tr8(uint2 (&v)[8], const uint32_t (&a)[8])
+{
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
 template <int DH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2)))
 void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_t* __restrict__ out)
@@ -944,15 +983,23 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
     constexpr int NB = BKV / 32;  // 32-key blocks per tile
     constexpr int KS = DH / 16;   // MFMA k-steps over the head dim for S^T
     constexpr int OT = DH / 32;   // 32-row blocks of O^T
-    constexpr int LDK = DH + 8;   // K tile row (bf16), padded
-    constexpr int LDV = BKV + 4;  // V^T tile row (bf16): 8 rows apart = 16 banks apart
-    __shared__ __align__(16) bf16_t Ks[BKV * LDK];
-    __shared__ __align__(16) bf16_t Vt[DH * LDV];
+    constexpr int ROWB = DH * 2;  // bytes of a K or V row
+    // ring depth: d_h 128 takes 4 slots (64 KB, 2 blocks per CU as its registers
+    // allow anyway), d_h 64 keeps 3 (48 KB: 3 blocks per CU)
+    constexpr int TILEB = BKV * ROWB, SLOTB = 2 * TILEB, NSLOT = DH == 128 ? 4 : 3;
+    constexpr int LOADS = TILEB / 1024 / 4;  // 1 KB wave loads per wave per tile, each of K and V
+    static_assert(LOADS * 4 * 1024 == TILEB, "tile / wave mismatch");
+    __shared__ __align__(16) unsigned char lds[NSLOT * SLOTB];
 
     const int qblocks = (S + BQ - 1) / BQ;
+    // Blocks go round-robin to the 8 XCDs; renumbered so that each XCD runs a
+    // contiguous range, every query block of a (sequence, head) shares one
+    // L2 for its K and V (about a quarter faster than spreading them).
+    const int nx = gridDim.x / 8, rx = gridDim.x % 8, xcd = blockIdx.x % 8;
+    const int lb = xcd * nx + min(xcd, rx) + blockIdx.x / 8;
     // heaviest (latest) query blocks first
-    const int qb = qblocks - 1 - (blockIdx.x % qblocks);
-    const int bh = blockIdx.x / qblocks;
+    const int qb = qblocks - 1 - (lb % qblocks);
+    const int bh = lb / qblocks;
     const int b = bh / H, hd = bh % H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lh = lane >> 5;
@@ -979,57 +1026,60 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
     float m_run = -INFINITY, l_run = 0.f;  // in log2 units
 
     const int kv_end = min(S, q0 + BQ);  // causal: keys < last query of the block
-    // Each thread stages CH (key pair, 8-column) chunks of K and V per tile:
-    // keys 2 kp and 2 kp + 1, head-dim columns dc .. dc + 7.  The next tile's
-    // chunks are loaded into registers while the current tile is computed.
-    // K chunks go to LDS as 16-byte row pieces, so dc runs fastest across the
-    // lanes (one row's bytes contiguous); V goes in transposed as 4-byte key
-    // pairs, so there kp runs fastest (consecutive lanes, consecutive words:
-    // with dc fastest the lanes of one key pair hit one bank).
-    constexpr int CH = (BKV / 2) * (DH / 8) / kThreads;
-    static_assert(CH * kThreads == (BKV / 2) * (DH / 8), "tile / thread mismatch");
-    uint4 rk[CH][2], rv[CH][2];
-    auto load_kv = [&](int k0) {
+    const int ntiles = (kv_end + BKV - 1) / BKV;
+    // Wave load j fills 1 KB block wave * LOADS + j of the K (V) tile, lane l
+    // its bytes 16 l .. 16 l + 15.  The resource ends at the sequence's last
+    // row: rows past S read as zeros (masked keys, multiplied by P = 0).
+    const i32x4_t rs = buffer_rsrc(base, (uint32_t)((size_t)S * row_stride * 2));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int lrow[LOADS], lcol[LOADS];
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int cc = tid + j * kThreads;
-            const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
-            const int kpv = cc % (BKV / 2), dcv = 8 * (cc / (BKV / 2));
+    for (int j = 0; j < LOADS; ++j) {
+        const int byte = (wave * LOADS + j) * 1024 + 16 * lane;
+        const int row = byte / ROWB, pos = (byte % ROWB) / 16;
+        lrow[j] = row;
+        lcol[j] = 16 * (pos ^ att_swz(row));
+    }
+    // Tiles past the last reload rows no wave reads, so that every iteration
+    // issues the same loads and waits for the same count.
+    auto issue = [&](int t) {
+        unsigned char* sk = lds + (t % NSLOT) * SLOTB;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int key = k0 + 2 * kp + e, keyv = k0 + 2 * kpv + e;
-                rk[j][e] = rv[j][e] = uint4{0u, 0u, 0u, 0u};
-                if (key < S) rk[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)key * row_stride + koff + dc);
-                if (keyv < S) rv[j][e] = *reinterpret_cast<const uint4*>(base + (size_t)keyv * row_stride + voff + dcv);
-            }
+        for (int j = 0; j < LOADS; ++j) {
+            const uint32_t ro = (uint32_t)(t * BKV + lrow[j]) * (uint32_t)(row_stride * 2) + lcol[j];
+            unsigned char* dk = sk + (wave_u * LOADS + j) * 1024;
+            zo_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dk, 16, ro + 2 * koff, 0, 0, 0);
+            zo_raw_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dk + TILEB), 16, ro + 2 * voff, 0,
+                                   0, 0);
         }
     };
-    auto store_kv = [&]() {
+    // this lane's read offsets in a slot: K rows 32 hblk + lr, chunk 2 ks + lh;
+    // V^T: key row (lane & 15) >> 2 of its group's four, columns 4 (lane & 3)
+    const int ksw = att_swz(lr);
+    const int g = lane >> 4, ve = (lane & 15) >> 2, vq = lane & 3;
+    const int vrow = 4 * (g >> 1) + ve, vsw = att_swz(vrow);
+    const int vhalf = 8 * (vq & 1);
+    int vcol[OT];
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int cc = tid + j * kThreads;
-            const int kp = cc / (DH / 8), dc = 8 * (cc % (DH / 8));
-            const int kpv = cc % (BKV / 2), dcv = 8 * (cc / (BKV / 2));
-            *reinterpret_cast<uint4*>(Ks + (2 * kp) * LDK + dc) = rk[j][0];
-            *reinterpret_cast<uint4*>(Ks + (2 * kp + 1) * LDK + dc) = rk[j][1];
-            // V^T: column pair (2 kpv, 2 kpv + 1) of row dcv + e, one 4-byte write each
-            const uint32_t a[4] = {rv[j][0].x, rv[j][0].y, rv[j][0].z, rv[j][0].w};
-            const uint32_t b4[4] = {rv[j][1].x, rv[j][1].y, rv[j][1].z, rv[j][1].w};
+    for (int t = 0; t < OT; ++t) vcol[t] = 16 * ((4 * t + 2 * (g & 1) + (vq >> 1)) ^ vsw) + vhalf;
+
+    for (int t = 0; t < NSLOT - 1; ++t) issue(t);
+    // Q in registers before the loop: a wait for it there is partial (the
+    // tiles' loads were issued after it), at the loop's entry it would be total
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint32_t*>(Vt + (dcv + 2 * e) * LDV + 2 * kpv) = (a[e] & 0xFFFFu) | (b4[e] << 16);
-                *reinterpret_cast<uint32_t*>(Vt + (dcv + 2 * e + 1) * LDV + 2 * kpv) =
-                    (a[e] >> 16) | (b4[e] & 0xFFFF0000u);
-            }
-        }
-    };
-    load_kv(0);
-    for (int k0 = 0; k0 < kv_end; k0 += BKV) {
-        __syncthreads();  // every wave is done with the previous tile
-        store_kv();
-        __syncthreads();
-        if (k0 + BKV < kv_end) load_kv(k0 + BKV);  // in flight during this tile's MFMAs
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int it = 0; it < ntiles; ++it) {
+        const int k0 = it * BKV;
+        // this wave's part of tile it landed (the later tiles may be in
+        // flight); after the barrier every part has, and no wave still reads
+        // the slot of tile it - 1, which is refilled
+        ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
+        ZO_WAIT_LGKM0();
+        asm volatile("s_barrier" ::: "memory");
+        issue(it + NSLOT - 1);
         if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
+        const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
+        const unsigned char* sv = sk + TILEB;
         // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
         // head-dim steps in two interleaved chains (even and odd steps), so
         // that consecutive MFMAs do not wait on each other's results.
@@ -1040,9 +1090,9 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         for (int ks = 0; ks < KS; ks += 2)
 #pragma unroll
             for (int hblk = 0; hblk < NB; ++hblk) {
-                const bf16_t* kr = Ks + (32 * hblk + lr) * LDK + 16 * ks + 8 * lh;
-                const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr);
-                const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 16);
+                const unsigned char* kr = sk + (32 * hblk + lr) * ROWB;
+                const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + lh) ^ ksw));
+                const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + 2 + lh) ^ ksw));
                 st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], st[hblk], 0, 0, 0);
                 sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks + 1], sx[hblk], 0, 0, 0);
             }
@@ -1098,22 +1148,36 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         }
         // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
         // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
-        // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4
+        // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
+        // dh = 32 t + lr) takes the same keys in the same order, from two
+        // transposing reads of four keys each (keys +0..3 and +8..11)
+        constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
 #pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk)
+        for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
+            uint32_t a[8];
+            uint2 v[8];
 #pragma unroll
-            for (int sblk = 0; sblk < 2; ++sblk)
+            for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+                for (int t = 0; t < OT; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t]);
+            ds_read_tr8(v, a);
+#pragma unroll
+            for (int u = 0; u < STEPS; ++u) {
+                const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
 #pragma unroll
                 for (int t = 0; t < OT; ++t) {
-                    // A = V^T rows dh = 32 t + lr, the same 8 keys in the same order
-                    const bf16_t* vr = Vt + (32 * t + lr) * LDV + 32 * hblk + 16 * sblk + 4 * lh;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                    const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
                     const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
                     const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
                     o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
                 }
+            }
+        }
     }
+    ZO_WAIT_VM(0);  // no load may land in LDS after the block ends
     if (myq >= S) return;
     const float inv = 1.0f / l_run;
     // O^T element r of block t: dh 32 t + 8 (r/4) + 4 lh + r%4, query myq
@@ -1374,6 +1438,7 @@ zo_status debug_attention(const void* qkv, void* out, int B, int S, int H, int d
     if (!qkv || !out || B <= 0 || S <= 0 || H <= 0) return fail(ZO_ERR_INVALID, "bad attention arguments");
     if (dh != 64 && dh != 128) return fail(ZO_ERR_UNSUPPORTED, "head dim must be 64 or 128");
     if ((int64_t)B * S * 3 * H * dh * 2 >= (1ll << 31)) return fail(ZO_ERR_UNSUPPORTED, "qkv must be under 2 GiB");
+    if (((uintptr_t)qkv | (uintptr_t)out) & 15) return fail(ZO_ERR_INVALID, "qkv and out must be 16-byte aligned");
     KernelTimer t("attention", s);
     launch_attention((const bf16_t*)qkv, B, S, H * dh, H, dh, (bf16_t*)out, s);
     return check_launch("attention");
