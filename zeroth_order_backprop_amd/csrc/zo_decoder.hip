@@ -1083,18 +1083,25 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
         // head-dim steps in two interleaved chains (even and odd steps), so
         // that consecutive MFMAs do not wait on each other's results.
+        // All of the tile's K fragments are read first (one LDS round trip
+        // instead of one per MFMA: left alone, the compiler waits before each)
         f32x16 st[NB], sx[NB];
+        bf16x8 kf[NB][KS];
+#pragma unroll
+        for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[hblk][ks] =
+                    *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2)
 #pragma unroll
             for (int hblk = 0; hblk < NB; ++hblk) {
-                const unsigned char* kr = sk + (32 * hblk + lr) * ROWB;
-                const bf16x8 k0f = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + lh) ^ ksw));
-                const bf16x8 k1f = *reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * ks + 2 + lh) ^ ksw));
-                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[ks], st[hblk], 0, 0, 0);
-                sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1f, qf[ks + 1], sx[hblk], 0, 0, 0);
+                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
+                sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
             }
 #pragma unroll
         for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
