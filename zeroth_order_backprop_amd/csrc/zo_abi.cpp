@@ -64,6 +64,8 @@ hipEvent_t take_event()
 }
 }  // namespace
 
+bool timing_active() { return g_timing; }
+
 KernelTimer::KernelTimer(const char* family, hipStream_t s) : slot_(-1), s_(s)
 {
     if (!g_timing || (!g_timing_family.empty() && g_timing_family != family)) return;
@@ -293,6 +295,7 @@ struct zo_model {
     size_t ws_bytes;
     std::vector<zo_param_info> layout;
     std::vector<uint64_t> offsets;
+    void* graphs = nullptr;  // captured decoder forwards (decoder_graphs_free)
 };
 
 extern "C" {
@@ -407,11 +410,12 @@ zo_status zo_model_create(const zo_model_desc* desc, void* params, uint64_t n_pa
 
 zo_status zo_model_destroy(zo_model* m)
 {
+    if (m) decoder_graphs_free(m->graphs);
     delete m;
     return ZO_OK;
 }
 
-static ModelView view_of(const zo_model* m)
+static ModelView view_of(zo_model* m)
 {
     ModelView v;
     v.desc = m->desc;
@@ -419,6 +423,7 @@ static ModelView view_of(const zo_model* m)
     v.workspace = m->workspace;
     v.ws_bytes = m->ws_bytes;
     v.offsets = m->offsets.data();
+    v.graphs = &m->graphs;
     return v;
 }
 

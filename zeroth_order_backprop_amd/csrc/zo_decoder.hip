@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <new>
+#include <vector>
 #include <math.h>
 #include <string.h>
 
@@ -1340,17 +1342,159 @@ zo_status decoder_check(const zo_model_desc& d)
 
 size_t decoder_workspace(const zo_model_desc& d) { return carve(d, nullptr).bytes; }
 
-zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
-                          hipStream_t s)
+// ---- captured forwards ----
+// A forward at the stored weights is the same ~90 launches for every
+// evaluation of a step; captured once into a HIP graph and replayed, the
+// launches reach the GPU together instead of one by one (between small
+// kernels the GPU otherwise idles several microseconds per launch).  One
+// entry per (tokens, batch, seq): the graph reads the weights, workspace and
+// tokens through the pointers it was captured with.  The first evaluation of
+// a key runs eagerly (every one-time set-up done), the second captures.
+namespace {
+struct FwdGraph {
+    const int32_t* tokens;
+    int64_t batch, seq;
+    hipGraphExec_t exec;  // null: seen once, not captured yet
+};
+struct GraphCache {
+    std::vector<FwdGraph> entries;
+    hipStream_t capture = nullptr;
+};
+constexpr size_t kMaxGraphs = 8;
+
+}  // namespace
+
+void decoder_graphs_free(void* cache)
+{
+    auto* gc = static_cast<GraphCache*>(cache);
+    if (!gc) return;
+    for (auto& f : gc->entries)
+        if (f.exec) hipGraphExecDestroy(f.exec);
+    if (gc->capture) hipStreamDestroy(gc->capture);
+    delete gc;
+}
+
+namespace {
+
+// The launches of one evaluation up to the per-row cross-entropy partials.
+zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Pert& p, const DecoderWs& w,
+                                hipStream_t s)
 {
     const zo_model_desc& d = m.desc;
     const int B = (int)b.batch, S = (int)b.seq, D = (int)d.d_model, F = (int)d.ffn, V = (int)d.vocab;
     const int H = (int)d.heads, dh = D / H, L = (int)d.layers;
     const int M = B * S;
-    DecoderWs w = carve(d, m.workspace);
     const bf16_t* P = (const bf16_t*)m.params;
     // tensor order: tok_emb, pos_emb, per layer (ln1_g, ln1_b, w_qkv, w_o, ln2_g, ln2_b, w_up, w_down), lnf_g, lnf_b
     auto off = [&](int idx) { return m.offsets[idx]; };
+    {
+        KernelTimer t("embed", s);
+        embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, V, P + off(0), off(0), P + off(1), off(1), p, w.h);
+        if (zo_status st = check_launch("embed")) return st;
+    }
+    for (int l = 0; l < L; ++l) {
+        const int t0 = 2 + 8 * l;
+        {
+            KernelTimer t("layernorm", s);
+            launch_layernorm(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p, w.x, s);
+            if (zo_status st = check_launch("layernorm")) return st;
+        }
+        GemmParams gq = {};
+        gq.A = w.x; gq.W = P + off(t0 + 2); gq.w_dir = off(t0 + 2); gq.C = w.qkv; gq.M = M; gq.N = 3 * D; gq.K = D;
+        if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
+        {
+            KernelTimer t("attention", s);
+            launch_attention(w.qkv, B, S, D, H, dh, w.att, s);
+            if (zo_status st = check_launch("attention")) return st;
+        }
+        GemmParams go = {};
+        go.A = w.att; go.W = P + off(t0 + 3); go.w_dir = off(t0 + 3); go.C = w.h; go.M = M; go.N = D; go.K = D;
+        if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
+        {
+            KernelTimer t("layernorm", s);
+            launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s);
+            if (zo_status st = check_launch("layernorm")) return st;
+        }
+        GemmParams gu = {};
+        gu.A = w.x; gu.W = P + off(t0 + 6); gu.w_dir = off(t0 + 6); gu.C = w.u; gu.M = M; gu.N = F; gu.K = D;
+        zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16")
+                                            : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16");
+        if (su) return su;
+        GemmParams gd = {};
+        gd.A = w.u; gd.W = P + off(t0 + 7); gd.w_dir = off(t0 + 7); gd.C = w.h; gd.M = M; gd.N = D; gd.K = F;
+        if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16")) return st;
+    }
+    const int tf = 2 + 8 * L;
+    {
+        KernelTimer t("layernorm", s);
+        launch_layernorm(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x, s);
+        if (zo_status st = check_launch("layernorm")) return st;
+    }
+    GemmParams gl = {};
+    gl.A = w.x; gl.W = P + off(0); gl.w_dir = off(0); gl.M = M; gl.N = V; gl.K = D;
+    gl.lm_max = w.lm_max; gl.lm_sum = w.lm_sum; gl.lm_pick = w.lm_pick; gl.tokens = b.tokens; gl.S = S;
+    if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
+    {
+        KernelTimer t("reduce", s);
+        const int lm_tiles = cdiv(V, gemm_tile_n(M, V, p.on != 0, EPI_LMHEAD));
+        ce_rows_kernel<<<cdiv(M, 64), kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, lm_tiles, M, S, w.ce_part);
+        if (zo_status st = check_launch("ce rows")) return st;
+    }
+    return ZO_OK;
+}
+
+// The captured forward for this batch, or null when the evaluation should
+// run eagerly (first sight of the batch).
+zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& w, hipGraphExec_t* out)
+{
+    *out = nullptr;
+    auto*& gc = reinterpret_cast<GraphCache*&>(*m.graphs);
+    if (!gc) {
+        gc = new (std::nothrow) GraphCache;
+        if (!gc) return fail(ZO_ERR_INVALID, "out of host memory");
+    }
+    for (auto& f : gc->entries)
+        if (f.tokens == b.tokens && f.batch == (int64_t)b.batch && f.seq == (int64_t)b.seq) {
+            if (f.exec) {
+                *out = f.exec;
+                return ZO_OK;
+            }
+            // seen once: capture now
+            if (!gc->capture && hipStreamCreateWithFlags(&gc->capture, hipStreamNonBlocking) != hipSuccess)
+                return fail(ZO_ERR_HIP, "cannot create the capture stream");
+            if (hipStreamBeginCapture(gc->capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
+                return fail(ZO_ERR_HIP, "cannot begin a graph capture");
+            const zo_status st = decoder_eval_launches(m, b, Pert{}, w, gc->capture);
+            hipGraph_t graph = nullptr;
+            const hipError_t e = hipStreamEndCapture(gc->capture, &graph);
+            if (st || e != hipSuccess || !graph) {
+                if (graph) hipGraphDestroy(graph);
+                return st ? st : fail(ZO_ERR_HIP, "graph capture failed: %s", hipGetErrorString(e));
+            }
+            hipGraphExec_t ex = nullptr;
+            const hipError_t ei = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
+            hipGraphDestroy(graph);
+            if (ei != hipSuccess || !ex) return fail(ZO_ERR_HIP, "graph instantiation failed: %s", hipGetErrorString(ei));
+            f.exec = ex;
+            *out = ex;
+            return ZO_OK;
+        }
+    if (gc->entries.size() >= kMaxGraphs) {
+        if (gc->entries.front().exec) hipGraphExecDestroy(gc->entries.front().exec);
+        gc->entries.erase(gc->entries.begin());
+    }
+    gc->entries.push_back(FwdGraph{b.tokens, (int64_t)b.batch, (int64_t)b.seq, nullptr});
+    return ZO_OK;
+}
+
+}  // namespace
+
+zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
+                          hipStream_t s)
+{
+    const zo_model_desc& d = m.desc;
+    const int M = (int)(b.batch * b.seq), S = (int)b.seq;
+    DecoderWs w = carve(d, m.workspace);
     const int n_evals = n == 0 ? 1 : n;
     for (int e = 0; e < n_evals; ++e) {
         Pert p = {};
@@ -1360,59 +1504,17 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             p.sigma = perts[e].sigma;
             p.on = 1;
         }
-        {
-            KernelTimer t("embed", s);
-            embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, V, P + off(0), off(0), P + off(1), off(1), p, w.h);
-            if (zo_status st = check_launch("embed")) return st;
+        hipGraphExec_t ex = nullptr;
+        if (!n && m.graphs && !timing_active())
+            if (zo_status st = forward_graph(m, b, w, &ex)) return st;
+        if (ex) {
+            if (hipGraphLaunch(ex, s) != hipSuccess) return fail(ZO_ERR_HIP, "graph launch failed");
+        } else if (zo_status st = decoder_eval_launches(m, b, p, w, s)) {
+            return st;
         }
-        for (int l = 0; l < L; ++l) {
-            const int t0 = 2 + 8 * l;
-            {
-                KernelTimer t("layernorm", s);
-                launch_layernorm(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p, w.x, s);
-                if (zo_status st = check_launch("layernorm")) return st;
-            }
-            GemmParams gq = {};
-            gq.A = w.x; gq.W = P + off(t0 + 2); gq.w_dir = off(t0 + 2); gq.C = w.qkv; gq.M = M; gq.N = 3 * D; gq.K = D;
-            if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
-            {
-                KernelTimer t("attention", s);
-                launch_attention(w.qkv, B, S, D, H, dh, w.att, s);
-                if (zo_status st = check_launch("attention")) return st;
-            }
-            GemmParams go = {};
-            go.A = w.att; go.W = P + off(t0 + 3); go.w_dir = off(t0 + 3); go.C = w.h; go.M = M; go.N = D; go.K = D;
-            if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
-            {
-                KernelTimer t("layernorm", s);
-                launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s);
-                if (zo_status st = check_launch("layernorm")) return st;
-            }
-            GemmParams gu = {};
-            gu.A = w.x; gu.W = P + off(t0 + 6); gu.w_dir = off(t0 + 6); gu.C = w.u; gu.M = M; gu.N = F; gu.K = D;
-            zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16")
-                                                : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16");
-            if (su) return su;
-            GemmParams gd = {};
-            gd.A = w.u; gd.W = P + off(t0 + 7); gd.w_dir = off(t0 + 7); gd.C = w.h; gd.M = M; gd.N = D; gd.K = F;
-            if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16")) return st;
-        }
-        const int tf = 2 + 8 * L;
-        {
-            KernelTimer t("layernorm", s);
-            launch_layernorm(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x, s);
-            if (zo_status st = check_launch("layernorm")) return st;
-        }
-        GemmParams gl = {};
-        gl.A = w.x; gl.W = P + off(0); gl.w_dir = off(0); gl.M = M; gl.N = V; gl.K = D;
-        gl.lm_max = w.lm_max; gl.lm_sum = w.lm_sum; gl.lm_pick = w.lm_pick; gl.tokens = b.tokens; gl.S = S;
-        if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
         {
             KernelTimer t("reduce", s);
-            const int nb = cdiv(M, 64);
-            const int lm_tiles = cdiv(V, gemm_tile_n(M, V, p.on != 0, EPI_LMHEAD));
-            ce_rows_kernel<<<nb, kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, lm_tiles, M, S, w.ce_part);
-            ce_final_kernel<<<1, kThreads, 0, s>>>(w.ce_part, nb, M, S, loss + e);
+            ce_final_kernel<<<1, kThreads, 0, s>>>(w.ce_part, cdiv(M, 64), M, S, loss + e);
             if (zo_status st = check_launch("ce reduce")) return st;
         }
     }

@@ -12,6 +12,9 @@ zo_status fail(zo_status st, const char* fmt, ...);
 // Checks the last launch on this thread; returns ZO_OK or ZO_ERR_HIP.
 zo_status check_launch(const char* what);
 
+// True while zo_timing_enable is on (launches are then bracketed one by one).
+bool timing_active();
+
 // Brackets the launches made during its lifetime with HIP events on `s` when
 // timing is enabled (zo_timing_enable); a no-op otherwise.
 class KernelTimer {

@@ -22,7 +22,13 @@ struct ModelView {
     void* workspace;
     size_t ws_bytes;
     const uint64_t* offsets;  // arena offset of each tensor, layout order (not owned)
+    // The model's cache of captured decoder forwards (HIP graphs), created on
+    // first use; null where the caller may not allocate: launches stay eager.
+    void** graphs = nullptr;
 };
+
+// Releases a model's captured forwards (and their capture stream).
+void decoder_graphs_free(void* cache);
 
 zo_status model_check_shape(const zo_model_desc& d);
 size_t model_workspace_bytes(const zo_model_desc& d);
