@@ -48,7 +48,7 @@ TRAFFIC = {
     "gemm_bf16:opt30b:r4": (2 * (3.5007 + 1.2035 + 4.5982 + 4.8141) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r4"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r5"}
 
 
 def parse():

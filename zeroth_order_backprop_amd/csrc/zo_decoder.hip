@@ -43,7 +43,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;
 
 constexpr int kThreads = 256;
-constexpr int kDmaThreads = 512, kDmaWavesM = 4;  // 256 x 256 stored-weight GEMM
+constexpr int kDmaThreads = 512;                  // 128-wide stored-weight GEMM tiles
+constexpr int kBigThreads = 256, kBigWavesM = 2;  // 256 x 256 tiles
 
 // A perturbation applied while reading weights.
 struct Pert {
@@ -592,27 +593,134 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 #define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
-// Large tiles (256 x 256): 8 waves, two per SIMD so that one wave's MFMAs
-// cover the other's LDS and barrier waits, in a 4 x 2 grid of 64 x 128 wave
-// tiles.  Two BK = 64 stages of (BM + BN) x 64 bf16 fill 128 KB of LDS; every
-// row of a stage is one whole 128-byte line of A or W, so each direct-to-LDS
-// load brings in full lines (BK = 32 stages fetch half lines: twice the
-// requests for the same bytes, measured 4-7 % slower even with a deeper ring).
-// Rows are 8 chunks of 16 B, chunk c of row r at position c ^ ((r >> 1) & 7),
-// so the 32 rows a fragment read touches spread over all banks.  The four
-// k-steps of a stage are read into alternating register sets, each while the
-// previous k-step's MFMAs run; stage kt+2 is loaded into stage kt's buffer
-// right after the barrier that ends every wave's reads of stage kt, so it has
-// one stage of MFMAs to land.
+// Writes a block tile of 16x16 accumulators: element r of a 16x16 block is
+// row 4 (lane / 16) + r, column lane % 16.  Same stores as gemm_epilogue_impl
+// (through LDS, 16-byte coalesced) and the same LM-head partials, reduced over
+// the 16 lanes of a row group.
+template <int BM, int BN, int EPI, int NT, int WGM, int RB, int CB>
+__device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn,
+                                                bf16_t* smem)
+{
+    constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
+    static_assert(WM == RB * 16 && WN == CB * 16, "wave tile mismatch");
+    const int M = g.M, N = g.N;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int l16 = lane & 15, lq = lane >> 4;
+    if constexpr (EPI != EPI_LMHEAD) {
+        constexpr int LDC = BN + 8;
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = wm * WM + i * 16 + 4 * lq + r;
+                    const int col = wn * WN + j * 16 + l16;
+                    float v = acc[i][j][r];
+                    if constexpr (EPI == EPI_GELU) v = gelu_erf(v);
+                    if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
+                    smem[row * LDC + col] = f2bf(v);
+                }
+        __syncthreads();
+        constexpr int CPR = BN / 8;
+#pragma unroll 4
+        for (int p = tid; p < BM * CPR; p += NT) {
+            const int row = p / CPR, cc = p % CPR;
+            const int gr = m0 + row, gc = n0 + 8 * cc;
+            if (gr >= M || gc >= N) continue;
+            uint4 v = *reinterpret_cast<const uint4*>(smem + row * LDC + 8 * cc);
+            uint4* dst = reinterpret_cast<uint4*>(g.C + (size_t)gr * N + gc);
+            if constexpr (EPI == EPI_RESID) {
+                const uint4 h = *dst;
+                auto add2 = [](uint32_t hw, uint32_t pw) {
+                    return pack2(bf2f(hw & 0xFFFF) + bf2f(pw & 0xFFFF), bf2f(hw >> 16) + bf2f(pw >> 16));
+                };
+                v = uint4{add2(h.x, v.x), add2(h.y, v.y), add2(h.z, v.z), add2(h.w, v.w)};
+            }
+            *dst = v;
+        }
+    } else {
+        static_assert(WGN == 2, "LM-head partials assume two wave columns");
+        __shared__ float part_m[2][BM], part_s[2][BM];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int lrow = wm * WM + i * 16 + 4 * lq + r;
+                const int row = m0 + lrow;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 16 + l16;
+                    if (col < N) mx = fmaxf(mx, acc[i][j][r]);
+                }
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float se = 0.f;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int col = n0 + wn * WN + j * 16 + l16;
+                    if (col < N) se += __expf(acc[i][j][r] - mx);
+                }
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+                if (l16 == 0) {
+                    part_m[wn][lrow] = mx;
+                    part_s[wn][lrow] = se;
+                }
+                if (row < M && (row % g.S) != g.S - 1) {
+                    const int target = g.tokens[row + 1];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int col = n0 + wn * WN + j * 16 + l16;
+                        if (col == target) g.lm_pick[row] = acc[i][j][r];
+                    }
+                    if ((unsigned)target >= (unsigned)N && tn == 0 && wn == 0 && l16 == 0)
+                        g.lm_pick[row] = __builtin_nanf("");
+                }
+            }
+        __syncthreads();
+        for (int lrow = tid; lrow < BM; lrow += NT) {
+            const int row = m0 + lrow;
+            if (row >= M) continue;
+            const float m1 = part_m[0][lrow], m2 = part_m[1][lrow];
+            const float mx = fmaxf(m1, m2);
+            float se = 0.f;
+            if (m1 > -INFINITY) se += part_s[0][lrow] * __expf(m1 - mx);
+            if (m2 > -INFINITY) se += part_s[1][lrow] * __expf(m2 - mx);
+            g.lm_max[(size_t)tn * M + row] = mx;
+            g.lm_sum[(size_t)tn * M + row] = se;
+        }
+    }
+}
+
+// Large tiles (256 x 256): 4 waves, one per SIMD, in a 2 x 2 grid of
+// 128 x 128 wave tiles of 16x16x32 MFMAs (64 accumulators of 4 in AGPRs).
+// Two BK = 64 stages of (BM + BN) x 64 bf16 fill 128 KB of LDS; every row of
+// a stage is one whole 128-byte line of A or W, so each direct-to-LDS load
+// brings in full lines.  Rows are 8 chunks of 16 B, chunk c of row r at
+// position c ^ ((r >> 1) & 7): the 16 rows a fragment read touches (one chunk
+// each) spread over all banks.  A stage is two 32-deep k-steps read into
+// alternating register sets.  With one wave per SIMD nothing covers a stall,
+// so the wave's instruction stream is spread evenly: one fragment read per
+// four MFMAs, and after the barrier one read and one stage load per four
+// (scheduling groups 0x008 MFMA, 0x100 LDS read, 0x020 global read; read and
+// load alternate in the source, since the compiler keeps LDS reads ahead of
+// the loads that write LDS).  The same kernel with the reads clustered (one
+// per MFMA over the first sixteen) measured 9% slower; eight waves of
+// 64 x 128 with 32x32x16 MFMAs 9-12% slower.
+// Stage kt+2 is loaded into stage kt's buffer right after the barrier that
+// ends every wave's reads of stage kt, so it has one stage of MFMAs to land.
 template <int BM, int BN, int EPI, int NT, int WGM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 {
     constexpr int BK = 64;
     constexpr int WGN = NT / 64 / WGM;
     constexpr int WM = BM / WGM, WN = BN / WGN;
-    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int RB = WM / 16, CB = WN / 16;
     constexpr int A_INS = BM * 8 / NT, B_INS = BN * 8 / NT;
-    constexpr int INS = A_INS + B_INS;  // load instructions per thread per stage
+    constexpr int INS = A_INS + B_INS;
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
     static_assert(INS < 64, "vmcnt range");
@@ -626,13 +734,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int m0 = tm * BM, n0 = tn * BN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
-    const int lr = lane & 31, lh = lane >> 5;
 
-    f32x16 acc[RB][CB];
+    f32x4 acc[RB][CB];
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{};
 
     const int KT = K / BK;
     const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
@@ -649,15 +756,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
         vob[j] = (min(n0 + row, N - 1) * K + 8 * lc) * 2;
     }
-    // Stages past the last reload the last k range into the buffer no wave
-    // reads again, so that every iteration issues the same loads.
     auto issue = [&](int kt) {
         bf16_t* sa = lds + (kt & 1) * STAGE;
         bf16_t* sb = sa + BM * BK;
         const int koff = min(kt, KT - 1) * BK * 2;
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
-            bf16_t* dst = sa + (j * NT + wave_u * 64) * 8;  // lane l lands at +16 l bytes
+            bf16_t* dst = sa + (j * NT + wave_u * 64) * 8;
             zo_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, voa[j], koff, 0, 0);
         }
 #pragma unroll
@@ -666,45 +771,51 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, vob[j], koff, 0, 0);
         }
     };
-    // fragment offsets (elements) of this lane for k-step ks of a stage; the
-    // swizzle depends on lr only, so fragments i > 0 sit at fixed offsets
-    int aoff[4], boff[4];
+    // 16x16x32 operands: lane l holds row (l & 15) of its block, k-chunk l >> 4
+    // of the 32-deep step; rows >> 1 & 7 of the swizzle come from l & 15 alone
+    const int r16 = lane & 15, kq = lane >> 4, sw = (r16 >> 1) & 7;
+    int aoff[2], boff[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int lc = 2 * ks + lh;
-        const int ra_ = wm * WM + lr, rb_ = wn * WN + lr;
-        aoff[ks] = ra_ * BK + (lc ^ ((ra_ >> 1) & 7)) * 8;
-        boff[ks] = BM * BK + rb_ * BK + (lc ^ ((rb_ >> 1) & 7)) * 8;
+    for (int s = 0; s < 2; ++s) {
+        aoff[s] = (wm * WM + r16) * BK + (((4 * s + kq) ^ sw) * 8);
+        boff[s] = BM * BK + (wn * WN + r16) * BK + (((4 * s + kq) ^ sw) * 8);
     }
     bf16x8 fa[2][RB], fb[2][CB];
-    auto read = [&](int kt, int ks, int slot) {
+    auto read = [&](int kt, int s, int slot) {
         const bf16_t* st = lds + (kt & 1) * STAGE;
 #pragma unroll
-        for (int j = 0; j < CB; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(st + boff[ks] + j * 32 * BK);
+        for (int j = 0; j < CB; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(st + boff[s] + j * 16 * BK);
 #pragma unroll
-        for (int i = 0; i < RB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks] + i * 32 * BK);
+        for (int i = 0; i < RB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(st + aoff[s] + i * 16 * BK);
     };
     auto mma = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int j = 0; j < CB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
     };
-    // One k-step's MFMAs with the next k-step's fragment reads spread one per
-    // MFMA (scheduling groups: 0x008 MFMA, 0x100 LDS read, 0x020 global read).
-    constexpr int NR = RB + CB, NM = RB * CB;
-    constexpr int PA = NR < NM ? NR : NM;
-    constexpr int NV = NM - PA;                              // MFMAs left for the loads
-    constexpr int VPER = NV > 0 ? (INS + NV - 1) / NV : 0;  // loads per such MFMA
-    auto spread_reads = [&]() {
-#pragma unroll
-        for (int i = 0; i < PA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr int NR = RB + CB, NM = RB * CB;  // fragment reads, MFMAs per k-step
+    // one fragment read / one stage load by index (reads: B fragments first)
+    auto read1 = [&](int kt, int s, int slot, int idx) {
+        const bf16_t* st = lds + (kt & 1) * STAGE;
+        if (idx < CB) fb[slot][idx] = *reinterpret_cast<const bf16x8*>(st + boff[s] + idx * 16 * BK);
+        else fa[slot][idx - CB] = *reinterpret_cast<const bf16x8*>(st + aoff[s] + (idx - CB) * 16 * BK);
+    };
+    auto issue1 = [&](int kt, int idx) {
+        bf16_t* sa = lds + (kt & 1) * STAGE;
+        bf16_t* sb = sa + BM * BK;
+        const int koff = min(kt, KT - 1) * BK * 2;
+        if (idx < A_INS) {
+            bf16_t* dst = sa + (idx * NT + wave_u * 64) * 8;
+            zo_raw_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, voa[idx], koff, 0, 0);
+        } else {
+            bf16_t* dst = sb + ((idx - A_INS) * NT + wave_u * 64) * 8;
+            zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, vob[idx - A_INS], koff, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - PA, 0);
     };
+    static_assert(NR == INS && NM % (2 * NR) == 0, "spread pattern assumes as many reads as loads");
+    constexpr int MPR = NM / NR;  // MFMAs per fragment read
 
     issue(0);
     ZO_WAIT_VM(0);
@@ -716,47 +827,37 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         __builtin_amdgcn_sched_barrier(0);
         read(kt, 1, 1);
         mma(0);
-        spread_reads();
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        read(kt, 2, 0);
-        mma(1);
-        spread_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        read(kt, 3, 1);
-        mma(0);
-        spread_reads();
-        __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 landed and this wave's reads of stage kt are in
-        // registers; after the barrier no wave reads stage kt's buffer
         ZO_WAIT_VM(0);
         ZO_WAIT_LGKM0();
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        read(kt + 1, 0, 0);
-        issue(kt + 2);
+#pragma unroll
+        for (int idx = 0; idx < NR; ++idx) {
+            read1(kt + 1, 0, 0, idx);
+            issue1(kt + 2, idx);
+        }
         mma(1);
 #pragma unroll
-        for (int i = 0; i < PA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR / 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, VPER, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MPR / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     read(KT - 1, 1, 1);
     mma(0);
-    read(KT - 1, 2, 0);
     mma(1);
-    read(KT - 1, 3, 1);
-    mma(0);
-    mma(1);
-    ZO_WAIT_VM(0);    // the trailing reload has landed before the buffers are reused
-    __syncthreads();  // every wave is done with the stage buffers
-    gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
+    ZO_WAIT_VM(0);
+    __syncthreads();
+    gemm_epilogue16<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
 template <int BM, int BN, int EPI, int NT, int WGM>
@@ -764,8 +865,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 256, NT
 {
     gemm_dma_body<BM, BN, EPI, NT, WGM>(g);
 }
-
-
 
 // Small tiles (128 x 128 or 128 x 64): two BK = 64 stages, NT/64 waves in a
 // WGM x (NT/64/WGM) grid.  LDS rows are 128 B (8 chunks of 16 B),
@@ -1229,7 +1328,7 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         KernelTimer timer(fam, s);
         kern<<<blocks, kThreads, lds, s>>>(gp, p);
     } else {
-        // 256-wide tiles: 8 waves of 64 x 128; 128-wide: 8 waves of 32 x 64,
+        // 256-wide tiles: 4 waves of 128 x 128; 128-wide: 8 waves of 32 x 64,
         // or 4 of 64 x 64 for the LM head (its cross-entropy epilogue needs
         // two wave columns); two BK = 64 stages throughout (K % 64 == 0)
         constexpr bool big = BM == 256;
@@ -1237,9 +1336,9 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         constexpr size_t stages = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
         void (*kern)(GemmParams);
-        int threads = (big || eight) ? kDmaThreads : kThreads;
+        int threads = big ? kBigThreads : eight ? kDmaThreads : kThreads;
         if constexpr (big)
-            kern = gemm_bf16_dma_kernel<BM, BN, EPI, kDmaThreads, kDmaWavesM>;
+            kern = gemm_bf16_dma_kernel<BM, BN, EPI, kBigThreads, kBigWavesM>;
         else if constexpr (eight)
             kern = gemm_bf16_k64_kernel<BM, BN, EPI, 512, 4>;
         else
