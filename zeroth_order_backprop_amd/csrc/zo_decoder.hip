@@ -1045,10 +1045,19 @@ __global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __rest
 // 4 q + r receives element r of the 8 bytes read by lanes q, 4 + q, 8 + q and
 // 12 + q (lane 4 e + q reads key e, head-dim columns 4 q .. 4 q + 3, so lane
 // 4 q + r gets keys 0..3 of column 4 q + r).  Rows are 16-byte chunks, chunk
-// c of row r at position c ^ (2 (r & 3) + ((r >> 2) & 1)): a K fragment read
-// (8 consecutive rows, one chunk) and a V^T read (4 consecutive rows, two
-// chunks) each touch every bank once.
-__device__ __forceinline__ int att_swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// c of row r at position c ^ s(r).  The LDS serves 256 bytes (64 banks) a
+// cycle: 16 lanes of a 16-byte read, 32 of an 8-byte one.  With 256-byte rows
+// (d_h 128) every row starts on bank 0: s(r) = 4 (r & 3) + ((r >> 2) & 3)
+// spreads the 16 rows of a K fragment read over the 16 bank groups and gives
+// the 4 rows of a V^T read (4 chunks each) disjoint groups.  With 128-byte rows
+// (d_h 64) odd rows start half-way: s(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)
+// does the same within each half.  (An earlier swizzle laid out for 32 banks
+// left 2-way conflicts on K and 4-way on V^T: 6e7 conflict cycles a call.)
+template <int DH>
+__device__ __forceinline__ int att_swz(int row)
+{
+    return DH == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
 
 // Eight transposing LDS reads and the wait for them in one asm statement, so
 // that no register they write is reused before its data lands.  (Through the
@@ -1139,7 +1148,7 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         const int byte = (wave * LOADS + j) * 1024 + 16 * lane;
         const int row = byte / ROWB, pos = (byte % ROWB) / 16;
         lrow[j] = row;
-        lcol[j] = 16 * (pos ^ att_swz(row));
+        lcol[j] = 16 * (pos ^ att_swz<DH>(row));
     }
     // Tiles past the last reload rows no wave reads, so that every iteration
     // issues the same loads and waits for the same count.
@@ -1156,13 +1165,17 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
     };
     // this lane's read offsets in a slot: K rows 32 hblk + lr, chunk 2 ks + lh;
     // V^T: key row (lane & 15) >> 2 of its group's four, columns 4 (lane & 3)
-    const int ksw = att_swz(lr);
+    const int ksw = att_swz<DH>(lr);
     const int g = lane >> 4, ve = (lane & 15) >> 2, vq = lane & 3;
-    const int vrow = 4 * (g >> 1) + ve, vsw = att_swz(vrow);
+    const int vrow = 4 * (g >> 1) + ve;
     const int vhalf = 8 * (vq & 1);
-    int vcol[OT];
+    // the swizzle of V^T rows vrow + 16 m + 8 h depends on h only
+    int vcol[OT][2];
 #pragma unroll
-    for (int t = 0; t < OT; ++t) vcol[t] = 16 * ((4 * t + 2 * (g & 1) + (vq >> 1)) ^ vsw) + vhalf;
+    for (int t = 0; t < OT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            vcol[t][h] = 16 * ((4 * t + 2 * (g & 1) + (vq >> 1)) ^ att_swz<DH>(8 * h + vrow)) + vhalf;
 
     for (int t = 0; t < NSLOT - 1; ++t) issue(t);
     // Q in registers before the loop: a wait for it there is partial (the
@@ -1270,7 +1283,7 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
                 for (int t = 0; t < OT; ++t)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t]);
+                        a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
             ds_read_tr8(v, a);
 #pragma unroll
             for (int u = 0; u < STEPS; ++u) {
