@@ -71,14 +71,14 @@ KernelTimer::KernelTimer(const char* family, hipStream_t s) : slot_(-1), s_(s)
     if (!g_timing || (!g_timing_family.empty() && g_timing_family != family)) return;
     TimedLaunch t{family, take_event(), take_event()};
     if (!t.start || !t.stop) return;
-    hipEventRecord(t.start, s);
+    (void)hipEventRecord(t.start, s);
     g_timed.push_back(t);
     slot_ = (int)g_timed.size() - 1;
 }
 
 KernelTimer::~KernelTimer()
 {
-    if (slot_ >= 0) hipEventRecord(g_timed[slot_].stop, s_);
+    if (slot_ >= 0) (void)hipEventRecord(g_timed[slot_].stop, s_);
 }
 
 static uint64_t align64(uint64_t x) { return (x + 63) / 64 * 64; }

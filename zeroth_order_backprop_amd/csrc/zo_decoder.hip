@@ -1481,8 +1481,8 @@ void decoder_graphs_free(void* cache)
     auto* gc = static_cast<GraphCache*>(cache);
     if (!gc) return;
     for (auto& f : gc->entries)
-        if (f.exec) hipGraphExecDestroy(f.exec);
-    if (gc->capture) hipStreamDestroy(gc->capture);
+        if (f.exec) (void)hipGraphExecDestroy(f.exec);
+    if (gc->capture) (void)hipStreamDestroy(gc->capture);
     delete gc;
 }
 
@@ -1580,19 +1580,19 @@ zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& 
             hipGraph_t graph = nullptr;
             const hipError_t e = hipStreamEndCapture(gc->capture, &graph);
             if (st || e != hipSuccess || !graph) {
-                if (graph) hipGraphDestroy(graph);
+                if (graph) (void)hipGraphDestroy(graph);
                 return st ? st : fail(ZO_ERR_HIP, "graph capture failed: %s", hipGetErrorString(e));
             }
             hipGraphExec_t ex = nullptr;
             const hipError_t ei = hipGraphInstantiate(&ex, graph, nullptr, nullptr, 0);
-            hipGraphDestroy(graph);
+            (void)hipGraphDestroy(graph);
             if (ei != hipSuccess || !ex) return fail(ZO_ERR_HIP, "graph instantiation failed: %s", hipGetErrorString(ei));
             f.exec = ex;
             *out = ex;
             return ZO_OK;
         }
     if (gc->entries.size() >= kMaxGraphs) {
-        if (gc->entries.front().exec) hipGraphExecDestroy(gc->entries.front().exec);
+        if (gc->entries.front().exec) (void)hipGraphExecDestroy(gc->entries.front().exec);
         gc->entries.erase(gc->entries.begin());
     }
     gc->entries.push_back(FwdGraph{b.tokens, (int64_t)b.batch, (int64_t)b.seq, nullptr});
