@@ -33,6 +33,9 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ void zo_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds, int size,
                                        int voffset, int soffset, int offset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.lds");
+// 16-byte buffer store (an offset past the resource's size writes nothing).
+__device__ void zo_raw_buffer_store_x4(i32x4_t data, i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
 namespace zo {
 namespace {
@@ -597,6 +600,32 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 // row 4 (lane / 16) + r, column lane % 16.  Same stores as gemm_epilogue_impl
 // (through LDS, 16-byte coalesced) and the same LM-head partials, reduced over
 // the 16 lanes of a row group.
+// The activated, bf16-rounded tile of 16x16 accumulators into `smem`, rows
+// padded by 8 bf16 (element r of a 16x16 block: row 4 (lane / 16) + r, column
+// lane % 16).
+template <int BM, int BN, int EPI, int NT, int WGM, int RB, int CB>
+__device__ __forceinline__ void epilogue16_stage(f32x4 (&acc)[RB][CB], bf16_t* smem)
+{
+    constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN, LDC = BN + 8;
+    static_assert(WM == RB * 16 && WN == CB * 16, "wave tile mismatch");
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * WM + i * 16 + 4 * lq + r;
+                const int col = wn * WN + j * 16 + l16;
+                float v = acc[i][j][r];
+                if constexpr (EPI == EPI_GELU) v = gelu_erf(v);
+                if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
+                smem[row * LDC + col] = f2bf(v);
+            }
+}
+
 template <int BM, int BN, int EPI, int NT, int WGM, int RB, int CB>
 __device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn,
                                                 bf16_t* smem)
@@ -712,6 +741,12 @@ __device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc
 // 64 x 128 with 32x32x16 MFMAs 9-12% slower.
 // Stage kt+2 is loaded into stage kt's buffer right after the barrier that
 // ends every wave's reads of stage kt, so it has one stage of MFMAs to land.
+// The grid is persistent (one block per CU walking its tiles in the order of
+// tile_of).  With the stored epilogues the next tile's first two stages are
+// issued before this tile's output stores: the stores, which all CUs issue at
+// about the same time and which the chip's write bandwidth then paces, drain
+// under the next tile's first k-step instead of before its first wait (vmcnt
+// counts loads and stores in issue order, so any later wait covers them).
 template <int BM, int BN, int EPI, int NT, int WGM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 {
@@ -723,39 +758,47 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     constexpr int INS = A_INS + B_INS;
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
-    static_assert(INS < 64, "vmcnt range");
+    // Stored epilogues overlap the next tile's first loads; the residual one
+    // (its h reads would need twice the registers) and the LM head's
+    // partials finish before the next tile starts.
+    constexpr bool OVERLAP = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RELU;
+    // output chunks (16 B) per row and per thread
+    constexpr int CPR = BN / 8, NST = BM * CPR / NT, LDC = BN + 8;
+    static_assert(NST * NT == BM * CPR, "tile / thread mismatch");
+    static_assert(INS + NST < 64, "vmcnt range");
     extern __shared__ __align__(16) bf16_t lds[];
 
     const int M = g.M, N = g.N, K = g.K;
     asm volatile("" ::"s"(g.C), "s"(g.lm_max), "s"(g.lm_sum), "s"(g.lm_pick), "s"(g.tokens), "s"(g.S));
-    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_of<4>(blockIdx.x, nbm, nbn, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN, ntiles = nbm * nbn;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
-
-    f32x4 acc[RB][CB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{};
-
     const int KT = K / BK;
     const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
     const i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
+    // the output (stored epilogues; the host keeps M N 2 under 2 GiB)
+    const i32x4_t rc = buffer_rsrc(g.C, OVERLAP ? (uint32_t)((size_t)M * N * 2) : 0u);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // the block's current tile and this thread's source offsets in it
+    int tile = blockIdx.x, m0 = 0, n0 = 0, tn = 0;
     int voa[A_INS], vob[B_INS];
+    auto set_tile = [&](int t) {
+        int tm;
+        tile_of<4>(t, nbm, nbn, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) {
-        const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-        voa[j] = (min(m0 + row, M - 1) * K + 8 * lc) * 2;
-    }
+        for (int j = 0; j < A_INS; ++j) {
+            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            voa[j] = (min(m0 + row, M - 1) * K + 8 * lc) * 2;
+        }
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) {
-        const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-        vob[j] = (min(n0 + row, N - 1) * K + 8 * lc) * 2;
-    }
+        for (int j = 0; j < B_INS; ++j) {
+            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+            vob[j] = (min(n0 + row, N - 1) * K + 8 * lc) * 2;
+        }
+    };
+    f32x4 acc[RB][CB];
     auto issue = [&](int kt) {
         bf16_t* sa = lds + (kt & 1) * STAGE;
         bf16_t* sb = sa + BM * BK;
@@ -817,11 +860,22 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     static_assert(NR == INS && NM % (2 * NR) == 0, "spread pattern assumes as many reads as loads");
     constexpr int MPR = NM / NR;  // MFMAs per fragment read
 
+    set_tile(tile);
     issue(0);
-    ZO_WAIT_VM(0);
+    issue(1);
+    bool stores_pending = false;  // the previous tile's output stores may be in flight
+    for (;;) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{};
+    // stage 0 landed (stage 1 and the previous tile's stores may remain)
+    if (stores_pending)
+        ZO_WAIT_VM(INS + NST);
+    else
+        ZO_WAIT_VM(INS);
     asm volatile("s_barrier" ::: "memory");
     read(0, 0, 0);
-    issue(1);
     ZO_WAIT_LGKM0();
     for (int kt = 0; kt < KT - 1; ++kt) {
         __builtin_amdgcn_sched_barrier(0);
@@ -855,9 +909,49 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     read(KT - 1, 1, 1);
     mma(0);
     mma(1);
-    ZO_WAIT_VM(0);
-    __syncthreads();
-    gemm_epilogue16<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
+    ZO_WAIT_VM(0);    // the trailing reloads have landed before the buffers are reused
+    __syncthreads();  // every wave is done with the stage buffers
+    const int next = tile + (int)gridDim.x;
+    const bool more = next < ntiles;
+    if constexpr (!OVERLAP) {
+        gemm_epilogue16<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
+        // (its stores then complete before the next tile's first wait ends)
+        if (!more) break;
+        __syncthreads();  // the epilogue's LDS use is over
+        tile = next;
+        set_tile(tile);
+        issue(0);
+        issue(1);
+    } else {
+        // The tile goes through LDS (rows padded by 8 bf16) into registers;
+        // once every wave has its chunks the next tile's first two stages are
+        // issued, and only then this tile's stores: the next tile's first
+        // wait then covers its own loads, not these stores.
+        epilogue16_stage<BM, BN, EPI, NT, WGM>(acc, lds);
+        __syncthreads();
+        uint4 vals[NST];
+        int offs[NST];
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+            const int p = k * NT + tid, row = p / CPR, cc = p % CPR;
+            const int gr = m0 + row, gc = n0 + 8 * cc;
+            vals[k] = *reinterpret_cast<const uint4*>(lds + row * LDC + 8 * cc);
+            offs[k] = (gr < M && gc < N) ? (gr * N + gc) * 2 : (int)0x80000000u;  // past the end: dropped
+        }
+        ZO_WAIT_LGKM0();
+        asm volatile("s_barrier" ::: "memory");  // every wave has read its chunks
+        if (more) {
+            tile = next;
+            set_tile(tile);
+            issue(0);
+            issue(1);
+        }
+#pragma unroll
+        for (int k = 0; k < NST; ++k) zo_raw_buffer_store_x4(__builtin_bit_cast(i32x4_t, vals[k]), rc, offs[k], 0, 0);
+        if (!more) break;
+        stores_pending = true;
+    }
+    }
 }
 
 template <int BM, int BN, int EPI, int NT, int WGM>
@@ -1321,6 +1415,20 @@ void launch_attention(const bf16_t* qkv, int B, int S, int d, int H, int dh, bf1
         attention_kernel<128><<<blocks, kThreads, 0, s>>>(qkv, S, d, H, out);
 }
 
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int BM, int BN, int EPI, bool PERT>
 zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
@@ -1364,7 +1472,8 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
             attr = true;
         }
         KernelTimer timer(fam, s);
-        kern<<<blocks, threads, lds, s>>>(gp);
+        // 256-wide tiles: a persistent grid of one block per CU walking its tiles
+        kern<<<big ? std::min(blocks, device_cus()) : blocks, threads, lds, s>>>(gp);
     }
     return check_launch("bf16 GEMM");
 }
@@ -1640,8 +1749,8 @@ zo_status debug_gemm_bf16(const void* A, const void* W, void* C, int M, int N, i
     if (K % 64) return fail(ZO_ERR_UNSUPPORTED, "K must be a multiple of 64");
     if (N % 8) return fail(ZO_ERR_UNSUPPORTED, "N must be a multiple of 8");
     if (((uintptr_t)A | (uintptr_t)W | (uintptr_t)C) & 15) return fail(ZO_ERR_INVALID, "A, W, C must be 16-byte aligned");
-    if ((int64_t)M * K * 2 >= (1ll << 31) || (int64_t)N * K * 2 >= (1ll << 31))
-        return fail(ZO_ERR_UNSUPPORTED, "A and W must each be under 2 GiB");
+    if ((int64_t)M * K * 2 >= (1ll << 31) || (int64_t)N * K * 2 >= (1ll << 31) || (int64_t)M * N * 2 >= (1ll << 31))
+        return fail(ZO_ERR_UNSUPPORTED, "A, W and C must each be under 2 GiB");
     GemmParams g = {};
     g.A = (const bf16_t*)A; g.W = (const bf16_t*)W; g.C = (bf16_t*)C; g.M = M; g.N = N; g.K = K;
     Pert p = {};
