@@ -48,7 +48,7 @@ TRAFFIC = {
     "gemm_bf16:opt30b:r5": (2 * (3.5108 + 1.2089 + 4.6368 + 4.8172) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r5"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r6"}
 
 
 def parse():

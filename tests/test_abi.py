@@ -87,6 +87,15 @@ def test_validation_rejects_before_launch():
     assert L.zo_update_buffer(ctypes.c_void_p(256), zo.ZO_BF16, Q, 16, 8, 1, 2, ctypes.c_void_p(512), 1e-3,
                               s) == zo.ZO_ERR_INVALID
     assert L.zo_debug_rng(0, 0, 0, 16, None, None, s) == zo.ZO_ERR_INVALID
+    # debug GEMM: K % 64, N % 8, alignment, and every operand under 2 GiB
+    A, W, C = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), ctypes.c_void_p(1 << 22)
+    gemm = L.zo_debug_gemm_bf16
+    assert gemm(A, W, C, 256, 256, 96, 0, s) == zo.ZO_ERR_UNSUPPORTED
+    assert gemm(A, W, C, 256, 260, 64, 0, s) == zo.ZO_ERR_UNSUPPORTED
+    assert gemm(ctypes.c_void_p((1 << 20) + 8), W, C, 256, 256, 64, 0, s) == zo.ZO_ERR_INVALID
+    assert gemm(A, W, C, 1 << 16, 1 << 14, 64, 0, s) == zo.ZO_ERR_UNSUPPORTED  # C: 2 GiB
+    assert gemm(A, W, C, 1 << 15, 256, 1 << 15, 0, s) == zo.ZO_ERR_UNSUPPORTED  # A: 2 GiB
+    assert gemm(None, W, C, 256, 256, 64, 0, s) == zo.ZO_ERR_INVALID
     # model creation: wrong arena size, misalignment, overlap, small workspace
     desc = zo.make_desc(**DESCS["lsq"][1])
     h = ctypes.c_void_p()
