@@ -45,7 +45,7 @@ TRAFFIC = {
     "sgemm:mlp:r4": 2 * 8495.5 * 1024 + 10240 * 1024,
     # the OPT-30B shape's four layer GEMMs (QKV, O, up, down), mean per launch:
     # FETCH_SIZE x 2 + WRITE_SIZE summed over one of each, divided by four
-    "gemm_bf16:opt30b:r5": (2 * (3.5108 + 1.2089 + 4.6368 + 4.8172) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
+    "gemm_bf16:opt30b:r6": (2 * (4.0400 + 1.2149 + 5.2949 + 4.8819) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
                            * 2**30 / 4,
 }
 KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r6"}
