@@ -46,8 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;
 
 constexpr int kThreads = 256;
-constexpr int kDmaThreads = 512;                  // 128-wide stored-weight GEMM tiles
-constexpr int kBigThreads = 256, kBigWavesM = 2;  // 256 x 256 tiles
+constexpr int kGemmThreads = 256, kGemmWavesM = 2;  // stored-weight GEMM tiles (256 or 128 wide)
 
 // A perturbation applied while reading weights.
 struct Pert {
@@ -724,29 +723,60 @@ __device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc
     }
 }
 
-// Large tiles (256 x 256): 4 waves, one per SIMD, in a 2 x 2 grid of
-// 128 x 128 wave tiles of 16x16x32 MFMAs (64 accumulators of 4 in AGPRs).
-// Two BK = 64 stages of (BM + BN) x 64 bf16 fill 128 KB of LDS; every row of
-// a stage is one whole 128-byte line of A or W, so each direct-to-LDS load
-// brings in full lines.  Rows are 8 chunks of 16 B, chunk c of row r at
-// position c ^ ((r >> 1) & 7): the 16 rows a fragment read touches (one chunk
-// each) spread over all banks.  A stage is two 32-deep k-steps read into
-// alternating register sets.  With one wave per SIMD nothing covers a stall,
-// so the wave's instruction stream is spread evenly: one fragment read per
-// four MFMAs, and after the barrier one read and one stage load per four
-// (scheduling groups 0x008 MFMA, 0x100 LDS read, 0x020 global read; read and
-// load alternate in the source, since the compiler keeps LDS reads ahead of
-// the loads that write LDS).  The same kernel with the reads clustered (one
-// per MFMA over the first sixteen) measured 9% slower; eight waves of
-// 64 x 128 with 32x32x16 MFMAs 9-12% slower.
+// Scheduling groups spreading NR fragment reads (and after the barrier NR
+// stage loads) evenly over NM MFMAs: read i follows MFMA (i + 1) NM / NR.
+template <int I, int NR, int NM>
+__device__ __forceinline__ void spread_pre()
+{
+    if constexpr (I < NR) {
+        constexpr int c = (I + 1) * NM / NR - I * NM / NR;
+        __builtin_amdgcn_sched_group_barrier(0x008, c, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        spread_pre<I + 1, NR, NM>();
+    }
+}
+template <int I, int NR, int NM>
+__device__ __forceinline__ void spread_post()
+{
+    if constexpr (I < NR) {
+        constexpr int c = (I + 1) * NM / NR - I * NM / NR, c1 = c / 2;
+        if constexpr (c1 > 0) __builtin_amdgcn_sched_group_barrier(0x008, c1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, c - c1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        spread_post<I + 1, NR, NM>();
+    }
+}
+
+// Stored-weight GEMM tiles, 4 waves of 16x16x32 MFMAs in a 2 x 2 grid.
+// 256 x 256 tiles: one wave per SIMD with a 128 x 128 wave tile (64
+// accumulators of 4 in AGPRs), 128 KB of stages.  128 x 128 and 128 x 64 tiles
+// (outputs too small to fill the CUs with 256-wide ones): 64 x 64 and 64 x 32
+// wave tiles, 64 or 48 KB of stages, two or three blocks per CU.
+// Two BK = 64 stages of (BM + BN) x 64 bf16; every row of a stage is one whole
+// 128-byte line of A or W, so each direct-to-LDS load brings in full lines.
+// Rows are 8 chunks of 16 B, chunk c of row r at position c ^ ((r >> 1) & 7):
+// the 16 rows a fragment read touches (one chunk each) spread over all banks.
+// A stage is two 32-deep k-steps read into alternating register sets.  With
+// one wave per SIMD nothing covers a stall, so the wave's instruction stream
+// is spread evenly: the k-step's fragment reads over its MFMAs (one per four
+// on 256-wide tiles), and after the barrier one read and one stage load per
+// such group (scheduling groups 0x008 MFMA, 0x100 LDS read, 0x020 global
+// read; read and load alternate in the source, since the compiler keeps LDS
+// reads ahead of the loads that write LDS).  On 256-wide tiles the same
+// kernel with the reads clustered (one per MFMA over the first sixteen)
+// measured 9% slower, eight waves of 64 x 128 with 32x32x16 MFMAs 9-12%
+// slower; on the 128-wide tiles this kernel is 4-11% faster than eight waves
+// of 32x32x16 MFMAs.
 // Stage kt+2 is loaded into stage kt's buffer right after the barrier that
 // ends every wave's reads of stage kt, so it has one stage of MFMAs to land.
-// The grid is persistent (one block per CU walking its tiles in the order of
-// tile_of).  With the stored epilogues the next tile's first two stages are
-// issued before this tile's output stores: the stores, which all CUs issue at
-// about the same time and which the chip's write bandwidth then paces, drain
-// under the next tile's first k-step instead of before its first wait (vmcnt
-// counts loads and stores in issue order, so any later wait covers them).
+// 256-wide tiles run a persistent grid (one block per CU walking its tiles in
+// the order of tile_of).  With the stored epilogues the next tile's first two
+// stages are issued before this tile's output stores: the stores, which all
+// CUs issue at about the same time and which the chip's write bandwidth then
+// paces, drain under the next tile's first k-step instead of before its first
+// wait (vmcnt counts loads and stores in issue order, so any later wait
+// covers them).
 template <int BM, int BN, int EPI, int NT, int WGM>
 __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 {
@@ -857,8 +887,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             zo_raw_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)dst, 16, vob[idx - A_INS], koff, 0, 0);
         }
     };
-    static_assert(NR == INS && NM % (2 * NR) == 0, "spread pattern assumes as many reads as loads");
-    constexpr int MPR = NM / NR;  // MFMAs per fragment read
+    static_assert(NR == INS, "spread pattern assumes as many reads as loads");
 
     set_tile(tile);
     issue(0);
@@ -881,11 +910,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         __builtin_amdgcn_sched_barrier(0);
         read(kt, 1, 1);
         mma(0);
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        spread_pre<0, NR, NM>();
         __builtin_amdgcn_sched_barrier(0);
         ZO_WAIT_VM(0);
         ZO_WAIT_LGKM0();
@@ -897,13 +922,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             issue1(kt + 2, idx);
         }
         mma(1);
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, MPR / 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MPR / 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+        spread_post<0, NR, NM>();
         __builtin_amdgcn_sched_barrier(0);
     }
     read(KT - 1, 1, 1);
@@ -955,116 +974,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
 }
 
 template <int BM, int BN, int EPI, int NT, int WGM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 256, NT / 256))) void gemm_bf16_dma_kernel(GemmParams g)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2))) void gemm_bf16_dma_kernel(GemmParams g)
 {
     gemm_dma_body<BM, BN, EPI, NT, WGM>(g);
-}
-
-// Small tiles (128 x 128 or 128 x 64): two BK = 64 stages, NT/64 waves in a
-// WGM x (NT/64/WGM) grid.  LDS rows are 128 B (8 chunks of 16 B),
-// chunk c of row r at position c ^ ((r >> 1) & 7): the 32 rows of a fragment
-// read (16 B each, half the wave on one chunk column) cover every bank
-// evenly.  Stage k+1 loads while stage k's MFMAs run.
-template <int BM, int BN, int EPI, int NT, int WGM>
-__global__ __launch_bounds__(NT) void gemm_bf16_k64_kernel(GemmParams g)
-{
-    constexpr int BK = 64;
-    constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
-    constexpr int RB = WM / 32, CB = WN / 32;
-    constexpr int A_INS = BM * 8 / NT, B_INS = BN * 8 / NT;
-    constexpr int STAGE = (BM + BN) * BK;
-    static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
-    extern __shared__ __align__(16) bf16_t lds[];
-
-    const int M = g.M, N = g.N, K = g.K;
-    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_of<8>(blockIdx.x, nbm, nbn, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int lr = lane & 31, lh = lane >> 5;
-
-    f32x16 acc[RB][CB];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
-
-    const int KT = K / BK;
-    auto issue = [&](int kt) {
-        bf16_t* sa = lds + (kt & 1) * STAGE;
-        bf16_t* sb = sa + BM * BK;
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int j = 0; j < A_INS; ++j) {
-            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-            const bf16_t* src = g.A + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sa + (j * NT + wave * 64) * 8;
-            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < B_INS; ++j) {
-            const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-            const bf16_t* src = g.W + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
-            bf16_t* dst = sb + (j * NT + wave * 64) * 8;
-            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
-    };
-
-    issue(0);
-    for (int kt = 0; kt < KT; ++kt) {
-        ZO_WAIT_VM(0);
-        asm volatile("s_barrier" ::: "memory");
-        if (kt + 1 < KT) issue(kt + 1);
-        const bf16_t* sa = lds + (kt & 1) * STAGE;
-        const bf16_t* sb = sa + BM * BK;
-        // Fragments of the four 16-deep steps.  With a fused epilogue (GELU,
-        // residual) all of them are read first and the MFMAs follow, the
-        // scheduling barriers keeping the compiler from moving each read down
-        // next to its MFMA (where it waits before every MFMA); with the plain
-        // store epilogue the reads stay per step, which measured faster there.
-        constexpr bool HOIST = EPI != EPI_STORE;
-        constexpr int NF = HOIST ? 4 : 1;
-        bf16x8 af[NF][RB], bfr[NF][CB];
-        auto read_step = [&](int ks, int f) {
-            const int lc = 2 * ks + lh;
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const int row = wm * WM + i * 32 + lr;
-                af[f][i] = *reinterpret_cast<const bf16x8*>(sa + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < CB; ++j) {
-                const int row = wn * WN + j * 32 + lr;
-                bfr[f][j] = *reinterpret_cast<const bf16x8*>(sb + (row * 8 + (lc ^ ((row >> 1) & 7))) * 8);
-            }
-        };
-        auto mma_step = [&](int f) {
-#pragma unroll
-            for (int i = 0; i < RB; ++i)
-#pragma unroll
-                for (int j = 0; j < CB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f][i], bfr[f][j], acc[i][j], 0, 0, 0);
-        };
-        if constexpr (HOIST) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) read_step(ks, ks);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) mma_step(ks);
-            __builtin_amdgcn_sched_barrier(0);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                read_step(ks, 0);
-                mma_step(0);
-            }
-        }
-        // every wave is done reading this stage before the next issue refills it
-        asm volatile("s_barrier" ::: "memory");
-    }
-    gemm_epilogue<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
 }
 
 // Per-row cross-entropy (logsumexp_r - pick_r) for rows r with r % S != S-1.
@@ -1449,21 +1361,12 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
         KernelTimer timer(fam, s);
         kern<<<blocks, kThreads, lds, s>>>(gp, p);
     } else {
-        // 256-wide tiles: 4 waves of 128 x 128; 128-wide: 8 waves of 32 x 64,
-        // or 4 of 64 x 64 for the LM head (its cross-entropy epilogue needs
-        // two wave columns); two BK = 64 stages throughout (K % 64 == 0)
+        // every tile: 4 waves of 16x16x32 MFMAs, two BK = 64 stages
         constexpr bool big = BM == 256;
-        constexpr bool eight = !big && EPI != EPI_LMHEAD;
         constexpr size_t stages = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
         constexpr size_t lds = std::max(stages, epilogue_lds_bytes<BM, BN>());
-        void (*kern)(GemmParams);
-        int threads = big ? kBigThreads : eight ? kDmaThreads : kThreads;
-        if constexpr (big)
-            kern = gemm_bf16_dma_kernel<BM, BN, EPI, kBigThreads, kBigWavesM>;
-        else if constexpr (eight)
-            kern = gemm_bf16_k64_kernel<BM, BN, EPI, 512, 4>;
-        else
-            kern = gemm_bf16_k64_kernel<BM, BN, EPI, kThreads, 2>;
+        void (*kern)(GemmParams) = gemm_bf16_dma_kernel<BM, BN, EPI, kGemmThreads, kGemmWavesM>;
+        const int threads = kGemmThreads;
         static bool attr = false;
         if (!attr) {
             if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
