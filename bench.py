@@ -48,7 +48,7 @@ TRAFFIC = {
     "gemm_bf16:opt30b:r6": (2 * (4.0400 + 1.2149 + 5.2949 + 4.8819) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r6"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r7"}
 
 
 def parse():
@@ -74,6 +74,8 @@ def parse():
     p.add_argument("--gemm", default=None, metavar="M,N,K",
                    help="instead of a step: time one stored-weight bf16 GEMM C = A W^T of this shape "
                         "(--steps calls after --warmup), for kernel measurements")
+    p.add_argument("--gemm-epi", type=int, default=0, choices=[0, 1, 2, 3],
+                   help="the --gemm epilogue: 0 store, 1 GELU, 2 ReLU, 3 residual (C += product)")
     p.add_argument("--attention", default=None, metavar="B,S,H,DH",
                    help="instead of a step: time the decoders' causal attention kernel on a bf16 QKV of this "
                         "shape (--steps calls after --warmup), for kernel measurements")
@@ -271,26 +273,27 @@ def cpu_baseline_probe_parallel(info, seconds=8.0):
                       f"({sum(r for r, _ in res)} steps in all)"}
 
 
-def gemm_only(torch, zo, shape, steps, warmup):
-    """One layer GEMM of the decoders, C = A W^T in bf16 (fp32 accumulate,
-    plain store), through the C ABI's debug entry; prints its time and rate."""
+def gemm_only(torch, zo, shape, steps, warmup, epi=0):
+    """One layer GEMM of the decoders, C = epi(A W^T) in bf16 (fp32 accumulate;
+    epilogue 0 plain store, 1 GELU, 2 ReLU, 3 residual), through the C ABI's
+    debug entry; prints its time and rate."""
     M, N, K = shape
     g = torch.Generator(device="cuda").manual_seed(0)
     A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
     W = (torch.randn(N, K, device="cuda", generator=g) * 0.05).to(torch.bfloat16).view(torch.int16)
     C = torch.zeros(M * N, dtype=torch.int16, device="cuda")
     for _ in range(max(warmup, 1)):
-        zo.debug_gemm_bf16(A, W, C, M, N, K, 0)
+        zo.debug_gemm_bf16(A, W, C, M, N, K, epi)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        zo.debug_gemm_bf16(A, W, C, M, N, K, 0)
+        zo.debug_gemm_bf16(A, W, C, M, N, K, epi)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    print(json.dumps({"gemm_bf16": {"M": M, "N": N, "K": K}, "calls": steps, "ms": round(ms, 4),
+    print(json.dumps({"gemm_bf16": {"M": M, "N": N, "K": K, "epi": epi}, "calls": steps, "ms": round(ms, 4),
                       "TFLOP/s": round(tflops, 1), "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}),
           flush=True)
 
@@ -443,7 +446,7 @@ def main():
     from zeroth_order_backprop_amd import inputs, zo
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.gemm:
-        gemm_only(torch, zo, [int(x) for x in args.gemm.split(",")], args.steps, args.warmup)
+        gemm_only(torch, zo, [int(x) for x in args.gemm.split(",")], args.steps, args.warmup, args.gemm_epi)
         return
     if args.attention:
         attention_only(torch, zo, [int(x) for x in args.attention.split(",")], args.steps, args.warmup)

@@ -33,9 +33,12 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ void zo_raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds, int size,
                                        int voffset, int soffset, int offset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.lds");
-// 16-byte buffer store (an offset past the resource's size writes nothing).
+// 16-byte buffer load / store (an offset past the resource's size reads
+// zeros, writes nothing).
 __device__ void zo_raw_buffer_store_x4(i32x4_t data, i32x4_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+__device__ i32x4_t zo_raw_buffer_load_x4(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
 namespace zo {
 namespace {
@@ -595,10 +598,6 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 #define ZO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define ZO_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
-// Writes a block tile of 16x16 accumulators: element r of a 16x16 block is
-// row 4 (lane / 16) + r, column lane % 16.  Same stores as gemm_epilogue_impl
-// (through LDS, 16-byte coalesced) and the same LM-head partials, reduced over
-// the 16 lanes of a row group.
 // The activated, bf16-rounded tile of 16x16 accumulators into `smem`, rows
 // padded by 8 bf16 (element r of a 16x16 block: row 4 (lane / 16) + r, column
 // lane % 16).
@@ -625,9 +624,13 @@ __device__ __forceinline__ void epilogue16_stage(f32x4 (&acc)[RB][CB], bf16_t* s
             }
 }
 
-template <int BM, int BN, int EPI, int NT, int WGM, int RB, int CB>
-__device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn,
-                                                bf16_t* smem)
+// The LM head's fused cross-entropy partials from a block tile of 16x16
+// accumulators (element r of a 16x16 block: row 4 (lane / 16) + r, column
+// lane % 16): per row the max and the sum of exp(logit - max) over the tile's
+// columns, reduced over the 16 lanes of a row group and the two wave columns,
+// plus the target logit when the target column lies in this tile.
+template <int BM, int BN, int NT, int WGM, int RB, int CB>
+__device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn)
 {
     constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
     static_assert(WM == RB * 16 && WN == CB * 16, "wave tile mismatch");
@@ -635,40 +638,7 @@ __device__ __forceinline__ void gemm_epilogue16(const GemmParams& g, f32x4 (&acc
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
     const int l16 = lane & 15, lq = lane >> 4;
-    if constexpr (EPI != EPI_LMHEAD) {
-        constexpr int LDC = BN + 8;
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-            for (int j = 0; j < CB; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * WM + i * 16 + 4 * lq + r;
-                    const int col = wn * WN + j * 16 + l16;
-                    float v = acc[i][j][r];
-                    if constexpr (EPI == EPI_GELU) v = gelu_erf(v);
-                    if constexpr (EPI == EPI_RELU) v = fmaxf(v, 0.0f);
-                    smem[row * LDC + col] = f2bf(v);
-                }
-        __syncthreads();
-        constexpr int CPR = BN / 8;
-#pragma unroll 4
-        for (int p = tid; p < BM * CPR; p += NT) {
-            const int row = p / CPR, cc = p % CPR;
-            const int gr = m0 + row, gc = n0 + 8 * cc;
-            if (gr >= M || gc >= N) continue;
-            uint4 v = *reinterpret_cast<const uint4*>(smem + row * LDC + 8 * cc);
-            uint4* dst = reinterpret_cast<uint4*>(g.C + (size_t)gr * N + gc);
-            if constexpr (EPI == EPI_RESID) {
-                const uint4 h = *dst;
-                auto add2 = [](uint32_t hw, uint32_t pw) {
-                    return pack2(bf2f(hw & 0xFFFF) + bf2f(pw & 0xFFFF), bf2f(hw >> 16) + bf2f(pw >> 16));
-                };
-                v = uint4{add2(h.x, v.x), add2(h.y, v.y), add2(h.z, v.z), add2(h.w, v.w)};
-            }
-            *dst = v;
-        }
-    } else {
+    {
         static_assert(WGN == 2, "LM-head partials assume two wave columns");
         __shared__ float part_m[2][BM], part_s[2][BM];
 #pragma unroll
@@ -788,10 +758,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     constexpr int INS = A_INS + B_INS;
     constexpr int STAGE = (BM + BN) * BK;
     static_assert(A_INS * NT == BM * 8 && B_INS * NT == BN * 8, "tile / thread mismatch");
-    // Stored epilogues overlap the next tile's first loads; the residual one
-    // (its h reads would need twice the registers) and the LM head's
+    // Stored epilogues overlap the next tile's first loads; the LM head's
     // partials finish before the next tile starts.
-    constexpr bool OVERLAP = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RELU;
+    constexpr bool OVERLAP = EPI != EPI_LMHEAD;
     // output chunks (16 B) per row and per thread
     constexpr int CPR = BN / 8, NST = BM * CPR / NT, LDC = BN + 8;
     static_assert(NST * NT == BM * CPR, "tile / thread mismatch");
@@ -933,7 +902,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int next = tile + (int)gridDim.x;
     const bool more = next < ntiles;
     if constexpr (!OVERLAP) {
-        gemm_epilogue16<BM, BN, EPI, NT, WGM>(g, acc, m0, n0, tn, lds);
+        lmhead_epilogue16<BM, BN, NT, WGM>(g, acc, m0, n0, tn);
         // (its stores then complete before the next tile's first wait ends)
         if (!more) break;
         __syncthreads();  // the epilogue's LDS use is over
@@ -942,20 +911,47 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         issue(0);
         issue(1);
     } else {
-        // The tile goes through LDS (rows padded by 8 bf16) into registers;
-        // once every wave has its chunks the next tile's first two stages are
-        // issued, and only then this tile's stores: the next tile's first
-        // wait then covers its own loads, not these stores.
+        // The tile goes through LDS (rows padded by 8 bf16) into registers
+        // (with the residual, h added there); once every wave has its chunks
+        // the next tile's first two stages are issued, and only then this
+        // tile's stores: the next tile's first wait then covers its own
+        // loads, not these stores.
         epilogue16_stage<BM, BN, EPI, NT, WGM>(acc, lds);
         __syncthreads();
+        // output chunk k of this thread: tile row p / CPR, 16-byte column p % CPR
+        const int cm0 = m0, cn0 = n0;
+        auto offs = [&](int k) {
+            const int p = k * NT + tid, gr = cm0 + p / CPR, gc = cn0 + 8 * (p % CPR);
+            return (gr < M && gc < N) ? (gr * N + gc) * 2 : (int)0x80000000u;  // past the end: dropped
+        };
+        if constexpr (EPI == EPI_RESID) {
+            // h + bf16(product), rounded once more to bf16, back into this
+            // thread's staged chunks; h read in batches of 8 chunks (every
+            // load of a batch in flight at once)
+            constexpr int HB = NST < 8 ? NST : 8;
+            static_assert(NST % HB == 0, "whole batches");
+            auto add2 = [](uint32_t hw, uint32_t pw) {
+                return pack2(bf2f(hw & 0xFFFF) + bf2f(pw & 0xFFFF), bf2f(hw >> 16) + bf2f(pw >> 16));
+            };
+#pragma unroll
+            for (int hb = 0; hb < NST / HB; ++hb) {
+                i32x4_t hv[HB];
+#pragma unroll
+                for (int k = 0; k < HB; ++k) hv[k] = zo_raw_buffer_load_x4(rc, offs(hb * HB + k), 0, 0);
+#pragma unroll
+                for (int k = 0; k < HB; ++k) {
+                    const int p = (hb * HB + k) * NT + tid;
+                    uint4* sp = reinterpret_cast<uint4*>(lds + (p / CPR) * LDC + 8 * (p % CPR));
+                    const uint4 h = __builtin_bit_cast(uint4, hv[k]), v = *sp;
+                    *sp = uint4{add2(h.x, v.x), add2(h.y, v.y), add2(h.z, v.z), add2(h.w, v.w)};
+                }
+            }
+        }
         uint4 vals[NST];
-        int offs[NST];
 #pragma unroll
         for (int k = 0; k < NST; ++k) {
-            const int p = k * NT + tid, row = p / CPR, cc = p % CPR;
-            const int gr = m0 + row, gc = n0 + 8 * cc;
-            vals[k] = *reinterpret_cast<const uint4*>(lds + row * LDC + 8 * cc);
-            offs[k] = (gr < M && gc < N) ? (gr * N + gc) * 2 : (int)0x80000000u;  // past the end: dropped
+            const int p = k * NT + tid;
+            vals[k] = *reinterpret_cast<const uint4*>(lds + (p / CPR) * LDC + 8 * (p % CPR));
         }
         ZO_WAIT_LGKM0();
         asm volatile("s_barrier" ::: "memory");  // every wave has read its chunks
@@ -966,7 +962,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             issue(1);
         }
 #pragma unroll
-        for (int k = 0; k < NST; ++k) zo_raw_buffer_store_x4(__builtin_bit_cast(i32x4_t, vals[k]), rc, offs[k], 0, 0);
+        for (int k = 0; k < NST; ++k) zo_raw_buffer_store_x4(__builtin_bit_cast(i32x4_t, vals[k]), rc, offs(k), 0, 0);
         if (!more) break;
         stores_pending = true;
     }
