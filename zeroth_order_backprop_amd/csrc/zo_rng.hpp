@@ -14,10 +14,11 @@
 // Box-Muller: u_r = ((x_even >> 8) + 1) 2^-24, u_t = (x_odd >> 8) 2^-24,
 // r = sqrt(-2 ln u_r), (z_even, z_odd) = r (cos 2 pi u_t, sin 2 pi u_t).
 //
-// The fp32 evaluation: ln u_r from the hardware log2 with the scaling carried
-// exactly, sin/cos of a quarter turn via their Taylor series on [-pi/4, pi/4]
-// after an exact integer quadrant reduction, and sqrt carried as a value plus
-// its residual so the final product is rounded once.
+// The fp32 evaluation works in base-2 logarithms: sqrt(-log2 u_r) from the
+// hardware log2 and rsq with one Newton correction carried as a residual, the
+// constant sqrt(2 ln 2) folded into minimax sin/cos polynomials of a quarter
+// turn after an exact integer quadrant reduction, and one rounding of the
+// final product.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,77 +57,85 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
     }
 }
 
-// ---- constants from the series definitions (evaluated at compile time) ----
-constexpr double kPi = 3.14159265358979323846264338327950288;
-constexpr double kHalfPi = kPi / 2.0;
+// ---- Box-Muller in base-2 logarithms ----
+// With m = -log2 u_r the radius is sqrt(-2 ln u_r) = K sqrt(m), K = sqrt(2 ln 2).
+// K is carried by the quarter-turn polynomials below, so the radius needs only
+// sqrt(m), and m itself is the hardware log2 negated (no rounded -2 ln 2 factor).
+//
+// K sin(pi t / 2) = t (kS1 + kS3 t^2 + kS5 t^4 + kS7 t^6) and
+// K cos(pi t / 2) = kC0 + kC2 t^2 + ... + kC8 t^8 on t in [-1/2, 1/2]: minimax
+// fits (Remez exchange, absolute error) with fp32 coefficients chosen for the
+// smallest error of the fp32 Horner evaluation over every reduced angle
+// t = i 2^-22; derived by gen_trig_coefs.py beside this header.  Evaluated in
+// fp32 they stay within 6.5e-8 (sin) and 7.7e-8 (cos) of the exact values;
+// kC0 is the fp32 value nearest K (0.13 of its last place off).
+constexpr float kS1 = 0x1.d976f4p+0f;    // 1.84947133
+constexpr float kS3 = -0x1.85688ep-1f;   // -0.760563314
+constexpr float kS5 = 0x1.80402cp-4f;    // 0.0938111991
+constexpr float kS7 = -0x1.625a8cp-8f;   // -0.00540700834
+constexpr float kC0 = 0x1.2d6abep+0f;    // 1.17741001
+constexpr float kC2 = -0x1.73dbb6p+0f;   // -1.45257127
+constexpr float kC4 = 0x1.31d74p-2f;     // 0.298672676
+constexpr float kC6 = -0x1.9267b8p-6f;   // -0.0245608613
+constexpr float kC8 = 0x1.16e82p-10f;    // 0.00106394477
 
-constexpr double cpow(double x, int n) { return n == 0 ? 1.0 : x * cpow(x, n - 1); }
-constexpr double cfact(int n) { return n <= 1 ? 1.0 : n * cfact(n - 1); }
-// sin(pi t / 2) = sum_k (-1)^k (pi/2)^(2k+1) t^(2k+1) / (2k+1)!
-constexpr double sin_coef(int k) { return (k % 2 ? -1.0 : 1.0) * cpow(kHalfPi, 2 * k + 1) / cfact(2 * k + 1); }
-// cos(pi t / 2) = sum_k (-1)^k (pi/2)^(2k) t^(2k) / (2k)!
-constexpr double cos_coef(int k) { return (k % 2 ? -1.0 : 1.0) * cpow(kHalfPi, 2 * k) / cfact(2 * k); }
-constexpr float kS1 = (float)sin_coef(0), kS3 = (float)sin_coef(1), kS5 = (float)sin_coef(2),
-                kS7 = (float)sin_coef(3), kS9 = (float)sin_coef(4);
-constexpr float kC2 = (float)cos_coef(1), kC4 = (float)cos_coef(2), kC6 = (float)cos_coef(3),
-                kC8 = (float)cos_coef(4), kC10 = (float)cos_coef(5);
-constexpr double kLn2 = 0.693147180559945309417232121458176568;
+// v_mul_legacy_f32: a product in which a zero operand gives 0 even against an
+// infinity (the LLVM intrinsic, reached through its symbol name).
+__device__ float fmul_zero_safe(float a, float b) __asm("llvm.amdgcn.fmul.legacy");
 
-// -2 ln(u_r) for u_r = (a + 1) 2^-24, a = x >> 8, as L + L_lo.  u_r is exact
-// in fp32; the hardware log2 (v_log_f32) is within one ulp on every one of
-// these 2^24 inputs, and the factor -2 ln 2 is applied in two parts so that
-// L + L_lo carries no further rounding.
-constexpr float kM2Ln2Hi = (float)(-2.0 * kLn2);
-constexpr float kM2Ln2Lo = (float)(-2.0 * kLn2 - (double)kM2Ln2Hi);
-__device__ __forceinline__ void minus_two_log_radius(uint32_t x, float& L, float& L_lo)
+// sqrt(-log2 u_r) for u_r = (a + 1) 2^-24, a = x >> 8, as R + R_lo.  u_r is
+// exact in fp32 and the hardware log2 (v_log_f32) is within one ulp on every
+// one of these 2^24 inputs.  R = m rsq(m) and R_lo = (m - R^2) rsq(m) / 2 is
+// one Newton correction, so R + R_lo is sqrt(m) to well below fp32 rounding.
+// The zero-safe multiply (0 times anything is 0) makes u_r = 1, m = 0, give
+// R = R_lo = 0 although rsq(0) is infinite.
+__device__ __forceinline__ void log2_radius(uint32_t x, float& R, float& R_lo)
 {
-    const float u = (float)((x >> 8) + 1u) * 0x1p-24f;
-    const float l2 = __builtin_amdgcn_logf(u);
-    L = l2 * kM2Ln2Hi;
-    L_lo = fmaf(l2, kM2Ln2Lo, fmaf(l2, kM2Ln2Hi, -L));
+    const float u = fmaf((float)(x >> 8), 0x1p-24f, 0x1p-24f);
+    const float m = -__builtin_amdgcn_logf(u);           // >= 0
+    const float y = __builtin_amdgcn_rsqf(m);
+    R = fmul_zero_safe(m, y);
+    const float res = fmaf(-R, R, m);
+    R_lo = fmul_zero_safe(res, 0.5f * y);
 }
 
-// (cos, sin) of 2 pi u_t for u_t = (x >> 8) 2^-24.
-__device__ __forceinline__ void unit_circle(uint32_t x, float& c, float& s)
+// K (cos, sin) of 2 pi u_t for u_t = (x >> 8) 2^-24.  The angle's 24 bits are
+// b = x >> 8; the nearest quarter turn is k = (b + 2^21) >> 22 and the rest
+// t = (b - k 2^22) 2^-22 is the sign-extended low 22 bits of b, read straight
+// from x.  Rotating (cos, sin)(pi t / 2) by k quarter turns swaps the pair for
+// odd k and negates: the cos part for k = 1, 2 and the sin part for k = 2, 3
+// (k mod 4).  With y = x + 2^29 (mod 2^32), bit 30 of y is k's low bit, bit 31
+// its high bit, and bit 31 of y + 2^30 is set exactly for k = 1, 2.
+__device__ __forceinline__ void unit_circle_k(uint32_t x, float& c, float& s)
 {
-    const uint32_t b = x >> 8;                           // 24-bit angle
-    const uint32_t k = (b + (1u << 21)) >> 22;           // nearest quarter turn, 0..4
-    const int ti = (int)b - (int)(k << 22);              // in [-2^21, 2^21)
+    const int ti = (int)(x << 2) >> 10;                  // bits 8..29 of x, sign-extended
     const float t = (float)ti * 0x1p-22f;                // exact, in [-1/2, 1/2)
     const float t2 = t * t;
-    float ps = kS9;
-    ps = fmaf(ps, t2, kS7);
-    ps = fmaf(ps, t2, kS5);
+    float ps = fmaf(kS7, t2, kS5);
     ps = fmaf(ps, t2, kS3);
     ps = fmaf(ps, t2, kS1);
-    const float st = ps * t;                             // sin(pi t / 2)
-    float pc = kC10;
-    pc = fmaf(pc, t2, kC8);
-    pc = fmaf(pc, t2, kC6);
-    pc = fmaf(pc, t2, kC4);
-    pc = fmaf(pc, t2, kC2);
-    const float ct = fmaf(pc, t2, 1.0f);                 // cos(pi t / 2)
-    // rotate by k quarter turns: (cos, sin)(theta + k pi/2)
-    const uint32_t q = k & 3u;
-    const float a0 = (q & 1u) ? st : ct;
-    const float a1 = (q & 1u) ? ct : st;
-    c = ((q + 1u) & 2u) ? -a0 : a0;                      // q = 1, 2 negate cos part
-    s = (q & 2u) ? -a1 : a1;                             // q = 2, 3 negate sin part
+    const float st = ps * t;                             // K sin(pi t / 2)
+    float ct = fmaf(kC8, t2, kC6);
+    ct = fmaf(ct, t2, kC4);
+    ct = fmaf(ct, t2, kC2);
+    ct = fmaf(ct, t2, kC0);                              // K cos(pi t / 2)
+    const uint32_t y = x + (1u << 29), y2 = x + (3u << 29);
+    const uint32_t odd = (uint32_t)((int)(y << 1) >> 31); // all ones for odd k
+    const uint32_t sb = __float_as_uint(st), cb = __float_as_uint(ct);
+    const uint32_t a0 = (odd & sb) | (~odd & cb);
+    const uint32_t a1 = (odd & cb) | (~odd & sb);
+    c = __uint_as_float(a0 ^ (y2 & 0x80000000u));
+    s = __uint_as_float(a1 ^ (y & 0x80000000u));
 }
 
 // Box-Muller pair from two words.
 __device__ __forceinline__ void box_muller(uint32_t x_even, uint32_t x_odd, float& z_even, float& z_odd)
 {
-    float L, L_lo;
-    minus_two_log_radius(x_even, L, L_lo);               // L >= 0
-    const float r = __builtin_amdgcn_sqrtf(L);
-    // r + r_lo = sqrt(L + L_lo) to well below fp32 rounding; r_lo = (L + L_lo - r^2) / (2 r)
-    const float res = fmaf(-r, r, L) + L_lo;
-    const float r_lo = (L > 0.0f) ? res * (0.5f * __builtin_amdgcn_rcpf(r)) : 0.0f;
-    float c, s;
-    unit_circle(x_odd, c, s);
-    z_even = fmaf(c, r, c * r_lo);
-    z_odd = fmaf(s, r, s * r_lo);
+    float R, R_lo, c, s;
+    log2_radius(x_even, R, R_lo);
+    unit_circle_k(x_odd, c, s);
+    z_even = fmaf(c, R, c * R_lo);
+    z_odd = fmaf(s, R, s * R_lo);
 }
 
 // Four Gaussians for elements 4q .. 4q+3 of counter stream `stream` of
