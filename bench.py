@@ -67,8 +67,9 @@ def parse():
                         "directions per branch instead of SPSA steps")
     p.add_argument("--dust", default=None, metavar="K1,K2",
                    help="MLP: Dust steps (activation noise) with K1 hidden-layer and K2 head draws")
-    p.add_argument("--mode", default=None, choices=["inplace", "fused"],
-                   help="step mode (default: in place for the decoders, fused for the fp32 models)")
+    p.add_argument("--mode", default=None, choices=["inplace", "fused", "copies"],
+                   help="step mode (default: copies for the GPT-small shape, in place for the OPT shapes, "
+                        "fused for the fp32 models)")
     p.add_argument("--dirs", default="gauss", choices=["gauss", "q8"],
                    help="direction distribution: Gaussian, or 8-bit packed (in-place decoder workloads)")
     p.add_argument("--gemm", default=None, metavar="M,N,K",
@@ -170,14 +171,20 @@ def build_decoder(torch, zo, inputs, name, dirs="gauss"):
     tok = torch.from_numpy(inputs.zipf_tokens(0, B, S, V)).cuda()
     batch = zo.make_batch(tokens=tok, batch=B, seq=S)
     M = B * S
+    # default mode: in place for the large shapes (the memory the pages
+    # save), copies for the GPT-small shape (its 64 evaluations of 4096 rows
+    # run 8 side by side; 2 GB of copies)
+    mode = "copies" if name == "gpt" else "inplace"
     gemm_flops = L * (2.0 * M * D * 3 * D + 2.0 * M * D * D + 2 * 2.0 * M * D * F)
     attn_flops = L * 2.0 * B * H * S * S * (D // H)  # causal half of 4 B H S^2 dh
     head_flops = 2.0 * M * D * V
     info = {
         "workload": f"decoder {name}: {L} layers, d={D}, {H} heads, FFN {F}, vocab {V}, bf16 "
-                    f"({total * 2 / 1e9:.2f} GB of weights in place); batch {B} x seq {S} "
-                    f"Zipf(1.1) tokens; N={N} probes, eps=1e-3, lr={lr:g}; in-place mode",
-        "probes": N, "eps": 1e-3, "lr": lr, "mode": "inplace", "batch": B, "params": int(total),
+                    f"({total * 2 / 1e9:.2f} GB of weights); batch {B} x seq {S} "
+                    f"Zipf(1.1) tokens; N={N} probes, eps=1e-3, lr={lr:g}; " + (
+                        "copies mode (D(W +- eps z_i) written to arena copies, evaluated side by side)"
+                        if mode == "copies" else "in-place mode"),
+        "probes": N, "eps": 1e-3, "lr": lr, "mode": mode, "batch": B, "params": int(total),
         "flops_per_eval": gemm_flops + attn_flops + head_flops, "gemm_flops_per_eval": gemm_flops,
         "head_flops_per_eval": head_flops, "attn_flops_per_eval": attn_flops,
         "dtype": "bf16", "kernel": "gemm_bf16", "peak_tflops": BF16_PEAK_TFLOPS,
@@ -460,12 +467,16 @@ def main():
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     if args.mode:
-        if args.mode == "fused" and args.dirs != "gauss":
-            print("bench.py: fused steps apply Gaussian directions only", file=sys.stderr)
+        if args.mode != "inplace" and args.dirs != "gauss":
+            print("bench.py: fused and copies steps apply Gaussian directions only", file=sys.stderr)
+            sys.exit(2)
+        if args.mode == "copies" and args.workload not in DECODERS:
+            print("bench.py: copies steps are for the decoder workloads", file=sys.stderr)
             sys.exit(2)
         info["mode"] = args.mode
-        info["workload"] = info["workload"].rsplit(";", 1)[0] + (
-            "; in-place mode" if args.mode == "inplace" else "; perturbed-tile (fused) mode")
+        info["workload"] = info["workload"].rsplit(";", 1)[0] + {
+            "inplace": "; in-place mode", "fused": "; perturbed-tile (fused) mode",
+            "copies": "; copies mode (D(W +- eps z_i) written to arena copies, evaluated side by side)"}[args.mode]
     N = info["probes"]
     pc = 1 if args.precond else 0
     split = None
@@ -497,7 +508,7 @@ def main():
     losses_all = torch.zeros(total_steps, n_loss, dtype=torch.float64, device="cuda")
     g_all = torch.zeros(total_steps, n_g, dtype=torch.float64, device="cuda")
     g2 = torch.zeros(2 * split[0] * split[1] if split else 1, dtype=torch.float64, device="cuda")
-    mode = zo.ZO_MODE_FUSED if info["mode"] == "fused" else zo.ZO_MODE_INPLACE
+    mode = {"fused": zo.ZO_MODE_FUSED, "copies": zo.ZO_MODE_COPIES}.get(info["mode"], zo.ZO_MODE_INPLACE)
 
     def step(seed):
         losses, g = losses_all[seed], g_all[seed]
@@ -607,9 +618,13 @@ def main():
     arena_bytes = info["params"] * (2 if info["dtype"] == "bf16" else 4)
     for fam in ("perturb", "update"):
         if fam in kernels:
-            gbs = 2.0 * arena_bytes / (kernels[fam]["avg_us"] * 1e-6) / 1e9
+            # a copies-mode perturbation reads the arena once and writes 2P copies:
+            # per step (launches + 2N) arena sizes
+            per_launch = (2.0 * arena_bytes if not (fam == "perturb" and info["mode"] == "copies") else
+                          (kernels[fam]["launches_per_step"] + 2 * N) * arena_bytes / kernels[fam]["launches_per_step"])
+            gbs = per_launch / (kernels[fam]["avg_us"] * 1e-6) / 1e9
             step_passes[fam] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                "avg_us": kernels[fam]["avg_us"], "bytes": 2 * arena_bytes,
+                                "avg_us": kernels[fam]["avg_us"], "bytes": int(per_launch),
                                 **({"probes": N} if fam == "update" else {}),
                                 **({"note": "arena resident in the last-level cache (not an HBM figure)"}
                                    if arena_bytes < 256e6 else {})}
@@ -645,7 +660,7 @@ def main():
                       if dust else {})},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None if (split or dust or args.dirs != "gauss" or args.mode == "fused")
+                     "traffic": None if (split or dust or args.dirs != "gauss" or args.mode in ("fused", "copies"))
                      else TRAFFIC.get(KERNEL_REV.get(args.workload) or "", None),
                      "kernel": ((f"gemm_f32 direction-product GEMM (split-bf16 MFMA), "
                                  f"{evals_per_step if split else 2 * N} evaluations per step"

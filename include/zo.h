@@ -60,7 +60,7 @@ typedef enum { ZO_MODEL_LSQ = 0, ZO_MODEL_MLP = 1, ZO_MODEL_DECODER = 2 } zo_mod
 
 typedef enum { ZO_ACT_GELU = 0, ZO_ACT_RELU = 1 } zo_act;
 
-typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1 } zo_mode;
+typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1, ZO_MODE_COPIES = 2 } zo_mode;
 
 /*
  * Direction distribution of a model (zo_model_desc.dirs).
@@ -225,6 +225,16 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
  * One SPSA step.  mode INPLACE: for i < N: perturb(+eps), L+, perturb(-2 eps),
  * L-, perturb(+eps).  mode FUSED: every evaluation sees D(W +- eps z_i) of the
  * unmodified W (one launch covers all 2N evaluations where the model allows).
+ * mode COPIES (decoder, Gaussian directions): the same evaluation weights as
+ * FUSED, D(W +- eps z_i), written out: one pass over W fills 2P copies of the
+ * arena for P probes, then one forward evaluates all 2P copies side by side
+ * (the rows of every copy in the same launches); P is chosen so a forward
+ * covers about 32768 token rows (at most 16 probes, at most N), and P = 1
+ * unless batch * seq is a multiple of 256.  The copies and their workspace
+ * (2P (arena + zo_workspace_bytes) bytes) are allocated on the model's first
+ * COPIES step and held until zo_model_destroy; ZO_ERR_WORKSPACE if the device
+ * cannot hold them for P = 1.  Losses equal FUSED's up to the order of the
+ * GEMM accumulations; W changes only in the update.
  * Then g_i = (L+_i - L-_i) / (2 eps) and zo_update.
  * losses_dev: device fp64 [2N] as (L+_0, L-_0, L+_1, ...); g_dev: device fp64
  * [N].  A non-finite loss leaves W unchanged by the update (in place: after
@@ -254,7 +264,8 @@ zo_status zo_step(zo_model* m, const zo_batch* b, const zo_step_cfg* cfg, double
  * calls that overlap on one GPU (concurrent streams or threads) race and give
  * undefined results; serialise them.  Nothing in the array needs to start at
  * zero.  With zo_timing_enable on, the timing bookkeeping allocates host
- * memory; leave it off here.
+ * memory; leave it off here.  mode COPIES needs device memory of its own and
+ * is refused here (ZO_ERR_UNSUPPORTED).
  */
 zo_status zo_step_noalloc(const zo_model_desc* desc, void* params, uint64_t n_params, const zo_batch* b,
                           const zo_step_cfg* cfg, double* losses_dev, double* g_dev, zo_stream s);

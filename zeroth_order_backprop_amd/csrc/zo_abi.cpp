@@ -296,6 +296,8 @@ struct zo_model {
     std::vector<zo_param_info> layout;
     std::vector<uint64_t> offsets;
     void* graphs = nullptr;  // captured decoder forwards (decoder_graphs_free)
+    void* copies = nullptr;  // the copies mode's arena copies + grouped workspace
+    size_t copies_bytes = 0;
 };
 
 extern "C" {
@@ -410,7 +412,13 @@ zo_status zo_model_create(const zo_model_desc* desc, void* params, uint64_t n_pa
 
 zo_status zo_model_destroy(zo_model* m)
 {
-    if (m) decoder_graphs_free(m->graphs);
+    if (m) {
+        decoder_graphs_free(m->graphs);
+        if (m->copies) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(m->copies);
+        }
+    }
     delete m;
     return ZO_OK;
 }
@@ -424,6 +432,8 @@ static ModelView view_of(zo_model* m)
     v.ws_bytes = m->ws_bytes;
     v.offsets = m->offsets.data();
     v.graphs = &m->graphs;
+    v.copies = &m->copies;
+    v.copies_bytes = &m->copies_bytes;
     return v;
 }
 
@@ -482,11 +492,66 @@ static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cf
     const uint32_t N = cfg->n_probes;
     if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
     if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
-    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
+    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED && cfg->mode != ZO_MODE_COPIES)
+        return fail(ZO_ERR_INVALID, "bad mode");
     if (cfg->precond != 0 && cfg->precond != 1) return fail(ZO_ERR_INVALID, "precond must be 0 or 1");
     if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
     if (cfg->mode == ZO_MODE_FUSED && d.dirs != ZO_DIRS_GAUSS)
         return fail(ZO_ERR_UNSUPPORTED, "fused steps apply Gaussian directions only; use the in-place mode");
+    if (cfg->mode == ZO_MODE_COPIES && (d.kind != ZO_MODEL_DECODER || d.dirs != ZO_DIRS_GAUSS))
+        return fail(ZO_ERR_UNSUPPORTED, "copies steps are for decoders with Gaussian directions");
+    return ZO_OK;
+}
+
+// ---- the copies mode ----
+// Evaluations at D(W +- eps z_i) materialised: 2P arena copies and the
+// workspace of 2P evaluations side by side, in one device buffer owned by the
+// model.  P: about kCopyRows token rows per forward, at most kMaxCopyProbes
+// and N, the grouped activations under 2 GiB per buffer (the GEMMs' 32-bit
+// offsets), and the buffer within half the free device memory.
+constexpr int64_t kCopyRows = 32768;
+constexpr uint32_t kMaxCopyProbes = 16;
+
+static uint64_t copy_stride(uint64_t n_params) { return (n_params + 127) / 128 * 128; }
+
+static uint32_t copies_probes(const zo_model_desc& d, uint32_t N, int64_t rows)
+{
+    int64_t p = rows % 256 ? 1 : std::max<int64_t>(1, (kCopyRows + 2 * rows - 1) / (2 * rows));
+    p = std::min<int64_t>(p, std::min<uint32_t>(N, kMaxCopyProbes));
+    const int64_t widest = std::max<int64_t>(3 * d.d_model, d.ffn);
+    while (p > 1 && 2 * p * rows * widest * 2 >= (1ll << 31)) --p;
+    return (uint32_t)p;
+}
+
+static size_t copies_bytes(const zo_model_desc& d, uint64_t n_params, uint32_t p)
+{
+    return 2 * p * copy_stride(n_params) * 2 + decoder_group_workspace(d, (int)(2 * p));
+}
+
+static zo_status copies_buffer(const ModelView& v, uint64_t n_params, uint32_t& p, void*& buf)
+{
+    if (!v.copies || !v.copies_bytes) return fail(ZO_ERR_UNSUPPORTED, "copies steps need zo_step (they allocate)");
+    size_t need = copies_bytes(v.desc, n_params, p);
+    if (*v.copies && *v.copies_bytes >= need) {
+        buf = *v.copies;
+        return ZO_OK;
+    }
+    if (*v.copies) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(*v.copies);
+        *v.copies = nullptr;
+        *v.copies_bytes = 0;
+    }
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return fail(ZO_ERR_HIP, "hipMemGetInfo failed");
+    while (p > 1 && need > free_b / 2) need = copies_bytes(v.desc, n_params, --p);
+    if (need > free_b) return fail(ZO_ERR_WORKSPACE, "copies steps need %zu bytes of device memory", need);
+    if (hipMalloc(v.copies, need) != hipSuccess) {
+        *v.copies = nullptr;
+        return fail(ZO_ERR_WORKSPACE, "cannot allocate %zu bytes for the copies step", need);
+    }
+    *v.copies_bytes = need;
+    buf = *v.copies;
     return ZO_OK;
 }
 
@@ -517,6 +582,27 @@ static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch&
             if (r2) return r2;
             if (f2) return f2;
             if (r3) return r3;
+        }
+    } else if (cfg.mode == ZO_MODE_COPIES) {
+        uint32_t P = copies_probes(d, N, (int64_t)d.batch * d.seq);
+        void* buf = nullptr;
+        if (zo_status r = copies_buffer(v, n_params, P, buf)) return r;
+        // layout: 2P copies of cs elements, then the workspace of 2P evaluations
+        const uint64_t cs = copy_stride(n_params);
+        void* ws = (char*)buf + 2 * (size_t)P * cs * 2;
+        const bool side_by_side = (int64_t)b.batch * b.seq % 256 == 0;
+        for (uint32_t k = 0; k < N; k += P) {
+            const uint32_t np = std::min(P, N - k);
+            if (zo_status r = launch_perturb_copies(v.params, buf, cs, n_params, cfg.seed, k, np, sig, st)) return r;
+            if (side_by_side) {
+                if (zo_status r = decoder_forward_groups(v, b, buf, (int)(2 * np), cs, ws, losses_dev + 2 * k, st))
+                    return r;
+                continue;
+            }
+            for (uint32_t c = 0; c < 2 * np; ++c)
+                if (zo_status r = decoder_forward_groups(v, b, (const uint16_t*)buf + c * cs, 1, 0, ws,
+                                                         losses_dev + 2 * k + c, st))
+                    return r;
         }
     } else {
         // evaluations (L+_0, L-_0, L+_1, ...) in launches of at most kMaxEvalsPerCall
@@ -572,6 +658,7 @@ zo_status zo_step_noalloc(const zo_model_desc* desc, void* params, uint64_t n_pa
                     (size_t)kScratchBytes);
     if (zo_status st = validate_batch(*desc, b)) return st;
     if (zo_status st = validate_step_cfg(*desc, cfg)) return st;
+    if (cfg->mode == ZO_MODE_COPIES) return fail(ZO_ERR_UNSUPPORTED, "copies steps allocate; use zo_step");
     void* scratch_dev = nullptr;
     if (zo_status st = scratch_of_current_device(&scratch_dev)) return st;
     if (overlap(params, n_params * dtype_size(desc->dtype), scratch_dev, kScratchBytes))
@@ -613,7 +700,8 @@ zo_status zo_replay_step(zo_model* m, const zo_step_cfg* cfg, const double* g_de
     const uint32_t N = cfg->n_probes;
     if (N == 0 || N > 1024) return fail(ZO_ERR_INVALID, "n_probes must be in 1..1024");
     if (!(cfg->eps > 0.0f)) return fail(ZO_ERR_INVALID, "eps must be positive");
-    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED) return fail(ZO_ERR_INVALID, "bad mode");
+    if (cfg->mode != ZO_MODE_INPLACE && cfg->mode != ZO_MODE_FUSED && cfg->mode != ZO_MODE_COPIES)
+        return fail(ZO_ERR_INVALID, "bad mode");
     hipStream_t st = (hipStream_t)s;
     if (cfg->mode == ZO_MODE_INPLACE) {
         // the step's perturb / restore passes, in its order, without the evaluations

@@ -88,6 +88,13 @@ __device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p)
 }
 
 // One perturbed weight (slow path: LN parameters, ragged ends).
+// Row groups: rows [g R, (g + 1) R) of a launch belong to evaluation g, whose
+// parameters sit g * stride elements after the first copy's (R = 0: one group).
+struct RowGroups {
+    int rows;
+    uint64_t stride;
+};
+
 __device__ __forceinline__ float weight1(const bf16_t* w, uint64_t i, uint64_t dir, const Pert& p)
 {
     float v = bf2f(w[i]);
@@ -129,10 +136,17 @@ __device__ __forceinline__ double wave_sumd(double v)
 __global__ __launch_bounds__(kThreads) void embed_kernel(const int32_t* __restrict__ tokens, int S, int d, int V,
                                                           const bf16_t* __restrict__ tok_emb, uint64_t tok_dir,
                                                           const bf16_t* __restrict__ pos_emb, uint64_t pos_dir,
-                                                          Pert p, bf16_t* __restrict__ h)
+                                                          Pert p, RowGroups gr, bf16_t* __restrict__ h)
 {
     const int t = blockIdx.x;
-    const int tok = tokens[t];
+    int tl = t;
+    if (gr.rows) {
+        const int gi = t / gr.rows;
+        tl = t - gi * gr.rows;
+        tok_emb += (uint64_t)gi * gr.stride;
+        pos_emb += (uint64_t)gi * gr.stride;
+    }
+    const int tok = tokens[tl];
     const int s = t % S;
     if ((unsigned)tok >= (unsigned)V) {
         for (int c = threadIdx.x; c < d; c += kThreads) h[(size_t)t * d + c] = (bf16_t)0x7FC0u;
@@ -156,11 +170,16 @@ template <int NQ>
 __global__ __launch_bounds__(kThreads) void layernorm_kernel(const bf16_t* __restrict__ h, int rows, int d,
                                                               const bf16_t* __restrict__ g, uint64_t g_dir,
                                                               const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
-                                                              bf16_t* __restrict__ x)
+                                                              RowGroups gr, bf16_t* __restrict__ x)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= rows) return;
+    if (gr.rows) {
+        const uint64_t go = (uint64_t)(t / gr.rows) * gr.stride;
+        g += go;
+        b += go;
+    }
     const int nq = d >> 2;
     const uint2* row = reinterpret_cast<const uint2*>(h + (size_t)t * d);
     float v[NQ][4];
@@ -222,11 +241,16 @@ template <int NO>
 __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* __restrict__ h, int d,
                                                                    const bf16_t* __restrict__ g, uint64_t g_dir,
                                                                    const bf16_t* __restrict__ b, uint64_t b_dir, Pert p,
-                                                                   bf16_t* __restrict__ x)
+                                                                   RowGroups gr, bf16_t* __restrict__ x)
 {
     __shared__ float part[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t t = blockIdx.x;
+    if (gr.rows) {
+        const uint64_t go = (uint64_t)(blockIdx.x / gr.rows) * gr.stride;
+        g += go;
+        b += go;
+    }
     const int no = d >> 3;
     const uint4* row = reinterpret_cast<const uint4*>(h + t * d);
     float v[NO][8];
@@ -299,14 +323,14 @@ __global__ __launch_bounds__(kThreads) void layernorm_wide_kernel(const bf16_t* 
 // row with the smallest register footprint that holds it (NQ groups of 4 per
 // lane) up to d = 2048, one block per row beyond.
 void launch_layernorm(const bf16_t* h, int rows, int d, const bf16_t* g, uint64_t g_dir, const bf16_t* b,
-                      uint64_t b_dir, const Pert& p, bf16_t* x, hipStream_t s)
+                      uint64_t b_dir, const Pert& p, bf16_t* x, hipStream_t s, RowGroups gr = RowGroups{0, 0})
 {
     const int nq = (d / 4 + 63) / 64;
     const dim3 grid((rows + 3) / 4);
-    if (nq <= 1) layernorm_kernel<1><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
-    else if (nq <= 3) layernorm_kernel<3><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
-    else if (nq <= 8) layernorm_kernel<8><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, x);
-    else layernorm_wide_kernel<kLnMaxQuads / 8><<<rows, kThreads, 0, s>>>(h, d, g, g_dir, b, b_dir, p, x);
+    if (nq <= 1) layernorm_kernel<1><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, gr, x);
+    else if (nq <= 3) layernorm_kernel<3><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, gr, x);
+    else if (nq <= 8) layernorm_kernel<8><<<grid, kThreads, 0, s>>>(h, rows, d, g, g_dir, b, b_dir, p, gr, x);
+    else layernorm_wide_kernel<kLnMaxQuads / 8><<<rows, kThreads, 0, s>>>(h, d, g, g_dir, b, b_dir, p, gr, x);
 }
 
 // ============================================================ bf16 GEMM
@@ -329,6 +353,11 @@ struct GemmParams {
     float* lm_pick;
     const int32_t* tokens;  // targets: row r's target is tokens[r + 1] (same sequence)
     int S;
+    // row groups (stored-weight kernels only): rows [g R, (g + 1) R) use the
+    // weights grp_stride * g elements after W and, in the LM head, the targets
+    // of row r - g R (R = grp_rows; 0: one group)
+    int grp_rows;
+    uint64_t grp_stride;
 };
 
 
@@ -630,7 +659,8 @@ __device__ __forceinline__ void epilogue16_stage(f32x4 (&acc)[RB][CB], bf16_t* s
 // columns, reduced over the 16 lanes of a row group and the two wave columns,
 // plus the target logit when the target column lies in this tile.
 template <int BM, int BN, int NT, int WGM, int RB, int CB>
-__device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn)
+__device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, const int32_t* tokens, f32x4 (&acc)[RB][CB],
+                                                  int m0, int n0, int tn)
 {
     constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
     static_assert(WM == RB * 16 && WN == CB * 16, "wave tile mismatch");
@@ -668,7 +698,7 @@ __device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, f32x4 (&a
                     part_s[wn][lrow] = se;
                 }
                 if (row < M && (row % g.S) != g.S - 1) {
-                    const int target = g.tokens[row + 1];
+                    const int target = tokens[row + 1];
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
                         const int col = n0 + wn * WN + j * 16 + l16;
@@ -774,7 +804,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int wm = wave / WGN, wn = wave % WGN;
     const int KT = K / BK;
     const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
-    const i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
+    i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
+    const int32_t* tok = g.tokens;
     // the output (stored epilogues; the host keeps M N 2 under 2 GiB)
     const i32x4_t rc = buffer_rsrc(g.C, OVERLAP ? (uint32_t)((size_t)M * N * 2) : 0u);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -786,6 +817,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         tile_of<4>(t, nbm, nbn, tm, tn);
         m0 = tm * BM;
         n0 = tn * BN;
+        if (g.grp_rows) {  // tiles never straddle groups (grp_rows % BM == 0)
+            const int gi = __builtin_amdgcn_readfirstlane(m0 / g.grp_rows);
+            rw = buffer_rsrc(g.W + (size_t)gi * g.grp_stride, (uint32_t)((size_t)N * K * 2));
+            tok = g.tokens - (size_t)gi * g.grp_rows;
+        }
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
             const int p = j * NT + tid, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
@@ -902,7 +938,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int next = tile + (int)gridDim.x;
     const bool more = next < ntiles;
     if constexpr (!OVERLAP) {
-        lmhead_epilogue16<BM, BN, NT, WGM>(g, acc, m0, n0, tn);
+        lmhead_epilogue16<BM, BN, NT, WGM>(g, tok, acc, m0, n0, tn);
         // (its stores then complete before the next tile's first wait ends)
         if (!more) break;
         __syncthreads();  // the epilogue's LDS use is over
@@ -1018,10 +1054,13 @@ __global__ __launch_bounds__(kThreads) void ce_rows_kernel(const float* __restri
     if (lane == 0) block_sum[blockIdx.x] = v;
 }
 
-// loss = (sum of block sums, fixed order) / (B (S-1))
+// loss = (sum of block sums, fixed order) / (B (S-1)), one block per row group
 __global__ __launch_bounds__(kThreads) void ce_final_kernel(const double* __restrict__ block_sum, int n_blocks,
                                                              int M, int S, double* __restrict__ loss)
 {
+    // block g: row group g's loss from its n_blocks partial sums
+    block_sum += (size_t)blockIdx.x * n_blocks;
+    loss += blockIdx.x;
     __shared__ double red[4];
     double v = 0.0;
     for (int i = threadIdx.x; i < n_blocks; i += kThreads) v += block_sum[i];
@@ -1417,9 +1456,10 @@ struct DecoderWs {
 
 constexpr int kLmTile = 128;  // narrowest LM-head tile: sizes the per-tile partials
 
-DecoderWs carve(const zo_model_desc& d, void* base)
+// Workspace for `groups` evaluations side by side (rows of every group).
+DecoderWs carve(const zo_model_desc& d, void* base, int groups = 1)
 {
-    const size_t M = (size_t)d.batch * d.seq;
+    const size_t M = (size_t)groups * d.batch * d.seq;
     const size_t D = d.d_model, F = d.ffn;
     const size_t tiles = cdiv((int)d.vocab, kLmTile);
     size_t off = 0;
@@ -1461,19 +1501,24 @@ zo_status decoder_check(const zo_model_desc& d)
 }
 
 size_t decoder_workspace(const zo_model_desc& d) { return carve(d, nullptr).bytes; }
+size_t decoder_group_workspace(const zo_model_desc& d, int groups) { return carve(d, nullptr, groups).bytes; }
 
 // ---- captured forwards ----
 // A forward at the stored weights is the same ~90 launches for every
 // evaluation of a step; captured once into a HIP graph and replayed, the
 // launches reach the GPU together instead of one by one (between small
 // kernels the GPU otherwise idles several microseconds per launch).  One
-// entry per (tokens, batch, seq): the graph reads the weights, workspace and
-// tokens through the pointers it was captured with.  The first evaluation of
-// a key runs eagerly (every one-time set-up done), the second captures.
+// entry per (tokens, batch, seq, weights, row groups): the graph reads the
+// weights, workspace and tokens through the pointers it was captured with.
+// The first evaluation of a key runs eagerly (every one-time set-up done), the
+// second captures.
 namespace {
 struct FwdGraph {
     const int32_t* tokens;
     int64_t batch, seq;
+    const void* params;
+    const void* ws;
+    int groups;
     hipGraphExec_t exec;  // null: seen once, not captured yet
 };
 struct GraphCache {
@@ -1497,62 +1542,71 @@ void decoder_graphs_free(void* cache)
 namespace {
 
 // The launches of one evaluation up to the per-row cross-entropy partials.
+// `groups` > 1: that many evaluations side by side, group g reading the
+// parameter arena copy at P + g * gstride (stored-weight kernels only; the
+// host keeps B S a multiple of 256 so that no GEMM tile straddles two groups).
 zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Pert& p, const DecoderWs& w,
-                                hipStream_t s)
+                                hipStream_t s, const bf16_t* P, int groups = 1, uint64_t gstride = 0)
 {
     const zo_model_desc& d = m.desc;
     const int B = (int)b.batch, S = (int)b.seq, D = (int)d.d_model, F = (int)d.ffn, V = (int)d.vocab;
     const int H = (int)d.heads, dh = D / H, L = (int)d.layers;
-    const int M = B * S;
-    const bf16_t* P = (const bf16_t*)m.params;
+    const int M = groups * B * S;
+    const RowGroups gr = groups > 1 ? RowGroups{B * S, gstride} : RowGroups{0, 0};
+    const int grp_rows = gr.rows;
     // tensor order: tok_emb, pos_emb, per layer (ln1_g, ln1_b, w_qkv, w_o, ln2_g, ln2_b, w_up, w_down), lnf_g, lnf_b
     auto off = [&](int idx) { return m.offsets[idx]; };
     {
         KernelTimer t("embed", s);
-        embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, V, P + off(0), off(0), P + off(1), off(1), p, w.h);
+        embed_kernel<<<M, kThreads, 0, s>>>(b.tokens, S, D, V, P + off(0), off(0), P + off(1), off(1), p, gr, w.h);
         if (zo_status st = check_launch("embed")) return st;
     }
     for (int l = 0; l < L; ++l) {
         const int t0 = 2 + 8 * l;
         {
             KernelTimer t("layernorm", s);
-            launch_layernorm(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p, w.x, s);
+            launch_layernorm(w.h, M, D, P + off(t0), off(t0), P + off(t0 + 1), off(t0 + 1), p, w.x, s, gr);
             if (zo_status st = check_launch("layernorm")) return st;
         }
         GemmParams gq = {};
         gq.A = w.x; gq.W = P + off(t0 + 2); gq.w_dir = off(t0 + 2); gq.C = w.qkv; gq.M = M; gq.N = 3 * D; gq.K = D;
+        gq.grp_rows = grp_rows; gq.grp_stride = gstride;
         if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
         {
             KernelTimer t("attention", s);
-            launch_attention(w.qkv, B, S, D, H, dh, w.att, s);
+            launch_attention(w.qkv, groups * B, S, D, H, dh, w.att, s);
             if (zo_status st = check_launch("attention")) return st;
         }
         GemmParams go = {};
         go.A = w.att; go.W = P + off(t0 + 3); go.w_dir = off(t0 + 3); go.C = w.h; go.M = M; go.N = D; go.K = D;
+        go.grp_rows = grp_rows; go.grp_stride = gstride;
         if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
         {
             KernelTimer t("layernorm", s);
-            launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s);
+            launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s, gr);
             if (zo_status st = check_launch("layernorm")) return st;
         }
         GemmParams gu = {};
         gu.A = w.x; gu.W = P + off(t0 + 6); gu.w_dir = off(t0 + 6); gu.C = w.u; gu.M = M; gu.N = F; gu.K = D;
+        gu.grp_rows = grp_rows; gu.grp_stride = gstride;
         zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16")
                                             : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16");
         if (su) return su;
         GemmParams gd = {};
         gd.A = w.u; gd.W = P + off(t0 + 7); gd.w_dir = off(t0 + 7); gd.C = w.h; gd.M = M; gd.N = D; gd.K = F;
+        gd.grp_rows = grp_rows; gd.grp_stride = gstride;
         if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16")) return st;
     }
     const int tf = 2 + 8 * L;
     {
         KernelTimer t("layernorm", s);
-        launch_layernorm(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x, s);
+        launch_layernorm(w.h, M, D, P + off(tf), off(tf), P + off(tf + 1), off(tf + 1), p, w.x, s, gr);
         if (zo_status st = check_launch("layernorm")) return st;
     }
     GemmParams gl = {};
     gl.A = w.x; gl.W = P + off(0); gl.w_dir = off(0); gl.M = M; gl.N = V; gl.K = D;
     gl.lm_max = w.lm_max; gl.lm_sum = w.lm_sum; gl.lm_pick = w.lm_pick; gl.tokens = b.tokens; gl.S = S;
+    gl.grp_rows = grp_rows; gl.grp_stride = gstride;
     if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
     {
         KernelTimer t("reduce", s);
@@ -1565,7 +1619,8 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
 
 // The captured forward for this batch, or null when the evaluation should
 // run eagerly (first sight of the batch).
-zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& w, hipGraphExec_t* out)
+zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& w, hipGraphExec_t* out,
+                        const bf16_t* P, int groups, uint64_t gstride)
 {
     *out = nullptr;
     auto*& gc = reinterpret_cast<GraphCache*&>(*m.graphs);
@@ -1574,7 +1629,8 @@ zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& 
         if (!gc) return fail(ZO_ERR_INVALID, "out of host memory");
     }
     for (auto& f : gc->entries)
-        if (f.tokens == b.tokens && f.batch == (int64_t)b.batch && f.seq == (int64_t)b.seq) {
+        if (f.tokens == b.tokens && f.batch == (int64_t)b.batch && f.seq == (int64_t)b.seq && f.params == P &&
+            f.ws == (const void*)w.h && f.groups == groups) {
             if (f.exec) {
                 *out = f.exec;
                 return ZO_OK;
@@ -1584,7 +1640,7 @@ zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& 
                 return fail(ZO_ERR_HIP, "cannot create the capture stream");
             if (hipStreamBeginCapture(gc->capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
                 return fail(ZO_ERR_HIP, "cannot begin a graph capture");
-            const zo_status st = decoder_eval_launches(m, b, Pert{}, w, gc->capture);
+            const zo_status st = decoder_eval_launches(m, b, Pert{}, w, gc->capture, P, groups, gstride);
             hipGraph_t graph = nullptr;
             const hipError_t e = hipStreamEndCapture(gc->capture, &graph);
             if (st || e != hipSuccess || !graph) {
@@ -1603,7 +1659,7 @@ zo_status forward_graph(const ModelView& m, const zo_batch& b, const DecoderWs& 
         if (gc->entries.front().exec) (void)hipGraphExecDestroy(gc->entries.front().exec);
         gc->entries.erase(gc->entries.begin());
     }
-    gc->entries.push_back(FwdGraph{b.tokens, (int64_t)b.batch, (int64_t)b.seq, nullptr});
+    gc->entries.push_back(FwdGraph{b.tokens, (int64_t)b.batch, (int64_t)b.seq, P, w.h, groups, nullptr});
     return ZO_OK;
 }
 
@@ -1626,10 +1682,10 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         }
         hipGraphExec_t ex = nullptr;
         if (!n && m.graphs && !timing_active())
-            if (zo_status st = forward_graph(m, b, w, &ex)) return st;
+            if (zo_status st = forward_graph(m, b, w, &ex, (const bf16_t*)m.params, 1, 0)) return st;
         if (ex) {
             if (hipGraphLaunch(ex, s) != hipSuccess) return fail(ZO_ERR_HIP, "graph launch failed");
-        } else if (zo_status st = decoder_eval_launches(m, b, p, w, s)) {
+        } else if (zo_status st = decoder_eval_launches(m, b, p, w, s, (const bf16_t*)m.params)) {
             return st;
         }
         {
@@ -1639,6 +1695,25 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
         }
     }
     return ZO_OK;
+}
+
+zo_status decoder_forward_groups(const ModelView& m, const zo_batch& b, const void* params, int groups,
+                                 uint64_t gstride, void* ws, double* loss, hipStream_t s)
+{
+    const int M = (int)(b.batch * b.seq), S = (int)b.seq;
+    if (groups < 1 || (groups > 1 && M % 256)) return fail(ZO_ERR_INVALID, "bad row groups");
+    const DecoderWs w = carve(m.desc, ws, groups);
+    hipGraphExec_t ex = nullptr;
+    if (m.graphs && !timing_active())
+        if (zo_status st = forward_graph(m, b, w, &ex, (const bf16_t*)params, groups, gstride)) return st;
+    if (ex) {
+        if (hipGraphLaunch(ex, s) != hipSuccess) return fail(ZO_ERR_HIP, "graph launch failed");
+    } else if (zo_status st = decoder_eval_launches(m, b, Pert{}, w, s, (const bf16_t*)params, groups, gstride)) {
+        return st;
+    }
+    KernelTimer t("reduce", s);
+    ce_final_kernel<<<groups, kThreads, 0, s>>>(w.ce_part, cdiv(M, 64), M, S, loss);
+    return check_launch("ce reduce");
 }
 
 // ------------------------------------------------------------ debug entries

@@ -186,6 +186,47 @@ __global__ __launch_bounds__(kThreads) void perturb_bf16(uint16_t* __restrict__ 
 }
 
 
+// ------------------------------------------------------- perturbed copies
+// The copies mode's evaluation weights: from one read of the bf16 arena w,
+// copy 2i receives D(w + sigma z_{p0+i}) and copy 2i+1 receives
+// D(w - sigma z_{p0+i}), i < np (copies `cstride` elements apart).  The
+// values are those a fused evaluation forms in its tiles, fma then one
+// rounding to bf16.
+__global__ __launch_bounds__(kThreads) void perturb_copies_bf16(const uint16_t* __restrict__ w,
+                                                                 uint16_t* __restrict__ out, uint64_t cstride,
+                                                                 uint64_t n_full, uint64_t n, Key key, uint32_t p0,
+                                                                 uint32_t np, float sigma)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 8 * threadIdx.x;
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(w + e), f);
+        for (uint32_t i = 0; i < np; ++i) {
+            const float4 za = gauss4(key, p0 + i, e >> 2);
+            const float4 zb = gauss4(key, p0 + i, (e >> 2) + 1);
+            const float z[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+            float a[8], b[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                a[t] = fmaf(sigma, z[t], f[t]);
+                b[t] = fmaf(-sigma, z[t], f[t]);
+            }
+            *reinterpret_cast<uint4*>(out + (uint64_t)(2 * i) * cstride + e) = pack8(a);
+            *reinterpret_cast<uint4*>(out + (uint64_t)(2 * i + 1) * cstride + e) = pack8(b);
+        }
+    }
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t e = n_full + threadIdx.x; e < n; e += kThreads) {
+        const float v = bf16_lo(w[e]);
+        for (uint32_t i = 0; i < np; ++i) {
+            const float z = gauss1(key, p0 + i, e);
+            store_elem(out + (uint64_t)(2 * i) * cstride, e, fmaf(sigma, z, v));
+            store_elem(out + (uint64_t)(2 * i + 1) * cstride, e, fmaf(-sigma, z, v));
+        }
+    }
+}
+
 
 // ----------------------------------------------------------------- update
 // Coefficients c_i = fp32(-lr * g_i / N) into LDS; returns false when any g_i
@@ -679,6 +720,18 @@ static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32
         update_q8<T><<<grid_for(n_full, kQ8PerIter), kThreads, 0, s>>>(w, n_full, n, j0, key, p0, n_probes, g, lr);
     }
     return check_launch("update (8-bit directions)");
+}
+
+zo_status launch_perturb_copies(const void* w, void* out, uint64_t cstride, uint64_t n, uint64_t seed,
+                                uint32_t p0, uint32_t np, float sigma, hipStream_t s)
+{
+    if (n == 0 || np == 0) return ZO_OK;
+    const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
+    KernelTimer timer("perturb", s);
+    perturb_copies_bf16<<<grid_for(n_full), kThreads, 0, s>>>((const uint16_t*)w, (uint16_t*)out, cstride, n_full,
+                                                              n, key, p0, np, sigma);
+    return check_launch("perturb copies");
 }
 
 // Each pass is one launch; the grid's last block also takes the ragged tail.

@@ -25,6 +25,10 @@ struct ModelView {
     // The model's cache of captured decoder forwards (HIP graphs), created on
     // first use; null where the caller may not allocate: launches stay eager.
     void** graphs = nullptr;
+    // The copies mode's device buffer (arena copies + grouped workspace) and
+    // its size, grown on demand; null where the caller may not allocate.
+    void** copies = nullptr;
+    size_t* copies_bytes = nullptr;
 };
 
 // Releases a model's captured forwards (and their capture stream).
@@ -55,6 +59,13 @@ zo_status mlp_dust_step(const ModelView& m, const zo_batch& b, uint64_t seed, in
                         float sigma2, float lr, double* losses, hipStream_t s);
 zo_status decoder_check(const zo_model_desc& d);
 size_t decoder_workspace(const zo_model_desc& d);
+// Workspace of `groups` decoder evaluations side by side.
+size_t decoder_group_workspace(const zo_model_desc& d, int groups);
+// `groups` evaluations in one pass: group g at the weights params + g * gstride
+// (arena copies, bf16 elements), workspace `ws` of decoder_group_workspace
+// bytes; loss[g] = group g's mean loss.  batch * seq % 256 == 0 when groups > 1.
+zo_status decoder_forward_groups(const ModelView& m, const zo_batch& b, const void* params, int groups,
+                                 uint64_t gstride, void* ws, double* loss, hipStream_t s);
 zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* perts, int n, double* loss,
                           hipStream_t s);
 

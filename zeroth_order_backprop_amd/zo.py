@@ -14,7 +14,7 @@ ZO_OK, ZO_ERR_INVALID, ZO_ERR_UNSUPPORTED, ZO_ERR_HIP, ZO_ERR_NONFINITE, ZO_ERR_
 ZO_F32, ZO_BF16 = 0, 1
 ZO_MODEL_LSQ, ZO_MODEL_MLP, ZO_MODEL_DECODER = 0, 1, 2
 ZO_ACT_GELU, ZO_ACT_RELU = 0, 1
-ZO_MODE_INPLACE, ZO_MODE_FUSED = 0, 1
+ZO_MODE_INPLACE, ZO_MODE_FUSED, ZO_MODE_COPIES = 0, 1, 2
 ZO_DIRS_GAUSS, ZO_DIRS_Q8 = 0, 1
 
 EXPORTS = [
