@@ -1422,17 +1422,28 @@ zo_status launch_gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const 
 template <int EPI, bool PERT>
 constexpr bool may_use_big_tiles() { return !(PERT && EPI == EPI_LMHEAD); }
 
-int gemm_tile_n(int M, int N, bool pert, int epi)
+// 256x256 tiles (one block per CU, persistent) when they keep the CUs busy:
+// at least one tile per CU and the last round of tiles at least 85% full
+// (384 tiles on 256 CUs leave a third of the second round idle, where 128x128
+// tiles at two or three blocks per CU spread evenly).  The GELU epilogue at
+// 256x256 spills registers and costs as much as the MFMAs at K = 768, so
+// short-K GELU products stay at 128x128.
+int gemm_tile_n(int M, int N, int K, bool pert, int epi)
 {
+    if (pert && epi == EPI_LMHEAD) return 128;
     const long big = (long)cdiv(M, 256) * cdiv(N, 256);
-    return (big >= 256 && !(pert && epi == EPI_LMHEAD)) ? 256 : 128;
+    const long cus = device_cus();
+    if (big < cus) return 128;
+    if (epi == EPI_GELU && K < 2048) return 128;
+    const long rounds = (big + cus - 1) / cus;
+    return big * 100 >= rounds * cus * 85 ? 256 : 128;
 }
 
 template <int EPI, bool PERT>
 zo_status gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
     if constexpr (may_use_big_tiles<EPI, PERT>()) {
-        if (gemm_tile_n(gp.M, gp.N, PERT, EPI) == 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
+        if (gemm_tile_n(gp.M, gp.N, gp.K, PERT, EPI) == 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
     }
     if constexpr (!PERT && EPI != EPI_LMHEAD) {
         // narrow outputs: 128 x 64 tiles when 128 x 128 would leave CUs idle
@@ -1610,7 +1621,7 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
     if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
     {
         KernelTimer t("reduce", s);
-        const int lm_tiles = cdiv(V, gemm_tile_n(M, V, p.on != 0, EPI_LMHEAD));
+        const int lm_tiles = cdiv(V, gemm_tile_n(M, V, D, p.on != 0, EPI_LMHEAD));
         ce_rows_kernel<<<cdiv(M, 64), kThreads, 0, s>>>(w.lm_max, w.lm_sum, w.lm_pick, lm_tiles, M, S, w.ce_part);
         if (zo_status st = check_launch("ce rows")) return st;
     }
