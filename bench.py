@@ -34,9 +34,9 @@ BF16_PEAK_TFLOPS = 2500.0
 # VALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz non-packed 32-bit lane operations per second
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU instructions per generated Gaussian (Philox4x32-10 quarter plus half a
-# Box-Muller pair): the perturb_f32 loop issues 292 per 8 elements including
-# its fma and address arithmetic
-C_Z = 37
+# Box-Muller pair): the perturb_bf16 loop issues 237 per 8 elements including
+# its fma, conversions and address arithmetic
+C_Z = 29.6
 # HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE, scaled by the same counters on a plain copy of known size
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
