@@ -42,13 +42,14 @@ C_Z = 29.6
 # (factors 2.00 / 1.00); see profiles/.  Keyed by the kernel revision they were
 # taken on -- set to None when that kernel changes.
 TRAFFIC = {
-    "sgemm:mlp:r4": 2 * 8495.5 * 1024 + 10240 * 1024,
-    # the OPT-30B shape's four layer GEMMs (QKV, O, up, down), mean per launch:
-    # FETCH_SIZE x 2 + WRITE_SIZE summed over one of each, divided by four
-    "gemm_bf16:opt30b:r6": (2 * (4.0400 + 1.2149 + 5.2949 + 4.8819) + (0.6562 + 0.2188 + 0.8750 + 0.2188))
+    "sgemm:mlp:r5": 2 * 8486.5 * 1024 + 10240 * 1024,
+    # the OPT-30B shape's four layer GEMMs (QKV, O, up, down) with the decoder's
+    # epilogues (store, residual, ReLU, residual), mean per launch: FETCH_SIZE x 2
+    # + WRITE_SIZE summed over one of each, divided by four
+    "gemm_bf16:opt30b:r8": (2 * (3.9972 + 1.3165 + 5.4844 + 4.9467) + (0.6562 + 0.2188 + 0.8757 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r4", "lsq": None, "opt30b": "gemm_bf16:opt30b:r7"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r5", "lsq": None, "opt30b": "gemm_bf16:opt30b:r8"}
 
 
 def parse():
