@@ -351,11 +351,10 @@ struct GemmParams {
     float* lm_max;
     float* lm_sum;
     float* lm_pick;
-    const int32_t* tokens;  // targets: row r's target is tokens[r + 1] (same sequence)
-    int S;
+    const int32_t* tokens;  // targets: row r's target is tokens[r + 1] (same sequence;
+    int S;                  // read by the perturbed-tile LM head only)
     // row groups (stored-weight kernels only): rows [g R, (g + 1) R) use the
-    // weights grp_stride * g elements after W and, in the LM head, the targets
-    // of row r - g R (R = grp_rows; 0: one group)
+    // weights grp_stride * g elements after W (R = grp_rows; 0: one group)
     int grp_rows;
     uint64_t grp_stride;
 };
@@ -656,18 +655,21 @@ __device__ __forceinline__ void epilogue16_stage(f32x4 (&acc)[RB][CB], bf16_t* s
 // The LM head's fused cross-entropy partials from a block tile of 16x16
 // accumulators (element r of a 16x16 block: row 4 (lane / 16) + r, column
 // lane % 16): per row the max and the sum of exp(logit - max) over the tile's
-// columns, reduced over the 16 lanes of a row group and the two wave columns,
-// plus the target logit when the target column lies in this tile.
+// columns, reduced over the 16 lanes of a row group and the two wave columns.
+// (The target logits come from lm_pick_kernel.)  Full tiles skip the column
+// bound checks; exp(x - m) is evaluated as 2^(x log2 e - m log2 e) with one fma.
 template <int BM, int BN, int NT, int WGM, int RB, int CB>
-__device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, const int32_t* tokens, f32x4 (&acc)[RB][CB],
-                                                  int m0, int n0, int tn)
+__device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, f32x4 (&acc)[RB][CB], int m0, int n0, int tn)
 {
     constexpr int WGN = NT / 64 / WGM, WM = BM / WGM, WN = BN / WGN;
     static_assert(WM == RB * 16 && WN == CB * 16, "wave tile mismatch");
+    constexpr float kLog2e = 1.44269504088896341f;
     const int M = g.M, N = g.N;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WGN, wn = wave % WGN;
     const int l16 = lane & 15, lq = lane >> 4;
+    const int cbase = n0 + wn * WN + l16;  // this lane's column of j = 0
+    const bool full = n0 + BN <= N;        // uniform
     {
         static_assert(WGN == 2, "LM-head partials assume two wave columns");
         __shared__ float part_m[2][BM], part_s[2][BM];
@@ -676,36 +678,32 @@ __device__ __forceinline__ void lmhead_epilogue16(const GemmParams& g, const int
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int lrow = wm * WM + i * 16 + 4 * lq + r;
-                const int row = m0 + lrow;
                 float mx = -INFINITY;
+                if (full) {
 #pragma unroll
-                for (int j = 0; j < CB; ++j) {
-                    const int col = n0 + wn * WN + j * 16 + l16;
-                    if (col < N) mx = fmaxf(mx, acc[i][j][r]);
+                    for (int j = 0; j < CB; ++j) mx = fmaxf(mx, acc[i][j][r]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < CB; ++j)
+                        if (cbase + 16 * j < N) mx = fmaxf(mx, acc[i][j][r]);
                 }
 #pragma unroll
                 for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                const float mxl = mx * kLog2e;
                 float se = 0.f;
+                if (full) {
 #pragma unroll
-                for (int j = 0; j < CB; ++j) {
-                    const int col = n0 + wn * WN + j * 16 + l16;
-                    if (col < N) se += __expf(acc[i][j][r] - mx);
+                    for (int j = 0; j < CB; ++j) se += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -mxl));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < CB; ++j)
+                        if (cbase + 16 * j < N) se += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -mxl));
                 }
 #pragma unroll
                 for (int o = 8; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
                 if (l16 == 0) {
                     part_m[wn][lrow] = mx;
                     part_s[wn][lrow] = se;
-                }
-                if (row < M && (row % g.S) != g.S - 1) {
-                    const int target = tokens[row + 1];
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) {
-                        const int col = n0 + wn * WN + j * 16 + l16;
-                        if (col == target) g.lm_pick[row] = acc[i][j][r];
-                    }
-                    if ((unsigned)target >= (unsigned)N && tn == 0 && wn == 0 && l16 == 0)
-                        g.lm_pick[row] = __builtin_nanf("");
                 }
             }
         __syncthreads();
@@ -805,7 +803,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int KT = K / BK;
     const i32x4_t ra = buffer_rsrc(g.A, (uint32_t)((size_t)M * K * 2));
     i32x4_t rw = buffer_rsrc(g.W, (uint32_t)((size_t)N * K * 2));
-    const int32_t* tok = g.tokens;
+
     // the output (stored epilogues; the host keeps M N 2 under 2 GiB)
     const i32x4_t rc = buffer_rsrc(g.C, OVERLAP ? (uint32_t)((size_t)M * N * 2) : 0u);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -820,7 +818,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
         if (g.grp_rows) {  // tiles never straddle groups (grp_rows % BM == 0)
             const int gi = __builtin_amdgcn_readfirstlane(m0 / g.grp_rows);
             rw = buffer_rsrc(g.W + (size_t)gi * g.grp_stride, (uint32_t)((size_t)N * K * 2));
-            tok = g.tokens - (size_t)gi * g.grp_rows;
         }
 #pragma unroll
         for (int j = 0; j < A_INS; ++j) {
@@ -938,7 +935,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
     const int next = tile + (int)gridDim.x;
     const bool more = next < ntiles;
     if constexpr (!OVERLAP) {
-        lmhead_epilogue16<BM, BN, NT, WGM>(g, tok, acc, m0, n0, tn);
+        lmhead_epilogue16<BM, BN, NT, WGM>(g, acc, m0, n0, tn);
         // (its stores then complete before the next tile's first wait ends)
         if (!more) break;
         __syncthreads();  // the epilogue's LDS use is over
@@ -1052,6 +1049,47 @@ __global__ __launch_bounds__(kThreads) void ce_rows_kernel(const float* __restri
     }
     v = wave_sumd(v);
     if (lane == 0) block_sum[blockIdx.x] = v;
+}
+
+// Target logits of the stored-weight LM head: pick[r] = x[r] . E[t] with
+// t = tokens[r + 1], the next token of the same sequence (rows at a sequence
+// end have none), E the token embedding (the tied head), fp32 accumulation of
+// the bf16 products.  The GEMM's cross-entropy partials then need no
+// per-element target test.  One wave per row, 16-byte loads (K % 8 == 0);
+// row groups read their own copy of E.  An id outside the vocabulary gives
+// the row a NaN loss.
+__global__ __launch_bounds__(kThreads) void lm_pick_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ emb,
+                                                            int K, const int32_t* __restrict__ tokens, int M, int S,
+                                                            int V, RowGroups gr, float* __restrict__ pick)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M || row % S == S - 1) return;
+    int rl = row;
+    if (gr.rows) {
+        const int gi = row / gr.rows;
+        rl = row - gi * gr.rows;
+        emb += (uint64_t)gi * gr.stride;
+    }
+    const int t = tokens[rl + 1];
+    if ((unsigned)t >= (unsigned)V) {
+        if (lane == 0) pick[row] = __builtin_nanf("");
+        return;
+    }
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)row * K);
+    const uint4* er = reinterpret_cast<const uint4*>(emb + (size_t)t * K);
+    float acc = 0.f;
+    for (int c = lane; c < K / 8; c += 64) {
+        const uint4 a = xr[c], b = er[c];
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(bf2f(aw[e] & 0xFFFF), bf2f(bw[e] & 0xFFFF), acc);
+            acc = fmaf(bf2f(aw[e] >> 16), bf2f(bw[e] >> 16), acc);
+        }
+    }
+    acc = wave_sumf(acc);
+    if (lane == 0) pick[row] = acc;
 }
 
 // loss = (sum of block sums, fixed order) / (B (S-1)), one block per row group
@@ -1619,6 +1657,13 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
     gl.lm_max = w.lm_max; gl.lm_sum = w.lm_sum; gl.lm_pick = w.lm_pick; gl.tokens = b.tokens; gl.S = S;
     gl.grp_rows = grp_rows; gl.grp_stride = gstride;
     if (zo_status st = gemm_any<EPI_LMHEAD>(gl, p, s, "lm_head")) return st;
+    if (!p.on) {
+        // the stored-weight head's target logits (the perturbed-tile head picks
+        // them in its epilogue)
+        KernelTimer t("lm_head", s);
+        lm_pick_kernel<<<cdiv(M, 4), kThreads, 0, s>>>(w.x, P + off(0), D, b.tokens, M, S, V, gr, w.lm_pick);
+        if (zo_status st = check_launch("lm pick")) return st;
+    }
     {
         KernelTimer t("reduce", s);
         const int lm_tiles = cdiv(V, gemm_tile_n(M, V, D, p.on != 0, EPI_LMHEAD));
