@@ -229,7 +229,7 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
  * FUSED, D(W +- eps z_i), written out: one pass over W fills 2P copies of the
  * arena for P probes, then one forward evaluates all 2P copies side by side
  * (the rows of every copy in the same launches); P is chosen so a forward
- * covers about 32768 token rows (at most 16 probes, at most N), and P = 1
+ * covers about 131072 token rows (at most 16 probes, at most N), and P = 1
  * unless batch * seq is a multiple of 256.  The copies and their workspace
  * (2P (arena + zo_workspace_bytes) bytes) are allocated on the model's first
  * COPIES step and held until zo_model_destroy; ZO_ERR_WORKSPACE if the device

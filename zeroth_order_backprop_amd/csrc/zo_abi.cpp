@@ -509,7 +509,7 @@ static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cf
 // model.  P: about kCopyRows token rows per forward, at most kMaxCopyProbes
 // and N, the grouped activations under 2 GiB per buffer (the GEMMs' 32-bit
 // offsets), and the buffer within half the free device memory.
-constexpr int64_t kCopyRows = 32768;
+constexpr int64_t kCopyRows = 131072;
 constexpr uint32_t kMaxCopyProbes = 16;
 
 static uint64_t copy_stride(uint64_t n_params) { return (n_params + 127) / 128 * 128; }
