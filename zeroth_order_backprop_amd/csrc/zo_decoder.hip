@@ -1316,7 +1316,12 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-        const float m_new = fmaxf(m_run, tmax);
+        // Lazy rescaling: the reference max m_run is kept until some query of
+        // the wave exceeds it by more than 8 (log2 units), so the weights
+        // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
+        // same relative precision) and most tiles skip the rescale of O.
+        const bool raise = __any(tmax > m_run + 8.0f);
+        const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
         const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         float psum = 0.f;
         bf16x8 pb[NB][2];
@@ -1340,7 +1345,7 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // rescale only when some query of the wave raised its max
-        if (__any(alpha != 1.0f)) {
+        if (raise) {
 #pragma unroll
             for (int t = 0; t < OT; ++t)
 #pragma unroll
