@@ -1164,6 +1164,26 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
+// Lane l and lane l ^ 32 combined through v_permlane32_swap (a VALU exchange
+// of the two half-waves, no LDS round trip).  Both results of the swap hold
+// one value of each half, so max and the sum come out the same in both lanes
+// (the sum in the same operand order: low half first).
+__device__ __forceinline__ float halves_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 template <int DH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2)))
 void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_t* __restrict__ out)
@@ -1256,128 +1276,290 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         for (int h = 0; h < 2; ++h)
             vcol[t][h] = 16 * ((4 * t + 2 * (g & 1) + (vq >> 1)) ^ att_swz<DH>(8 * h + vrow)) + vhalf;
 
-    for (int t = 0; t < NSLOT - 1; ++t) issue(t);
-    // Q in registers before the loop: a wait for it there is partial (the
-    // tiles' loads were issued after it), at the loop's entry it would be total
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-    for (int it = 0; it < ntiles; ++it) {
-        const int k0 = it * BKV;
-        // this wave's part of tile it landed (the later tiles may be in
-        // flight); after the barrier every part has, and no wave still reads
-        // the slot of tile it - 1, which is refilled
-        ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
-        ZO_WAIT_LGKM0();
-        asm volatile("s_barrier" ::: "memory");
-        issue(it + NSLOT - 1);
-        if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
-        const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
-        const unsigned char* sv = sk + TILEB;
-        // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
-        // head-dim steps in two interleaved chains (even and odd steps), so
-        // that consecutive MFMAs do not wait on each other's results.
-        // All of the tile's K fragments are read first (one LDS round trip
-        // instead of one per MFMA: left alone, the compiler waits before each)
-        f32x16 st[NB], sx[NB];
-        bf16x8 kf[NB][KS];
-#pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[hblk][ks] =
-                    *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ks += 2)
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk) {
-                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
-                sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
-            }
-#pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
-        // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
-        if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
-            const int last = min(myq, S - 1);
+    // d_h 128 has the registers for two tiles' K fragment sets: the next
+    // tile's are read while this tile's scores are formed and its softmax
+    // runs, which takes the LDS round trip off the critical path; the
+    // cross-half reductions go through v_permlane32_swap.  (d_h 64, at three
+    // waves per SIMD, has no such room: it reads each tile's fragments right
+    // before its MFMAs.)
+    if constexpr (DH == 128) {
+        bf16x8 kf[2][NB][KS];
+        auto read_k = [&](int t, bf16x8 (&dst)[NB][KS]) {
+            const unsigned char* sk = lds + (t % NSLOT) * SLOTB;
 #pragma unroll
             for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
+                for (int ks = 0; ks < KS; ++ks)
+                    dst[hblk][ks] =
+                        *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
+        };
+
+        for (int t = 0; t < NSLOT - 1; ++t) issue(t);
+        // Q in registers before the loop: a wait for it there is partial (the
+        // tiles' loads were issued after it), at the loop's entry it would be total
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+        // tile 0 landed for every wave: its K fragments into set 0
+        ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
+        asm volatile("s_barrier" ::: "memory");
+        read_k(0, kf[0]);
+        // One key tile; KC is the K fragment set holding tile it.
+        auto step = [&](int it, auto KC) {
+            constexpr int kc = decltype(KC)::value;
+            const int k0 = it * BKV;
+            // This wave's part of tile it + 1 (whose K fragments this iteration
+            // reads) landed, later tiles may be in flight; after the barrier every
+            // part has, and no wave still reads the slot of tile it - 1 (its K
+            // fragments were read two iterations ago, its V^T in the last), which
+            // is refilled.
+            ZO_WAIT_VM(2 * LOADS * (NSLOT - 3));
+            ZO_WAIT_LGKM0();
+            asm volatile("s_barrier" ::: "memory");
+            issue(it + NSLOT - 1);
+            // every key of this tile (and of all later ones) is after all of this
+            // wave's queries
+            if (k0 > qw + 31) return;
+            const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
+            const unsigned char* sv = sk + TILEB;
+            // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
+            // head-dim steps in two interleaved chains (even and odd steps), so
+            // that consecutive MFMAs do not wait on each other's results.
+            __builtin_amdgcn_sched_barrier(0);
+            auto& kcur = kf[kc];
+            f32x16 st[NB], sx[NB];
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks += 2)
+#pragma unroll
+                for (int hblk = 0; hblk < NB; ++hblk) {
+                    st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
+                    sx[hblk] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
                 }
-        }
-        // running max in log2 units: max(s c) = c max(s) for c > 0
-        float tmax = -INFINITY;
+            // the next tile's K fragments, under these MFMAs and the softmax (a
+            // tile past the last one is read into registers no result uses)
+            __builtin_amdgcn_sched_barrier(0);
+            read_k(it + 1, kf[1 - kc]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk)
+            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
+            // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
+            if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
+                const int last = min(myq, S - 1);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-        // Lazy rescaling: the reference max m_run is kept until some query of
-        // the wave exceeds it by more than 8 (log2 units), so the weights
-        // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
-        // same relative precision) and most tiles skip the rescale of O.
-        const bool raise = __any(tmax > m_run + 8.0f);
-        const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        float psum = 0.f;
-        bf16x8 pb[NB][2];
+                for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-        for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-            for (int sblk = 0; sblk < 2; ++sblk) {
-                uint32_t w4[4];
-#pragma unroll
-                for (int t = 0; t < 8; t += 2) {
-                    // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
-                    psum += e0 + e1;
-                    w4[t >> 1] = pack2(e0, e1);
-                }
-                const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
-                pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
+                    }
             }
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // rescale only when some query of the wave raised its max
-        if (raise) {
+            // running max in log2 units: max(s c) = c max(s) for c > 0
+            float tmax = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < OT; ++t)
+            for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        }
-        // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
-        // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
-        // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
-        // dh = 32 t + lr) takes the same keys in the same order, from two
-        // transposing reads of four keys each (keys +0..3 and +8..11)
-        constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
+            tmax = halves_max(tmax) * c;
+            // Lazy rescaling: the reference max m_run is kept until some query of
+            // the wave exceeds it by more than 8 (log2 units), so the weights
+            // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
+            // same relative precision) and most tiles skip the rescale of O.
+            const bool raise = __any(tmax > m_run + 8.0f);
+            const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            float psum = 0.f;
+            bf16x8 pb[NB][2];
 #pragma unroll
-        for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
-            uint32_t a[8];
-            uint2 v[8];
+            for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-            for (int u = 0; u < STEPS; ++u)
+                for (int sblk = 0; sblk < 2; ++sblk) {
+                    uint32_t w4[4];
+#pragma unroll
+                    for (int t = 0; t < 8; t += 2) {
+                        // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
+                        const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
+                        const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
+                        psum += e0 + e1;
+                        w4[t >> 1] = pack2(e0, e1);
+                    }
+                    const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
+                    pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
+                }
+            psum = halves_sum(psum);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            // rescale only when some query of the wave raised its max
+            if (raise) {
 #pragma unroll
                 for (int t = 0; t < OT; ++t)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
-            ds_read_tr8(v, a);
+                    for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+            }
+            // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
+            // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
+            // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
+            // dh = 32 t + lr) takes the same keys in the same order, from two
+            // transposing reads of four keys each (keys +0..3 and +8..11)
+            constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
 #pragma unroll
-            for (int u = 0; u < STEPS; ++u) {
-                const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
+            for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
+                uint32_t a[8];
+                uint2 v[8];
 #pragma unroll
-                for (int t = 0; t < OT; ++t) {
-                    const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
-                    const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
-                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
+                for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+                    for (int t = 0; t < OT; ++t)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
+                ds_read_tr8(v, a);
+#pragma unroll
+                for (int u = 0; u < STEPS; ++u) {
+                    const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
+#pragma unroll
+                    for (int t = 0; t < OT; ++t) {
+                        const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
+                        const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+                        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
+                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        // two tiles per trip so that each K fragment set stays in its registers
+        int it = 0;
+#pragma unroll 1
+        for (; it + 1 < ntiles; it += 2) {
+            step(it, IntC<0>{});
+            step(it + 1, IntC<1>{});
+        }
+        if (it < ntiles) step(it, IntC<0>{});
+    } else {
+        for (int t = 0; t < NSLOT - 1; ++t) issue(t);
+        // Q in registers before the loop: a wait for it there is partial (the
+        // tiles' loads were issued after it), at the loop's entry it would be total
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+        for (int it = 0; it < ntiles; ++it) {
+            const int k0 = it * BKV;
+            // this wave's part of tile it landed (the later tiles may be in
+            // flight); after the barrier every part has, and no wave still reads
+            // the slot of tile it - 1, which is refilled
+            ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
+            ZO_WAIT_LGKM0();
+            asm volatile("s_barrier" ::: "memory");
+            issue(it + NSLOT - 1);
+            if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
+            const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
+            const unsigned char* sv = sk + TILEB;
+            // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
+            // head-dim steps in two interleaved chains (even and odd steps), so
+            // that consecutive MFMAs do not wait on each other's results.
+            // All of the tile's K fragments are read first (one LDS round trip
+            // instead of one per MFMA: left alone, the compiler waits before each)
+            f32x16 st[NB], sx[NB];
+            bf16x8 kf[NB][KS];
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[hblk][ks] =
+                        *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks += 2)
+#pragma unroll
+                for (int hblk = 0; hblk < NB; ++hblk) {
+                    st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
+                    sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
+                }
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
+            // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
+            if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
+                const int last = min(myq, S - 1);
+#pragma unroll
+                for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
+                        st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
+                    }
+            }
+            // running max in log2 units: max(s c) = c max(s) for c > 0
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
+            // Lazy rescaling: the reference max m_run is kept until some query of
+            // the wave exceeds it by more than 8 (log2 units), so the weights
+            // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
+            // same relative precision) and most tiles skip the rescale of O.
+            const bool raise = __any(tmax > m_run + 8.0f);
+            const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            float psum = 0.f;
+            bf16x8 pb[NB][2];
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+                for (int sblk = 0; sblk < 2; ++sblk) {
+                    uint32_t w4[4];
+#pragma unroll
+                    for (int t = 0; t < 8; t += 2) {
+                        // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
+                        const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
+                        const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
+                        psum += e0 + e1;
+                        w4[t >> 1] = pack2(e0, e1);
+                    }
+                    const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
+                    pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
+                }
+            psum += __shfl_xor(psum, 32, 64);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            // rescale only when some query of the wave raised its max
+            if (raise) {
+#pragma unroll
+                for (int t = 0; t < OT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+            }
+            // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
+            // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
+            // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
+            // dh = 32 t + lr) takes the same keys in the same order, from two
+            // transposing reads of four keys each (keys +0..3 and +8..11)
+            constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
+#pragma unroll
+            for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
+                uint32_t a[8];
+                uint2 v[8];
+#pragma unroll
+                for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+                    for (int t = 0; t < OT; ++t)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
+                ds_read_tr8(v, a);
+#pragma unroll
+                for (int u = 0; u < STEPS; ++u) {
+                    const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
+#pragma unroll
+                    for (int t = 0; t < OT; ++t) {
+                        const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
+                        const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+                        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
+                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
+                    }
                 }
             }
         }
