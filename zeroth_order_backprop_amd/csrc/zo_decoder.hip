@@ -1138,24 +1138,28 @@ __device__ __forceinline__ int att_swz(int row)
     return DH == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
 }
 
-// Eight transposing LDS reads and the wait for them in one asm statement, so
-// that no register they write is reused before its data lands.  (Through the
-// builtin, the compiler waits for every direct-to-LDS load in flight, the
-// next tiles' included, before each such read.)
-__device__ __forceinline__ void ds_read_tr8(uint2 (&v)[8], const uint32_t (&a)[8])
+// Eight transposing LDS reads at per-lane addresses a[] plus a common
+// immediate offset OFF (the 16-bit offset field, so that a ring slot known at
+// compile time costs no address arithmetic), and the wait for them, in one
+// asm statement: no register they write is reused before its data lands.
+// (Through the builtin, the compiler waits for every direct-to-LDS load in
+// flight, the next tiles' included, before each such read.)
+template <int OFF>
+__device__ __forceinline__ void ds_read_tr8_off(uint2 (&v)[8], const uint32_t (&a)[8])
 {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\t"
-        "ds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\t"
-        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
         : "memory");
 }
 
@@ -1197,6 +1201,7 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
     // allow anyway), d_h 64 keeps 3 (48 KB: 3 blocks per CU)
     constexpr int TILEB = BKV * ROWB, SLOTB = 2 * TILEB, NSLOT = DH == 128 ? 4 : 3;
     constexpr int LOADS = TILEB / 1024 / 4;  // 1 KB wave loads per wave per tile, each of K and V
+    constexpr int STEPS = 8 / (2 * OT);      // P V^T k-steps per group of eight transposing reads
     static_assert(LOADS * 4 * 1024 == TILEB, "tile / wave mismatch");
     __shared__ __align__(16) unsigned char lds[NSLOT * SLOTB];
 
@@ -1282,288 +1287,181 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
     // cross-half reductions go through v_permlane32_swap.  (d_h 64, at three
     // waves per SIMD, has no such room: it reads each tile's fragments right
     // before its MFMAs.)
-    if constexpr (DH == 128) {
-        bf16x8 kf[2][NB][KS];
-        auto read_k = [&](int t, bf16x8 (&dst)[NB][KS]) {
-            const unsigned char* sk = lds + (t % NSLOT) * SLOTB;
+    // K fragments: d_h 128 has the registers for two tiles' sets, so the next
+    // tile's are read while this tile's scores are formed and its softmax
+    // runs (the LDS round trip leaves the critical path); d_h 64, at three
+    // waves per SIMD, reads each tile's right before its MFMAs.
+    constexpr bool PREK = DH == 128;
+    static_assert(2 * NB % STEPS == 0, "whole V^T read groups");
+    bf16x8 kf[PREK ? 2 : 1][NB][KS];
+    // ring slot T: its K tile at a compile-time LDS offset
+    auto read_k = [&](auto T, bf16x8 (&dst)[NB][KS]) {
+        const unsigned char* sk = lds + decltype(T)::value * SLOTB;
 #pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk)
+        for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    dst[hblk][ks] =
-                        *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
-        };
+            for (int ks = 0; ks < KS; ++ks)
+                dst[hblk][ks] =
+                    *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
+    };
+    // this lane's V^T read addresses for one group of eight reads in slot 0
+    // (the slot and the group's first key row go into the offset field)
+    uint32_t va[8];
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+        for (int t = 0; t < OT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                va[(u * OT + t) * 2 + h] = lds_addr(lds + TILEB + (16 * u + 8 * h + vrow) * ROWB + vcol[t][h]);
 
-        for (int t = 0; t < NSLOT - 1; ++t) issue(t);
-        // Q in registers before the loop: a wait for it there is partial (the
-        // tiles' loads were issued after it), at the loop's entry it would be total
+    for (int t = 0; t < NSLOT - 1; ++t) issue(t);
+    // Q in registers before the loop: a wait for it there is partial (the
+    // tiles' loads were issued after it), at the loop's entry it would be total
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    if constexpr (PREK) {
         // tile 0 landed for every wave: its K fragments into set 0
         ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
         asm volatile("s_barrier" ::: "memory");
-        read_k(0, kf[0]);
-        // One key tile; KC is the K fragment set holding tile it.
-        auto step = [&](int it, auto KC) {
-            constexpr int kc = decltype(KC)::value;
-            const int k0 = it * BKV;
-            // This wave's part of tile it + 1 (whose K fragments this iteration
-            // reads) landed, later tiles may be in flight; after the barrier every
-            // part has, and no wave still reads the slot of tile it - 1 (its K
-            // fragments were read two iterations ago, its V^T in the last), which
-            // is refilled.
-            ZO_WAIT_VM(2 * LOADS * (NSLOT - 3));
-            ZO_WAIT_LGKM0();
-            asm volatile("s_barrier" ::: "memory");
-            issue(it + NSLOT - 1);
-            // every key of this tile (and of all later ones) is after all of this
-            // wave's queries
-            if (k0 > qw + 31) return;
-            const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
-            const unsigned char* sv = sk + TILEB;
-            // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
-            // head-dim steps in two interleaved chains (even and odd steps), so
-            // that consecutive MFMAs do not wait on each other's results.
+        read_k(IntC<0>{}, kf[0]);
+    }
+    // One key tile: it, its ring slot SL = it % NSLOT and (PREK) the K
+    // fragment set KC = it % 2 holding it.
+    auto step = [&](int it, auto KC, auto SL) {
+        constexpr int kc = decltype(KC)::value, sl = decltype(SL)::value;
+        const int k0 = it * BKV;
+        // This wave's part of tile it (PREK: of tile it + 1, whose K
+        // fragments this iteration reads) landed, later tiles may be in
+        // flight; after the barrier every part has, and no wave still reads
+        // the slot of tile it - 1 (PREK: its K fragments were read two
+        // iterations ago), which is refilled.
+        ZO_WAIT_VM(2 * LOADS * (NSLOT - (PREK ? 3 : 2)));
+        ZO_WAIT_LGKM0();
+        asm volatile("s_barrier" ::: "memory");
+        issue(it + NSLOT - 1);
+        // every key of this tile (and of all later ones) is after all of this
+        // wave's queries
+        if (k0 > qw + 31) return;
+        // all of the tile's K fragments are read before the first MFMA (one
+        // LDS round trip instead of one per MFMA: left alone, the compiler
+        // waits before each)
+        if constexpr (!PREK) read_k(SL, kf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        // S^T [BKV keys][32 queries] as NB 32x32 blocks, each one chain of
+        // MFMAs over the head dim (a dependent MFMA issues back to back)
+        f32x16 st[NB];
+#pragma unroll
+        for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hblk = 0; hblk < NB; ++hblk)
+                st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc][hblk][ks], qf[ks], st[hblk], 0, 0, 0);
+        if constexpr (PREK) {
+            // the next tile's K fragments, under these MFMAs and the softmax
+            // (a tile past the last one is read into registers no result uses)
             __builtin_amdgcn_sched_barrier(0);
-            auto& kcur = kf[kc];
-            f32x16 st[NB], sx[NB];
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ks += 2)
-#pragma unroll
-                for (int hblk = 0; hblk < NB; ++hblk) {
-                    st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
-                    sx[hblk] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
-                }
-            // the next tile's K fragments, under these MFMAs and the softmax (a
-            // tile past the last one is read into registers no result uses)
+            read_k(IntC<(sl + 1) % NSLOT>{}, kf[1 - kc]);
             __builtin_amdgcn_sched_barrier(0);
-            read_k(it + 1, kf[1 - kc]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
-            // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
-            if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
-                const int last = min(myq, S - 1);
-#pragma unroll
-                for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
-                    }
-            }
-            // running max in log2 units: max(s c) = c max(s) for c > 0
-            float tmax = -INFINITY;
+        }
+        // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
+        if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
+            const int last = min(myq, S - 1);
 #pragma unroll
             for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
-            tmax = halves_max(tmax) * c;
-            // Lazy rescaling: the reference max m_run is kept until some query of
-            // the wave exceeds it by more than 8 (log2 units), so the weights
-            // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
-            // same relative precision) and most tiles skip the rescale of O.
-            const bool raise = __any(tmax > m_run + 8.0f);
-            const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            float psum = 0.f;
-            bf16x8 pb[NB][2];
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                for (int sblk = 0; sblk < 2; ++sblk) {
-                    uint32_t w4[4];
-#pragma unroll
-                    for (int t = 0; t < 8; t += 2) {
-                        // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
-                        const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
-                        const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
-                        psum += e0 + e1;
-                        w4[t >> 1] = pack2(e0, e1);
-                    }
-                    const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
-                    pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
                 }
-            psum = halves_sum(psum);
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // rescale only when some query of the wave raised its max
-            if (raise) {
+        }
+        // running max in log2 units: max(s c) = c max(s) for c > 0
+        float tmax = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < OT; ++t)
+        for (int hblk = 0; hblk < NB; ++hblk)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
+        tmax = halves_max(tmax) * c;
+        // Lazy rescaling: the reference max m_run is kept until some query of
+        // the wave exceeds it by more than 8 (log2 units), so the weights
+        // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
+        // same relative precision) and most tiles skip the rescale of O.
+        const bool raise = __any(tmax > m_run + 8.0f);
+        const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float psum = 0.f;
+        bf16x8 pb[NB][2];
+#pragma unroll
+        for (int hblk = 0; hblk < NB; ++hblk)
+#pragma unroll
+            for (int sblk = 0; sblk < 2; ++sblk) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int t = 0; t < 8; t += 2) {
+                    // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
+                    psum += e0 + e1;
+                    w4[t >> 1] = pack2(e0, e1);
+                }
+                const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
+                pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
             }
-            // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
-            // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
-            // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
-            // dh = 32 t + lr) takes the same keys in the same order, from two
-            // transposing reads of four keys each (keys +0..3 and +8..11)
-            constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
+        psum = halves_sum(psum);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // rescale only when some query of the wave raised its max
+        if (raise) {
 #pragma unroll
-            for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
-                uint32_t a[8];
-                uint2 v[8];
+            for (int t = 0; t < OT; ++t)
 #pragma unroll
-                for (int u = 0; u < STEPS; ++u)
+                for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        }
+        // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
+        // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
+        // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
+        // dh = 32 t + lr) takes the same keys in the same order, from two
+        // transposing reads of four keys each (keys +0..3 and +8..11).  Groups
+        // of eight reads cover STEPS such steps, at the slot's and the
+        // group's offset.
+        auto pv = [&](auto S0) {
+            constexpr int s0 = decltype(S0)::value;
+            uint2 v[8];
+            ds_read_tr8_off<sl * SLOTB + 16 * s0 * ROWB>(v, va);
 #pragma unroll
-                    for (int t = 0; t < OT; ++t)
+            for (int u = 0; u < STEPS; ++u) {
+                const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
-                ds_read_tr8(v, a);
-#pragma unroll
-                for (int u = 0; u < STEPS; ++u) {
-                    const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
-#pragma unroll
-                    for (int t = 0; t < OT; ++t) {
-                        const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
-                        const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
-                        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
-                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
-                    }
+                for (int t = 0; t < OT; ++t) {
+                    const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
+                    const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, packed), pb[hblk][sblk],
+                                                                  o[t], 0, 0, 0);
                 }
             }
         };
-        // two tiles per trip so that each K fragment set stays in its registers
-        int it = 0;
+        pv(IntC<0>{});
+        if constexpr (2 * NB > STEPS) pv(IntC<STEPS>{});
+        static_assert(2 * NB <= 2 * STEPS, "at most two V^T read groups");
+    };
+    // NSLOT tiles per trip: every ring slot (and K fragment set) is a
+    // compile-time choice; the trips end on a multiple of NSLOT, so the
+    // tail's slots are known too
+    static_assert(NSLOT == 3 || NSLOT == 4, "unrolled ring");
+    static_assert(!PREK || NSLOT % 2 == 0, "K fragment sets alternate within a trip");
+    int it = 0;
 #pragma unroll 1
-        for (; it + 1 < ntiles; it += 2) {
-            step(it, IntC<0>{});
-            step(it + 1, IntC<1>{});
-        }
-        if (it < ntiles) step(it, IntC<0>{});
-    } else {
-        for (int t = 0; t < NSLOT - 1; ++t) issue(t);
-        // Q in registers before the loop: a wait for it there is partial (the
-        // tiles' loads were issued after it), at the loop's entry it would be total
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
-        for (int it = 0; it < ntiles; ++it) {
-            const int k0 = it * BKV;
-            // this wave's part of tile it landed (the later tiles may be in
-            // flight); after the barrier every part has, and no wave still reads
-            // the slot of tile it - 1, which is refilled
-            ZO_WAIT_VM(2 * LOADS * (NSLOT - 2));
-            ZO_WAIT_LGKM0();
-            asm volatile("s_barrier" ::: "memory");
-            issue(it + NSLOT - 1);
-            if (k0 > qw + 31) continue;  // every key of this tile is after all of this wave's queries
-            const unsigned char* sk = lds + (it % NSLOT) * SLOTB;
-            const unsigned char* sv = sk + TILEB;
-            // S^T [BKV keys][32 queries] as NB 32x32 blocks.  Each block sums its
-            // head-dim steps in two interleaved chains (even and odd steps), so
-            // that consecutive MFMAs do not wait on each other's results.
-            // All of the tile's K fragments are read first (one LDS round trip
-            // instead of one per MFMA: left alone, the compiler waits before each)
-            f32x16 st[NB], sx[NB];
-            bf16x8 kf[NB][KS];
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kf[hblk][ks] =
-                        *reinterpret_cast<const bf16x8*>(sk + (32 * hblk + lr) * ROWB + 16 * ((2 * ks + lh) ^ ksw));
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = sx[hblk] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ks += 2)
-#pragma unroll
-                for (int hblk = 0; hblk < NB; ++hblk) {
-                    st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks], qf[ks], st[hblk], 0, 0, 0);
-                    sx[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[hblk][ks + 1], qf[ks + 1], sx[hblk], 0, 0, 0);
-                }
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk) st[hblk] += sx[hblk];
-            // element r of block hblk: key k0 + 32 hblk + 8 (r/4) + 4 lh + r%4, query myq
-            if (k0 + BKV - 1 > qw) {  // diagonal tile: some key may follow some query of the wave
-                const int last = min(myq, S - 1);
-#pragma unroll
-                for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * hblk + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        st[hblk][r] = key <= last ? st[hblk][r] : -INFINITY;
-                    }
-            }
-            // running max in log2 units: max(s c) = c max(s) for c > 0
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[hblk][r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * c;
-            // Lazy rescaling: the reference max m_run is kept until some query of
-            // the wave exceeds it by more than 8 (log2 units), so the weights
-            // 2^(s c - m) stay at most 256 (fp32 sums and bf16 P carry them at the
-            // same relative precision) and most tiles skip the rescale of O.
-            const bool raise = __any(tmax > m_run + 8.0f);
-            const float m_new = raise ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            float psum = 0.f;
-            bf16x8 pb[NB][2];
-#pragma unroll
-            for (int hblk = 0; hblk < NB; ++hblk)
-#pragma unroll
-                for (int sblk = 0; sblk < 2; ++sblk) {
-                    uint32_t w4[4];
-#pragma unroll
-                    for (int t = 0; t < 8; t += 2) {
-                        // exp2(s c - m): one fma per score; exp2(-inf) = 0 for masked keys
-                        const float e0 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t], c, -m_new));
-                        const float e1 = __builtin_amdgcn_exp2f(fmaf(st[hblk][8 * sblk + t + 1], c, -m_new));
-                        psum += e0 + e1;
-                        w4[t >> 1] = pack2(e0, e1);
-                    }
-                    const uint4 u = {w4[0], w4[1], w4[2], w4[3]};
-                    pb[hblk][sblk] = __builtin_bit_cast(bf16x8, u);
-                }
-            psum += __shfl_xor(psum, 32, 64);
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // rescale only when some query of the wave raised its max
-            if (raise) {
-#pragma unroll
-                for (int t = 0; t < OT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-            }
-            // O^T += V^T P^T over the BKV keys in 2 NB MFMA k-steps; step (hblk, sblk)
-            // uses accumulator elements 8 sblk .. 8 sblk + 7 of block hblk, i.e.
-            // keys 32 hblk + 16 sblk + 8 (t/4) + 4 lh + t%4: the A operand (V^T rows
-            // dh = 32 t + lr) takes the same keys in the same order, from two
-            // transposing reads of four keys each (keys +0..3 and +8..11)
-            constexpr int STEPS = 8 / (2 * OT);  // (hblk, sblk) steps per eight reads
-#pragma unroll
-            for (int s0 = 0; s0 < 2 * NB; s0 += STEPS) {
-                uint32_t a[8];
-                uint2 v[8];
-#pragma unroll
-                for (int u = 0; u < STEPS; ++u)
-#pragma unroll
-                    for (int t = 0; t < OT; ++t)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            a[(u * OT + t) * 2 + h] = lds_addr(sv + (16 * (s0 + u) + 8 * h + vrow) * ROWB + vcol[t][h]);
-                ds_read_tr8(v, a);
-#pragma unroll
-                for (int u = 0; u < STEPS; ++u) {
-                    const int hblk = (s0 + u) >> 1, sblk = (s0 + u) & 1;
-#pragma unroll
-                    for (int t = 0; t < OT; ++t) {
-                        const uint2 lo = v[(u * OT + t) * 2], hi = v[(u * OT + t) * 2 + 1];
-                        const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
-                        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
-                        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hblk][sblk], o[t], 0, 0, 0);
-                    }
-                }
-            }
-        }
+    for (; it + NSLOT - 1 < ntiles; it += NSLOT) {
+        step(it, IntC<0>{}, IntC<0>{});
+        step(it + 1, IntC<PREK ? 1 : 0>{}, IntC<1>{});
+        step(it + 2, IntC<0>{}, IntC<2>{});
+        if constexpr (NSLOT == 4) step(it + 3, IntC<PREK ? 1 : 0>{}, IntC<3>{});
     }
+    if (it < ntiles) step(it, IntC<0>{}, IntC<0>{});
+    if (it + 1 < ntiles) step(it + 1, IntC<PREK ? 1 : 0>{}, IntC<1>{});
+    if constexpr (NSLOT == 4)
+        if (it + 2 < ntiles) step(it + 2, IntC<0>{}, IntC<2>{});
     ZO_WAIT_VM(0);  // no load may land in LDS after the block ends
     if (myq >= S) return;
     const float inv = 1.0f / l_run;
