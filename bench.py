@@ -194,6 +194,18 @@ def build_decoder(torch, zo, inputs, name, dirs="gauss"):
     return model, batch, (tok,), info
 
 
+def valu_fields(fam, gaussians, seconds):
+    """The Gaussian passes are VALU-bound.  The perturbation loop's count of
+    c_z instructions per Gaussian prices it against the VALU peak; the update
+    loops share their loads, stores and addressing between N directions, so
+    for them the line gives the instructions per Gaussian the measured rate
+    would leave at the VALU peak."""
+    rate = gaussians / seconds
+    if fam == "perturb":
+        return {"frac_valu_peak_generation": round(rate * C_Z / VALU_PEAK_LANE_OPS, 4), "c_z": C_Z}
+    return {"valu_instr_per_gaussian_at_peak": round(VALU_PEAK_LANE_OPS / rate, 2)}
+
+
 def measure_passes(torch, zo):
     """Perturb and update passes over an OPT-1.3B-sized parameter count, with
     Gaussian and with 8-bit packed directions; the update also at N = 32."""
@@ -232,6 +244,8 @@ def measure_passes(torch, zo):
                 gbs = 2.0 * n * esz / t / 1e9
                 out[f"{fam}_{name}{suffix}"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                 "ms": round(t * 1e3, 4), "elements": n, "probes": 1}
+                if dirs == zo.ZO_DIRS_GAUSS:
+                    out[f"{fam}_{name}{suffix}"].update(valu_fields(fam, n, t))
             # many probes: the update regenerates N directions per element
             zo.timing_reset()
             zo.timing_enable(True)
@@ -243,6 +257,8 @@ def measure_passes(torch, zo):
             t = ms / k * 1e-3
             out[f"update_{name}{suffix}_N32"] = {"directions_per_s": round(32 * n / t, 1), "ms": round(t * 1e3, 3),
                                                  "elements": n, "probes": 32}
+            if dirs == zo.ZO_DIRS_GAUSS:
+                out[f"update_{name}{suffix}_N32"].update(valu_fields("update", 32 * n, t))
             zo.timing_reset()
         del w
         torch.cuda.empty_cache()
@@ -626,6 +642,9 @@ def main():
             gbs = per_launch / (kernels[fam]["avg_us"] * 1e-6) / 1e9
             step_passes[fam] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                 "avg_us": kernels[fam]["avg_us"], "bytes": int(per_launch),
+                                **(valu_fields(fam, info["params"] * (1 if fam == "perturb" else N),
+                                               kernels[fam]["avg_us"] * 1e-6)
+                                   if args.dirs == "gauss" and info["mode"] != "copies" else {}),
                                 **({"probes": N} if fam == "update" else {}),
                                 **({"note": "arena resident in the last-level cache (not an HBM figure)"}
                                    if arena_bytes < 256e6 else {})}
