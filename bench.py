@@ -188,6 +188,9 @@ def build_decoder(torch, zo, inputs, name, dirs="gauss"):
         "probes": N, "eps": 1e-3, "lr": lr, "mode": mode, "batch": B, "params": int(total),
         "flops_per_eval": gemm_flops + attn_flops + head_flops, "gemm_flops_per_eval": gemm_flops,
         "head_flops_per_eval": head_flops, "attn_flops_per_eval": attn_flops,
+        # per layer GEMM (timing sub-families gemm_bf16.<name>), all layers
+        "gemm_parts_flops_per_eval": {"qkv": L * 2.0 * M * D * 3 * D, "o": L * 2.0 * M * D * D,
+                                      "up": L * 2.0 * M * D * F, "down": L * 2.0 * M * F * D},
         "dtype": "bf16", "kernel": "gemm_bf16", "peak_tflops": BF16_PEAK_TFLOPS,
         "decoder_shape": {"layers": L, "d": D, "heads": H, "ffn": F, "vocab": V, "act": act, "batch": B, "seq": S},
     }
@@ -243,6 +246,7 @@ def measure_passes(torch, zo):
                 t = ms / k * 1e-3
                 gbs = 2.0 * n * esz / t / 1e9
                 out[f"{fam}_{name}{suffix}"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                                "frac_copy": round(gbs / out[f"copy_{name}"]["GB/s"], 4),
                                                 "ms": round(t * 1e3, 4), "elements": n, "probes": 1}
                 if dirs == zo.ZO_DIRS_GAUSS:
                     out[f"{fam}_{name}{suffix}"].update(valu_fields(fam, n, t))
@@ -660,6 +664,16 @@ def main():
     if "attention" in kernels:
         t = kernels["attention"]["ms_per_step"] * 1e-3
         kernels["attention"]["TFLOP/s"] = round(evals_per_step * info["attn_flops_per_eval"] / t / 1e12, 1)
+    if "gemm_bf16" in kernels and "gemm_parts_flops_per_eval" in info:
+        # each layer GEMM on its own: algorithmic flops over its launches' time
+        parts = {}
+        for part, fl in info["gemm_parts_flops_per_eval"].items():
+            ms, n = zo.timing_query(f"gemm_bf16.{part}")
+            if n:
+                tflops = evals_per_step * fl * instr_steps / (ms * 1e-3) / 1e12
+                parts[part] = {"avg_us": round(ms / n * 1e3, 2), "launches_per_step": n / instr_steps,
+                               "TFLOP/s": round(tflops, 1), "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+        kernels["gemm_bf16"]["parts"] = parts
     zo.timing_reset()
     timed = all_losses[args.warmup:args.warmup + args.steps]
     line = {

@@ -385,12 +385,15 @@ zo_status zo_debug_layernorm(const void* h_dev, const void* g_dev, const void* b
  * grouped by family: "perturb", "update", "gemm_f32" (fp32 GEMMs that carry
  * directions), "gemm_f32_base" (fp32 work on the stored weights alone: input
  * splitting, the stored product, clean evaluations), "reduce", "gemm_bf16",
- * "attention", "layernorm", "embed", "lm_head", "debug".  zo_timing_query
- * returns the summed elapsed milliseconds and the launch count of one family
- * since the last reset; it synchronises the recorded events, so call it after
- * the stream work is complete.  zo_timing_select restricts the bracketing to
- * one family (NULL: every family), so that timing one kernel adds no events
- * around the others.  Not thread-safe across concurrent callers.
+ * "attention", "layernorm", "embed", "lm_head", "debug".  The decoder's layer
+ * GEMMs are the sub-families "gemm_bf16.qkv", "gemm_bf16.o", "gemm_bf16.up" and
+ * "gemm_bf16.down" of "gemm_bf16": a family name covers its sub-families
+ * ("<family>.<name>") in both calls below.  zo_timing_query returns the summed
+ * elapsed milliseconds and the launch count of one family since the last
+ * reset; it synchronises the recorded events, so call it after the stream
+ * work is complete.  zo_timing_select restricts the bracketing to one family
+ * (NULL: every family), so that timing one kernel adds no events around the
+ * others.  Not thread-safe across concurrent callers.
  */
 zo_status zo_timing_enable(int32_t on);
 zo_status zo_timing_select(const char* family);

@@ -123,7 +123,11 @@ def attention_error_bound(qkv, H):
 
 @pytest.mark.parametrize("B,S,H,dh", [(2, 64, 2, 64), (1, 200, 3, 64), (2, 512, 2, 64), (1, 300, 2, 128),
                                       (1, 128, 1, 128), (1, 1100, 2, 64), (1, 2048, 1, 64), (4, 1024, 32, 64),
-                                      (1, 2048, 2, 128)])
+                                      (1, 2048, 2, 128),
+                                      # sequences shorter than one key tile, a query block or the
+                                      # four-tile trip of the d_h 128 loop (its tail of 1-3 tiles)
+                                      (1, 1, 1, 128), (2, 1, 2, 64), (3, 5, 2, 128), (2, 33, 1, 64),
+                                      (1, 97, 2, 128), (1, 129, 1, 128), (1, 191, 1, 64)])
 def test_attention(B, S, H, dh):
     rng = np.random.default_rng(S + dh)
     d = H * dh

@@ -79,3 +79,33 @@ def test_inplace_step_with_graphs_equals_eager(n):
         assert np.array_equal(g, res[0][1])
         assert torch.equal(w, res[0][2])
     assert not torch.equal(res[0][2], w0)
+
+
+def test_timing_subfamilies_cover_the_layer_gemms():
+    """The layer GEMMs are timed as gemm_bf16.{qkv,o,up,down}; the family name
+    covers them (query and selection), one launch of each per layer."""
+    layers = 2
+    model, b, tok, arena, obatch = decoder_setup(layers=layers)
+    zo.timing_reset()
+    zo.timing_enable(True)
+    try:
+        out = torch.zeros(1, dtype=torch.float64, device=DEV)
+        model.forward_loss(b, out)
+        torch.cuda.synchronize()
+        total = zo.timing_query("gemm_bf16")
+        parts = {p: zo.timing_query(f"gemm_bf16.{p}") for p in ("qkv", "o", "up", "down")}
+        assert all(n == layers for _, n in parts.values()), parts
+        assert total[1] == 4 * layers
+        assert abs(total[0] - sum(ms for ms, _ in parts.values())) <= 1e-6 * max(1.0, total[0])
+        assert zo.timing_query("gemm_bf")[1] == 0  # a prefix that is not a family name covers nothing
+        # selecting the family brackets its sub-families and nothing else
+        zo.timing_reset()
+        zo.timing_select("gemm_bf16")
+        model.forward_loss(b, out)
+        torch.cuda.synchronize()
+        assert zo.timing_query("gemm_bf16")[1] == 4 * layers
+        assert zo.timing_query("attention")[1] == 0
+    finally:
+        zo.timing_select(None)
+        zo.timing_enable(False)
+        zo.timing_reset()

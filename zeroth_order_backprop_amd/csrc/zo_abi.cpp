@@ -66,9 +66,17 @@ hipEvent_t take_event()
 
 bool timing_active() { return g_timing; }
 
+// A launch of family `have` belongs to the queried or selected family `want`
+// when the two are equal or `have` is a sub-family "want.<name>".
+static bool family_match(const std::string& have, const std::string& want)
+{
+    return have == want || (have.size() > want.size() && have.compare(0, want.size(), want) == 0 &&
+                            have[want.size()] == '.');
+}
+
 KernelTimer::KernelTimer(const char* family, hipStream_t s) : slot_(-1), s_(s)
 {
-    if (!g_timing || (!g_timing_family.empty() && g_timing_family != family)) return;
+    if (!g_timing || (!g_timing_family.empty() && !family_match(family, g_timing_family))) return;
     TimedLaunch t{family, take_event(), take_event()};
     if (!t.start || !t.stop) return;
     (void)hipEventRecord(t.start, s);
@@ -344,8 +352,9 @@ zo_status zo_timing_query(const char* family, double* total_ms, int64_t* launche
     if (!family || !total_ms || !launches) return fail(ZO_ERR_INVALID, "null argument");
     double sum = 0.0;
     int64_t n = 0;
+    const std::string want = family;
     for (auto& t : g_timed) {
-        if (t.family != family) continue;
+        if (!family_match(t.family, want)) continue;
         if (hipEventSynchronize(t.stop) != hipSuccess) return fail(ZO_ERR_HIP, "event synchronise failed");
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) return fail(ZO_ERR_HIP, "event elapsed failed");

@@ -1705,7 +1705,7 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
         GemmParams gq = {};
         gq.A = w.x; gq.W = P + off(t0 + 2); gq.w_dir = off(t0 + 2); gq.C = w.qkv; gq.M = M; gq.N = 3 * D; gq.K = D;
         gq.grp_rows = grp_rows; gq.grp_stride = gstride;
-        if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16")) return st;
+        if (zo_status st = gemm_any<EPI_STORE>(gq, p, s, "gemm_bf16.qkv")) return st;
         {
             KernelTimer t("attention", s);
             launch_attention(w.qkv, groups * B, S, D, H, dh, w.att, s);
@@ -1714,7 +1714,7 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
         GemmParams go = {};
         go.A = w.att; go.W = P + off(t0 + 3); go.w_dir = off(t0 + 3); go.C = w.h; go.M = M; go.N = D; go.K = D;
         go.grp_rows = grp_rows; go.grp_stride = gstride;
-        if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16")) return st;
+        if (zo_status st = gemm_any<EPI_RESID>(go, p, s, "gemm_bf16.o")) return st;
         {
             KernelTimer t("layernorm", s);
             launch_layernorm(w.h, M, D, P + off(t0 + 4), off(t0 + 4), P + off(t0 + 5), off(t0 + 5), p, w.x, s, gr);
@@ -1723,13 +1723,13 @@ zo_status decoder_eval_launches(const ModelView& m, const zo_batch& b, const Per
         GemmParams gu = {};
         gu.A = w.x; gu.W = P + off(t0 + 6); gu.w_dir = off(t0 + 6); gu.C = w.u; gu.M = M; gu.N = F; gu.K = D;
         gu.grp_rows = grp_rows; gu.grp_stride = gstride;
-        zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16")
-                                            : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16");
+        zo_status su = d.act == ZO_ACT_GELU ? gemm_any<EPI_GELU>(gu, p, s, "gemm_bf16.up")
+                                            : gemm_any<EPI_RELU>(gu, p, s, "gemm_bf16.up");
         if (su) return su;
         GemmParams gd = {};
         gd.A = w.u; gd.W = P + off(t0 + 7); gd.w_dir = off(t0 + 7); gd.C = w.h; gd.M = M; gd.N = D; gd.K = F;
         gd.grp_rows = grp_rows; gd.grp_stride = gstride;
-        if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16")) return st;
+        if (zo_status st = gemm_any<EPI_RESID>(gd, p, s, "gemm_bf16.down")) return st;
     }
     const int tf = 2 + 8 * L;
     {
