@@ -480,7 +480,7 @@ def main():
         attention_only(torch, zo, [int(x) for x in args.attention.split(",")], args.steps, args.warmup)
         return
     if args.dirs != "gauss" and args.workload not in DECODERS:
-        print("bench.py: 8-bit directions apply in place; use a decoder workload (the fp32 ones run fused)",
+        print("bench.py: 8-bit directions apply in place or in copies; use a decoder workload (the fp32 ones run fused)",
               file=sys.stderr)
         sys.exit(2)
     if args.workload in DECODERS:
@@ -488,8 +488,8 @@ def main():
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     if args.mode:
-        if args.mode != "inplace" and args.dirs != "gauss":
-            print("bench.py: fused and copies steps apply Gaussian directions only", file=sys.stderr)
+        if args.mode == "fused" and args.dirs != "gauss":
+            print("bench.py: fused steps apply Gaussian directions only", file=sys.stderr)
             sys.exit(2)
         if args.mode == "copies" and args.workload not in DECODERS:
             print("bench.py: copies steps are for the decoder workloads", file=sys.stderr)

@@ -73,9 +73,9 @@ typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1, ZO_MODE_COPIES = 2 } zo_m
  *    used as a code k into T[k] = Phi^-1((k + 1/2) / 256) / r, r^2 the mean of
  *    the 256 squared quantiles, rounded once to fp32: a 256-level quantised
  *    Gaussian with mean 0 and variance 1.  Perturb, update, replay and in-place
- *    steps support it for every model; evaluations that apply directions
- *    inside the GEMMs (zo_forward_loss with perturbations, fused steps) return
- *    ZO_ERR_UNSUPPORTED for it.
+ *    steps support it for every model, copies steps for decoders; evaluations
+ *    that apply directions inside the GEMMs (zo_forward_loss with
+ *    perturbations, fused steps) return ZO_ERR_UNSUPPORTED for it.
  */
 typedef enum { ZO_DIRS_GAUSS = 0, ZO_DIRS_Q8 = 1 } zo_dirs;
 
@@ -225,7 +225,7 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
  * One SPSA step.  mode INPLACE: for i < N: perturb(+eps), L+, perturb(-2 eps),
  * L-, perturb(+eps).  mode FUSED: every evaluation sees D(W +- eps z_i) of the
  * unmodified W (one launch covers all 2N evaluations where the model allows).
- * mode COPIES (decoder, Gaussian directions): the same evaluation weights as
+ * mode COPIES (decoder, Gaussian or 8-bit directions): the same evaluation weights as
  * FUSED, D(W +- eps z_i), written out: one pass over W fills 2P copies of the
  * arena for P probes, then one forward evaluates all 2P copies side by side
  * (the rows of every copy in the same launches); P is chosen so a forward

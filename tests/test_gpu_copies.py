@@ -93,15 +93,9 @@ def test_copies_refusals():
     with pytest.raises(zo.ZoError) as e:
         model.step(batch, 0, 1, 1e-3, 1e-3, zo.ZO_MODE_COPIES, losses, g)
     assert e.value.status == zo.ZO_ERR_UNSUPPORTED
-    # 8-bit directions
-    m8, b8, keep8, _, _ = decoder_setup(batch=2, seq=128, max_seq=128)
-    d8 = zo.make_desc(zo.ZO_MODEL_DECODER, batch=2, seq=128, layers=2, d_model=128, heads=2, ffn=256, vocab=500,
-                      max_seq=128, act=zo.ZO_ACT_GELU, dirs=zo.ZO_DIRS_Q8)
-    q8 = zo.Model(d8, m8.arena.clone())
-    with pytest.raises(zo.ZoError) as e:
-        q8.step(b8, 0, 1, 1e-3, 1e-3, zo.ZO_MODE_COPIES, losses, g)
-    assert e.value.status == zo.ZO_ERR_UNSUPPORTED
+    # (8-bit directions are supported: test_gpu_dirs8.test_copies_step_q8_vs_oracle)
     # the step that cannot allocate
+    m8, b8, keep8, _, _ = decoder_setup(batch=2, seq=128, max_seq=128)
     before = m8.arena.clone()
     with pytest.raises(zo.ZoError) as e:
         zo.step_noalloc(m8.desc, m8.arena, b8, 0, 1, 1e-3, 1e-3, zo.ZO_MODE_COPIES, losses, g)

@@ -233,3 +233,37 @@ def test_passes_larger_than_last_level_cache(dtype):
         assert np.array_equal(got, want), (j0, cnt)
     del w
     torch.cuda.empty_cache()
+
+
+# rows per evaluation 2 x 128 = 256: the copies side by side in one forward;
+# 2 x 64 = 128: evaluated one by one
+@pytest.mark.parametrize("kw,n", [(dict(batch=2, seq=128, max_seq=128), 3), (dict(batch=2, seq=64), 2)])
+def test_copies_step_q8_vs_oracle(kw, n):
+    """Copies steps with 8-bit directions: every evaluation sees
+    D(W +- eps T[code]), the weights the oracle's fused step forms with the
+    same directions; losses at the bf16 loss bar, the updated weights within
+    the bound the loss noise in g allows (plus two bf16 ulps of rounding)."""
+    model, b, tok, arena, obatch = decoder_setup(**kw)
+    desc = zo.ModelDesc.from_buffer_copy(model.desc)
+    desc.dirs = zo.ZO_DIRS_Q8
+    arena.desc = dict(arena.desc, dirs="q8")
+    m8 = zo.Model(desc, model.arena)
+    seed, lr = 6, 1e-3
+    losses = torch.zeros(2 * n, dtype=torch.float64, device=DEV)
+    g = torch.zeros(n, dtype=torch.float64, device=DEV)
+    m8.step(b, seed, n, 1e-3, lr, zo.ZO_MODE_COPIES, losses, g)
+    torch.cuda.synchronize()
+    ol, og = oracle.spsa_step(arena, obatch, seed=seed, n_probes=n, eps=1e-3, lr=lr, mode="fused")
+    np.testing.assert_allclose(losses.cpu().numpy(), ol, rtol=2e-3)
+    gg = g.cpu().numpy()
+    Z = np.stack([oracle.directions("q8", seed, i, 0, arena.data.size).astype(np.float64) for i in range(n)])
+    bound = (lr / n) * (np.abs(gg - og) @ np.abs(Z))
+    w = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    wo = arena.values()
+    assert (np.abs(w - wo) <= bound + 2 * _ulp_bf16(np.maximum(np.abs(w), np.abs(wo)))).all()
+    # the copies hold the 8-bit directions: the losses differ from a Gaussian step's
+    gl = torch.zeros(2 * n, dtype=torch.float64, device=DEV)
+    model2, b2, *_ = decoder_setup(**kw)
+    model2.step(b2, seed, n, 1e-3, lr, zo.ZO_MODE_COPIES, gl, torch.zeros(n, dtype=torch.float64, device=DEV))
+    torch.cuda.synchronize()
+    assert not np.array_equal(gl.cpu().numpy(), losses.cpu().numpy())

@@ -507,8 +507,8 @@ static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cf
     if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
     if (cfg->mode == ZO_MODE_FUSED && d.dirs != ZO_DIRS_GAUSS)
         return fail(ZO_ERR_UNSUPPORTED, "fused steps apply Gaussian directions only; use the in-place mode");
-    if (cfg->mode == ZO_MODE_COPIES && (d.kind != ZO_MODEL_DECODER || d.dirs != ZO_DIRS_GAUSS))
-        return fail(ZO_ERR_UNSUPPORTED, "copies steps are for decoders with Gaussian directions");
+    if (cfg->mode == ZO_MODE_COPIES && d.kind != ZO_MODEL_DECODER)
+        return fail(ZO_ERR_UNSUPPORTED, "copies steps are for decoders");
     return ZO_OK;
 }
 
@@ -602,7 +602,8 @@ static zo_status run_step(const ModelView& v, uint64_t n_params, const zo_batch&
         const bool side_by_side = (int64_t)b.batch * b.seq % 256 == 0;
         for (uint32_t k = 0; k < N; k += P) {
             const uint32_t np = std::min(P, N - k);
-            if (zo_status r = launch_perturb_copies(v.params, buf, cs, n_params, cfg.seed, k, np, sig, st)) return r;
+            if (zo_status r = launch_perturb_copies(v.params, buf, cs, n_params, cfg.seed, k, np, sig, st, d.dirs))
+                return r;
             if (side_by_side) {
                 if (zo_status r = decoder_forward_groups(v, b, buf, (int)(2 * np), cs, ws, losses_dev + 2 * k, st))
                     return r;

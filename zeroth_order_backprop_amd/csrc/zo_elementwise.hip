@@ -539,6 +539,48 @@ __global__ __launch_bounds__(kThreads) void perturb_q8(T* __restrict__ w, uint64
     perturb_q8_tail(w, n_full, n, j0, key, probe, sigma, tab);
 }
 
+// The copies mode's evaluation weights with 8-bit directions: as
+// perturb_copies_bf16, the direction values T[code] of one Philox block per
+// 16 elements (a thread's 8 elements are half a block, words w0, w0 + 1).
+__global__ __launch_bounds__(kThreads) void perturb_copies_q8(const uint16_t* __restrict__ w,
+                                                              uint16_t* __restrict__ out, uint64_t cstride,
+                                                              uint64_t n_full, uint64_t n, Key key, uint32_t p0,
+                                                              uint32_t np, float sigma)
+{
+    __shared__ float tab[256];
+    dirs8::load_table(tab);
+    __syncthreads();
+    const uint64_t stride = (uint64_t)gridDim.x * kElemsPerIter;
+    for (uint64_t base = (uint64_t)blockIdx.x * kElemsPerIter; base < n_full; base += stride) {
+        const uint64_t e = base + 8 * threadIdx.x;
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(w + e), f);
+        const int w0 = (int)(e >> 2) & 3;  // 0 or 2
+        for (uint32_t i = 0; i < np; ++i) {
+            const uint4 c = dirs8::block(key, p0 + i, e >> 4);
+            const uint32_t lo = w0 == 0 ? c.x : c.z, hi = w0 == 0 ? c.y : c.w;
+            float a[8], b[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float z = dirs8::code(tab, t < 4 ? lo : hi, t & 3);
+                a[t] = fmaf(sigma, z, f[t]);
+                b[t] = fmaf(-sigma, z, f[t]);
+            }
+            *reinterpret_cast<uint4*>(out + (uint64_t)(2 * i) * cstride + e) = pack8(a);
+            *reinterpret_cast<uint4*>(out + (uint64_t)(2 * i + 1) * cstride + e) = pack8(b);
+        }
+    }
+    if (blockIdx.x != gridDim.x - 1) return;
+    for (uint64_t e = n_full + threadIdx.x; e < n; e += kThreads) {
+        const float v = bf16_lo(w[e]);
+        for (uint32_t i = 0; i < np; ++i) {
+            const float z = dirs8::value1(tab, key, p0 + i, e);
+            store_elem(out + (uint64_t)(2 * i) * cstride, e, fmaf(sigma, z, v));
+            store_elem(out + (uint64_t)(2 * i + 1) * cstride, e, fmaf(-sigma, z, v));
+        }
+    }
+}
+
 // The update for few directions (HBM-bound) in the streaming pattern; more
 // directions make it VALU-bound, and update_q8 below generates each block once
 // per thread instead.
@@ -723,14 +765,18 @@ static zo_status launch_update_q8(T* w, uint64_t n, uint64_t j0, Key key, uint32
 }
 
 zo_status launch_perturb_copies(const void* w, void* out, uint64_t cstride, uint64_t n, uint64_t seed,
-                                uint32_t p0, uint32_t np, float sigma, hipStream_t s)
+                                uint32_t p0, uint32_t np, float sigma, hipStream_t s, int dirs)
 {
     if (n == 0 || np == 0) return ZO_OK;
     const Key key = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     const uint64_t n_full = n / kElemsPerIter * kElemsPerIter;
     KernelTimer timer("perturb", s);
-    perturb_copies_bf16<<<grid_for(n_full), kThreads, 0, s>>>((const uint16_t*)w, (uint16_t*)out, cstride, n_full,
-                                                              n, key, p0, np, sigma);
+    if (dirs == ZO_DIRS_Q8)
+        perturb_copies_q8<<<grid_for(n_full), kThreads, 0, s>>>((const uint16_t*)w, (uint16_t*)out, cstride, n_full,
+                                                                n, key, p0, np, sigma);
+    else
+        perturb_copies_bf16<<<grid_for(n_full), kThreads, 0, s>>>((const uint16_t*)w, (uint16_t*)out, cstride,
+                                                                  n_full, n, key, p0, np, sigma);
     return check_launch("perturb copies");
 }
 

@@ -47,9 +47,10 @@ zo_status launch_restore_update(void* w, int dtype, uint64_t n, uint64_t seed, u
                                 float lr, float sigma, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 zo_status launch_debug_rng(uint64_t seed, uint32_t probe, uint64_t j0, uint64_t n, uint32_t* words,
                            float* z, hipStream_t s);
-// Copies 2i / 2i+1 (cstride elements apart, from `out`) = D(w +- sigma z_{p0+i}), i < np; bf16.
+// Copies 2i / 2i+1 (cstride elements apart, from `out`) = D(w +- sigma z_{p0+i}), i < np; bf16,
+// Gaussian or 8-bit directions.
 zo_status launch_perturb_copies(const void* w, void* out, uint64_t cstride, uint64_t n, uint64_t seed,
-                                uint32_t p0, uint32_t np, float sigma, hipStream_t s);
+                                uint32_t p0, uint32_t np, float sigma, hipStream_t s, int dirs = ZO_DIRS_GAUSS);
 zo_status launch_debug_box_muller(const uint32_t* pairs, uint64_t n_pairs, float* z, hipStream_t s);
 // g_i = (L[2i] - L[2i+1]) / (2 (double)sigma), i < n
 zo_status launch_gscalar(const double* losses, uint32_t n, float sigma, double* g, hipStream_t s);
