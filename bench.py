@@ -488,9 +488,6 @@ def main():
     else:
         model, batch, keep, info = (build_mlp if args.workload == "mlp" else build_lsq)(torch, zo, inputs)
     if args.mode:
-        if args.mode == "fused" and args.dirs != "gauss":
-            print("bench.py: fused steps apply Gaussian directions only", file=sys.stderr)
-            sys.exit(2)
         if args.mode == "copies" and args.workload not in DECODERS:
             print("bench.py: copies steps are for the decoder workloads", file=sys.stderr)
             sys.exit(2)

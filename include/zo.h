@@ -73,9 +73,10 @@ typedef enum { ZO_MODE_INPLACE = 0, ZO_MODE_FUSED = 1, ZO_MODE_COPIES = 2 } zo_m
  *    used as a code k into T[k] = Phi^-1((k + 1/2) / 256) / r, r^2 the mean of
  *    the 256 squared quantiles, rounded once to fp32: a 256-level quantised
  *    Gaussian with mean 0 and variance 1.  Perturb, update, replay and in-place
- *    steps support it for every model, copies steps for decoders; evaluations
- *    that apply directions inside the GEMMs (zo_forward_loss with
- *    perturbations, fused steps) return ZO_ERR_UNSUPPORTED for it.
+ *    steps support it for every model; copies steps and the evaluations that
+ *    apply directions as the weights are read (zo_forward_loss with
+ *    perturbations, fused steps) support it for decoders and return
+ *    ZO_ERR_UNSUPPORTED for it on the fp32 models.
  */
 typedef enum { ZO_DIRS_GAUSS = 0, ZO_DIRS_Q8 = 1 } zo_dirs;
 

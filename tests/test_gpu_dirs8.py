@@ -267,3 +267,38 @@ def test_copies_step_q8_vs_oracle(kw, n):
     model2.step(b2, seed, n, 1e-3, lr, zo.ZO_MODE_COPIES, gl, torch.zeros(n, dtype=torch.float64, device=DEV))
     torch.cuda.synchronize()
     assert not np.array_equal(gl.cpu().numpy(), losses.cpu().numpy())
+
+
+@pytest.mark.parametrize("kw,n", [(dict(), 3), (dict(act="relu", seq=37, vocab=333), 2)])
+def test_fused_step_q8_decoder_vs_oracle(kw, n):
+    """Fused steps of a decoder with 8-bit directions: every evaluation
+    perturbs the weight tiles as they are loaded and the LayerNorm parameters
+    and embeddings as they are read, with T[code]; the oracle's fused step
+    with the same directions is the reference (losses at the bf16 bar, the
+    update within the bound the loss noise in g allows)."""
+    model, b, tok, arena, obatch = decoder_setup(**kw)
+    desc = zo.ModelDesc.from_buffer_copy(model.desc)
+    desc.dirs = zo.ZO_DIRS_Q8
+    arena.desc = dict(arena.desc, dirs="q8")
+    m8 = zo.Model(desc, model.arena)
+    seed, lr = 9, 1e-3
+    losses = torch.zeros(2 * n, dtype=torch.float64, device=DEV)
+    g = torch.zeros(n, dtype=torch.float64, device=DEV)
+    m8.step(b, seed, n, 1e-3, lr, zo.ZO_MODE_FUSED, losses, g)
+    torch.cuda.synchronize()
+    ol, og = oracle.spsa_step(arena, obatch, seed=seed, n_probes=n, eps=1e-3, lr=lr, mode="fused")
+    np.testing.assert_allclose(losses.cpu().numpy(), ol, rtol=2e-3)
+    gg = g.cpu().numpy()
+    Z = np.stack([oracle.directions("q8", seed, i, 0, arena.data.size).astype(np.float64) for i in range(n)])
+    bound = (lr / n) * (np.abs(gg - og) @ np.abs(Z))
+    w = oracle.bf16_bits_to_f64(m8.arena.cpu().numpy().view(np.uint16))
+    wo = arena.values()
+    assert (np.abs(w - wo) <= bound + 2 * _ulp_bf16(np.maximum(np.abs(w), np.abs(wo)))).all()
+    # the same evaluations through zo_forward_loss with a perturbation list,
+    # and the in-place step's L+ (the perturbed weights written out) agree
+    m8b, b2, *_ = decoder_setup(**kw)
+    m8b = zo.Model(desc, m8b.arena)
+    lf = torch.zeros(2, dtype=torch.float64, device=DEV)
+    m8b.forward_loss(b2, lf, perts=[(seed, 0, 1e-3), (seed, 0, -1e-3)])
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(lf.cpu().numpy(), losses.cpu().numpy()[:2], rtol=1e-12)

@@ -483,8 +483,8 @@ zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, 
     if (zo_status st = validate_batch(m->desc, b)) return st;
     if (n_perts < 0 || (n_perts > 0 && !perts)) return fail(ZO_ERR_INVALID, "bad perturbation list");
     if (n_perts > kMaxEvalsPerCall) return fail(ZO_ERR_INVALID, "at most %d perturbations per call", kMaxEvalsPerCall);
-    if (n_perts > 0 && m->desc.dirs != ZO_DIRS_GAUSS)
-        return fail(ZO_ERR_UNSUPPORTED, "perturbed evaluations apply Gaussian directions only; use zo_perturb");
+    if (n_perts > 0 && m->desc.dirs != ZO_DIRS_GAUSS && m->desc.kind != ZO_MODEL_DECODER)
+        return fail(ZO_ERR_UNSUPPORTED, "perturbed evaluations with 8-bit directions are for decoders; use zo_perturb");
     return model_forward(view_of(m), *b, n_perts ? perts : nullptr, n_perts, loss_dev, (hipStream_t)s);
 }
 
@@ -505,8 +505,8 @@ static zo_status validate_step_cfg(const zo_model_desc& d, const zo_step_cfg* cf
         return fail(ZO_ERR_INVALID, "bad mode");
     if (cfg->precond != 0 && cfg->precond != 1) return fail(ZO_ERR_INVALID, "precond must be 0 or 1");
     if (cfg->precond && !(cfg->curv_floor > 0.0f)) return fail(ZO_ERR_INVALID, "curv_floor must be positive");
-    if (cfg->mode == ZO_MODE_FUSED && d.dirs != ZO_DIRS_GAUSS)
-        return fail(ZO_ERR_UNSUPPORTED, "fused steps apply Gaussian directions only; use the in-place mode");
+    if (cfg->mode == ZO_MODE_FUSED && d.dirs != ZO_DIRS_GAUSS && d.kind != ZO_MODEL_DECODER)
+        return fail(ZO_ERR_UNSUPPORTED, "fused steps with 8-bit directions are for decoders; use the in-place mode");
     if (cfg->mode == ZO_MODE_COPIES && d.kind != ZO_MODEL_DECODER)
         return fail(ZO_ERR_UNSUPPORTED, "copies steps are for decoders");
     return ZO_OK;

@@ -27,6 +27,7 @@
 #include "zo_math.hpp"
 #include "zo_models.hpp"
 #include "zo_rng.hpp"
+#include "zo_dirs8.hpp"
 
 // The buffer-resource direct-to-LDS load (llvm.amdgcn.raw.buffer.load.lds).
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -56,7 +57,8 @@ struct Pert {
     Key key;
     uint32_t probe;
     float sigma;
-    int on;  // 0: stored weights as they are
+    int on;    // 0: stored weights as they are
+    int dirs;  // ZO_DIRS_GAUSS, or ZO_DIRS_Q8: values T[code] from the code object's table (L1-resident)
 };
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -73,15 +75,35 @@ __device__ __forceinline__ bf16_t f2bf(float x) { return (bf16_t)(pack2(x, 0.0f)
 
 __device__ __forceinline__ float round_bf(float x) { return bf2f(f2bf(x)); }
 
+// Word k of a Philox block.
+__device__ __forceinline__ uint32_t word_of(uint4 c, uint32_t k)
+{
+    return k == 0 ? c.x : k == 1 ? c.y : k == 2 ? c.z : c.w;
+}
+
 // 8 consecutive bf16 weights starting at arena index j (j % 8 == 0 not
 // required, j % 4 == 0 required), perturbed in place in the uint4.
 __device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p)
 {
-    const float4 za = gauss4(p.key, p.probe, j >> 2);
-    const float4 zb = gauss4(p.key, p.probe, (j >> 2) + 1);
     float f[8] = {bf2f(v.x & 0xFFFF), bf2f(v.x >> 16), bf2f(v.y & 0xFFFF), bf2f(v.y >> 16),
                   bf2f(v.z & 0xFFFF), bf2f(v.z >> 16), bf2f(v.w & 0xFFFF), bf2f(v.w >> 16)};
-    const float z[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+    float z[8];
+    if (p.dirs == ZO_DIRS_Q8) {
+        // words j/4 and j/4 + 1 of the stream: one Philox block (two when
+        // the pair straddles blocks)
+        const uint64_t k0 = j >> 2;
+        const uint4 c0 = dirs8::block(p.key, p.probe, k0 >> 2);
+        const uint32_t w0 = (uint32_t)(k0 & 3u);
+        const uint32_t lo = word_of(c0, w0);
+        const uint32_t hi = w0 < 3 ? word_of(c0, w0 + 1) : dirs8::block(p.key, p.probe, (k0 >> 2) + 1).x;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) z[t] = dirs8::code(dirs8::kTableDev.v, t < 4 ? lo : hi, t & 3);
+    } else {
+        const float4 za = gauss4(p.key, p.probe, j >> 2);
+        const float4 zb = gauss4(p.key, p.probe, (j >> 2) + 1);
+        z[0] = za.x; z[1] = za.y; z[2] = za.z; z[3] = za.w;
+        z[4] = zb.x; z[5] = zb.y; z[6] = zb.z; z[7] = zb.w;
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) f[t] = fmaf(p.sigma, z[t], f[t]);
     return uint4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
@@ -100,9 +122,14 @@ __device__ __forceinline__ float weight1(const bf16_t* w, uint64_t i, uint64_t d
     float v = bf2f(w[i]);
     if (p.on) {
         const uint64_t j = dir + i;
-        const float4 z = gauss4(p.key, p.probe, j >> 2);
-        const uint32_t s = (uint32_t)(j & 3u);
-        const float zz = s == 0 ? z.x : s == 1 ? z.y : s == 2 ? z.z : z.w;
+        float zz;
+        if (p.dirs == ZO_DIRS_Q8) {
+            zz = dirs8::value1(dirs8::kTableDev.v, p.key, p.probe, j);
+        } else {
+            const float4 z = gauss4(p.key, p.probe, j >> 2);
+            const uint32_t s = (uint32_t)(j & 3u);
+            zz = s == 0 ? z.x : s == 1 ? z.y : s == 2 ? z.z : z.w;
+        }
         v = round_bf(fmaf(p.sigma, zz, v));
     }
     return v;
@@ -1827,6 +1854,7 @@ zo_status decoder_forward(const ModelView& m, const zo_batch& b, const zo_pert* 
             p.probe = perts[e].probe;
             p.sigma = perts[e].sigma;
             p.on = 1;
+            p.dirs = d.dirs;
         }
         hipGraphExec_t ex = nullptr;
         if (!n && m.graphs && !timing_active())
