@@ -82,8 +82,9 @@ __device__ __forceinline__ uint32_t word_of(uint4 c, uint32_t k)
 }
 
 // 8 consecutive bf16 weights starting at arena index j (j % 8 == 0 not
-// required, j % 4 == 0 required), perturbed in place in the uint4.
-__device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p)
+// required, j % 4 == 0 required), perturbed in place in the uint4; `tab`:
+// the 8-bit table (an LDS copy where the caller has one).
+__device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p, const float* tab)
 {
     float f[8] = {bf2f(v.x & 0xFFFF), bf2f(v.x >> 16), bf2f(v.y & 0xFFFF), bf2f(v.y >> 16),
                   bf2f(v.z & 0xFFFF), bf2f(v.z >> 16), bf2f(v.w & 0xFFFF), bf2f(v.w >> 16)};
@@ -97,7 +98,7 @@ __device__ __forceinline__ uint4 perturb8(uint4 v, uint64_t j, const Pert& p)
         const uint32_t lo = word_of(c0, w0);
         const uint32_t hi = w0 < 3 ? word_of(c0, w0 + 1) : dirs8::block(p.key, p.probe, (k0 >> 2) + 1).x;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) z[t] = dirs8::code(dirs8::kTableDev.v, t < 4 ? lo : hi, t & 3);
+        for (int t = 0; t < 8; ++t) z[t] = dirs8::code(tab, t < 4 ? lo : hi, t & 3);
     } else {
         const float4 za = gauss4(p.key, p.probe, j >> 2);
         const float4 zb = gauss4(p.key, p.probe, (j >> 2) + 1);
@@ -538,6 +539,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
     constexpr int A_PER = A_CH / kThreads, B_PER = B_CH / kThreads;
     static_assert(A_CH % kThreads == 0 && B_CH % kThreads == 0, "tile / thread mismatch");
     extern __shared__ __align__(16) bf16_t lds[];
+    // 8-bit directions: the code table in LDS (a dependent lookup per weight)
+    __shared__ float q8tab[PERT ? 256 : 1];
+    if constexpr (PERT) {
+        if (p.dirs == ZO_DIRS_Q8) dirs8::load_table(q8tab);
+        __syncthreads();
+    }
     // stage st: A tile at lds + st * BM * LDK, B tile at lds + 2 BM LDK + st * BN * LDK
     auto As = [&](int st) { return lds + st * (BM * LDK); };
     auto Bs = [&](int st) { return lds + 2 * (BM * LDK) + st * (BN * LDK); };
@@ -590,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
             uint4 v = rb[t];
             if constexpr (PERT) {
                 const int gn = n0 + r, gk = k0 + kc;
-                if (gn < N && gk < K) v = perturb8(v, g.w_dir + (uint64_t)gn * K + gk, p);
+                if (gn < N && gk < K) v = perturb8(v, g.w_dir + (uint64_t)gn * K + gk, p, q8tab);
             }
             *reinterpret_cast<uint4*>(Bs(stage) + r * LDK + kc) = v;
         }
