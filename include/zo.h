@@ -209,7 +209,8 @@ zo_status zo_perturb(zo_model* m, uint64_t seed, uint32_t probe, float sigma, zo
  * Otherwise loss_dev[k] = loss at D(W + perts[k].sigma z_{perts[k].probe});
  * the weights in memory are not modified (the perturbation is applied inside
  * the kernels, tile by tile).  loss_dev: device, fp64, >= max(1, n_perts).
- * perts: host array.
+ * perts: host array.  With 8-bit directions only decoders take perturbations
+ * (ZO_ERR_UNSUPPORTED otherwise).
  */
 zo_status zo_forward_loss(zo_model* m, const zo_batch* b, const zo_pert* perts, int32_t n_perts,
                           double* loss_dev, zo_stream s);
@@ -225,7 +226,8 @@ zo_status zo_update(zo_model* m, uint64_t seed, uint32_t n_probes, const double*
 /*
  * One SPSA step.  mode INPLACE: for i < N: perturb(+eps), L+, perturb(-2 eps),
  * L-, perturb(+eps).  mode FUSED: every evaluation sees D(W +- eps z_i) of the
- * unmodified W (one launch covers all 2N evaluations where the model allows).
+ * unmodified W (one launch covers all 2N evaluations where the model allows;
+ * with 8-bit directions decoders only).
  * mode COPIES (decoder, Gaussian or 8-bit directions): the same evaluation weights as
  * FUSED, D(W +- eps z_i), written out: one pass over W fills 2P copies of the
  * arena for P probes, then one forward evaluates all 2P copies side by side
