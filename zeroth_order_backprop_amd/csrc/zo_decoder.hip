@@ -632,6 +632,112 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams g, Pert 
     gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, tn, lds);
 }
 
+// The perturbed-tile product with the block's weight panel resident in LDS:
+// a block owns 64 output columns, writes D(W + sigma z) of those 64 rows over
+// all of K into LDS once (rows padded by 8 bf16: the 16 rows of a fragment
+// read then start 4 banks apart), and walks the 128-row tiles mt = ms,
+// ms + msplit, ... of the activations, which stream through a two-stage
+// register-staged ring.  Each weight's direction is thus generated once per
+// block instead of once per 128-row tile; the products and their summation
+// order are those of gemm_bf16_kernel<128, 64, EPI, true>.  Needs K % 64 == 0
+// and 64 (K + 8) + 2 128 72 bf16 of LDS (K <= 960).
+constexpr int kPanelBN = 64, kPanelBM = 128, kPanelMaxK = 960;
+constexpr size_t panel_lds_bytes(int K) { return ((size_t)kPanelBN * (K + 8) + 2 * kPanelBM * 72) * sizeof(bf16_t); }
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_pert_panel_kernel(GemmParams g, Pert p, int msplit)
+{
+    constexpr int BM = kPanelBM, BN = kPanelBN, BK = 64, LDK = BK + 8;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int RB = WM / 32, CB = WN / 32;
+    constexpr int A_CH = BM * BK / 8, A_PER = A_CH / kThreads;
+    static_assert(A_CH % kThreads == 0 && EPI != EPI_LMHEAD, "tile / thread mismatch");
+    extern __shared__ __align__(16) bf16_t lds[];
+    __shared__ float q8tab[256];
+    if (p.dirs == ZO_DIRS_Q8) dirs8::load_table(q8tab);
+    __syncthreads();
+
+    const int M = g.M, N = g.N, K = g.K, LDW = K + 8;
+    bf16_t* wp = lds;  // [BN][LDW]
+    auto As = [&](int st) { return lds + BN * LDW + st * (BM * LDK); };
+    const int npanels = (N + BN - 1) / BN;
+    const int pn = blockIdx.x % npanels, ms = blockIdx.x / npanels;
+    const int n0 = pn * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lh = lane >> 5;
+
+    // the perturbed panel
+    const int cpr = K / 8;
+    for (int c = tid; c < BN * cpr; c += kThreads) {
+        const int r = c / cpr, kc = 8 * (c % cpr);
+        const int gn = n0 + r;
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (gn < N) {
+            v = *reinterpret_cast<const uint4*>(g.W + (size_t)gn * K + kc);
+            v = perturb8(v, g.w_dir + (uint64_t)gn * K + kc, p, q8tab);
+        }
+        *reinterpret_cast<uint4*>(wp + r * LDW + kc) = v;
+    }
+
+    uint4 ra[A_PER];
+    auto load = [&](int m0, int k0) {
+#pragma unroll
+        for (int t = 0; t < A_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            const int gm = m0 + r, gk = k0 + kc;
+            ra[t] = gm < M ? *reinterpret_cast<const uint4*>(g.A + (size_t)gm * K + gk) : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int stage) {
+#pragma unroll
+        for (int t = 0; t < A_PER; ++t) {
+            const int c = tid + t * kThreads;
+            const int r = c / (BK / 8), kc = 8 * (c % (BK / 8));
+            *reinterpret_cast<uint4*>(As(stage) + r * LDK + kc) = ra[t];
+        }
+    };
+    const int KT = K / BK, nmt = (M + BM - 1) / BM;
+    for (int mt = ms; mt < nmt; mt += msplit) {
+        const int m0 = mt * BM;
+        f32x16 acc[RB][CB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
+        load(m0, 0);
+        store(0);
+        __syncthreads();  // (the first trip: the panel is complete too)
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT) load(m0, (kt + 1) * BK);
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 16) {
+                bf16x8 af[RB], bfr[CB];
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8*>(As(cur) + (wm * WM + i * 32 + lr) * LDK + ks + 8 * lh);
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(wp + (wn * WN + j * 32 + lr) * LDW + kt * BK + ks +
+                                                              8 * lh);
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < CB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < KT) store(cur ^ 1);
+            __syncthreads();
+        }
+        // the epilogue stages the tile in the ring's LDS (every wave is done
+        // with it), then the next tile refills the ring
+        gemm_epilogue<BM, BN, EPI>(g, acc, m0, n0, pn, As(0));
+        __syncthreads();
+    }
+}
+
 // The same product with the stage tiles written to LDS directly by the loads
 // (global_load_lds, 16 B per lane) for the stored-weight path: no register
 // staging.  Rows past M or N load a clamped (valid) row and are never stored.
@@ -1603,9 +1709,35 @@ int gemm_tile_n(int M, int N, int K, bool pert, int epi)
     return big * 100 >= rounds * cus * 85 ? 256 : 128;
 }
 
+// The panel-resident perturbed-tile product (see gemm_pert_panel_kernel):
+// about one block per CU, each panel's 128-row tiles split among msplit blocks.
+template <int EPI>
+zo_status launch_gemm_panel(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
+{
+    const int npanels = cdiv(gp.N, kPanelBN), nmt = cdiv(gp.M, kPanelBM);
+    const int msplit = std::max(1, std::min(nmt, (device_cus() + npanels / 2) / npanels));
+    const size_t lds = panel_lds_bytes(gp.K);
+    auto kern = gemm_pert_panel_kernel<EPI>;
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)panel_lds_bytes(kPanelMaxK)) != hipSuccess)
+            return fail(ZO_ERR_HIP, "cannot reserve %zu bytes of LDS", panel_lds_bytes(kPanelMaxK));
+        attr = true;
+    }
+    KernelTimer timer(fam, s);
+    kern<<<npanels * msplit, kThreads, lds, s>>>(gp, p, msplit);
+    return check_launch("bf16 GEMM (weight panel)");
+}
+
 template <int EPI, bool PERT>
 zo_status gemm(const GemmParams& gp, const Pert& p, hipStream_t s, const char* fam)
 {
+    if constexpr (PERT && EPI != EPI_LMHEAD) {
+        // short K: the perturbed weight panel stays in LDS, each direction
+        // generated once per block
+        if (gp.K <= kPanelMaxK && gp.K % 64 == 0) return launch_gemm_panel<EPI>(gp, p, s, fam);
+    }
     if constexpr (may_use_big_tiles<EPI, PERT>()) {
         if (gemm_tile_n(gp.M, gp.N, gp.K, PERT, EPI) == 256) return launch_gemm<256, 256, EPI, PERT>(gp, p, s, fam);
     }
