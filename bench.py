@@ -465,8 +465,9 @@ def cpu_baseline(info):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the step shards by probes, see the design notes", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "across GPUs the step would shard by probes (each GPU evaluates its own probes, "
+              "one all-gather of the scalars g_i, every replica runs the same update)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -48,7 +48,7 @@ typedef void* zo_stream; /* a hipStream_t */
 typedef enum {
     ZO_OK = 0,
     ZO_ERR_INVALID = -1,     /* bad argument: null, size, alignment, overlap */
-    ZO_ERR_UNSUPPORTED = -2, /* dtype or shape this build does not handle */
+    ZO_ERR_UNSUPPORTED = -2, /* dtype or shape the library does not handle */
     ZO_ERR_HIP = -3,         /* a HIP launch or runtime call failed */
     ZO_ERR_NONFINITE = -4,   /* a loss was NaN or infinite */
     ZO_ERR_WORKSPACE = -5    /* workspace smaller than zo_workspace_bytes() */
