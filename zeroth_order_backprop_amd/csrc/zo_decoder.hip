@@ -1490,19 +1490,14 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         __builtin_amdgcn_sched_barrier(0);
         // S^T [BKV keys][32 queries] as NB 32x32 blocks, each one chain of
         // MFMAs over the head dim (a dependent MFMA issues back to back).
-        // While a wave issues its MFMA runs it takes issue priority over the
-        // SIMD's other waves, whose softmax VALU work fills the MFMA pipe's
-        // shadow (1-4% on the decoder shapes).
         f32x16 st[NB];
 #pragma unroll
         for (int hblk = 0; hblk < NB; ++hblk) st[hblk] = f32x16{};
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int hblk = 0; hblk < NB; ++hblk)
                 st[hblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc][hblk][ks], qf[ks], st[hblk], 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
         if constexpr (PREK) {
             // the next tile's K fragments, under these MFMAs and the softmax
             // (a tile past the last one is read into registers no result uses)
@@ -1569,7 +1564,10 @@ void attention_kernel(const bf16_t* __restrict__ qkv, int S, int d, int H, bf16_
         // dh = 32 t + lr) takes the same keys in the same order, from two
         // transposing reads of four keys each (keys +0..3 and +8..11).  Groups
         // of eight reads cover STEPS such steps, at the slot's and the
-        // group's offset.
+        // group's offset.  While a wave issues these MFMA runs it takes issue
+        // priority over the SIMD's other waves, whose score and softmax work
+        // fills the MFMA pipe's shadow (about 2% at d_h 128; raising it for
+        // the S^T runs too gains nothing).
         auto pv = [&](auto S0) {
             constexpr int s0 = decltype(S0)::value;
             uint2 v[8];
