@@ -49,7 +49,7 @@ TRAFFIC = {
     "gemm_bf16:opt30b:r8": (2 * (3.9972 + 1.3165 + 5.4844 + 4.9467) + (0.6562 + 0.2188 + 0.8757 + 0.2188))
                            * 2**30 / 4,
 }
-KERNEL_REV = {"mlp": "sgemm:mlp:r5", "lsq": None, "opt30b": "gemm_bf16:opt30b:r8"}
+KERNEL_REV = {"mlp": "sgemm:mlp:r5", "lsq": None, "opt30b": "gemm_bf16:opt30b:r9"}
 
 
 def parse():

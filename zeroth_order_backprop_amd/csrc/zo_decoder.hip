@@ -1110,7 +1110,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             for (int hb = 0; hb < NST / HB; ++hb) {
                 i32x4_t hv[HB];
 #pragma unroll
-                for (int k = 0; k < HB; ++k) hv[k] = zo_raw_buffer_load_x4(rc, offs(hb * HB + k), 0, 0);
+                // non-temporal (aux bit 1, nt): each h line is read once, so it
+                // should not displace the operand panels the XCD's other tiles
+                // are still reading from L2
+                for (int k = 0; k < HB; ++k) hv[k] = zo_raw_buffer_load_x4(rc, offs(hb * HB + k), 0, 2);
 #pragma unroll
                 for (int k = 0; k < HB; ++k) {
                     const int p = (hb * HB + k) * NT + tid;
@@ -1135,7 +1138,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmParams& g)
             issue(1);
         }
 #pragma unroll
-        for (int k = 0; k < NST; ++k) zo_raw_buffer_store_x4(__builtin_bit_cast(i32x4_t, vals[k]), rc, offs(k), 0, 0);
+        // non-temporal stores, for the same reason as the residual's reads
+        // (O / down GEMMs 3-4% faster, OPT-1.3B-shaped QKV 2.5%)
+        for (int k = 0; k < NST; ++k) zo_raw_buffer_store_x4(__builtin_bit_cast(i32x4_t, vals[k]), rc, offs(k), 0, 2);
         if (!more) break;
         stores_pending = true;
     }
